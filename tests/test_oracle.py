@@ -1,0 +1,394 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each test ties the oracle to something other than itself: the figures the
+pages print, closed forms, special cases that reduce to a library routine
+(PyTorch's fp64 scaled_dot_product_attention on the CPU), invariants the
+pages state (MHA and MQA as the two ends of GQA; GQA equals MHA with every
+K/V head repeated G times), and brute force on tiny shapes.  A last group
+plants plausible mistakes in a copy of the reference and checks that the pins
+catch every one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import np_oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def sdpa_ref(q, k, v, q_start, kv_len, causal, scale):
+    """PyTorch fp64 SDPA (CPU, math path) row by row with an explicit mask.
+
+    q [B,Sq,H,d], k/v [B,K,Sk,d]; enable_gqa broadcasts KV head h // G."""
+    B, Sq, H, d = q.shape
+    K, Sk = k.shape[1], k.shape[2]
+    out = np.full(q.shape, np.nan)
+    for b in range(B):
+        qt = torch.from_numpy(q[b]).permute(1, 0, 2).unsqueeze(0)        # [1,H,Sq,d]
+        kt = torch.from_numpy(k[b]).unsqueeze(0)                          # [1,K,Sk,d]
+        vt = torch.from_numpy(v[b]).unsqueeze(0)
+        pos = q_start[b] + np.arange(Sq)[:, None]
+        j = np.arange(Sk)[None, :]
+        allowed = j < min(kv_len[b], Sk)
+        if causal:
+            allowed = allowed & (j <= pos)
+        mask = torch.from_numpy(np.broadcast_to(allowed, (Sq, Sk)).copy())
+        o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale,
+                                           enable_gqa=(H != K))
+        o = o[0].permute(1, 0, 2).numpy()
+        rows_ok = np.broadcast_to(allowed, (Sq, Sk)).any(axis=1)
+        out[b][rows_ok] = o[rows_ok]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# cache size: the figures printed on the pages
+# ---------------------------------------------------------------------------
+
+def _golden_cases():
+    cases = []
+    with open(os.path.join(HERE, "golden", "kv_cache_size.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line.startswith("case "):
+                continue
+            parts = line.split()
+            kv = dict(p.split("=", 1) for p in parts[2:])
+            cases.append((parts[1], kv))
+    return cases
+
+
+@pytest.mark.parametrize("name,kv", _golden_cases(), ids=[c[0] for c in _golden_cases()])
+def test_cache_size_matches_printed_figures(oracle_lib, name, kv):
+    elems = oracle.kv_cache_elems(int(kv["layers"]), int(kv["kv_heads"]), int(kv["head_dim"]),
+                                  int(kv["seq_len"]), int(kv["batch"]))
+    value = elems * int(kv["bytes_per_elem"]) / float(kv["unit"])
+    printed = float(kv["printed"])
+    assert abs(value - printed) < 10.0 ** (-int(kv["digits"])), (name, value, printed)
+
+
+def test_cache_size_exact_counts(oracle_lib):
+    # concept page 关键参数 #2: 2*64*2048*128*80 and 2*8*2048*128*80
+    assert oracle.kv_cache_elems(80, 64, 128, 2048, 1) == 2_684_354_560
+    assert oracle.kv_cache_elems(80, 8, 128, 2048, 1) == 335_544_320
+    # the MHA/GQA ratio is H/K
+    assert oracle.kv_cache_elems(80, 64, 128, 2048, 1) // oracle.kv_cache_elems(80, 8, 128, 2048, 1) == 8
+
+
+@pytest.mark.parametrize("K,d,expect", [(8, 128, 2048), (64, 128, 16384), (1, 128, 256), (2, 64, 256)])
+def test_cache_elems_per_token(oracle_lib, K, d, expect):
+    assert oracle.cache_elems_per_token(K, d) == expect
+    assert oracle.kv_cache_elems(1, K, d, 1, 1) == expect
+
+
+# ---------------------------------------------------------------------------
+# attention: library routine, brute force, special cases
+# ---------------------------------------------------------------------------
+
+SHAPES = [
+    # B, Sq, H, K, d, Sk
+    (1, 1, 1, 1, 4, 1),
+    (2, 3, 4, 2, 8, 9),
+    (1, 5, 8, 1, 16, 12),   # MQA
+    (2, 4, 6, 6, 8, 7),     # MHA
+    (3, 2, 8, 4, 64, 33),
+    (1, 8, 8, 2, 64, 8),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_c_oracle_vs_torch_sdpa_and_numpy(oracle_lib, shape, causal):
+    B, Sq, H, K, d, Sk = shape
+    rng = np.random.default_rng(hash(shape) % 2**32 + causal)
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    kv_len = rng.integers(1, Sk + 1, size=B).astype(np.int32)
+    # causal rows: the last query sits on the last valid key
+    q_start = np.maximum(kv_len - Sq, 0).astype(np.int32) if causal else np.zeros(B, np.int32)
+    scale = 1.0 / math.sqrt(d)
+    got = oracle.attention(q, k, v, q_start, kv_len, causal, scale)
+    ref_t = sdpa_ref(q, k, v, q_start, kv_len, causal, scale)
+    ref_n = np_oracle.gqa_reference(q, k, v, q_start, kv_len, causal, scale)
+    ok = ~np.isnan(ref_t)
+    assert np.array_equal(ok, ~np.isnan(got))
+    np.testing.assert_allclose(got[ok], ref_t[ok], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[ok], ref_n[ok], rtol=0, atol=1e-12)
+
+
+def test_rows_entry_matches_full(oracle_lib):
+    rng = np.random.default_rng(7)
+    B, Sq, H, K, d, Sk = 2, 6, 8, 2, 16, 10
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    qs, kl = np.array([2, 4], np.int32), np.array([8, 10], np.int32)
+    full = oracle.attention(q, k, v, qs, kl, True, 0.3)
+    rows = np.array([[b, i, h] for b in range(B) for i in range(Sq) for h in range(H)], np.int32)
+    sel = oracle.attention_rows(q, k, v, qs, kl, True, 0.3, rows)
+    assert np.array_equal(sel, full.reshape(-1, d))
+
+
+def test_mha_end_is_per_head_attention(oracle_lib):
+    """K = H (G = 1): each head uses its own K/V head (plain multi-head attention)."""
+    rng = np.random.default_rng(11)
+    B, H, d, Sk = 2, 4, 8, 6
+    q, k, v = rand(rng, B, 1, H, d), rand(rng, B, H, Sk, d), rand(rng, B, H, Sk, d)
+    got = oracle.attention(q, k, v, [Sk - 1] * B, [Sk] * B, False, 0.5)
+    for b in range(B):
+        for h in range(H):
+            s = 0.5 * (k[b, h] @ q[b, 0, h])
+            w = np.exp(s - s.max())
+            np.testing.assert_allclose(got[b, 0, h], (w @ v[b, h]) / w.sum(), atol=1e-13)
+
+
+def test_mqa_end_shares_one_head(oracle_lib):
+    """K = 1: every query head reads the single K/V head."""
+    rng = np.random.default_rng(12)
+    B, H, d, Sk = 1, 8, 8, 9
+    q, k, v = rand(rng, B, 1, H, d), rand(rng, B, 1, Sk, d), rand(rng, B, 1, Sk, d)
+    got = oracle.attention(q, k, v, [Sk - 1], [Sk], False, 0.4)
+    for h in range(H):
+        one = oracle.attention(q[:, :, h:h + 1], k, v, [Sk - 1], [Sk], False, 0.4)
+        assert np.array_equal(got[0, 0, h], one[0, 0, 0])
+
+
+@pytest.mark.parametrize("H,K", [(8, 2), (8, 4), (6, 3), (64, 8), (4, 1)])
+def test_gqa_equals_mha_with_repeated_kv(oracle_lib, H, K):
+    """Head h reads KV head h // G: GQA equals MHA on K/V repeated G times per head."""
+    rng = np.random.default_rng(H * 100 + K)
+    B, Sq, d, Sk = 2, 3, 8, 7
+    G = H // K
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    qs, kl = np.array([4, 2], np.int32), np.array([7, 5], np.int32)
+    gqa = oracle.attention(q, k, v, qs, kl, True, 0.35)
+    mha = oracle.attention(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1), qs, kl, True, 0.35)
+    np.testing.assert_allclose(gqa, mha, rtol=0, atol=1e-13)
+    if K > 1 and G > 1:
+        # the strided map h % K is a different answer: the pin discriminates
+        wrong = oracle.attention(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1)), qs, kl, True, 0.35)
+        assert np.max(np.abs(wrong - gqa)) > 1e-3
+
+
+def test_group_id_recovered_from_constant_v(oracle_lib):
+    """V of KV head g is the constant g: every output of head h is h // G."""
+    rng = np.random.default_rng(3)
+    B, H, K, d, Sk = 2, 16, 4, 8, 11
+    q, k = rand(rng, B, 2, H, d), rand(rng, B, K, Sk, d)
+    v = np.broadcast_to(np.arange(K, dtype=np.float64)[None, :, None, None], (B, K, Sk, d)).copy()
+    out = oracle.attention(q, k, v, [5, 9], [Sk, Sk], True, 0.3)
+    for h in range(H):
+        np.testing.assert_allclose(out[:, :, h], h // (H // K), rtol=1e-14, atol=1e-14)
+
+
+def test_single_visible_key_returns_v0_exactly(oracle_lib):
+    rng = np.random.default_rng(4)
+    B, Sq, H, K, d, Sk = 1, 4, 4, 2, 8, 4
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    out = oracle.attention(q, k, v, [0], [Sk], True, 0.125)
+    for h in range(H):
+        assert np.array_equal(out[0, 0, h], v[0, h // 2, 0])   # p = e^0 = 1, l = 1
+    dec = oracle.attention(q[:, :1], k, v, [0], [1], False, 0.125)
+    assert np.array_equal(dec[0, 0, 3], v[0, 1, 0])
+
+
+def test_zero_query_gives_mean_of_visible_values(oracle_lib):
+    rng = np.random.default_rng(5)
+    B, H, K, d, Sk = 1, 4, 2, 8, 10
+    q = np.zeros((B, 3, H, d))
+    k, v = rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    out = oracle.attention(q, k, v, [2], [Sk], True, 0.7)
+    for i in range(3):
+        for h in range(H):
+            np.testing.assert_allclose(out[0, i, h], v[0, h // 2, :2 + i + 1].mean(axis=0), atol=1e-14)
+
+
+@pytest.mark.parametrize("d", [4, 64, 128])
+def test_two_key_closed_form(oracle_lib, d):
+    """Two keys: out = v1 * sigmoid(scale (s1 - s2)) + v2 * (1 - sigmoid(...)), scale = 1/sqrt(d)."""
+    q = np.zeros((1, 1, 1, d)); q[0, 0, 0, 0] = 1.0
+    k = np.zeros((1, 1, 2, d)); k[0, 0, 0, 0] = 3.0; k[0, 0, 1, 0] = -1.0
+    v = np.zeros((1, 1, 2, d)); v[0, 0, 0, :] = 1.0; v[0, 0, 1, :] = -2.0
+    scale = 1.0 / math.sqrt(d)
+    w1 = 1.0 / (1.0 + math.exp(-scale * 4.0))
+    out = oracle.attention(q, k, v, [1], [2], False, scale)
+    np.testing.assert_allclose(out[0, 0, 0], w1 * 1.0 + (1 - w1) * -2.0, atol=1e-15)
+
+
+def test_causal_row_equals_decode_over_prefix(oracle_lib):
+    """Causal row i (position p + i) sees exactly keys 0..p+i: a decode with ctx = p+i+1."""
+    rng = np.random.default_rng(6)
+    B, Sq, H, K, d, Sk = 1, 5, 4, 2, 8, 9
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    p = 3
+    pre = oracle.attention(q, k, v, [p], [Sk], True, 0.3)
+    for i in range(Sq):
+        dec = oracle.attention(q[:, i:i + 1], k, v, [p + i], [p + i + 1], False, 0.3)
+        assert np.array_equal(pre[0, i], dec[0, 0])
+
+
+def test_no_visible_key_is_reported(oracle_lib):
+    q, k, v = np.ones((1, 1, 2, 4)), np.ones((1, 1, 3, 4)), np.ones((1, 1, 3, 4))
+    out = oracle.attention(q, k, v, [0], [0], False, 1.0)
+    assert np.isnan(out).all()
+
+
+# ---------------------------------------------------------------------------
+# the rewrites the GPU path relies on are exact (inference-optimisation page
+# §9.2.1 online softmax; §10.2 split and merge)
+# ---------------------------------------------------------------------------
+
+def test_online_softmax_equals_three_pass(oracle_lib):
+    rng = np.random.default_rng(8)
+    B, Sq, H, K, d, Sk = 2, 3, 4, 2, 8, 20
+    q, k, v = 3 * rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    qs, kl = np.array([10, 17], np.int32), np.array([20, 19], np.int32)
+    ref = oracle.attention(q, k, v, qs, kl, True, 0.4)
+    onl = np_oracle.online_softmax_attention(q, k, v, qs, kl, True, 0.4)
+    np.testing.assert_allclose(onl, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("segment", [1, 3, 16, 64, 1000])
+def test_split_merge_equals_three_pass(oracle_lib, segment):
+    rng = np.random.default_rng(9)
+    B, H, K, d, Sk = 3, 8, 2, 16, 70
+    q, k, v = 4 * rand(rng, B, 1, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    kl = np.array([70, 1, 33], np.int32)
+    ref = oracle.attention(q, k, v, kl - 1, kl, False, 0.25)
+    got = np_oracle.split_merge_attention(q, k, v, kl, 0.25, segment)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# cache append and paged gather: pure data movement
+# ---------------------------------------------------------------------------
+
+def _coded_rows(B, s, K, d, base=0):
+    """Unique float32 codes: row (b, t, g) column c holds b*1e6 + t*1e3 + g*10 + c/1e3."""
+    b, t, g, c = np.meshgrid(np.arange(B), np.arange(s), np.arange(K), np.arange(d), indexing="ij")
+    return (base + b * 1e6 + t * 1e3 + g * 10 + c / 1e3).astype(np.float32)
+
+
+def test_append_contiguous_places_every_row(oracle_lib):
+    B, s, K, d, S = 3, 5, 2, 4, 12
+    cache = np.full((B, K, S, d), -7.0, np.float32)
+    new = _coded_rows(B, s, K, d)
+    start = np.array([0, 4, 9], np.int32)          # the last one runs past S_max by 2 rows
+    dropped = oracle.kv_append(cache, new, start)
+    assert dropped == 2 * K
+    for b in range(B):
+        for g in range(K):
+            for p in range(S):
+                t = p - start[b]
+                if 0 <= t < s:
+                    assert np.array_equal(cache[b, g, p], new[b, t, g])
+                else:
+                    assert (cache[b, g, p] == -7.0).all()
+
+
+def test_append_paged_and_gather_roundtrip(oracle_lib):
+    rng = np.random.default_rng(10)
+    B, K, d, bs = 3, 2, 4, 16
+    ctx = np.array([1, 16, 37], np.int32)
+    nb = (ctx + bs - 1) // bs
+    n_pool = int(nb.sum()) + 2
+    perm = rng.permutation(n_pool).astype(np.int32)
+    table = np.full((B, int(nb.max())), -1, np.int32)
+    off = 0
+    for b in range(B):
+        table[b, :nb[b]] = perm[off:off + nb[b]]
+        off += nb[b]
+    pool = np.full((n_pool, K, bs, d), -7.0, np.float32)
+    s = int(ctx.max())
+    new = _coded_rows(B, s, K, d)
+    # append each sequence's first ctx[b] tokens one at a time (decode-style)
+    for t in range(s):
+        for b in range(B):
+            if t < ctx[b]:
+                oracle.kv_append_paged(pool, new[b:b + 1, t:t + 1], [t], table[b:b + 1])
+    got = oracle.gather_paged(pool.astype(np.float64), table, ctx, s)
+    for b in range(B):
+        for g in range(K):
+            assert np.array_equal(got[b, g, :ctx[b]], new[b, :ctx[b], g].astype(np.float64))
+            assert np.isnan(got[b, g, ctx[b]:]).all()
+    # slots outside every sequence keep the sentinel
+    assert (pool == -7.0).sum() == (n_pool * bs - int(ctx.sum())) * K * d
+
+
+def test_paged_attention_equals_contiguous(oracle_lib):
+    rng = np.random.default_rng(13)
+    B, H, K, d, bs = 2, 4, 2, 8, 16
+    ctx = np.array([5, 40], np.int32)
+    nb = (ctx + bs - 1) // bs
+    n_pool = int(nb.sum())
+    perm = rng.permutation(n_pool).astype(np.int32)
+    table = np.full((B, int(nb.max())), -1, np.int32)
+    table[0, :nb[0]] = perm[:nb[0]]
+    table[1, :nb[1]] = perm[nb[0]:]
+    pool_k, pool_v = rand(rng, n_pool, K, bs, d), rand(rng, n_pool, K, bs, d)
+    q = rand(rng, B, 1, H, d)
+    rows, out = oracle.paged_attention_rows(q, pool_k, pool_v, table, ctx, 0.3)
+    S = int(ctx.max())
+    kc = oracle.gather_paged(pool_k, table, ctx, S)
+    vc = oracle.gather_paged(pool_v, table, ctx, S)
+    ref = sdpa_ref(q, np.nan_to_num(kc), np.nan_to_num(vc), ctx - 1, ctx, False, 0.3)
+    np.testing.assert_allclose(out.reshape(B, H, d), ref[:, 0], atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: a broken copy of the reference must fail some pin
+# ---------------------------------------------------------------------------
+
+def _mutant(kind):
+    def ref(q, k, v, q_start, kv_len, causal, scale):
+        B, Sq, H, d = q.shape
+        K = k.shape[1]
+        G = H // K
+        out = np.full(q.shape, np.nan)
+        for b in range(B):
+            for i in range(Sq):
+                qpos = q_start[b] + i
+                n = min(kv_len[b], k.shape[2])
+                if causal:
+                    n = min(n, qpos + (0 if kind == "causal_excludes_self" else 1))
+                if n <= 0:
+                    continue
+                for h in range(H):
+                    g = h % K if kind == "strided_group_map" else h // G
+                    sc = 1.0 if kind == "dropped_scale" else scale
+                    kk = k[b, g, :n]
+                    if kind == "transposed_k":
+                        kk = k[b, g, :n][:, ::-1]
+                    s = sc * (kk @ q[b, i, h])
+                    p = np.exp(s - s.max())
+                    l = p.sum() if kind != "unnormalised" else 1.0
+                    out[b, i, h] = (p @ v[b, g, :n]) / l
+        return out
+    return ref
+
+
+def _pins_pass(ref):
+    rng = np.random.default_rng(21)
+    B, Sq, H, K, d, Sk = 2, 3, 8, 2, 8, 9
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    qs, kl = np.array([3, 6], np.int32), np.array([9, 9], np.int32)
+    got = ref(q, k, v, qs, kl, True, 0.35)
+    want = sdpa_ref(q, k, v, qs, kl, True, 0.35)
+    ok = ~np.isnan(want)
+    if not np.array_equal(ok, ~np.isnan(got)):
+        return False
+    return bool(np.max(np.abs(got[ok] - want[ok])) < 1e-12)
+
+
+@pytest.mark.parametrize("kind", ["strided_group_map", "dropped_scale", "causal_excludes_self",
+                                  "transposed_k", "unnormalised"])
+def test_planted_mistakes_are_caught(kind):
+    assert _pins_pass(_mutant("none"))
+    assert not _pins_pass(_mutant(kind))
