@@ -1,0 +1,359 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped-query attention hot path on one MI355X.
+
+A step is one decode step of the Llama-3-8B-shaped workload (B=32, H=32,
+K=8, d=128, bf16, contexts drawn from U[1024, 4096]): gqa_kv_append of every
+sequence's newest token, then gqa_decode over the whole cache.  `value` is
+the step's algorithmic bytes (the K/V rows every query must read once, plus
+Q, O and the appended rows) divided by the step time, in GB/s.
+
+The same JSON line also carries
+  * roofline: the decode kernel alone (HBM bound), timed with HIP events on
+    the stream it runs on, against MI355X's 8 TB/s;
+  * prefill: the causal prefill workload (B=4, s=4096, H=32, K=8, d=128,
+    bf16, append included) in TFLOP/s against the 2.5 PFLOP/s dense bf16
+    matrix-core peak;
+  * decode_workloads: the other decode shapes (Llama-2-70B contiguous and its
+    MHA / MQA variants, paged long-context) in GB/s;
+  * cpu_baseline: the CPU oracle on the host cores, on the same step.
+
+The K/V caches are rotated over several copies so that the ~256 MB
+Infinity Cache cannot serve them between steps; inputs are resident in HBM
+before the timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "GQA decode HBM GB/s (% of peak) + causal prefill TFLOP/s (% MFMA peak), bf16"
+MALL_BYTES = 256 * 2**20
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
+    ap.add_argument("--only", default=None, help="profile one kernel: decode|prefill|decode70b|paged")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# device helpers
+# ---------------------------------------------------------------------------
+
+def up(x: np.ndarray):
+    import torch
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def decode_bytes(wl, ctx):
+    """Algorithmic bytes of one decode: each valid K and V row once, Q read, O written."""
+    es = 2 if wl.dtype == "bf16" else 4
+    kv = 2 * wl.K * wl.d * es * int(np.sum(ctx, dtype=np.int64))
+    qo = 2 * wl.B * wl.H * wl.d * es
+    return kv + qo
+
+
+def append_bytes(wl, s_new):
+    es = 2 if wl.dtype == "bf16" else 4
+    return 2 * 2 * wl.B * s_new * wl.K * wl.d * es   # K and V rows, read once and written once
+
+
+def causal_flops(wl):
+    """4 * B * H * d * sum_{i<s} (i+1): QK^T and PV over the visible (lower-triangle) keys."""
+    return 4 * wl.B * wl.H * wl.d * (wl.s * (wl.s + 1) // 2)
+
+
+class DecodeBench:
+    """Device-resident copies of one decode workload, rotated per call."""
+
+    def __init__(self, wl, copies=None):
+        import torch
+        from grouped_query_attention_gqa_amd import binding
+        from grouped_query_attention_gqa_amd import workloads as W
+        self.wl = wl
+        t0 = time.time()
+        inp = W.make_decode(wl, fill="zero")
+        self.inp = inp
+        self.ctx = inp.ctx
+        self.max_ctx = int(inp.ctx.max())
+        self.alg_bytes = decode_bytes(wl, inp.ctx)
+        valid = self.alg_bytes
+        n = copies if copies is not None else max(1, min(4, math.ceil(3 * MALL_BYTES / max(valid, 1))))
+        self.q = up(inp.q)
+        self.ctx_d = up(inp.ctx)
+        kn, vn = inp.new_token_rows()
+        self.k_new, self.v_new = up(kn), up(vn)
+        self.start = up((inp.ctx - 1).astype(np.int32))
+        self.caches = []
+        k0, v0 = up(inp.k), up(inp.v)
+        bt = None if inp.block_table is None else up(inp.block_table)
+        for i in range(n):
+            k = k0 if i == 0 else k0.clone()
+            v = v0 if i == 0 else v0.clone()
+            self.caches.append(binding.KVCache(k, v, bt))
+        self.out = torch.empty_like(self.q)
+        nbytes = binding.gqa_decode_workspace_bytes(wl.B, wl.H, wl.K, wl.d, self.max_ctx)
+        self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        log(f"{wl.name}: {n} cache copies, sum ctx {int(inp.ctx.sum())}, "
+            f"{self.alg_bytes / 1e6:.1f} MB per decode, setup {time.time() - t0:.1f}s")
+
+    def append(self, i):
+        from grouped_query_attention_gqa_amd import binding
+        binding.gqa_kv_append(self.caches[i % len(self.caches)], self.k_new, self.v_new, self.start)
+
+    def decode(self, i):
+        from grouped_query_attention_gqa_amd import binding
+        binding.gqa_decode(self.q, self.caches[i % len(self.caches)], self.ctx_d, self.max_ctx, out=self.out,
+                           scale=self.wl.scale, workspace=self.ws)
+
+
+def time_decode_only(db: DecodeBench, iters: int, warmup: int):
+    """Average decode kernel time (ms) from HIP events on the launch stream."""
+    import torch
+    for i in range(warmup):
+        db.decode(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        db.decode(i)
+        b.record()
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in evs]
+    return float(np.mean(ts)), float(np.median(ts))
+
+
+# ---------------------------------------------------------------------------
+# traffic figures from the committed rocprofv3 counter summaries
+# ---------------------------------------------------------------------------
+
+def kernel_source_hash(name: str) -> str:
+    path = os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def committed_traffic(key: str, source: str, launches_units: float):
+    """HBM bytes per launch from profiles/traffic.json, if taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = table.get(key)
+    if not ent or ent.get("source_sha") != kernel_source_hash(source):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host cores
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(db: DecodeBench, budget_s: float = 12.0):
+    import oracle
+    wl, inp = db.wl, db.inp
+    oracle._load()
+    q64 = oracle.to_f64(inp.q, wl.dtype)
+    seqs = list(range(wl.B))
+    prepared = []
+    for b in seqs:
+        n = int(inp.ctx[b])
+        prepared.append((b, n, oracle.to_f64(inp.k[b:b + 1, :, :n], wl.dtype),
+                         oracle.to_f64(inp.v[b:b + 1, :, :n], wl.dtype)))
+    rows = np.array([[0, 0, h] for h in range(wl.H)], np.int32)
+    kn, vn = inp.new_token_rows()
+    done_bytes, t_total, passes = 0, 0.0, 0
+    while t_total < budget_s and passes < 50:
+        t0 = time.perf_counter()
+        for b, n, kb, vb in prepared:
+            # the oracle's append of the newest token, then its attention rows
+            kc = inp.k[b:b + 1].copy()
+            oracle.kv_append(kc, kn[b:b + 1], [n - 1])
+            oracle.attention_rows(q64[b:b + 1], kb, vb, [n - 1], [n], False, wl.scale, rows)
+        t_total += time.perf_counter() - t0
+        done_bytes += db.alg_bytes + append_bytes(wl, 1)
+        passes += 1
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {
+        "value": round(done_bytes / t_total / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"the whole {wl.name} decode step (all {wl.B} sequences x {wl.H} heads, append + "
+                  f"attention, fp64), {passes} pass(es) in {t_total:.1f} s on {threads} threads",
+    }
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU; --gpus above 1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.stderr.write("bench.py: only --gpus 1 is supported (single-GPU build)\n")
+        sys.exit(2)
+    import torch
+    from grouped_query_attention_gqa_amd import binding
+    from grouped_query_attention_gqa_amd import workloads as W
+    if not torch.cuda.is_available():
+        sys.stderr.write("bench.py needs a GPU\n")
+        sys.exit(1)
+    binding.load_library()
+    torch.cuda.set_device(0)
+
+    if args.only:
+        return profile_only(args)
+
+    # ---- headline: Llama-3-8B-shaped decode step ---------------------------
+    wl = W.WORKLOADS["llama3_8b_decode"]
+    db = DecodeBench(wl)
+    step_bytes = db.alg_bytes + append_bytes(wl, 1)
+    for i in range(args.warmup):
+        db.append(i)
+        db.decode(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        db.append(i)
+        ev[i][0].record()
+        db.decode(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = db.alg_bytes / (dec_ms * 1e-3) / 1e9
+    traffic = committed_traffic("decode/llama3_8b_decode", "row_attention.hip", 1)
+    log(f"decode step {ms_step * 1e3:.1f} us ({value:.0f} GB/s); decode kernel {dec_ms * 1e3:.1f} us "
+        f"({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of peak)")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "K": wl.K, "d": wl.d,
+                   "ctx": "U[1024,4096] per sequence", "sum_ctx": int(db.ctx.sum()),
+                   "step": "gqa_kv_append (newest token) + gqa_decode", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "row_attention_kernel<128,4,bf16> (gqa_decode)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": db.alg_bytes, "avg_launch_us": round(dec_ms * 1e3, 2)},
+    }
+    del db
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        # ---- causal prefill ------------------------------------------------
+        result["prefill"] = bench_prefill(W.WORKLOADS["causal_prefill_4k"], max(3, args.steps // 5), 2)
+        torch.cuda.empty_cache()
+        # ---- the other decode shapes --------------------------------------
+        extra = {}
+        for name in ("llama2_70b_decode", "paged_long_decode", "llama2_70b_decode_mha", "llama2_70b_decode_mqa"):
+            w = W.WORKLOADS[name]
+            d2 = DecodeBench(w)
+            mean_ms, med_ms = time_decode_only(d2, max(5, args.steps // 2), 3)
+            gbs = d2.alg_bytes / (mean_ms * 1e-3) / 1e9
+            extra[name] = {"us": round(mean_ms * 1e3, 2), "GB/s": round(gbs, 1),
+                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": d2.alg_bytes}
+            log(f"{name}: {mean_ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+            del d2
+            torch.cuda.empty_cache()
+        result["decode_workloads"] = extra
+
+    if not args.no_cpu_baseline:
+        wl = W.WORKLOADS["llama3_8b_decode"]
+        db = DecodeBench(wl, copies=1)
+        result["cpu_baseline"] = cpu_baseline(db)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+
+    print(json.dumps(result), flush=True)
+
+
+def bench_prefill(wl, iters, warmup):
+    import torch
+    from grouped_query_attention_gqa_amd import binding
+    from grouped_query_attention_gqa_amd import workloads as W
+    inp = W.make_prefill(wl)
+    q, kn, vn, start = up(inp.q), up(inp.k_new), up(inp.v_new), up(inp.start_pos)
+    kc = torch.zeros(wl.B, wl.K, wl.s, wl.d, dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    cache = binding.KVCache(kc, vc)
+    out = torch.empty_like(q)
+    for _ in range(warmup):
+        binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    flops = causal_flops(wl)
+    tf = flops / (ms * 1e-3) / 1e12
+    log(f"prefill {wl.name}: {ms * 1e3:.1f} us (append + attention), {tf:.1f} TFLOP/s "
+        f"({100 * tf / BF16_MFMA_PEAK_TFLOPS:.1f}% of bf16 MFMA peak)")
+    return {"workload": wl.name, "B": wl.B, "s": wl.s, "H": wl.H, "K": wl.K, "d": wl.d,
+            "us_per_call": round(ms * 1e3, 2), "flops": flops, "TFLOP/s": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "note": "time covers the append and the attention kernel"}}
+
+
+def profile_only(args):
+    """A short run of one kernel, for rocprofv3 (no JSON contract)."""
+    import torch
+    from grouped_query_attention_gqa_amd import workloads as W
+    if args.only == "prefill":
+        r = bench_prefill(W.WORKLOADS["causal_prefill_4k"], args.steps, args.warmup)
+        print(json.dumps(r), flush=True)
+        return
+    name = {"decode": "llama3_8b_decode", "decode70b": "llama2_70b_decode", "paged": "paged_long_decode",
+            "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa"}[args.only]
+    db = DecodeBench(W.WORKLOADS[name])
+    mean_ms, med_ms = time_decode_only(db, args.steps, args.warmup)
+    print(json.dumps({"workload": name, "decode_us": round(mean_ms * 1e3, 2),
+                      "GB/s": round(db.alg_bytes / (mean_ms * 1e-3) / 1e9, 1), "bytes": db.alg_bytes}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,258 @@
+"""ctypes binding of libgqa.so (include/gqa.h) for PyTorch tensors.
+
+Argument marshalling only: shapes, dtypes and devices are checked, pointers
+and the current HIP stream are handed to the C ABI, and a non-zero status is
+raised as GqaError.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback path.  If the library is missing the first call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+_lock = threading.Lock()
+
+GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_LAUNCH, GQA_ERR_DEVICE_ARG = range(6)
+GQA_F32, GQA_BF16 = 0, 1
+
+EXPORTED_SYMBOLS = (
+    "gqa_abi_version", "gqa_status_string", "gqa_cache_elems_per_token",
+    "gqa_kv_append", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_prefill",
+)
+
+
+class GqaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({_status_text(status)})")
+
+
+class _CacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("S_max", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+def library_path() -> str:
+    return os.environ.get("GQA_LIBRARY", os.path.join(_HERE, "libgqa.so"))
+
+
+def load_library():
+    """Load libgqa.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
+                               f"`python -m grouped_query_attention_gqa_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        cp = ctypes.POINTER(_CacheStruct)
+        lib.gqa_abi_version.restype = i32
+        lib.gqa_abi_version.argtypes = []
+        lib.gqa_status_string.restype = ctypes.c_char_p
+        lib.gqa_status_string.argtypes = [i32]
+        lib.gqa_cache_elems_per_token.restype = i32
+        lib.gqa_cache_elems_per_token.argtypes = [i32, i32]
+        lib.gqa_decode_workspace_bytes.restype = sz
+        lib.gqa_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+        lib.gqa_kv_append.restype = i32
+        lib.gqa_kv_append.argtypes = [cp, vp, vp, vp, i32, i32, vp]
+        lib.gqa_decode.restype = i32
+        lib.gqa_decode.argtypes = [vp, cp, vp, i32, i32, i32, ctypes.c_float, vp, vp, sz, vp]
+        lib.gqa_prefill.restype = i32
+        lib.gqa_prefill.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp]
+        if lib.gqa_abi_version() != 1:
+            raise RuntimeError("libgqa.so ABI version mismatch")
+        _lib = lib
+        return lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return load_library().gqa_status_string(status).decode()
+    except Exception:
+        return "?"
+
+
+def _check(status: int, what: str):
+    if status != GQA_OK:
+        raise GqaError(status, what)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return GQA_BF16
+    if t == torch.float32:
+        return GQA_F32
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions")
+
+
+class KVCache:
+    """One layer's cache: contiguous [B,K,S_max,d] or paged [N,K,bs,d] + block table."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, block_table: Optional[torch.Tensor] = None):
+        _need(k, "cache k", dim=4)
+        _need(v, "cache v", dtype=k.dtype, dim=4)
+        if k.shape != v.shape:
+            raise ValueError("cache k and v must have the same shape")
+        self.k, self.v, self.block_table = k, v, block_table
+        self.dtype = k.dtype
+        self.num_kv_heads = int(k.shape[1])
+        self.head_dim = int(k.shape[3])
+        self.paged = block_table is not None
+        s = _CacheStruct()
+        s.k, s.v = k.data_ptr(), v.data_ptr()
+        s.num_kv_heads, s.head_dim, s.dtype = self.num_kv_heads, self.head_dim, _dtype_code(k.dtype)
+        if self.paged:
+            _need(block_table, "block_table", dtype=torch.int32, dim=2)
+            s.block_table = block_table.data_ptr()
+            s.max_blocks_per_seq = int(block_table.shape[1])
+            s.block_size = int(k.shape[2])
+            s.num_blocks = int(k.shape[0])
+            self.capacity = s.max_blocks_per_seq * s.block_size
+        else:
+            s.block_table = None
+            s.S_max = int(k.shape[2])
+            self.capacity = s.S_max
+        self._struct = s
+
+    @property
+    def struct(self):
+        return ctypes.byref(self._struct)
+
+
+# ---------------------------------------------------------------------------
+# host-only helpers
+# ---------------------------------------------------------------------------
+
+def gqa_cache_elems_per_token(num_kv_heads: int, head_dim: int) -> int:
+    return int(load_library().gqa_cache_elems_per_token(num_kv_heads, head_dim))
+
+
+def gqa_decode_workspace_bytes(B: int, num_heads: int, num_kv_heads: int, head_dim: int, max_ctx: int) -> int:
+    return int(load_library().gqa_decode_workspace_bytes(B, num_heads, num_kv_heads, head_dim, max_ctx))
+
+
+# Default decode workspaces, one per (device, stream), zero-filled once; the
+# library leaves them zeroed after every completed call.
+_workspaces: dict = {}
+
+
+def _default_workspace(device: torch.device, stream_handle: int, nbytes: int) -> torch.Tensor:
+    key = (device.index, stream_handle)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------------------
+# the three calls
+# ---------------------------------------------------------------------------
+
+def gqa_kv_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, start_pos: torch.Tensor,
+                  stream=None) -> None:
+    """Write k_new/v_new [B,s_new,K,d] at positions start_pos[b] + t."""
+    _need(k_new, "k_new", dtype=cache.dtype, dim=4)
+    _need(v_new, "v_new", dtype=cache.dtype, dim=4)
+    _need(start_pos, "start_pos", dtype=torch.int32, dim=1)
+    B, s_new, K, d = k_new.shape
+    if v_new.shape != k_new.shape or K != cache.num_kv_heads or d != cache.head_dim or start_pos.shape[0] != B:
+        raise ValueError("append shapes disagree with the cache")
+    st = load_library().gqa_kv_append(cache.struct, _ptr(k_new), _ptr(v_new), _ptr(start_pos), B, s_new,
+                                      _stream(stream))
+    _check(st, "gqa_kv_append")
+
+
+def gqa_decode(q: torch.Tensor, cache: KVCache, ctx_lens: torch.Tensor, max_ctx: int,
+               out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step: q [B,1,H,d] against the first ctx_lens[b] cached tokens."""
+    _need(q, "q", dtype=cache.dtype, dim=4)
+    _need(ctx_lens, "ctx_lens", dtype=torch.int32, dim=1)
+    B, one, H, d = q.shape
+    if one != 1 or d != cache.head_dim or ctx_lens.shape[0] != B:
+        raise ValueError("decode shapes disagree with the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, dim=4)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    nbytes = int(lib.gqa_decode_workspace_bytes(B, H, cache.num_kv_heads, d, int(max_ctx)))
+    hs = _stream(stream)
+    if workspace is None and nbytes > 0:
+        workspace = _default_workspace(q.device, hs.value or 0, nbytes)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gqa_decode(_ptr(q), cache.struct, _ptr(ctx_lens), int(max_ctx), B, H, ctypes.c_float(scale),
+                        _ptr(out), _ptr(workspace), ws_bytes, hs)
+    _check(st, "gqa_decode")
+    return out
+
+
+def gqa_prefill(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: KVCache,
+                start_pos: torch.Tensor, causal: bool = True, out: Optional[torch.Tensor] = None,
+                scale: Optional[float] = None, stream=None) -> torch.Tensor:
+    """Append k_new/v_new [B,s,K,d] and attend q [B,s,H,d] (causal by default)."""
+    _need(q, "q", dtype=cache.dtype, dim=4)
+    _need(k_new, "k_new", dtype=cache.dtype, dim=4)
+    _need(v_new, "v_new", dtype=cache.dtype, dim=4)
+    _need(start_pos, "start_pos", dtype=torch.int32, dim=1)
+    B, s, H, d = q.shape
+    if k_new.shape != (B, s, cache.num_kv_heads, d) or v_new.shape != k_new.shape or start_pos.shape[0] != B:
+        raise ValueError("prefill shapes disagree")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, dim=4)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = load_library().gqa_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), cache.struct, _ptr(start_pos), B, s, H,
+                                    ctypes.c_float(scale), int(bool(causal)), _ptr(out), _stream(stream))
+    _check(st, "gqa_prefill")
+    return out

@@ -1,0 +1,356 @@
+// api.hip -- the C ABI declared in include/gqa.h: argument checks, split
+// planning and kernel dispatch.  Every check that needs no device runs before
+// any HIP call, so invalid calls fail the same way on a machine without a GPU.
+#include "../../include/gqa.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "kernels.h"
+
+namespace gqa {
+
+int32_t pow2_at_least(int32_t g)
+{
+    int32_t p = 1;
+    while (p < g) p <<= 1;
+    return p;
+}
+
+static int env_int(const char *name, int dflt)
+{
+    const char *s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    return std::atoi(s);
+}
+
+// Keys per decode split.  Aim at ~2048 workgroups (8 per CU on 256 CUs) for
+// the largest row, with splits of at least 256 keys so each workgroup streams
+// enough bytes to hide its start-up; GQA_DECODE_SPLIT_TOKENS overrides.
+int32_t plan_decode_split(int32_t B, int32_t K, int32_t max_ctx)
+{
+    const int over = env_int("GQA_DECODE_SPLIT_TOKENS", 0);
+    if (over > 0) return (int32_t)(((int64_t)over + kKeyTile - 1) / kKeyTile * kKeyTile);
+    const int64_t target_wg = 2048;
+    int64_t split = ((int64_t)B * K * max_ctx + target_wg - 1) / target_wg;
+    split = (split + kKeyTile - 1) / kKeyTile * kKeyTile;
+    if (split < 256) split = 256;
+    const int64_t whole = ((int64_t)max_ctx + kKeyTile - 1) / kKeyTile * kKeyTile;
+    if (split > whole) split = whole < kKeyTile ? kKeyTile : whole;
+    return (int32_t)split;
+}
+
+}  // namespace gqa
+
+using namespace gqa;
+
+namespace {
+
+bool check_mode() { return std::getenv("GQA_CHECK") && std::atoi(std::getenv("GQA_CHECK")) != 0; }
+bool debug_mode() { return std::getenv("GQA_DEBUG") && std::atoi(std::getenv("GQA_DEBUG")) != 0; }
+
+gqa_status fail(gqa_status s, const char *what)
+{
+    if (debug_mode()) std::fprintf(stderr, "[gqa] %s: %s\n", gqa_status_string(s), what);
+    return s;
+}
+
+bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int32_t x)
+{
+    int r = 0;
+    while ((1 << r) < x) ++r;
+    return r;
+}
+
+// Validates a cache descriptor and fills the kernel view.
+gqa_status make_view(const gqa_kv_cache *c, CacheView *out)
+{
+    if (!c) return fail(GQA_ERR_INVALID_ARG, "cache descriptor is NULL");
+    if (!c->k || !c->v) return fail(GQA_ERR_INVALID_ARG, "cache k/v pointer is NULL");
+    if (c->num_kv_heads <= 0) return fail(GQA_ERR_INVALID_ARG, "num_kv_heads <= 0");
+    if (c->head_dim <= 0) return fail(GQA_ERR_INVALID_ARG, "head_dim <= 0");
+    if (c->head_dim != 64 && c->head_dim != 128) return fail(GQA_ERR_UNSUPPORTED, "head_dim not 64 or 128");
+    if (c->dtype != GQA_F32 && c->dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "unknown dtype");
+    CacheView v{};
+    v.k = static_cast<char *>(c->k);
+    v.v = static_cast<char *>(c->v);
+    v.block_table = c->block_table;
+    v.K = c->num_kv_heads;
+    v.d = c->head_dim;
+    v.elem_bytes = c->dtype == GQA_BF16 ? 2 : 4;
+    if (c->block_table == nullptr) {
+        if (c->S_max <= 0) return fail(GQA_ERR_INVALID_ARG, "S_max <= 0");
+        v.S_max = c->S_max;
+        v.capacity = c->S_max;
+    } else {
+        if (!is_pow2(c->block_size) || c->block_size > 1024)
+            return fail(GQA_ERR_INVALID_ARG, "block_size not a power of two in [1, 1024]");
+        if (c->max_blocks_per_seq <= 0) return fail(GQA_ERR_INVALID_ARG, "max_blocks_per_seq <= 0");
+        if (c->num_blocks <= 0) return fail(GQA_ERR_INVALID_ARG, "num_blocks <= 0");
+        const int64_t cap = (int64_t)c->max_blocks_per_seq * c->block_size;
+        if (cap > 0x7fffffffLL) return fail(GQA_ERR_INVALID_ARG, "paged capacity exceeds 2^31-1 tokens");
+        v.max_blocks = c->max_blocks_per_seq;
+        v.log2_bs = ilog2(c->block_size);
+        v.num_blocks = c->num_blocks;
+        v.capacity = (int32_t)cap;
+    }
+    *out = v;
+    return GQA_OK;
+}
+
+gqa_status check_heads(int32_t H, int32_t K)
+{
+    if (H <= 0) return fail(GQA_ERR_INVALID_ARG, "num_heads <= 0");
+    if (H % K != 0) return fail(GQA_ERR_INVALID_ARG, "num_heads is not a multiple of num_kv_heads");
+    if (H / K > 64) return fail(GQA_ERR_UNSUPPORTED, "group size H/K above 64");
+    return GQA_OK;
+}
+
+gqa_status launch_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess) {
+        if (debug_mode()) std::fprintf(stderr, "[gqa] %s: %s\n", what, hipGetErrorString(e));
+        return GQA_ERR_LAUNCH;
+    }
+    return GQA_OK;
+}
+
+// GQA_CHECK=1: copy a device int32 array back (synchronising) for validation.
+bool fetch_i32(const int32_t *dev, size_t n, std::vector<int32_t> &host)
+{
+    host.resize(n);
+    if (n == 0) return true;
+    return hipMemcpy(host.data(), dev, n * sizeof(int32_t), hipMemcpyDeviceToHost) == hipSuccess;
+}
+
+// Checks that every position in [lo[b], hi[b]) fits the cache, through the
+// block table when paged.
+gqa_status check_positions(const CacheView &v, const std::vector<int32_t> &lo,
+                           const std::vector<int32_t> &hi)
+{
+    std::vector<int32_t> table;
+    if (v.block_table) {
+        if (!fetch_i32(v.block_table, (size_t)lo.size() * v.max_blocks, table))
+            return fail(GQA_ERR_LAUNCH, "block table copy failed");
+    }
+    for (size_t b = 0; b < lo.size(); ++b) {
+        if (lo[b] < 0 || hi[b] > v.capacity || hi[b] < lo[b])
+            return fail(GQA_ERR_DEVICE_ARG, "position outside the cache capacity");
+        if (!v.block_table) continue;
+        const int bs = 1 << v.log2_bs;
+        for (int64_t lb = lo[b] / bs; lb * bs < hi[b]; ++lb) {
+            const int32_t blk = table[b * v.max_blocks + lb];
+            if (blk < 0 || blk >= v.num_blocks) return fail(GQA_ERR_DEVICE_ARG, "block id out of range");
+        }
+    }
+    return GQA_OK;
+}
+
+struct DecodeLayout {
+    int32_t split = 0, max_splits = 0;
+    size_t o_bytes = 0, ml_bytes = 0, cnt_bytes = 0, total = 0;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool decode_layout(int64_t rows, int32_t H, int32_t K, int32_t d, int32_t max_ctx, DecodeLayout *L)
+{
+    if (rows <= 0 || H <= 0 || K <= 0 || d <= 0 || max_ctx <= 0) return false;
+    L->split = plan_decode_split((int32_t)(rows > 0x7fffffff ? 0x7fffffff : rows), K, max_ctx);
+    L->max_splits = (int32_t)(((int64_t)max_ctx + L->split - 1) / L->split);
+    if (L->max_splits <= 1) {
+        L->max_splits = 1;
+        return true;   // one split per row: no workspace needed
+    }
+    L->o_bytes = align256((size_t)rows * H * L->max_splits * d * sizeof(float));
+    L->ml_bytes = align256((size_t)rows * H * L->max_splits * 2 * sizeof(float));
+    L->cnt_bytes = align256((size_t)rows * K * sizeof(int32_t));
+    L->total = L->o_bytes + L->ml_bytes + L->cnt_bytes;
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gqa_abi_version(void) { return GQA_ABI_VERSION; }
+
+const char *gqa_status_string(int32_t s)
+{
+    switch (s) {
+    case GQA_OK: return "ok";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case GQA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GQA_ERR_LAUNCH: return "HIP launch or runtime failure";
+    case GQA_ERR_DEVICE_ARG: return "device-resident argument out of range";
+    default: return "unknown status";
+    }
+}
+
+int32_t gqa_cache_elems_per_token(int32_t num_kv_heads, int32_t head_dim)
+{
+    if (num_kv_heads <= 0 || head_dim <= 0) return -1;
+    const int64_t n = 2LL * num_kv_heads * head_dim;
+    return n > 0x7fffffffLL ? -1 : (int32_t)n;
+}
+
+size_t gqa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_ctx)
+{
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return 0;
+    DecodeLayout L;
+    if (!decode_layout(B, num_heads, num_kv_heads, head_dim, max_ctx, &L)) return 0;
+    return L.total;
+}
+
+gqa_status gqa_kv_append(const gqa_kv_cache *cache, const void *k_new, const void *v_new,
+                         const int32_t *start_pos, int32_t B, int32_t s_new, void *stream)
+{
+    CacheView v;
+    gqa_status st = make_view(cache, &v);
+    if (st != GQA_OK) return st;
+    if (B < 0 || s_new < 0) return fail(GQA_ERR_INVALID_ARG, "B or s_new negative");
+    if (B == 0 || s_new == 0) return GQA_OK;
+    if (!k_new || !v_new || !start_pos) return fail(GQA_ERR_INVALID_ARG, "NULL k_new/v_new/start_pos");
+    if (check_mode()) {
+        std::vector<int32_t> sp;
+        if (!fetch_i32(start_pos, B, sp)) return fail(GQA_ERR_LAUNCH, "start_pos copy failed");
+        std::vector<int32_t> hi(B);
+        for (int b = 0; b < B; ++b) hi[b] = (int32_t)std::min<int64_t>((int64_t)sp[b] + s_new, 0x7fffffff);
+        if ((st = check_positions(v, sp, hi)) != GQA_OK) return st;
+    }
+    AppendParams p{};
+    p.cache = v;
+    p.k_new = static_cast<const char *>(k_new);
+    p.v_new = static_cast<const char *>(v_new);
+    p.start_pos = start_pos;
+    p.B = B;
+    p.s_new = s_new;
+    return launch_status(launch_kv_append(p, static_cast<hipStream_t>(stream)), "kv_append");
+}
+
+gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *ctx_lens,
+                      int32_t max_ctx, int32_t B, int32_t num_heads, float scale, void *out,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    CacheView v;
+    gqa_status st = make_view(cache, &v);
+    if (st != GQA_OK) return st;
+    if ((st = check_heads(num_heads, v.K)) != GQA_OK) return st;
+    if (B < 0) return fail(GQA_ERR_INVALID_ARG, "B negative");
+    if (B == 0) return GQA_OK;
+    if (B > 65535) return fail(GQA_ERR_UNSUPPORTED, "B above 65535");
+    if (!q || !out || !ctx_lens) return fail(GQA_ERR_INVALID_ARG, "NULL q/out/ctx_lens");
+    if (max_ctx <= 0) return fail(GQA_ERR_INVALID_ARG, "max_ctx <= 0");
+    if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
+    DecodeLayout L;
+    if (!decode_layout(B, num_heads, v.K, v.d, max_ctx, &L)) return fail(GQA_ERR_INVALID_ARG, "bad sizes");
+    if (L.total > 0 && (!workspace || workspace_bytes < L.total))
+        return fail(GQA_ERR_WORKSPACE, "workspace smaller than gqa_decode_workspace_bytes()");
+    if (check_mode()) {
+        std::vector<int32_t> cl;
+        if (!fetch_i32(ctx_lens, B, cl)) return fail(GQA_ERR_LAUNCH, "ctx_lens copy failed");
+        for (int b = 0; b < B; ++b)
+            if (cl[b] < 1 || cl[b] > max_ctx) return fail(GQA_ERR_DEVICE_ARG, "ctx_lens outside [1, max_ctx]");
+        std::vector<int32_t> lo(B, 0);
+        if ((st = check_positions(v, lo, cl)) != GQA_OK) return st;
+    }
+    RowAttnParams p{};
+    p.cache = v;
+    p.q = static_cast<const char *>(q);
+    p.out = static_cast<char *>(out);
+    p.ctx_lens = ctx_lens;
+    char *ws = static_cast<char *>(workspace);
+    if (L.total > 0) {
+        p.ws_o = reinterpret_cast<float *>(ws);
+        p.ws_ml = reinterpret_cast<float *>(ws + L.o_bytes);
+        p.counters = reinterpret_cast<int32_t *>(ws + L.o_bytes + L.ml_bytes);
+    }
+    p.B = B;
+    p.Sq = 1;
+    p.H = num_heads;
+    p.G = num_heads / v.K;
+    p.prefill = 0;
+    p.causal = 0;
+    p.split = L.split;
+    p.max_splits = L.max_splits;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return launch_status(launch_row_attention(p, pow2_at_least(p.G), static_cast<hipStream_t>(stream)),
+                         "decode");
+}
+
+gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
+                       const gqa_kv_cache *cache, const int32_t *start_pos, int32_t B, int32_t s,
+                       int32_t num_heads, float scale, int32_t causal, void *out, void *stream)
+{
+    CacheView v;
+    gqa_status st = make_view(cache, &v);
+    if (st != GQA_OK) return st;
+    if ((st = check_heads(num_heads, v.K)) != GQA_OK) return st;
+    if (B < 0 || s < 0) return fail(GQA_ERR_INVALID_ARG, "B or s negative");
+    if (B == 0 || s == 0) return GQA_OK;
+    if (!q || !k_new || !v_new || !start_pos || !out) return fail(GQA_ERR_INVALID_ARG, "NULL pointer");
+    if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
+    const bool bf16 = v.elem_bytes == 2;
+    if (!bf16 && (int64_t)B * s > 65535) return fail(GQA_ERR_UNSUPPORTED, "fp32 prefill limited to B*s <= 65535 rows");
+    if (check_mode()) {
+        std::vector<int32_t> sp;
+        if (!fetch_i32(start_pos, B, sp)) return fail(GQA_ERR_LAUNCH, "start_pos copy failed");
+        std::vector<int32_t> lo(B, 0), hi(B);
+        for (int b = 0; b < B; ++b) {
+            if (sp[b] < 0) return fail(GQA_ERR_DEVICE_ARG, "start_pos negative");
+            hi[b] = (int32_t)std::min<int64_t>((int64_t)sp[b] + s, 0x7fffffff);
+        }
+        if ((st = check_positions(v, lo, hi)) != GQA_OK) return st;
+    }
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    AppendParams ap{};
+    ap.cache = v;
+    ap.k_new = static_cast<const char *>(k_new);
+    ap.v_new = static_cast<const char *>(v_new);
+    ap.start_pos = start_pos;
+    ap.B = B;
+    ap.s_new = s;
+    if ((st = launch_status(launch_kv_append(ap, hs), "prefill append")) != GQA_OK) return st;
+
+    const float scale_log2 = scale * 1.4426950408889634f;
+    if (bf16) {
+        PrefillParams pp{};
+        pp.cache = v;
+        pp.q = static_cast<const char *>(q);
+        pp.out = static_cast<char *>(out);
+        pp.start_pos = start_pos;
+        pp.B = B;
+        pp.s = s;
+        pp.H = num_heads;
+        pp.G = num_heads / v.K;
+        pp.causal = causal != 0;
+        pp.scale_log2 = scale_log2;
+        return launch_status(launch_prefill_mfma(pp, hs), "prefill");
+    }
+    RowAttnParams p{};
+    p.cache = v;
+    p.q = static_cast<const char *>(q);
+    p.out = static_cast<char *>(out);
+    p.start_pos = start_pos;
+    p.B = B;
+    p.Sq = s;
+    p.H = num_heads;
+    p.G = num_heads / v.K;
+    p.prefill = 1;
+    p.causal = causal != 0;
+    p.max_splits = 1;   // one workgroup walks a row's whole key range
+    p.split = (int32_t)std::min<int64_t>(((int64_t)v.capacity + kKeyTile - 1) / kKeyTile * kKeyTile,
+                                         0x7fffffc0LL);
+    p.scale_log2 = scale_log2;
+    return launch_status(launch_row_attention(p, pow2_at_least(p.G), hs), "prefill (fp32)");
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// common.h -- device helpers shared by the libgqa kernels (not a public header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int kWave = 64;   // CDNA wavefront width
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32 (bf16 is the upper 16 bits of a binary32)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Two bf16 products summed into an fp32 accumulator (v_dot2_f32_bf16).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)
+{
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// (lo16(a), lo16(b)) and (hi16(a), hi16(b)): pair element e of two rows.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b)
+{
+    return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b)
+{
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Butterfly reductions over aligned groups of `width` lanes (width a power of
+// two <= 64).  Every lane of a group ends with the same value.
+template <int width>
+__device__ __forceinline__ float group_max(float x)
+{
+#pragma unroll
+    for (int m = width / 2; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+    return x;
+}
+template <int width>
+__device__ __forceinline__ float group_sum(float x)
+{
+#pragma unroll
+    for (int m = width / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+    return x;
+}
+
+// 16-byte global load / store helpers.
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+}  // namespace gqa

@@ -1,0 +1,90 @@
+// kernels.h -- launch parameters shared by the C-ABI layer and the kernels
+// (internal; the public interface is include/gqa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// Where the cache rows of one layer live.
+struct CacheView {
+    char *k;                    // base of the K cache / pool
+    char *v;                    // base of the V cache / pool
+    const int32_t *block_table; // nullptr: contiguous [B, K, S_max, d]
+    int32_t max_blocks;         // paged: columns of block_table
+    int32_t log2_bs;            // paged: log2(block_size)
+    int32_t num_blocks;         // paged: rows of the pool
+    int32_t S_max;              // contiguous capacity per sequence
+    int32_t K;                  // KV heads
+    int32_t d;                  // head dim
+    int32_t elem_bytes;         // 2 (bf16) or 4 (fp32)
+    int32_t capacity;           // tokens a sequence can hold
+};
+
+struct AppendParams {
+    CacheView cache;
+    const char *k_new;          // [B, s_new, K, d]
+    const char *v_new;
+    const int32_t *start_pos;   // [B]
+    int32_t B;
+    int32_t s_new;
+};
+
+// Row-wise attention on the vector ALUs: decode (one query row per
+// sequence, keys [0, ctx)) and the fp32 prefill (s rows per sequence).
+struct RowAttnParams {
+    CacheView cache;
+    const char *q;              // [B, Sq, H, d]
+    char *out;                  // [B, Sq, H, d]
+    const int32_t *ctx_lens;    // decode: [B] keys per sequence
+    const int32_t *start_pos;   // prefill: [B] position of query row 0
+    float *ws_o;                // [B*Sq, H, max_splits, d] partial outputs (unnormalised)
+    float *ws_ml;               // [B*Sq, H, max_splits, 2] partial (max, sum) in log2 units
+    int32_t *counters;          // [B*Sq, K] finished-split counters
+    int32_t B;
+    int32_t Sq;                 // query rows per sequence
+    int32_t H;
+    int32_t G;                  // H / K
+    int32_t prefill;            // 0: decode rows; 1: prefill rows
+    int32_t causal;
+    int32_t split;              // keys per split (multiple of the key tile)
+    int32_t max_splits;
+    float scale_log2;           // softmax scale * log2(e)
+};
+
+// Causal / full prefill on the matrix cores (bf16).
+struct PrefillParams {
+    CacheView cache;
+    const char *q;              // [B, s, H, d]
+    char *out;                  // [B, s, H, d]
+    const int32_t *start_pos;   // [B]
+    int32_t B;
+    int32_t s;
+    int32_t H;
+    int32_t G;
+    int32_t causal;
+    float scale_log2;
+};
+
+// Row index of cache entry (b, g, pos) in units of one head row, or -1 when
+// the block id the table gives is outside the pool.
+__device__ __forceinline__ int64_t cache_row(const CacheView &c, int b, int g, int pos)
+{
+    if (c.block_table == nullptr) return ((int64_t)b * c.K + g) * c.S_max + pos;
+    const int32_t blk = c.block_table[(int64_t)b * c.max_blocks + (pos >> c.log2_bs)];
+    if (blk < 0 || blk >= c.num_blocks) return -1;
+    return (((int64_t)blk * c.K + g) << c.log2_bs) + (pos & ((1 << c.log2_bs) - 1));
+}
+
+hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
+hipError_t launch_row_attention(const RowAttnParams &p, int gp, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillParams &p, hipStream_t stream);
+
+// Decode split planning (host-only, deterministic).
+constexpr int kKeyTile = 64;
+int32_t plan_decode_split(int32_t B, int32_t K, int32_t max_ctx);
+int32_t pow2_at_least(int32_t g);
+
+}  // namespace gqa

@@ -8,7 +8,9 @@ Recipe (fixed so that every run sees the same bits):
 
 * ``numpy.random.Generator(PCG64(seed))`` with ``seed = 1000 + config id``;
 * draw order: context lengths, then the block permutation (paged only), then
-  Q, then K, then V;
+  Q, then K, then V; each of Q, K, V takes one 63-bit seed from that
+  generator and is filled in 2^24-element chunks, chunk c drawn from
+  ``PCG64(tensor seed).jumped(c)``;
 * values are ``standard_normal(float32)`` (times 0.5 for the causal-prefill
   workload), rounded to bf16 with round-to-nearest-even for the bf16
   workloads, kept as fp32 for the fp32 workloads;
@@ -25,6 +27,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -124,17 +127,38 @@ def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
+_CHUNK = 1 << 24
+
+
 def _normal(rng: np.random.Generator, shape, dtype: str, scale: float) -> np.ndarray:
-    """standard_normal(float32) * scale, stored as bf16 bits or fp32, drawn in chunks."""
+    """standard_normal(float32) * scale, stored as bf16 bits or fp32.
+
+    One 63-bit seed is drawn from ``rng`` per tensor; the tensor is filled in
+    2^24-element chunks, chunk c from ``PCG64(seed).jumped(c)``, so the chunks
+    can be drawn in parallel and the result does not depend on the thread
+    count."""
     n = int(np.prod(shape))
+    seed = int(rng.integers(0, 2**63 - 1))
     out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
-    chunk = 1 << 24
-    for s0 in range(0, n, chunk):
-        m = min(chunk, n - s0)
-        x = rng.standard_normal(m, dtype=np.float32)
+
+    def fill(c):
+        s0 = c * _CHUNK
+        m = min(_CHUNK, n - s0)
+        g = np.random.Generator(np.random.PCG64(seed).jumped(c))
+        x = g.standard_normal(m, dtype=np.float32)
         if scale != 1.0:
             x *= np.float32(scale)
         out[s0:s0 + m] = f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+    chunks = (n + _CHUNK - 1) // _CHUNK
+    if chunks <= 1:
+        for c in range(chunks):
+            fill(c)
+    else:
+        import concurrent.futures
+        workers = max(1, min(16, os.cpu_count() or 1, chunks))
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(fill, range(chunks)))
     return out.reshape(shape)
 
 

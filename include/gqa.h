@@ -1,0 +1,163 @@
+/*
+ * gqa.h -- C ABI of libgqa.so: grouped-query attention on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operation (the "Grouped-Query Attention" concept page, compassingai.com,
+ * section 技术原理, steps 2-4): the H query heads are split into K groups of
+ * G = H / K heads; query head h belongs to group g = h / G and attends to the
+ * single K/V head g of the cache:
+ *
+ *     out[b, i, h, :] = softmax(q[b, i, h, :] . K_g^T * scale) V_g
+ *
+ * over the keys visible to that query row.  H must be a multiple of K; K = H
+ * is multi-head attention and K = 1 multi-query attention (same page, and the
+ * inference-optimisation page, iopencloud.com, §7.1).
+ *
+ * Layouts (all row-major, element type given by gqa_kv_cache.dtype):
+ *   queries / outputs   [B, s, H, d]        (concept page, steps 2 and 4)
+ *   new keys / values   [B, s_new, K, d]    (concept page, 技术原理: a new token
+ *                                            writes K/V of shape [B, 1, K, d])
+ *   contiguous cache    [B, K, S_max, d]    for K and for V separately
+ *   paged cache pool    [num_blocks, K, block_size, d]; token t of sequence b
+ *                       lives in physical block block_table[b, t / block_size],
+ *                       slot t % block_size (inference-optimisation page §8.2)
+ *
+ * Conventions
+ *   - Ownership: the caller owns every buffer (queries, cache, block table,
+ *     context lengths, outputs, workspace).  The library never allocates or
+ *     frees memory and keeps no state besides cached device properties.
+ *   - Pointers are device pointers unless stated otherwise; the
+ *     gqa_kv_cache descriptor itself is a host struct.
+ *   - Asynchrony: every call enqueues its kernels on `stream` (a hipStream_t
+ *     passed as void*, NULL = the default stream) and returns; no call
+ *     synchronises unless GQA_CHECK=1 is set in the environment.
+ *   - Errors: arguments that the host can check are checked before anything
+ *     is enqueued; a bad one returns GQA_ERR_INVALID_ARG / GQA_ERR_UNSUPPORTED
+ *     / GQA_ERR_WORKSPACE and nothing runs.  A failed launch returns
+ *     GQA_ERR_LAUNCH.  Nothing is thrown across the ABI.
+ *   - Device-resident integers (start positions, context lengths, block ids)
+ *     are the caller's contract.  Kernels never access memory outside the
+ *     buffers described by the arguments whatever those integers hold:
+ *     positions past the cache capacity and block ids outside
+ *     [0, num_blocks) are skipped (append) or read as zeros (attention), and a
+ *     context length below 1 yields an all-zero output row.  With GQA_CHECK=1
+ *     the host copies them back, validates them and returns
+ *     GQA_ERR_DEVICE_ARG before launching if one is out of range.
+ *   - Supported: dtype GQA_BF16 or GQA_F32, head_dim 64 or 128,
+ *     1 <= K <= H, H % K == 0, G = H / K <= 64, block_size a power of two in
+ *     [1, 1024].
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ABI_VERSION 1
+
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, H % K != 0, ... */
+    GQA_ERR_UNSUPPORTED = 2,   /* valid but not built: head_dim, dtype, G > 64 */
+    GQA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+    GQA_ERR_LAUNCH = 4,        /* a HIP call or kernel launch failed */
+    GQA_ERR_DEVICE_ARG = 5     /* GQA_CHECK=1 only: a device-resident integer is out of range */
+} gqa_status;
+
+typedef enum {
+    GQA_F32 = 0,               /* IEEE binary32 */
+    GQA_BF16 = 1               /* bfloat16 (upper half of a binary32), stored as 16-bit words */
+} gqa_dtype;
+
+/* One layer's KV cache for K KV heads of width head_dim. */
+typedef struct {
+    void *k;                      /* contiguous: [B, K, S_max, d]; paged: [num_blocks, K, block_size, d] */
+    void *v;                      /* same layout and size as k */
+    const int32_t *block_table;   /* NULL: contiguous cache; else device [B, max_blocks_per_seq] */
+    int32_t max_blocks_per_seq;   /* paged: columns of block_table */
+    int32_t block_size;           /* paged: tokens per block (16 in the workloads here) */
+    int32_t num_blocks;           /* paged: blocks in the pool */
+    int32_t S_max;                /* contiguous: token capacity per sequence */
+    int32_t num_kv_heads;         /* K */
+    int32_t head_dim;             /* d */
+    int32_t dtype;                /* gqa_dtype */
+} gqa_kv_cache;
+
+/* ABI version of the loaded library (GQA_ABI_VERSION). */
+int32_t gqa_abi_version(void);
+
+/* Short English text for a status code (static storage). */
+const char *gqa_status_string(int32_t status);
+
+/*
+ * Cache elements one token adds to one layer: a K row and a V row for each
+ * KV head, 2 * K * d (concept page, 关键参数 #2).  Returns -1 if K or d is not
+ * positive.  Host-only; no GPU needed.
+ */
+int32_t gqa_cache_elems_per_token(int32_t num_kv_heads, int32_t head_dim);
+
+/*
+ * Append s_new tokens to every sequence of the cache:
+ *     pos = start_pos[b] + t,  cache row (b, g, pos) <- new row (b, t, g)
+ * for t < s_new, g < K (through the block table when the cache is paged).
+ * k_new, v_new: device [B, s_new, K, d] in the cache dtype.
+ * start_pos: device int32 [B].  The copy is bit-exact.  Rows whose position is
+ * past the capacity (S_max, or max_blocks_per_seq * block_size) or whose block
+ * id is outside [0, num_blocks) are not written.
+ */
+gqa_status gqa_kv_append(const gqa_kv_cache *cache, const void *k_new, const void *v_new,
+                         const int32_t *start_pos, int32_t B, int32_t s_new, void *stream);
+
+/*
+ * Workspace bytes gqa_decode needs for these sizes.  max_ctx is a host-side
+ * upper bound of every ctx_lens[b] the call will see.  Host-only; no GPU
+ * needed.  Returns 0 on invalid sizes.
+ */
+size_t gqa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t max_ctx);
+
+/*
+ * One decode step: each sequence's single query row attends to the first
+ * ctx_lens[b] cached tokens (the newest token included: append it first).
+ *   q:   device [B, 1, H, d];  out: device [B, 1, H, d]  (cache dtype)
+ *   ctx_lens: device int32 [B], each in [1, max_ctx]
+ *   max_ctx: host upper bound of ctx_lens, used to plan the key splits
+ *   scale: the softmax scale, normally 1 / sqrt(d)
+ * The keys are cut into splits (flash-decoding, inference-optimisation page
+ * §10.2); every split keeps an online-softmax state (§9.2.1) and the splits of
+ * one (sequence, KV head) are merged with their global max and sum.  One
+ * K/V row read from memory serves all G heads of its group.
+ * workspace: device buffer of at least gqa_decode_workspace_bytes(...) bytes.
+ * It MUST be zero-filled before its first use; every completed call leaves it
+ * ready for the next one.  Calls that may run concurrently need separate
+ * workspaces.
+ */
+gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *ctx_lens,
+                      int32_t max_ctx, int32_t B, int32_t num_heads, float scale, void *out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Prefill: write the new tokens' K/V into the cache (exactly the bytes
+ * gqa_kv_append writes) and attend every new query row to the cache.
+ *   q: device [B, s, H, d];  k_new, v_new: device [B, s, K, d];  out: device [B, s, H, d]
+ *   start_pos: device int32 [B], the position of query row 0 (0 for a fresh
+ *              prompt; > 0 continues a sequence whose earlier tokens are
+ *              already cached)
+ *   causal != 0: row i (position start_pos[b] + i) sees keys 0 .. start_pos[b] + i
+ *   causal == 0: every row sees keys 0 .. start_pos[b] + s - 1
+ * bf16 runs on the matrix cores (bf16 products, fp32 accumulation and
+ * softmax statistics); fp32 runs on the vector ALUs in fp32 throughout.
+ */
+gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
+                       const gqa_kv_cache *cache, const int32_t *start_pos, int32_t B, int32_t s,
+                       int32_t num_heads, float scale, int32_t causal, void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

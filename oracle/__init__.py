@@ -69,6 +69,8 @@ def _load():
         lib.oracle_kv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
         lib.oracle_kv_append_paged.restype = i64
         lib.oracle_kv_append_paged.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32]
+        lib.oracle_gather_paged_raw.restype = i64
+        lib.oracle_gather_paged_raw.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, i32, i32, i32, vp]
         lib.oracle_gather_paged.restype = i64
         lib.oracle_gather_paged.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, i32, i32, vp]
         _lib = lib
@@ -205,6 +207,22 @@ def gather_paged(pool_f64: np.ndarray, block_table, ctx_lens, S_out: int) -> np.
     out = np.empty((B, K, S_out, d), dtype=np.float64)
     bad = _load().oracle_gather_paged(_ptr(pool_f64), _ptr(bt), bt.shape[1], N, bs, _ptr(cl),
                                       B, K, d, S_out, _ptr(out))
+    if bad:
+        raise ValueError(f"{bad} visible positions map to invalid physical blocks")
+    return out
+
+
+def gather_paged_raw(pool: np.ndarray, block_table, ctx_lens, S_out: int, fill) -> np.ndarray:
+    """Contiguous [B,K,S_out,d] copy of a paged pool in its stored format (no decoding);
+    positions past each ctx_lens[b] hold ``fill``."""
+    pool = np.ascontiguousarray(pool)
+    N, K, bs, d = pool.shape
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    B = bt.shape[0]
+    cl = _i32(ctx_lens, B)
+    out = np.full((B, K, S_out, d), fill, dtype=pool.dtype)
+    bad = _load().oracle_gather_paged_raw(_ptr(pool), pool.dtype.itemsize, _ptr(bt), bt.shape[1], N, bs,
+                                          _ptr(cl), B, K, d, S_out, _ptr(out))
     if bad:
         raise ValueError(f"{bad} visible positions map to invalid physical blocks")
     return out

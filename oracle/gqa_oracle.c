@@ -251,6 +251,30 @@ int64_t oracle_kv_append_paged(void *pool, const void *new_rows, const int32_t *
 }
 
 /*
+ * The same gather for raw elements of elem_bytes bytes (no decoding): rows
+ * that no valid block provides are left as the caller filled them.
+ */
+int64_t oracle_gather_paged_raw(const void *pool, int elem_bytes, const int32_t *block_table,
+                                int max_blocks, int num_blocks, int block_size,
+                                const int32_t *ctx_lens, int B, int K, int d, int S_out, void *out)
+{
+    const size_t row_bytes = (size_t)d * (size_t)elem_bytes;
+    int64_t bad = 0;
+    for (int b = 0; b < B; ++b)
+        for (int g = 0; g < K; ++g)
+            for (int64_t t = 0; t < S_out && t < ctx_lens[b]; ++t) {
+                if (t / block_size >= max_blocks) { ++bad; continue; }
+                const int32_t phys = block_table[(int64_t)b * max_blocks + t / block_size];
+                if (phys < 0 || phys >= num_blocks) { ++bad; continue; }
+                const char *src = (const char *)pool +
+                                  (((int64_t)phys * K + g) * block_size + t % block_size) * row_bytes;
+                char *dst = (char *)out + (((int64_t)b * K + g) * S_out + t) * row_bytes;
+                memcpy(dst, src, row_bytes);
+            }
+    return bad;
+}
+
+/*
  * Gather a paged pool into a contiguous [B, K, S_out, d] array of doubles:
  *   out[b, g, t, :] = pool[block_table[b, t / block_size], g, t % block_size, :]
  * for t < min(ctx_lens[b], S_out); other positions are set to NaN.  The

@@ -1,0 +1,172 @@
+"""Helpers for the GPU tests: moving the generated inputs to the device,
+calling the library through the binding, and evaluating the oracle on the
+same bits.  Nothing here computes attention itself."""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from grouped_query_attention_gqa_amd import binding
+from grouped_query_attention_gqa_amd import workloads as W
+
+BF16_TOL = 2e-2     # bf16 inputs, fp32 accumulation, against the fp64 oracle
+F32_TOL = 1e-5      # fp32 path
+
+requires_gpu = pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")
+DEV = "cuda"
+
+
+def say(*a):
+    """Name the case on stdout before a GPU step (flushed)."""
+    print("[gpu-case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(DEV)
+    if x.dtype == np.float32:
+        return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    if x.dtype == np.int32:
+        return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+    raise TypeError(x.dtype)
+
+
+def from_dev(t: torch.Tensor) -> np.ndarray:
+    """Raw stored values back on the host (bf16 as uint16 bits)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def as_f64(x: np.ndarray, dtype: str) -> np.ndarray:
+    return oracle.to_f64(x, dtype)
+
+
+def check_close(got: np.ndarray, want: np.ndarray, tol: float, what: str):
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    err = np.abs(got - want)
+    worst = float(err.max()) if err.size else 0.0
+    assert worst <= tol, f"{what}: max abs error {worst:.3e} > {tol:.1e}"
+    return worst
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+class DecodeRun:
+    """Device copies of a DecodeInputs and one library call on them."""
+
+    def __init__(self, inp: W.DecodeInputs):
+        self.inp = inp
+        self.q = to_dev(inp.q)
+        self.k = to_dev(inp.k)
+        self.v = to_dev(inp.v)
+        self.ctx = to_dev(inp.ctx)
+        self.bt = None if inp.block_table is None else to_dev(inp.block_table)
+        self.cache = binding.KVCache(self.k, self.v, self.bt)
+        self.max_ctx = int(inp.ctx.max())
+
+    def run(self, out=None) -> torch.Tensor:
+        out = binding.gqa_decode(self.q, self.cache, self.ctx, self.max_ctx, out=out, scale=self.inp.wl.scale)
+        torch.cuda.synchronize()
+        return out
+
+
+def oracle_decode_rows(inp: W.DecodeInputs, seqs=None, heads=None):
+    """Oracle outputs (fp64) for the listed sequences and heads; returns (rows, out)."""
+    wl = inp.wl
+    seqs = range(wl.B) if seqs is None else seqs
+    heads = range(wl.H) if heads is None else heads
+    rows_all, outs = [], []
+    for b in seqs:
+        n = int(inp.ctx[b])
+        if inp.block_table is None:
+            kb = inp.k[b:b + 1, :, :n]
+            vb = inp.v[b:b + 1, :, :n]
+        else:
+            fill = W.sentinel(wl.dtype, "nan")
+            kb = oracle.gather_paged_raw(inp.k, inp.block_table[b:b + 1], inp.ctx[b:b + 1], n, fill)
+            vb = oracle.gather_paged_raw(inp.v, inp.block_table[b:b + 1], inp.ctx[b:b + 1], n, fill)
+        rows = np.array([[0, 0, h] for h in heads], dtype=np.int32)
+        o = oracle.attention_rows(as_f64(inp.q[b:b + 1], wl.dtype), as_f64(kb, wl.dtype), as_f64(vb, wl.dtype),
+                                  [n - 1], [n], False, wl.scale, rows)
+        rows[:, 0] = b
+        rows_all.append(rows)
+        outs.append(o)
+    return np.concatenate(rows_all), np.concatenate(outs)
+
+
+def gpu_rows(out_np: np.ndarray, rows: np.ndarray, dtype: str) -> np.ndarray:
+    """Pick (b, i, h) rows from a [B, s, H, d] output and decode to fp64."""
+    sel = out_np[rows[:, 0], rows[:, 1], rows[:, 2]]
+    return as_f64(sel, dtype)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+class PrefillRun:
+    def __init__(self, inp: W.PrefillInputs, paged_blocks=None, S_max=None, prior=None):
+        """prior: optional (k_prior, v_prior) [B, start, K, d] rows already in the cache."""
+        wl = inp.wl
+        self.inp = inp
+        self.q = to_dev(inp.q)
+        self.kn = to_dev(inp.k_new)
+        self.vn = to_dev(inp.v_new)
+        self.start = to_dev(inp.start_pos)
+        S = int(inp.start_pos.max()) + wl.s if S_max is None else S_max
+        self.S_max = S
+        if paged_blocks is None:
+            cache_np = np.full((wl.B, wl.K, S, wl.d), W.sentinel(wl.dtype, "nan"), dtype=W.storage_dtype(wl.dtype))
+            self.k = to_dev(cache_np)
+            self.v = to_dev(cache_np)
+            self.cache = binding.KVCache(self.k, self.v)
+            self.table = None
+        else:
+            table, n_pool = paged_blocks
+            pool = np.full((n_pool, wl.K, wl.block_size, wl.d), W.sentinel(wl.dtype, "nan"),
+                           dtype=W.storage_dtype(wl.dtype))
+            self.k = to_dev(pool)
+            self.v = to_dev(pool)
+            self.table = table
+            self.cache = binding.KVCache(self.k, self.v, to_dev(table))
+        if prior is not None:
+            kp, vp = prior
+            zero = torch.zeros(wl.B, dtype=torch.int32, device=DEV)
+            binding.gqa_kv_append(self.cache, to_dev(kp), to_dev(vp), zero)
+
+    def run(self, causal=True) -> torch.Tensor:
+        out = binding.gqa_prefill(self.q, self.kn, self.vn, self.cache, self.start, causal=causal,
+                                  scale=self.inp.wl.scale)
+        torch.cuda.synchronize()
+        return out
+
+
+def oracle_prefill_rows(inp: W.PrefillInputs, rows, causal=True, prior=None):
+    """Oracle rows (b, i, h) of a prefill whose cache holds prior rows then the new ones."""
+    wl = inp.wl
+    if prior is None:
+        k_all, v_all = inp.k_new, inp.v_new
+    else:
+        k_all = np.concatenate([prior[0], inp.k_new], axis=1)
+        v_all = np.concatenate([prior[1], inp.v_new], axis=1)
+    # the oracle's own append builds the head-major cache [B, K, S, d]
+    S = k_all.shape[1]
+    kc = np.full((wl.B, wl.K, S, wl.d), W.sentinel(wl.dtype, "nan"), dtype=k_all.dtype)
+    vc = np.full_like(kc, W.sentinel(wl.dtype, "nan"))
+    zero = np.zeros(wl.B, dtype=np.int32)
+    oracle.kv_append(kc, k_all, zero)
+    oracle.kv_append(vc, v_all, zero)
+    kc, vc = as_f64(kc, wl.dtype), as_f64(vc, wl.dtype)
+    kv_len = inp.start_pos + wl.s
+    return oracle.attention_rows(as_f64(inp.q, wl.dtype), kc, vc, inp.start_pos, kv_len, causal, wl.scale, rows)

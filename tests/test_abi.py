@@ -1,0 +1,134 @@
+"""The C ABI without a GPU: the library loads, exports what include/gqa.h
+declares, and rejects bad arguments before anything reaches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from grouped_query_attention_gqa_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(gqa_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("gqa_kv_append", "gqa_decode", "gqa_prefill", "gqa_decode_workspace_bytes",
+              "gqa_cache_elems_per_token"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(binding.EXPORTED_SYMBOLS)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.gqa_abi_version() == 1
+    assert lib.gqa_status_string(0) == b"ok"
+    assert b"workspace" in lib.gqa_status_string(3)
+
+
+@pytest.mark.parametrize("K,d,expect", [(8, 128, 2048), (64, 128, 16384), (1, 128, 256), (2, 64, 256),
+                                        (0, 128, -1), (8, 0, -1)])
+def test_cache_elems_per_token(lib, K, d, expect):
+    # 2*K*d elements per token per layer (concept page, key parameters #2)
+    assert binding.gqa_cache_elems_per_token(K, d) == expect
+
+
+def test_workspace_plan(lib):
+    # Llama-2-70B decode shape: 512-key splits, 16 per 8192-token row
+    n = binding.gqa_decode_workspace_bytes(16, 64, 8, 128, 8192)
+    per = 16 * 64 * 16
+    align = lambda x: (x + 255) // 256 * 256
+    assert n == align(per * 128 * 4) + align(per * 2 * 4) + align(16 * 8 * 4)
+    # a 128-token row fits one split: no workspace at all
+    assert binding.gqa_decode_workspace_bytes(1, 8, 2, 64, 128) == 0
+    assert binding.gqa_decode_workspace_bytes(1, 8, 3, 64, 128) == 0   # H % K != 0 -> 0
+    assert binding.gqa_decode_workspace_bytes(0, 8, 2, 64, 128) == 0
+
+
+def _cache(**kw):
+    s = binding._CacheStruct()
+    s.k, s.v = 0x10000, 0x20000          # never dereferenced: every case fails validation
+    s.block_table = None
+    s.S_max, s.num_kv_heads, s.head_dim, s.dtype = 128, 2, 64, binding.GQA_F32
+    s.max_blocks_per_seq, s.block_size, s.num_blocks = 0, 16, 0
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+FAKE = ctypes.c_void_p(0x30000)
+
+
+def _decode(lib, cache, B=1, H=8, max_ctx=128, scale=0.125, ws=None, ws_bytes=0):
+    return lib.gqa_decode(FAKE, ctypes.byref(cache), FAKE, max_ctx, B, H, ctypes.c_float(scale), FAKE,
+                          ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    (dict(num_kv_heads=3), binding.GQA_ERR_INVALID_ARG),     # 8 % 3 != 0
+    (dict(num_kv_heads=0), binding.GQA_ERR_INVALID_ARG),
+    (dict(head_dim=96), binding.GQA_ERR_UNSUPPORTED),
+    (dict(head_dim=-1), binding.GQA_ERR_INVALID_ARG),
+    (dict(dtype=7), binding.GQA_ERR_UNSUPPORTED),
+    (dict(S_max=0), binding.GQA_ERR_INVALID_ARG),
+    (dict(k=None), binding.GQA_ERR_INVALID_ARG),
+    (dict(block_table=0x40000, block_size=12, max_blocks_per_seq=4, num_blocks=4), binding.GQA_ERR_INVALID_ARG),
+    (dict(block_table=0x40000, block_size=16, max_blocks_per_seq=0, num_blocks=4), binding.GQA_ERR_INVALID_ARG),
+])
+def test_decode_rejects_bad_cache(lib, case, expect):
+    assert _decode(lib, _cache(**case)) == expect
+
+
+def test_decode_rejects_bad_sizes(lib):
+    c = _cache()
+    assert _decode(lib, c, H=0) == binding.GQA_ERR_INVALID_ARG
+    assert _decode(lib, c, B=-1) == binding.GQA_ERR_INVALID_ARG
+    assert _decode(lib, c, max_ctx=0) == binding.GQA_ERR_INVALID_ARG
+    assert _decode(lib, c, scale=float("nan")) == binding.GQA_ERR_INVALID_ARG
+    assert _decode(lib, _cache(num_kv_heads=1), H=128) == binding.GQA_ERR_UNSUPPORTED   # G = 128 > 64
+    assert lib.gqa_decode(None, ctypes.byref(c), FAKE, 128, 1, 8, ctypes.c_float(1.0), FAKE, None, 0,
+                          None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_decode(FAKE, None, FAKE, 128, 1, 8, ctypes.c_float(1.0), FAKE, None, 0,
+                          None) == binding.GQA_ERR_INVALID_ARG
+    assert _decode(lib, c, B=0) == binding.GQA_OK                         # empty batch: nothing to do
+
+
+def test_decode_rejects_small_workspace(lib):
+    c = _cache(S_max=8192, num_kv_heads=8, head_dim=128, dtype=binding.GQA_BF16)
+    need = lib.gqa_decode_workspace_bytes(16, 64, 8, 128, 8192)
+    assert need > 0
+    assert _decode(lib, c, B=16, H=64, max_ctx=8192) == binding.GQA_ERR_WORKSPACE
+    assert _decode(lib, c, B=16, H=64, max_ctx=8192, ws=FAKE, ws_bytes=need - 1) == binding.GQA_ERR_WORKSPACE
+
+
+def test_append_and_prefill_reject_bad_args(lib):
+    c = _cache()
+    assert lib.gqa_kv_append(ctypes.byref(c), None, FAKE, FAKE, 1, 1, None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_kv_append(ctypes.byref(c), FAKE, FAKE, FAKE, -1, 1, None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_kv_append(ctypes.byref(c), FAKE, FAKE, FAKE, 1, 0, None) == binding.GQA_OK
+    assert lib.gqa_kv_append(ctypes.byref(_cache(head_dim=80)), FAKE, FAKE, FAKE, 1, 1,
+                             None) == binding.GQA_ERR_UNSUPPORTED
+    pf = lambda cache, H=8, s=4, scale=0.125: lib.gqa_prefill(FAKE, FAKE, FAKE, ctypes.byref(cache), FAKE, 1, s,
+                                                              H, ctypes.c_float(scale), 1, FAKE, None)
+    assert pf(_cache(), H=7) == binding.GQA_ERR_INVALID_ARG
+    assert pf(_cache(), s=-2) == binding.GQA_ERR_INVALID_ARG
+    assert pf(_cache(), scale=float("inf")) == binding.GQA_ERR_INVALID_ARG
+    assert pf(_cache(), s=0) == binding.GQA_OK
+    assert lib.gqa_prefill(FAKE, FAKE, None, ctypes.byref(_cache()), FAKE, 1, 4, 8, ctypes.c_float(0.1), 1, FAKE,
+                           None) == binding.GQA_ERR_INVALID_ARG
