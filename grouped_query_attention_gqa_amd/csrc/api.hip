@@ -4,6 +4,7 @@
 #include "../../include/gqa.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -152,6 +153,16 @@ gqa_status check_positions(const CacheView &v, const std::vector<int32_t> &lo,
     return GQA_OK;
 }
 
+// Epoch of a decode call: the upper half of every split counter it touches.
+// 0x7F8xxxxx with a non-zero payload is a signalling-NaN bit pattern, which
+// the kernels never store (their partial results are computed values), so a
+// counter word left over from partial data can never carry a live epoch.
+uint32_t next_epoch()
+{
+    static std::atomic<uint32_t> calls{0};
+    return 0x7F800000u | (1u + calls.fetch_add(1, std::memory_order_relaxed) % 0x7FFFFEu);
+}
+
 struct DecodeLayout {
     int32_t split = 0, max_splits = 0;
     size_t o_bytes = 0, ml_bytes = 0, cnt_bytes = 0, total = 0;
@@ -168,10 +179,10 @@ bool decode_layout(int64_t rows, int32_t H, int32_t K, int32_t d, int32_t max_ct
         L->max_splits = 1;
         return true;   // one split per row: no workspace needed
     }
+    L->cnt_bytes = align256((size_t)rows * K * sizeof(unsigned long long));
     L->o_bytes = align256((size_t)rows * H * L->max_splits * d * sizeof(float));
     L->ml_bytes = align256((size_t)rows * H * L->max_splits * 2 * sizeof(float));
-    L->cnt_bytes = align256((size_t)rows * K * sizeof(int32_t));
-    L->total = L->o_bytes + L->ml_bytes + L->cnt_bytes;
+    L->total = L->cnt_bytes + L->o_bytes + L->ml_bytes;
     return true;
 }
 
@@ -269,10 +280,11 @@ gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *c
     p.ctx_lens = ctx_lens;
     char *ws = static_cast<char *>(workspace);
     if (L.total > 0) {
-        p.ws_o = reinterpret_cast<float *>(ws);
-        p.ws_ml = reinterpret_cast<float *>(ws + L.o_bytes);
-        p.counters = reinterpret_cast<int32_t *>(ws + L.o_bytes + L.ml_bytes);
+        p.counters = reinterpret_cast<unsigned long long *>(ws);
+        p.ws_o = reinterpret_cast<float *>(ws + L.cnt_bytes);
+        p.ws_ml = reinterpret_cast<float *>(ws + L.cnt_bytes + L.o_bytes);
     }
+    p.epoch = next_epoch();
     p.B = B;
     p.Sq = 1;
     p.H = num_heads;

@@ -42,7 +42,8 @@ struct RowAttnParams {
     const int32_t *start_pos;   // prefill: [B] position of query row 0
     float *ws_o;                // [B*Sq, H, max_splits, d] partial outputs (unnormalised)
     float *ws_ml;               // [B*Sq, H, max_splits, 2] partial (max, sum) in log2 units
-    int32_t *counters;          // [B*Sq, K] finished-split counters
+    unsigned long long *counters; // [B*Sq, K] finished-split counters: (epoch << 32) | count
+    uint32_t epoch;             // tag of this call (see plan in api.hip)
     int32_t B;
     int32_t Sq;                 // query rows per sequence
     int32_t H;

@@ -29,8 +29,9 @@
 //    exp2 of a score minus any reference <= the true max is exact algebra,
 //    the final o / l cancels the reference.
 //  * The last workgroup of a (row, group) to finish merges the splits (an
-//    atomic counter per (row, group) in the workspace), so a decode step is
-//    one kernel launch.
+//    atomic counter per (row, group) in the workspace, tagged with the call's
+//    epoch so no clearing pass is needed), so a decode step is one kernel
+//    launch.
 #include "common.h"
 #include "kernels.h"
 
@@ -367,10 +368,21 @@ __global__ __launch_bounds__(NT) void row_attention_kernel(RowAttnParams p)
     }
     __threadfence();
     __syncthreads();
-    int32_t *counter = p.counters + rc.rowseq * K + g;
+    // Count finished splits.  The counter word carries this call's epoch in
+    // its upper half, so whatever an earlier call left in the word (another
+    // layout's partials included) reads as "no split finished yet".
+    unsigned long long *counter = p.counters + rc.rowseq * K + g;
     if (tid == 0) {
-        const int done = atomicAdd(counter, 1);
-        lds_flag = (done == n_splits - 1);
+        const unsigned long long tag = (unsigned long long)p.epoch << 32;
+        unsigned long long cur = *reinterpret_cast<volatile unsigned long long *>(counter);
+        unsigned long long next;
+        while (true) {
+            next = ((cur >> 32) == p.epoch) ? cur + 1 : (tag | 1ull);
+            const unsigned long long prev = atomicCAS(counter, cur, next);
+            if (prev == cur) break;
+            cur = prev;
+        }
+        lds_flag = ((uint32_t)next == (uint32_t)n_splits);
     }
     __syncthreads();
     if (!lds_flag) return;
@@ -403,7 +415,7 @@ __global__ __launch_bounds__(NT) void row_attention_kernel(RowAttnParams p)
                 make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
         }
     }
-    if (tid == 0) atomicExch(counter, 0);   // ready for the next call
+    if (tid == 0) atomicExch(counter, 0ull);   // leave the word clear
 }
 
 template <int D, bool BF16>

@@ -131,9 +131,11 @@ size_t gqa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_h
  * §10.2); every split keeps an online-softmax state (§9.2.1) and the splits of
  * one (sequence, KV head) are merged with their global max and sum.  One
  * K/V row read from memory serves all G heads of its group.
- * workspace: device buffer of at least gqa_decode_workspace_bytes(...) bytes.
- * It MUST be zero-filled before its first use; every completed call leaves it
- * ready for the next one.  Calls that may run concurrently need separate
+ * workspace: device buffer of at least gqa_decode_workspace_bytes(...) bytes
+ * (may be NULL when that is 0).  Zero-fill a new workspace once; after that it
+ * can be reused by any sequence of calls, with any sizes, one call at a time:
+ * the split counters it holds are tagged with a per-call epoch and cleared by
+ * the call that finishes them.  Calls that may run concurrently need separate
  * workspaces.
  */
 gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *ctx_lens,

@@ -75,8 +75,9 @@ class DecodeRun:
         self.cache = binding.KVCache(self.k, self.v, self.bt)
         self.max_ctx = int(inp.ctx.max())
 
-    def run(self, out=None) -> torch.Tensor:
-        out = binding.gqa_decode(self.q, self.cache, self.ctx, self.max_ctx, out=out, scale=self.inp.wl.scale)
+    def run(self, out=None, workspace=None) -> torch.Tensor:
+        out = binding.gqa_decode(self.q, self.cache, self.ctx, self.max_ctx, out=out, scale=self.inp.wl.scale,
+                                 workspace=workspace)
         torch.cuda.synchronize()
         return out
 

@@ -125,6 +125,19 @@ def test_decode_split_size_invariance(split, monkeypatch):
     check_close(gpu_rows(other, rows, "bf16"), want, BF16_TOL, f"split {split} vs oracle")
 
 
+def test_decode_workspace_reused_across_layouts():
+    """One workspace serves calls whose split layouts overlap each other's bytes."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    a = W.make_decode(W.WORKLOADS["llama2_70b_decode"].replace(B=2, ctx=("fixed", 3000)))
+    b = W.make_decode(W.WORKLOADS["llama3_8b_decode"].replace(B=8, ctx=("uniform", 300, 1300)))
+    c = W.make_decode(W.WORKLOADS["llama2_70b_decode_mqa"].replace(B=3, ctx=("uniform", 900, 5000)))
+    for inp, what in ((a, "A"), (b, "B"), (c, "C"), (a, "A again"), (b, "B again")):
+        say("workspace reuse", what)
+        out = from_dev(DecodeRun(inp).run(workspace=ws))
+        rows, want = oracle_decode_rows(inp)
+        check_close(gpu_rows(out, rows, "bf16"), want, BF16_TOL, f"workspace reuse {what}")
+
+
 # full-size workloads, sampled rows -------------------------------------------
 
 def _sample_seqs(inp, n=6):
