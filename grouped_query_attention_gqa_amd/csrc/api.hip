@@ -4,7 +4,6 @@
 #include "../../include/gqa.h"
 
 #include <algorithm>
-#include <atomic>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
@@ -29,17 +28,21 @@ static int env_int(const char *name, int dflt)
     return std::atoi(s);
 }
 
-// Keys per decode split.  Aim at ~2048 workgroups (8 per CU on 256 CUs) for
-// the largest row, with splits of at least 256 keys so each workgroup streams
-// enough bytes to hide its start-up; GQA_DECODE_SPLIT_TOKENS overrides.
+// Keys per decode split.  A split is one workgroup's stream of 64-key tiles;
+// longer splits amortise the workgroup's start-up (q load, pipeline fill,
+// partial write) and shorter ones give more workgroups.  Measured on MI355X:
+// about 512 workgroups for the longest row, splits clamped to [256, 2048]
+// keys, is best for the Llama-shaped decodes (ragged and paged included,
+// where max_ctx overstates the work).  GQA_DECODE_SPLIT_TOKENS overrides.
 int32_t plan_decode_split(int32_t B, int32_t K, int32_t max_ctx)
 {
     const int over = env_int("GQA_DECODE_SPLIT_TOKENS", 0);
     if (over > 0) return (int32_t)(((int64_t)over + kKeyTile - 1) / kKeyTile * kKeyTile);
-    const int64_t target_wg = 2048;
+    const int64_t target_wg = 512;
     int64_t split = ((int64_t)B * K * max_ctx + target_wg - 1) / target_wg;
     split = (split + kKeyTile - 1) / kKeyTile * kKeyTile;
     if (split < 256) split = 256;
+    if (split > 2048) split = 2048;
     const int64_t whole = ((int64_t)max_ctx + kKeyTile - 1) / kKeyTile * kKeyTile;
     if (split > whole) split = whole < kKeyTile ? kKeyTile : whole;
     return (int32_t)split;
@@ -153,19 +156,9 @@ gqa_status check_positions(const CacheView &v, const std::vector<int32_t> &lo,
     return GQA_OK;
 }
 
-// Epoch of a decode call: the upper half of every split counter it touches.
-// 0x7F8xxxxx with a non-zero payload is a signalling-NaN bit pattern, which
-// the kernels never store (their partial results are computed values), so a
-// counter word left over from partial data can never carry a live epoch.
-uint32_t next_epoch()
-{
-    static std::atomic<uint32_t> calls{0};
-    return 0x7F800000u | (1u + calls.fetch_add(1, std::memory_order_relaxed) % 0x7FFFFEu);
-}
-
 struct DecodeLayout {
     int32_t split = 0, max_splits = 0;
-    size_t o_bytes = 0, ml_bytes = 0, cnt_bytes = 0, total = 0;
+    size_t o_bytes = 0, ml_bytes = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -179,10 +172,9 @@ bool decode_layout(int64_t rows, int32_t H, int32_t K, int32_t d, int32_t max_ct
         L->max_splits = 1;
         return true;   // one split per row: no workspace needed
     }
-    L->cnt_bytes = align256((size_t)rows * K * sizeof(unsigned long long));
     L->o_bytes = align256((size_t)rows * H * L->max_splits * d * sizeof(float));
     L->ml_bytes = align256((size_t)rows * H * L->max_splits * 2 * sizeof(float));
-    L->total = L->cnt_bytes + L->o_bytes + L->ml_bytes;
+    L->total = L->o_bytes + L->ml_bytes;
     return true;
 }
 
@@ -280,11 +272,9 @@ gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *c
     p.ctx_lens = ctx_lens;
     char *ws = static_cast<char *>(workspace);
     if (L.total > 0) {
-        p.counters = reinterpret_cast<unsigned long long *>(ws);
-        p.ws_o = reinterpret_cast<float *>(ws + L.cnt_bytes);
-        p.ws_ml = reinterpret_cast<float *>(ws + L.cnt_bytes + L.o_bytes);
+        p.ws_o = reinterpret_cast<float *>(ws);
+        p.ws_ml = reinterpret_cast<float *>(ws + L.o_bytes);
     }
-    p.epoch = next_epoch();
     p.B = B;
     p.Sq = 1;
     p.H = num_heads;

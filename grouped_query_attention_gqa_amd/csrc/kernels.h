@@ -42,8 +42,6 @@ struct RowAttnParams {
     const int32_t *start_pos;   // prefill: [B] position of query row 0
     float *ws_o;                // [B*Sq, H, max_splits, d] partial outputs (unnormalised)
     float *ws_ml;               // [B*Sq, H, max_splits, 2] partial (max, sum) in log2 units
-    unsigned long long *counters; // [B*Sq, K] finished-split counters: (epoch << 32) | count
-    uint32_t epoch;             // tag of this call (see plan in api.hip)
     int32_t B;
     int32_t Sq;                 // query rows per sequence
     int32_t H;
@@ -75,6 +73,21 @@ __device__ __forceinline__ int64_t cache_row(const CacheView &c, int b, int g, i
 {
     if (c.block_table == nullptr) return ((int64_t)b * c.K + g) * c.S_max + pos;
     const int32_t blk = c.block_table[(int64_t)b * c.max_blocks + (pos >> c.log2_bs)];
+    if (blk < 0 || blk >= c.num_blocks) return -1;
+    return (((int64_t)blk * c.K + g) << c.log2_bs) + (pos & ((1 << c.log2_bs) - 1));
+}
+
+// The same lookup for loads where all active lanes of a wave ask for
+// positions inside one 16-aligned group of 16 tokens.  With blocks of 16 or
+// more tokens that group lies in one block, so one wave-uniform table read (a
+// scalar load, which does not wait behind the wave's outstanding vector
+// loads) serves the whole wave.
+__device__ __forceinline__ int64_t cache_row_wave(const CacheView &c, int b, int g, int pos)
+{
+    if (c.block_table == nullptr) return ((int64_t)b * c.K + g) * c.S_max + pos;
+    if (c.log2_bs < 4) return cache_row(c, b, g, pos);
+    const int lead = __builtin_amdgcn_readfirstlane(pos);
+    const int32_t blk = c.block_table[(int64_t)b * c.max_blocks + (lead >> c.log2_bs)];
     if (blk < 0 || blk >= c.num_blocks) return -1;
     return (((int64_t)blk * c.K + g) << c.log2_bs) + (pos & ((1 << c.log2_bs) - 1));
 }

@@ -125,7 +125,8 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
             const int key = pidx / C::CPR, ch = pidx % C::CPR;
             kreg[li] = make_uint4(0, 0, 0, 0);
             if (j0 + key < kv_len) {
-                const int64_t row = cache_row(cache, b, g, j0 + key);
+                // a wave's 64 / CPR keys lie in one 16-key group of the tile
+                const int64_t row = cache_row_wave(cache, b, g, j0 + key);
                 if (row >= 0) kreg[li] = ld16(cache.k + row * (D * 2) + ch * 16);
             }
         }
@@ -134,7 +135,8 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
             const int key = v_kq * C::KPT_V + k;
             vreg[k] = make_uint4(0, 0, 0, 0);
             if (j0 + key < kv_len) {
-                const int64_t row = cache_row(cache, b, g, j0 + key);
+                // a wave covers keys 16w .. 16w+15 of the tile
+                const int64_t row = cache_row_wave(cache, b, g, j0 + key);
                 if (row >= 0) vreg[k] = ld16(cache.v + row * (D * 2) + v_c * 16);
             }
         }

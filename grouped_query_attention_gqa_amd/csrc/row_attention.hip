@@ -28,10 +28,10 @@
 //    more than 2^8 (in exp2 units), so the accumulators are rescaled rarely;
 //    exp2 of a score minus any reference <= the true max is exact algebra,
 //    the final o / l cancels the reference.
-//  * The last workgroup of a (row, group) to finish merges the splits (an
-//    atomic counter per (row, group) in the workspace, tagged with the call's
-//    epoch so no clearing pass is needed), so a decode step is one kernel
-//    launch.
+//  * A row whose keys fit one split is normalised and stored by its single
+//    workgroup; otherwise every split stores (m, l, o) in the workspace and a
+//    small second kernel merges them (a kernel boundary orders the stores
+//    without any cache-flushing fence inside the hot kernel).
 #include "common.h"
 #include "kernels.h"
 
@@ -110,7 +110,6 @@ __global__ __launch_bounds__(NT) void row_attention_kernel(RowAttnParams p)
     __shared__ float lds_alpha[GP];
     __shared__ float lds_m[GP];
     __shared__ float lds_l[GP];
-    __shared__ int lds_flag;
 
     uint4 *Ks = reinterpret_cast<uint4 *>(lds_kv);
     uint4 *Vs = reinterpret_cast<uint4 *>(lds_kv + C::KV_BYTES);
@@ -181,7 +180,8 @@ __global__ __launch_bounds__(NT) void row_attention_kernel(RowAttnParams p)
             kreg[li] = make_uint4(0, 0, 0, 0);
             vreg[li] = make_uint4(0, 0, 0, 0);
             if (t < nvalid) {
-                const int64_t row = cache_row(cache, rc.b, g, tile0 + t);
+                // a wave's 64 / CPR rows lie in one 16-row group of the tile
+                const int64_t row = cache_row_wave(cache, rc.b, g, tile0 + t);
                 if (row >= 0) {
                     const int64_t off = row * C::RB + pc * 16;
                     kreg[li] = ld16(cache.k + off);
@@ -353,7 +353,8 @@ __global__ __launch_bounds__(NT) void row_attention_kernel(RowAttnParams p)
         return;
     }
 
-    // ---- several splits: publish the partial state -------------------------
+    // ---- several splits: publish the partial state; the merge kernel below
+    // combines them once every split of the launch has finished -------------
     const int64_t head0 = rc.rowseq * H + (int64_t)g * G;
     for (int idx = tid; idx < G * D; idx += NT) {
         const int r = idx / D, col = idx % D;
@@ -366,30 +367,22 @@ __global__ __launch_bounds__(NT) void row_attention_kernel(RowAttnParams p)
         p.ws_ml[((head0 + tid) * p.max_splits + split_idx) * 2 + 0] = lds_m[tid];
         p.ws_ml[((head0 + tid) * p.max_splits + split_idx) * 2 + 1] = lds_l[tid];
     }
-    __threadfence();
-    __syncthreads();
-    // Count finished splits.  The counter word carries this call's epoch in
-    // its upper half, so whatever an earlier call left in the word (another
-    // layout's partials included) reads as "no split finished yet".
-    unsigned long long *counter = p.counters + rc.rowseq * K + g;
-    if (tid == 0) {
-        const unsigned long long tag = (unsigned long long)p.epoch << 32;
-        unsigned long long cur = *reinterpret_cast<volatile unsigned long long *>(counter);
-        unsigned long long next;
-        while (true) {
-            next = ((cur >> 32) == p.epoch) ? cur + 1 : (tag | 1ull);
-            const unsigned long long prev = atomicCAS(counter, cur, next);
-            if (prev == cur) break;
-            cur = prev;
-        }
-        lds_flag = ((uint32_t)next == (uint32_t)n_splits);
-    }
-    __syncthreads();
-    if (!lds_flag) return;
-    __threadfence();
+}
 
-    // ---- last split to finish: merge with the global max and sum ----------
-    for (int idx = tid; idx < G * D / 4; idx += NT) {
+// Merge of the split partials of one (row, KV group) with their global max
+// and sum: M = max_s m_s, L = sum_s l_s 2^(m_s - M),
+// out = sum_s o_s 2^(m_s - M) / L (m in log2 units).  Rows that fit one split
+// were finished by the split kernel and are skipped.
+template <int D, bool BF16>
+__global__ __launch_bounds__(NT) void merge_splits_kernel(RowAttnParams p)
+{
+    const int g = blockIdx.x;
+    const RowCtx rc = row_context(p, blockIdx.y);
+    const int n_splits = (rc.n_vis + p.split - 1) / p.split;
+    if (n_splits <= 1) return;
+    const int G = p.G;
+    const int64_t head0 = rc.rowseq * p.H + (int64_t)g * G;
+    for (int idx = threadIdx.x; idx < G * D / 4; idx += NT) {
         const int r = (4 * idx) / D, col = (4 * idx) % D;
         const float *ml = p.ws_ml + (head0 + r) * p.max_splits * 2;
         float M = -INFINITY;
@@ -399,11 +392,11 @@ __global__ __launch_bounds__(NT) void row_attention_kernel(RowAttnParams p)
         for (int sp = 0; sp < n_splits; ++sp) {
             const float w = fast_exp2(ml[2 * sp] - M);
             L += ml[2 * sp + 1] * w;
-            const float *os = p.ws_o + ((head0 + r) * p.max_splits + sp) * D + col;
-            O.x += os[0] * w;
-            O.y += os[1] * w;
-            O.z += os[2] * w;
-            O.w += os[3] * w;
+            const float4 os = *reinterpret_cast<const float4 *>(p.ws_o + ((head0 + r) * p.max_splits + sp) * D + col);
+            O.x += os.x * w;
+            O.y += os.y * w;
+            O.z += os.z * w;
+            O.w += os.w * w;
         }
         const float inv = 1.f / L;
         const int64_t o = (head0 + r) * D + col;
@@ -415,7 +408,6 @@ __global__ __launch_bounds__(NT) void row_attention_kernel(RowAttnParams p)
                 make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
         }
     }
-    if (tid == 0) atomicExch(counter, 0ull);   // leave the word clear
 }
 
 template <int D, bool BF16>
@@ -431,6 +423,9 @@ hipError_t launch_d(const RowAttnParams &p, int gp, dim3 grid, hipStream_t s)
     case 64: hipLaunchKernelGGL((row_attention_kernel<D, 64, BF16>), grid, dim3(NT), 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.max_splits <= 1) return e;
+    hipLaunchKernelGGL((merge_splits_kernel<D, BF16>), dim3(grid.y, grid.z), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
 

@@ -132,11 +132,10 @@ size_t gqa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_h
  * one (sequence, KV head) are merged with their global max and sum.  One
  * K/V row read from memory serves all G heads of its group.
  * workspace: device buffer of at least gqa_decode_workspace_bytes(...) bytes
- * (may be NULL when that is 0).  Zero-fill a new workspace once; after that it
- * can be reused by any sequence of calls, with any sizes, one call at a time:
- * the split counters it holds are tagged with a per-call epoch and cleared by
- * the call that finishes them.  Calls that may run concurrently need separate
- * workspaces.
+ * (may be NULL when that is 0) for the per-split partial results; it needs no
+ * initialisation.  When a row needs several splits a second, small kernel
+ * merges them on the same stream.  Calls that may run concurrently need
+ * separate workspaces.
  */
 gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *ctx_lens,
                       int32_t max_ctx, int32_t B, int32_t num_heads, float scale, void *out,

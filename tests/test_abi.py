@@ -50,11 +50,11 @@ def test_cache_elems_per_token(lib, K, d, expect):
 
 
 def test_workspace_plan(lib):
-    # Llama-2-70B decode shape: 512-key splits, 16 per 8192-token row
+    # Llama-2-70B decode shape: 2048-key splits, 4 per 8192-token row
     n = binding.gqa_decode_workspace_bytes(16, 64, 8, 128, 8192)
-    per = 16 * 64 * 16
+    per = 16 * 64 * 4
     align = lambda x: (x + 255) // 256 * 256
-    assert n == align(16 * 8 * 8) + align(per * 128 * 4) + align(per * 2 * 4)
+    assert n == align(per * 128 * 4) + align(per * 2 * 4)
     # a 128-token row fits one split: no workspace at all
     assert binding.gqa_decode_workspace_bytes(1, 8, 2, 64, 128) == 0
     assert binding.gqa_decode_workspace_bytes(1, 8, 3, 64, 128) == 0   # H % K != 0 -> 0
