@@ -21,33 +21,6 @@ int32_t pow2_at_least(int32_t g)
     return p;
 }
 
-static int env_int(const char *name, int dflt)
-{
-    const char *s = std::getenv(name);
-    if (!s || !*s) return dflt;
-    return std::atoi(s);
-}
-
-// Keys per decode split.  A split is one workgroup's stream of 64-key tiles;
-// longer splits amortise the workgroup's start-up (q load, pipeline fill,
-// partial write) and shorter ones give more workgroups.  Measured on MI355X:
-// about 512 workgroups for the longest row, splits clamped to [256, 2048]
-// keys, is best for the Llama-shaped decodes (ragged and paged included,
-// where max_ctx overstates the work).  GQA_DECODE_SPLIT_TOKENS overrides.
-int32_t plan_decode_split(int32_t B, int32_t K, int32_t max_ctx)
-{
-    const int over = env_int("GQA_DECODE_SPLIT_TOKENS", 0);
-    if (over > 0) return (int32_t)(((int64_t)over + kKeyTile - 1) / kKeyTile * kKeyTile);
-    const int64_t target_wg = 512;
-    int64_t split = ((int64_t)B * K * max_ctx + target_wg - 1) / target_wg;
-    split = (split + kKeyTile - 1) / kKeyTile * kKeyTile;
-    if (split < 256) split = 256;
-    if (split > 2048) split = 2048;
-    const int64_t whole = ((int64_t)max_ctx + kKeyTile - 1) / kKeyTile * kKeyTile;
-    if (split > whole) split = whole < kKeyTile ? kKeyTile : whole;
-    return (int32_t)split;
-}
-
 }  // namespace gqa
 
 using namespace gqa;
@@ -156,26 +129,20 @@ gqa_status check_positions(const CacheView &v, const std::vector<int32_t> &lo,
     return GQA_OK;
 }
 
+// Decode workspace: the launch's tile prefix (read by the merge kernel) and
+// two partial-result slots per workgroup.
 struct DecodeLayout {
-    int32_t split = 0, max_splits = 0;
-    size_t o_bytes = 0, ml_bytes = 0, total = 0;
+    size_t prefix_bytes = 0, o_bytes = 0, ml_bytes = 0, total = 0;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-bool decode_layout(int64_t rows, int32_t H, int32_t K, int32_t d, int32_t max_ctx, DecodeLayout *L)
+void decode_layout(int32_t G, int32_t d, DecodeLayout *L)
 {
-    if (rows <= 0 || H <= 0 || K <= 0 || d <= 0 || max_ctx <= 0) return false;
-    L->split = plan_decode_split((int32_t)(rows > 0x7fffffff ? 0x7fffffff : rows), K, max_ctx);
-    L->max_splits = (int32_t)(((int64_t)max_ctx + L->split - 1) / L->split);
-    if (L->max_splits <= 1) {
-        L->max_splits = 1;
-        return true;   // one split per row: no workspace needed
-    }
-    L->o_bytes = align256((size_t)rows * H * L->max_splits * d * sizeof(float));
-    L->ml_bytes = align256((size_t)rows * H * L->max_splits * 2 * sizeof(float));
-    L->total = L->o_bytes + L->ml_bytes;
-    return true;
+    L->prefix_bytes = align256((size_t)(kStreamRows + 1) * sizeof(int32_t));
+    L->o_bytes = align256((size_t)kStreamWGs * 2 * G * d * sizeof(float));
+    L->ml_bytes = align256((size_t)kStreamWGs * 2 * G * 2 * sizeof(float));
+    L->total = L->prefix_bytes + L->o_bytes + L->ml_bytes;
 }
 
 }  // namespace
@@ -207,9 +174,10 @@ int32_t gqa_cache_elems_per_token(int32_t num_kv_heads, int32_t head_dim)
 size_t gqa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_ctx)
 {
-    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return 0;
+    if (B <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_ctx <= 0) return 0;
+    if (num_heads % num_kv_heads != 0) return 0;
     DecodeLayout L;
-    if (!decode_layout(B, num_heads, num_kv_heads, head_dim, max_ctx, &L)) return 0;
+    decode_layout(num_heads / num_kv_heads, head_dim, &L);
     return L.total;
 }
 
@@ -249,13 +217,12 @@ gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *c
     if ((st = check_heads(num_heads, v.K)) != GQA_OK) return st;
     if (B < 0) return fail(GQA_ERR_INVALID_ARG, "B negative");
     if (B == 0) return GQA_OK;
-    if (B > 65535) return fail(GQA_ERR_UNSUPPORTED, "B above 65535");
     if (!q || !out || !ctx_lens) return fail(GQA_ERR_INVALID_ARG, "NULL q/out/ctx_lens");
     if (max_ctx <= 0) return fail(GQA_ERR_INVALID_ARG, "max_ctx <= 0");
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
     DecodeLayout L;
-    if (!decode_layout(B, num_heads, v.K, v.d, max_ctx, &L)) return fail(GQA_ERR_INVALID_ARG, "bad sizes");
-    if (L.total > 0 && (!workspace || workspace_bytes < L.total))
+    decode_layout(num_heads / v.K, v.d, &L);
+    if (!workspace || workspace_bytes < L.total)
         return fail(GQA_ERR_WORKSPACE, "workspace smaller than gqa_decode_workspace_bytes()");
     if (check_mode()) {
         std::vector<int32_t> cl;
@@ -271,18 +238,18 @@ gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *c
     p.out = static_cast<char *>(out);
     p.ctx_lens = ctx_lens;
     char *ws = static_cast<char *>(workspace);
-    if (L.total > 0) {
-        p.ws_o = reinterpret_cast<float *>(ws);
-        p.ws_ml = reinterpret_cast<float *>(ws + L.o_bytes);
-    }
+    p.prefix = reinterpret_cast<int32_t *>(ws);
+    p.ws_o = reinterpret_cast<float *>(ws + L.prefix_bytes);
+    p.ws_ml = reinterpret_cast<float *>(ws + L.prefix_bytes + L.o_bytes);
+    p.total_rows = B;
     p.B = B;
     p.Sq = 1;
     p.H = num_heads;
     p.G = num_heads / v.K;
     p.prefill = 0;
     p.causal = 0;
-    p.split = L.split;
-    p.max_splits = L.max_splits;
+    p.whole_items = 0;
+    p.num_wgs = kStreamWGs;
     p.scale_log2 = scale * 1.4426950408889634f;
     return launch_status(launch_row_attention(p, pow2_at_least(p.G), static_cast<hipStream_t>(stream)),
                          "decode");
@@ -301,7 +268,6 @@ gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
     if (!q || !k_new || !v_new || !start_pos || !out) return fail(GQA_ERR_INVALID_ARG, "NULL pointer");
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
     const bool bf16 = v.elem_bytes == 2;
-    if (!bf16 && (int64_t)B * s > 65535) return fail(GQA_ERR_UNSUPPORTED, "fp32 prefill limited to B*s <= 65535 rows");
     if (check_mode()) {
         std::vector<int32_t> sp;
         if (!fetch_i32(start_pos, B, sp)) return fail(GQA_ERR_LAUNCH, "start_pos copy failed");
@@ -342,15 +308,15 @@ gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
     p.q = static_cast<const char *>(q);
     p.out = static_cast<char *>(out);
     p.start_pos = start_pos;
+    p.total_rows = (int64_t)B * s;
     p.B = B;
     p.Sq = s;
     p.H = num_heads;
     p.G = num_heads / v.K;
     p.prefill = 1;
     p.causal = causal != 0;
-    p.max_splits = 1;   // one workgroup walks a row's whole key range
-    p.split = (int32_t)std::min<int64_t>(((int64_t)v.capacity + kKeyTile - 1) / kKeyTile * kKeyTile,
-                                         0x7fffffc0LL);
+    p.whole_items = 1;   // no workspace here: every item stays in one workgroup
+    p.num_wgs = kStreamWGs;
     p.scale_log2 = scale_log2;
     return launch_status(launch_row_attention(p, pow2_at_least(p.G), hs), "prefill (fp32)");
 }

@@ -48,22 +48,33 @@ __device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Butterfly reductions over aligned groups of `width` lanes (width a power of
-// two <= 64).  Every lane of a group ends with the same value.
-template <int width>
-__device__ __forceinline__ float group_max(float x)
+// All-reduce over aligned groups of `width` lanes (width a power of two <=
+// 64); every lane of a group ends with the group's result.  Within a 16-lane
+// row the steps are DPP lane permutations fused into the max/add (quad swaps,
+// half-row mirror, row mirror: after each step the value is uniform over the
+// lanes combined so far, so a mirror pairs complete sub-groups); only the
+// steps across rows go through ds_bpermute.
+template <int ctrl>
+__device__ __forceinline__ float dpp_f32(float x)
 {
-#pragma unroll
-    for (int m = width / 2; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
+}
+template <int width, bool is_max>
+__device__ __forceinline__ float group_reduce(float x)
+{
+    auto op = [](float a, float b) { return is_max ? fmaxf(a, b) : a + b; };
+    if constexpr (width >= 2) x = op(x, dpp_f32<0xB1>(x));    // quad_perm [1,0,3,2]
+    if constexpr (width >= 4) x = op(x, dpp_f32<0x4E>(x));    // quad_perm [2,3,0,1]
+    if constexpr (width >= 8) x = op(x, dpp_f32<0x141>(x));   // row_half_mirror
+    if constexpr (width >= 16) x = op(x, dpp_f32<0x140>(x));  // row_mirror
+    if constexpr (width >= 32) x = op(x, __shfl_xor(x, 16, kWave));
+    if constexpr (width >= 64) x = op(x, __shfl_xor(x, 32, kWave));
     return x;
 }
 template <int width>
-__device__ __forceinline__ float group_sum(float x)
-{
-#pragma unroll
-    for (int m = width / 2; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
-    return x;
-}
+__device__ __forceinline__ float group_max(float x) { return group_reduce<width, true>(x); }
+template <int width>
+__device__ __forceinline__ float group_sum(float x) { return group_reduce<width, false>(x); }
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }

@@ -34,22 +34,29 @@ struct AppendParams {
 
 // Row-wise attention on the vector ALUs: decode (one query row per
 // sequence, keys [0, ctx)) and the fp32 prefill (s rows per sequence).
+constexpr int kStreamRows = 512;    // rows per launch (row tables in LDS)
+constexpr int kStreamWGs = 512;     // workgroups per launch: two per MI355X CU
+
 struct RowAttnParams {
     CacheView cache;
     const char *q;              // [B, Sq, H, d]
     char *out;                  // [B, Sq, H, d]
     const int32_t *ctx_lens;    // decode: [B] keys per sequence
     const int32_t *start_pos;   // prefill: [B] position of query row 0
-    float *ws_o;                // [B*Sq, H, max_splits, d] partial outputs (unnormalised)
-    float *ws_ml;               // [B*Sq, H, max_splits, 2] partial (max, sum) in log2 units
+    int32_t *prefix;            // workspace: [kStreamRows + 1] tile prefix of the launch
+    float *ws_o;                // workspace: [W, 2, G, d] partial outputs (unnormalised)
+    float *ws_ml;               // workspace: [W, 2, G, 2] partial (max, sum), log2 units
+    int64_t total_rows;         // B * Sq
+    int64_t row0;               // first row of this launch
+    int32_t rows;               // rows of this launch
     int32_t B;
     int32_t Sq;                 // query rows per sequence
     int32_t H;
     int32_t G;                  // H / K
     int32_t prefill;            // 0: decode rows; 1: prefill rows
     int32_t causal;
-    int32_t split;              // keys per split (multiple of the key tile)
-    int32_t max_splits;
+    int32_t whole_items;        // 1: slices snap to item starts (no partial pieces, no workspace)
+    int32_t num_wgs;            // W
     float scale_log2;           // softmax scale * log2(e)
 };
 
@@ -96,9 +103,7 @@ hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_row_attention(const RowAttnParams &p, int gp, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams &p, hipStream_t stream);
 
-// Decode split planning (host-only, deterministic).
-constexpr int kKeyTile = 64;
-int32_t plan_decode_split(int32_t B, int32_t K, int32_t max_ctx);
+constexpr int kKeyTile = 64;   // prefill key tile
 int32_t pow2_at_least(int32_t g);
 
 }  // namespace gqa

@@ -1,0 +1,690 @@
+// stream_attention.hip -- grouped-query attention of single query rows on the
+// vector ALUs: the decode step (memory-bound) and the fp32 prefill.
+//
+// What it computes ("Grouped-Query Attention" concept page, 技术原理 steps 2-4):
+// for every query row and every KV group g, the G query heads g*G .. g*G+G-1
+// attend to K/V head g with softmax(q K_g^T * scale) V_g over the row's
+// visible keys.
+//
+// How (designed for CDNA4; flash-decoding on the inference-optimisation page
+// §10.2-§10.3 is prior art, not the blueprint):
+//  * Work list.  Every (query row, KV group) item is cut into tiles of 8 KB
+//    of K (32 keys at d = 128 in bf16); the tiles of all items form one flat
+//    list and each of the W workgroups (two per CU) takes an equal contiguous
+//    slice of it.  Ragged and paged contexts are
+//    balanced exactly, and no workgroup starts just to find nothing to do.
+//  * Memory pipeline.  K, V (and the item's q rows) of the next three tiles
+//    are in flight as LDS-direct loads (global_load_lds_dwordx4: HBM -> LDS
+//    without registers) while the current tile is used; the loads of one
+//    tile are waited for with an explicit vmcnt, so the pipeline also runs
+//    across item boundaries.  Every K and V row is read from HBM once and
+//    then serves all G heads of its group from LDS (the group broadcast).
+//  * Scores: thread (head r, key t) computes the full dot product of its
+//    register-resident q row with the K row from LDS (v_dot2_f32_bf16: two
+//    bf16 products per instruction into fp32).  K rows are XOR-swizzled in LDS
+//    so 16 lanes reading 16 rows hit 16 bank groups.
+//  * Online softmax per item (inference-optimisation page §9.2.1), in exp2
+//    units; the reference maximum only moves when a tile maximum exceeds it
+//    by 2^8, so the accumulators are rarely rescaled (the final o / l
+//    cancels the reference).
+//  * Weighted V sum: wave w owns column pieces w*CPW .. (w+1)*CPW-1 of all G
+//    heads; a lane holds fp32 accumulators for up to 8 heads x 8 columns and
+//    two keys at a time are paired (v_perm) so one v_dot2 adds
+//    p_t v_t + p_t+1 v_t+1.  Key groups are reduced with lane shuffles.
+//  * An item whose tiles all fall in one workgroup is normalised and stored
+//    there; an item cut by slice boundaries leaves one partial (m, l, o) per
+//    workgroup and merge_pieces_kernel combines them with their global max
+//    and sum (page §10.2) after the main kernel.
+#include <utility>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace gqa {
+namespace {
+
+constexpr int NT = 256;            // threads per workgroup (4 waves); two workgroups per CU
+constexpr int NW = NT / kWave;     // waves per workgroup
+constexpr float TAU = 8.0f;        // lazy-rescale threshold (log2 units)
+constexpr int LDS_LIMIT = 80 * 1024;   // half of a CU's 160 KB: two workgroups per CU
+constexpr int K_TILE_BYTES = 8192; // bytes of K (and of V) per tile
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef const __attribute__((address_space(1))) void gbl_void_t;
+
+// 16 zero bytes: the source of LDS-direct loads for rows past the end of an
+// item and for padded heads.
+__device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
+
+// One LDS-direct 16-byte load per lane: lane i's bytes land at
+// lds_wave_base + 16 i.  Written as inline assembly so that the compiler does
+// not track these loads: it would otherwise wait for every one in flight
+// before each LDS read.  The kernel waits for them itself (wait_tiles).
+__device__ __forceinline__ void dma16(const void *src, void *lds_wave_base)
+{
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t *)lds_wave_base;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Wait until at most n_after tiles of L loads each are in flight.  Loads
+// return in issue order, so the tile issued before them has landed.
+template <int L>
+__device__ __forceinline__ void wait_tiles(int n_after)
+{
+    switch (n_after) {
+    case 0: wait_vm<0>(); break;
+    case 1: wait_vm<L>(); break;
+    default: wait_vm<2 * L>(); break;
+    }
+}
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
+
+// Workgroup barrier without the memory fence of __syncthreads() (that fence
+// would wait for every LDS-direct load in flight).  LDS stores are completed
+// first; the empty asm statements keep the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void barrier()
+{
+    wait_lds();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int D, int GP, bool BF16>
+struct Cfg {
+    static constexpr int ES = BF16 ? 2 : 4;           // element bytes
+    static constexpr int RB = D * ES;                 // row bytes
+    static constexpr int CPR = RB / 16;               // 16-byte pieces per row
+    static constexpr int CE = 16 / ES;                // elements per piece
+    static constexpr int TT = K_TILE_BYTES / RB;      // keys per tile
+    static constexpr int RPK = 1024 / RB;             // rows per 1 KB load block
+    static constexpr int LK = TT * RB / 1024 / NW;    // LDS-direct loads per wave per tile, each of K and V
+    static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
+    static constexpr int Q_BYTES = GP * RB;
+    static constexpr int QN = (Q_BYTES + 1023) / 1024; // 1 KB q loads per tile
+    static constexpr int Q_SLOT = QN * 1024;
+    static constexpr int K_BYTES = TT * RB;
+    static constexpr int STAGE = 2 * K_BYTES + Q_SLOT;
+    // score phase
+    static constexpr int TPH0 = (NT / GP) < kWave ? (NT / GP) : kWave;
+    static constexpr int TPH = TPH0 < TT ? TPH0 : TT;  // threads per head
+    static constexpr int NS = TT / TPH;                // keys per score thread
+    static constexpr int S_THREADS = GP * TPH;
+    static constexpr int QW = RB / 4;                  // 32-bit words of a q row
+    // weighted-sum phase
+    static constexpr int CPW = CPR / NW;               // column pieces per wave
+    static constexpr int HPT = GP < 8 ? GP : 8;        // heads per lane
+    static constexpr int HG = GP / HPT;                // head sets
+    static constexpr int TGL = kWave / (CPW * HG);     // key groups per wave
+    static constexpr int TPT = TT / TGL;               // keys per lane per tile
+    // LDS
+    static constexpr int P_BYTES = TT * GP * (BF16 ? 2 : 4);
+    static constexpr int OTHER = P_BYTES + 3 * GP * 4 + (2 * kStreamRows + 1) * 4 + NW * 4 + 256;
+    // two workgroups per CU when two stages fit in half the LDS, else one
+    static constexpr int LIMIT = (LDS_LIMIT - OTHER) / STAGE >= 2 ? LDS_LIMIT : 2 * LDS_LIMIT;
+    static constexpr int NBUF0 = (LIMIT - OTHER) / STAGE;
+    static constexpr int NBUF = NBUF0 > 4 ? 4 : NBUF0;
+    // vector-memory loads per wave per tile (waves below Q_EXTRA load one more q block)
+    static constexpr int L0 = 2 * LK + QN / NW;
+    static constexpr int Q_EXTRA = QN % NW;
+
+    static_assert(LK >= 1 && LK * 1024 * NW == K_BYTES, "K tile does not split into 1 KB loads per wave");
+    static_assert(CPW >= 1 && CPW * NW == CPR, "column pieces do not split over the waves");
+    static_assert(TGL >= 1 && TGL * CPW * HG == kWave, "weighted-sum lanes");
+    static_assert(!BF16 || TPT % 2 == 0, "key pairs need an even key count per lane");
+    static_assert(NS * TPH == TT && S_THREADS <= NT, "score layout");
+    static_assert(NBUF >= 2 && NBUF <= 4, "stage count (the waits assume at most two tiles ahead)");
+};
+
+// ---------------------------------------------------------------------------
+// the flat tile list
+// ---------------------------------------------------------------------------
+
+// Visible keys of query row `row` (b * Sq + i), clamped to the cache capacity.
+__device__ __forceinline__ int row_visible(const RowAttnParams &p, int64_t row)
+{
+    const int b = (int)(row / p.Sq);
+    const int i = (int)(row % p.Sq);
+    int64_t n;
+    if (!p.prefill) {
+        n = p.ctx_lens[b];
+    } else {
+        const int64_t start = p.start_pos[b];
+        n = p.causal ? start + i + 1 : start + p.Sq;
+    }
+    if (n > p.cache.capacity) n = p.cache.capacity;
+    if (n < 0) n = 0;
+    return (int)n;
+}
+
+// For the rows of this launch (local rows 0 .. rows-1, at most kStreamRows):
+// nvis[r] = visible keys, prefix[r] = K * sum_{r' < r} tiles(r'),
+// prefix[rows] = the number of tiles T.  Every thread of the workgroup calls
+// it; thread i handles the consecutive rows i*per .. i*per+per-1, so any row
+// count up to kStreamRows is covered whatever the workgroup size.
+__device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, int32_t *nvis, int *lds_waves)
+{
+    static_assert(kStreamRows % NT == 0, "rows per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rows = p.rows;
+    const int per = (rows + NT - 1) / NT;
+    const int r0 = tid * per;
+    int local = 0;
+    for (int k = 0; k < per; ++k) {
+        const int r = r0 + k;
+        if (r < rows) {
+            const int n = row_visible(p, p.row0 + r);
+            nvis[r] = n;
+            local += (n + tt - 1) / tt;
+        }
+    }
+    int x = local;   // inclusive scan over the wave, then over the waves
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) lds_waves[wave] = x;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += lds_waves[w];
+    int run = before + x - local;
+    for (int k = 0; k < per; ++k) {
+        const int r = r0 + k;
+        if (r < rows) {
+            prefix[r] = run * p.cache.K;
+            run += (nvis[r] + tt - 1) / tt;
+        }
+    }
+    if (tid == NT - 1) prefix[rows] = (before + x) * p.cache.K;
+    __syncthreads();
+}
+
+struct Cursor {
+    int row;       // local query row
+    int g;         // KV group
+    int j;         // tile within the item
+    int tiles;     // tiles of the item
+    int n_vis;     // visible keys of the row
+    int item0;     // flat index of the item's first tile
+};
+
+__device__ __forceinline__ Cursor cursor_at(const int32_t *prefix, const int32_t *nvis, int rows, int tau, int tt)
+{
+    // last row whose prefix is <= tau (rows without tiles share their prefix)
+    int lo = 0, hi = rows - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= tau) lo = mid; else hi = mid - 1;
+    }
+    Cursor c;
+    c.row = lo;
+    c.n_vis = nvis[lo];
+    c.tiles = (c.n_vis + tt - 1) / tt;
+    const int off = tau - prefix[lo];
+    c.g = off / c.tiles;
+    c.j = off % c.tiles;
+    c.item0 = prefix[lo] + c.g * c.tiles;
+    return c;
+}
+
+__device__ __forceinline__ void cursor_next(const int32_t *nvis, int rows, int K, Cursor &c, int tt)
+{
+    if (++c.j < c.tiles) return;
+    c.j = 0;
+    c.item0 += c.tiles;
+    if (++c.g < K) return;
+    c.g = 0;
+    do {
+        ++c.row;
+        if (c.row >= rows) return;
+        c.n_vis = nvis[c.row];
+        c.tiles = (c.n_vis + tt - 1) / tt;
+    } while (c.tiles == 0);
+}
+
+__device__ __forceinline__ int64_t slice_start(int64_t w, int64_t T, int64_t W) { return w * T / W; }
+
+// ---------------------------------------------------------------------------
+// main kernel
+// ---------------------------------------------------------------------------
+
+template <int D, int GP, bool BF16>
+__global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p)
+{
+    using C = Cfg<D, GP, BF16>;
+    __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE];
+    __shared__ __attribute__((aligned(16))) char lds_p[C::P_BYTES];
+    __shared__ float lds_alpha[GP], lds_m[GP], lds_l[GP];
+    __shared__ int32_t lds_prefix[kStreamRows + 1];
+    __shared__ int32_t lds_nvis[kStreamRows];
+    __shared__ int lds_waves[NW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const CacheView &cache = p.cache;
+    const int G = p.G, H = p.H;
+
+    // ---- the flat tile list and this workgroup's slice ---------------------
+    build_tables(p, C::TT, lds_prefix, lds_nvis, lds_waves);
+    if (blockIdx.x == 0 && p.prefix != nullptr)   // the merge kernel reads it from the workspace
+        for (int r = tid; r <= p.rows; r += NT) p.prefix[r] = lds_prefix[r];
+    const int T = lds_prefix[p.rows];
+    const int64_t W = gridDim.x;
+    int tau0 = (int)slice_start(blockIdx.x, T, W), tau1 = (int)slice_start(blockIdx.x + 1, T, W);
+    if (p.whole_items) {
+        // slices start at item starts, so no item is cut (no partial pieces)
+        auto snap = [&](int tau) {
+            if (tau >= T) return T;
+            const Cursor c = cursor_at(lds_prefix, lds_nvis, p.rows, tau, C::TT);
+            return c.j == 0 ? tau : c.item0 + c.tiles;
+        };
+        tau0 = snap(tau0);
+        tau1 = snap(tau1);
+        if (blockIdx.x == 0) {
+            // rows without a visible key (a violated contract) get zeros
+            for (int r = 0; r < p.rows; ++r) {
+                if (lds_nvis[r] > 0) continue;
+                for (int idx = tid; idx < H * D; idx += NT) {
+                    const int64_t o = ((int64_t)p.row0 + r) * H * D + idx;
+                    if constexpr (BF16) reinterpret_cast<uint16_t *>(p.out)[o] = 0;
+                    else reinterpret_cast<float *>(p.out)[o] = 0.f;
+                }
+            }
+        }
+    }
+    if (tau0 >= tau1) return;
+    const bool q_extra = wave < C::Q_EXTRA;
+    const int q_loads = C::QN / NW + (q_extra ? 1 : 0);
+
+    // ---- LDS-direct loads of one tile into one stage ----------------------
+    auto issue = [&](const Cursor &c, int stage) {
+        char *base = smem + stage * C::STAGE;
+        const int tile0 = c.j * C::TT;
+        const int nvalid = min(C::TT, c.n_vis - tile0);
+        const int64_t row_g = (int64_t)p.row0 + c.row;
+        const int b = (int)(row_g / p.Sq);
+#pragma unroll
+        for (int k = 0; k < C::LK; ++k) {
+            const int blk = wave + NW * k;              // 1 KB block of the tile
+            const int t = blk * C::RPK + lane / C::CPR; // row of this lane
+            const int piece = lane % C::CPR;
+            const void *srck = &kZero16;
+            const void *srcv = &kZero16;
+            if (blk * C::RPK < nvalid) {
+                int64_t r = -1;
+                if (cache.block_table == nullptr || cache.log2_bs >= 4) {
+                    // the block's RPK consecutive rows lie in one 16-row group,
+                    // hence in one cache block: one lookup per wave
+                    const int64_t row0 = cache_row_wave(cache, b, c.g, tile0 + blk * C::RPK);
+                    if (row0 >= 0 && t < nvalid) r = row0 + (t - blk * C::RPK);
+                } else if (t < nvalid) {
+                    r = cache_row(cache, b, c.g, tile0 + t);   // blocks shorter than 16 rows
+                }
+                if (r >= 0) {
+                    srck = cache.k + r * C::RB + (piece ^ (t & C::SWZ)) * 16;
+                    srcv = cache.v + r * C::RB + piece * 16;
+                }
+            }
+            dma16(srck, base + blk * 1024);
+            dma16(srcv, base + C::K_BYTES + blk * 1024);
+        }
+        for (int k = 0; k < q_loads; ++k) {
+            const int qblk = wave + NW * k;
+            const int off = qblk * 1024 + lane * 16;
+            const int r = off / C::RB;
+            const void *src = &kZero16;
+            if (r < G)
+                src = p.q + ((row_g * H + (int64_t)c.g * G + r) * D) * C::ES + (off % C::RB);
+            dma16(src, base + 2 * C::K_BYTES + qblk * 1024);
+        }
+    };
+
+    // ---- per-thread state ---------------------------------------------------
+    const bool s_thread = tid < C::S_THREADS;
+    const int s_r = tid / C::TPH;                     // head (padded group)
+    const int s_j = tid % C::TPH;
+    uint32_t qw[C::QW];
+    float m_ref = -INFINITY, l_run = 0.f;
+
+    const int v_cl = lane % C::CPW;                   // column piece within the wave
+    const int v_rest = lane / C::CPW;
+    const int v_hg = v_rest % C::HG;
+    const int v_tg = v_rest / C::HG;
+    const int v_c = wave * C::CPW + v_cl;             // column piece of the row
+    float acc[C::HPT][C::CE];
+
+    // ---- prologue: the first NBUF-1 tiles -----------------------------------
+    Cursor pc = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);
+    const int pre = min(C::NBUF - 1, tau1 - tau0);
+    for (int i = 0; i < pre; ++i) {
+        issue(pc, i);
+        cursor_next(lds_nvis, p.rows, cache.K, pc, C::TT);
+    }
+    Cursor cc = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);
+    int piece0 = tau0;                                // first tile of the current piece
+
+    for (int tau = tau0; tau < tau1; ++tau) {
+        const int stage = (tau - tau0) % C::NBUF;
+        const char *base = smem + stage * C::STAGE;
+        // tile tau's loads are the oldest in flight: wait for them, then let
+        // every wave see them (and be done with the stage refilled below)
+        const int n_after = min(C::NBUF - 2, tau1 - 1 - tau);
+        if (q_extra) wait_tiles<C::L0 + 1>(n_after);
+        else wait_tiles<C::L0>(n_after);
+        barrier();
+        if (tau + C::NBUF - 1 < tau1) {
+            issue(pc, (tau - tau0 + C::NBUF - 1) % C::NBUF);
+            cursor_next(lds_nvis, p.rows, cache.K, pc, C::TT);
+        }
+        const uint4 *Ks = reinterpret_cast<const uint4 *>(base);
+        const uint4 *Vs = reinterpret_cast<const uint4 *>(base + C::K_BYTES);
+        const uint4 *Qs = reinterpret_cast<const uint4 *>(base + 2 * C::K_BYTES);
+        const int tile0 = cc.j * C::TT;
+        const int nvalid = min(C::TT, cc.n_vis - tile0);
+        const bool item_first = cc.j == 0 || tau == tau0;
+        const bool item_last = cc.j == cc.tiles - 1 || tau == tau1 - 1;
+
+        if (item_first) {
+            if (s_thread) {
+#pragma unroll
+                for (int w = 0; w < C::QW / 4; ++w) {
+                    const uint4 x = Qs[s_r * C::CPR + w];
+                    qw[4 * w + 0] = x.x; qw[4 * w + 1] = x.y; qw[4 * w + 2] = x.z; qw[4 * w + 3] = x.w;
+                }
+            }
+            m_ref = -INFINITY;
+            l_run = 0.f;
+#pragma unroll
+            for (int i = 0; i < C::HPT; ++i)
+#pragma unroll
+                for (int e = 0; e < C::CE; ++e) acc[i][e] = 0.f;
+            piece0 = tau;
+        }
+
+        // ---- scores and online softmax ---------------------------------------
+        if (s_thread) {
+            float s[C::NS];
+            float mt = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < C::NS; ++k) {
+                const int t = s_j + k * C::TPH;
+                float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                for (int pcs = 0; pcs < C::CPR; ++pcs) {
+                    const uint4 kv = Ks[t * C::CPR + (pcs ^ (t & C::SWZ))];
+                    if constexpr (BF16) {
+                        a0 = dot2_bf16(qw[4 * pcs + 0], kv.x, a0);
+                        a1 = dot2_bf16(qw[4 * pcs + 1], kv.y, a1);
+                        a0 = dot2_bf16(qw[4 * pcs + 2], kv.z, a0);
+                        a1 = dot2_bf16(qw[4 * pcs + 3], kv.w, a1);
+                    } else {
+                        a0 = fmaf(__uint_as_float(qw[4 * pcs + 0]), __uint_as_float(kv.x), a0);
+                        a1 = fmaf(__uint_as_float(qw[4 * pcs + 1]), __uint_as_float(kv.y), a1);
+                        a0 = fmaf(__uint_as_float(qw[4 * pcs + 2]), __uint_as_float(kv.z), a0);
+                        a1 = fmaf(__uint_as_float(qw[4 * pcs + 3]), __uint_as_float(kv.w), a1);
+                    }
+                }
+                s[k] = (t < nvalid) ? (a0 + a1) * p.scale_log2 : -INFINITY;
+                mt = fmaxf(mt, s[k]);
+            }
+            mt = group_max<C::TPH>(mt);
+            float alpha = 1.f;
+            if (mt > m_ref + TAU) {
+                alpha = fast_exp2(m_ref - mt);   // 0 on an item's first tile
+                m_ref = mt;
+            }
+            float ps = 0.f;
+#pragma unroll
+            for (int k = 0; k < C::NS; ++k) {
+                const int t = s_j + k * C::TPH;
+                const float pk = fast_exp2(s[k] - m_ref);
+                if constexpr (BF16) {
+                    const uint32_t pb = f32_to_bf16_rne(pk);
+                    ps += __uint_as_float(pb << 16);   // the sum of what the V product uses
+                    reinterpret_cast<uint16_t *>(lds_p)[((t >> 1) * GP + s_r) * 2 + (t & 1)] = (uint16_t)pb;
+                } else {
+                    ps += pk;
+                    reinterpret_cast<float *>(lds_p)[t * GP + s_r] = pk;
+                }
+            }
+            ps = group_sum<C::TPH>(ps);
+            l_run = l_run * alpha + ps;
+            if (s_j == 0) {
+                lds_alpha[s_r] = alpha;
+                if (item_last) {
+                    lds_m[s_r] = m_ref;
+                    lds_l[s_r] = l_run;
+                }
+            }
+        }
+        barrier();
+
+        // ---- o = o * alpha + sum_t p_t v_t ------------------------------------
+        {
+            float al[C::HPT];
+            bool any = false;
+#pragma unroll
+            for (int i = 0; i < C::HPT; ++i) {
+                al[i] = lds_alpha[v_hg * C::HPT + i];
+                any |= (al[i] != 1.f);
+            }
+            if (any) {
+#pragma unroll
+                for (int i = 0; i < C::HPT; ++i)
+#pragma unroll
+                    for (int e = 0; e < C::CE; ++e) acc[i][e] *= al[i];
+            }
+            if constexpr (BF16) {
+                const uint32_t *P2 = reinterpret_cast<const uint32_t *>(lds_p);
+#pragma unroll
+                for (int kp = 0; kp < C::TPT / 2; ++kp) {
+                    const int t = v_tg * C::TPT + 2 * kp;
+                    const uint4 a = Vs[t * C::CPR + v_c];
+                    const uint4 bb = Vs[(t + 1) * C::CPR + v_c];
+                    uint32_t vv[8];
+                    vv[0] = pair_lo(a.x, bb.x); vv[1] = pair_hi(a.x, bb.x);
+                    vv[2] = pair_lo(a.y, bb.y); vv[3] = pair_hi(a.y, bb.y);
+                    vv[4] = pair_lo(a.z, bb.z); vv[5] = pair_hi(a.z, bb.z);
+                    vv[6] = pair_lo(a.w, bb.w); vv[7] = pair_hi(a.w, bb.w);
+#pragma unroll
+                    for (int i = 0; i < C::HPT; ++i) {
+                        const uint32_t pp = P2[(t >> 1) * GP + v_hg * C::HPT + i];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[i][e] = dot2_bf16(pp, vv[e], acc[i][e]);
+                    }
+                }
+            } else {
+                const float *Pf = reinterpret_cast<const float *>(lds_p);
+#pragma unroll
+                for (int k = 0; k < C::TPT; ++k) {
+                    const int t = v_tg * C::TPT + k;
+                    const uint4 a = Vs[t * C::CPR + v_c];
+                    const float vf[4] = {__uint_as_float(a.x), __uint_as_float(a.y),
+                                         __uint_as_float(a.z), __uint_as_float(a.w)};
+#pragma unroll
+                    for (int i = 0; i < C::HPT; ++i) {
+                        const float pk = Pf[t * GP + v_hg * C::HPT + i];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[i][e] = fmaf(pk, vf[e], acc[i][e]);
+                    }
+                }
+            }
+        }
+
+        // ---- end of a piece: reduce the key groups and store ------------------
+        if (item_last) {
+#pragma unroll
+            for (int m = C::CPW * C::HG; m < kWave; m <<= 1)
+#pragma unroll
+                for (int i = 0; i < C::HPT; ++i)
+#pragma unroll
+                    for (int e = 0; e < C::CE; ++e) acc[i][e] += __shfl_xor(acc[i][e], m, kWave);
+            const bool whole = (piece0 == cc.item0) && (cc.j == cc.tiles - 1);
+            const int64_t head0 = ((int64_t)p.row0 + cc.row) * H + (int64_t)cc.g * G;
+            if (v_tg == 0) {
+#pragma unroll
+                for (int i = 0; i < C::HPT; ++i) {
+                    const int r = v_hg * C::HPT + i;
+                    if (r >= G) continue;
+                    const int col = v_c * C::CE;
+                    if (whole) {
+                        const float inv = 1.f / lds_l[r];
+                        const int64_t o = (head0 + r) * D + col;
+                        if constexpr (BF16) {
+                            uint4 w;
+                            w.x = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
+                            w.y = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
+                            w.z = pack_bf16x2(acc[i][4] * inv, acc[i][5] * inv);
+                            w.w = pack_bf16x2(acc[i][6] * inv, acc[i][7] * inv);
+                            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p.out) + o) = w;
+                        } else {
+                            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.out) + o) =
+                                make_float4(acc[i][0] * inv, acc[i][1] * inv, acc[i][2] * inv, acc[i][3] * inv);
+                        }
+                    } else {
+                        const int slot = (tau0 < cc.item0) ? 1 : 0;
+                        float *dst = p.ws_o + (((int64_t)blockIdx.x * 2 + slot) * G + r) * D + col;
+#pragma unroll
+                        for (int e = 0; e < C::CE; e += 4)
+                            *reinterpret_cast<float4 *>(dst + e) =
+                                make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
+                        if (v_c == 0) {
+                            float *ml = p.ws_ml + (((int64_t)blockIdx.x * 2 + slot) * G + r) * 2;
+                            ml[0] = lds_m[r];
+                            ml[1] = lds_l[r];
+                        }
+                    }
+                }
+            }
+            // These stores share the vector-memory counter with the loads in
+            // flight; they can only make the next waits longer, never shorter.
+        }
+        cursor_next(lds_nvis, p.rows, cache.K, cc, C::TT);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// planning (many rows) and merging
+// ---------------------------------------------------------------------------
+
+// Merge of the pieces of one (row, KV group) item with their global max and
+// sum: M = max_s m_s, L = sum_s l_s 2^(m_s - M), out = sum_s o_s 2^(m_s - M) / L
+// (m in log2 units).  Items held by one workgroup were stored by it; rows
+// without a visible key get zeros.
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void merge_pieces_kernel(RowAttnParams p, int tt, int W)
+{
+    const int g = blockIdx.x;
+    const int row = blockIdx.y;                       // local row of this launch
+    const int G = p.G;
+    const int64_t head0 = ((int64_t)p.row0 + row) * p.H + (int64_t)g * G;
+    const int n_vis = row_visible(p, (int64_t)p.row0 + row);
+    if (n_vis <= 0) {
+        for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+            const int64_t o = head0 * D + idx;
+            if constexpr (BF16) reinterpret_cast<uint16_t *>(p.out)[o] = 0;
+            else reinterpret_cast<float *>(p.out)[o] = 0.f;
+        }
+        return;
+    }
+    const int64_t T = p.prefix[p.rows];
+    const int64_t tiles = (n_vis + tt - 1) / tt;
+    const int64_t a = p.prefix[row] + (int64_t)g * tiles, e = a + tiles - 1;
+    auto owner = [&](int64_t x) {
+        int64_t w = x * W / T;
+        while (w + 1 < W && slice_start(w + 1, T, W) <= x) ++w;
+        while (w > 0 && slice_start(w, T, W) > x) --w;
+        return w;
+    };
+    const int64_t wa = owner(a), wb = owner(e);
+    if (wa == wb) return;
+    for (int idx = threadIdx.x; idx < G * D / 4; idx += 256) {
+        const int r = (4 * idx) / D, col = (4 * idx) % D;
+        // workgroups whose slice is empty (fewer tiles than workgroups) hold nothing
+        float M = -INFINITY;
+        for (int64_t w = wa; w <= wb; ++w) {
+            if (slice_start(w, T, W) == slice_start(w + 1, T, W)) continue;
+            const int slot = slice_start(w, T, W) < a ? 1 : 0;
+            M = fmaxf(M, p.ws_ml[((w * 2 + slot) * G + r) * 2]);
+        }
+        float L = 0.f;
+        float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int64_t w = wa; w <= wb; ++w) {
+            if (slice_start(w, T, W) == slice_start(w + 1, T, W)) continue;
+            const int slot = slice_start(w, T, W) < a ? 1 : 0;
+            const float *ml = p.ws_ml + ((w * 2 + slot) * G + r) * 2;
+            const float wt = fast_exp2(ml[0] - M);
+            L += ml[1] * wt;
+            const float4 os = *reinterpret_cast<const float4 *>(p.ws_o + ((w * 2 + slot) * G + r) * D + col);
+            O.x += os.x * wt;
+            O.y += os.y * wt;
+            O.z += os.z * wt;
+            O.w += os.w * wt;
+        }
+        const float inv = 1.f / L;
+        const int64_t o = (head0 + r) * D + col;
+        if constexpr (BF16) {
+            *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) + o) =
+                make_uint2(pack_bf16x2(O.x * inv, O.y * inv), pack_bf16x2(O.z * inv, O.w * inv));
+        } else {
+            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.out) + o) =
+                make_float4(O.x * inv, O.y * inv, O.z * inv, O.w * inv);
+        }
+    }
+}
+
+template <int D, bool BF16>
+hipError_t launch_d(const RowAttnParams &p, int gp, hipStream_t s)
+{
+    const int tt = K_TILE_BYTES / (D * (BF16 ? 2 : 4));
+    const int W = p.num_wgs;
+    switch (gp) {
+    case 1: hipLaunchKernelGGL((stream_attention_kernel<D, 1, BF16>), dim3(W), dim3(NT), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((stream_attention_kernel<D, 2, BF16>), dim3(W), dim3(NT), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((stream_attention_kernel<D, 4, BF16>), dim3(W), dim3(NT), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((stream_attention_kernel<D, 8, BF16>), dim3(W), dim3(NT), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((stream_attention_kernel<D, 16, BF16>), dim3(W), dim3(NT), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((stream_attention_kernel<D, 32, BF16>), dim3(W), dim3(NT), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((stream_attention_kernel<D, 64, BF16>), dim3(W), dim3(NT), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.whole_items) return e;
+    hipLaunchKernelGGL((merge_pieces_kernel<D, BF16>), dim3(p.cache.K, p.rows), dim3(256), 0, s, p, tt, W);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Rows are processed in launches of at most kStreamRows rows (the row tables
+// live in LDS); launches on one stream run in order and share the workspace.
+hipError_t launch_row_attention(const RowAttnParams &p0, int gp, hipStream_t stream)
+{
+    if (p0.total_rows <= 0) return hipSuccess;
+    if (p0.cache.K > 65535 || p0.num_wgs <= 0) return hipErrorInvalidValue;
+    const bool bf16 = p0.cache.elem_bytes == 2;
+    for (int64_t r0 = 0; r0 < p0.total_rows; r0 += kStreamRows) {
+        RowAttnParams p = p0;
+        p.row0 = r0;
+        p.rows = (int32_t)(p0.total_rows - r0 < kStreamRows ? p0.total_rows - r0 : kStreamRows);
+        hipError_t e = hipErrorInvalidValue;
+        if (p.cache.d == 128) e = bf16 ? launch_d<128, true>(p, gp, stream) : launch_d<128, false>(p, gp, stream);
+        else if (p.cache.d == 64) e = bf16 ? launch_d<64, true>(p, gp, stream) : launch_d<64, false>(p, gp, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace gqa

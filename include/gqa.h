@@ -113,9 +113,9 @@ gqa_status gqa_kv_append(const gqa_kv_cache *cache, const void *k_new, const voi
                          const int32_t *start_pos, int32_t B, int32_t s_new, void *stream);
 
 /*
- * Workspace bytes gqa_decode needs for these sizes.  max_ctx is a host-side
- * upper bound of every ctx_lens[b] the call will see.  Host-only; no GPU
- * needed.  Returns 0 on invalid sizes.
+ * Workspace bytes gqa_decode needs for these sizes (a few MB at most; the
+ * amount depends on G = H / K and d only, the other sizes are checked).
+ * Host-only; no GPU needed.  Returns 0 on invalid sizes.
  */
 size_t gqa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_ctx);
@@ -127,15 +127,17 @@ size_t gqa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_h
  *   ctx_lens: device int32 [B], each in [1, max_ctx]
  *   max_ctx: host upper bound of ctx_lens, used to plan the key splits
  *   scale: the softmax scale, normally 1 / sqrt(d)
- * The keys are cut into splits (flash-decoding, inference-optimisation page
- * §10.2); every split keeps an online-softmax state (§9.2.1) and the splits of
- * one (sequence, KV head) are merged with their global max and sum.  One
- * K/V row read from memory serves all G heads of its group.
+ * The (sequence, KV head, 64-key tile) work is split evenly over one
+ * workgroup per compute unit (flash-decoding's split of the keys,
+ * inference-optimisation page §10.2); every piece keeps an online-softmax
+ * state (§9.2.1) and the pieces of one (sequence, KV head) are merged with
+ * their global max and sum.  One K/V row read from memory serves all G heads
+ * of its group.
  * workspace: device buffer of at least gqa_decode_workspace_bytes(...) bytes
- * (may be NULL when that is 0) for the per-split partial results; it needs no
- * initialisation.  When a row needs several splits a second, small kernel
- * merges them on the same stream.  Calls that may run concurrently need
- * separate workspaces.
+ * (a tile table and two partial results per workgroup; it needs no
+ * initialisation).  A (sequence, KV head) whose keys are shared by several
+ * workgroups is merged by a second, small kernel on the same stream.  Calls
+ * that may run concurrently need separate workspaces.
  */
 gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *ctx_lens,
                       int32_t max_ctx, int32_t B, int32_t num_heads, float scale, void *out,

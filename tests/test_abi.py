@@ -50,13 +50,12 @@ def test_cache_elems_per_token(lib, K, d, expect):
 
 
 def test_workspace_plan(lib):
-    # Llama-2-70B decode shape: 2048-key splits, 4 per 8192-token row
-    n = binding.gqa_decode_workspace_bytes(16, 64, 8, 128, 8192)
-    per = 16 * 64 * 4
+    # tile prefix of one launch (513 int32) + two partial slots per workgroup (256)
     align = lambda x: (x + 255) // 256 * 256
-    assert n == align(per * 128 * 4) + align(per * 2 * 4)
-    # a 128-token row fits one split: no workspace at all
-    assert binding.gqa_decode_workspace_bytes(1, 8, 2, 64, 128) == 0
+    for (B, H, K, d) in [(16, 64, 8, 128), (1, 8, 2, 64), (64, 64, 1, 128)]:
+        G = H // K
+        n = binding.gqa_decode_workspace_bytes(B, H, K, d, 8192)
+        assert n == align(513 * 4) + align(256 * 2 * G * d * 4) + align(256 * 2 * G * 2 * 4)
     assert binding.gqa_decode_workspace_bytes(1, 8, 3, 64, 128) == 0   # H % K != 0 -> 0
     assert binding.gqa_decode_workspace_bytes(0, 8, 2, 64, 128) == 0
 

@@ -106,23 +106,33 @@ def test_decode_f32_multi_split(H, K, d):
     _decode_case(inp, f"fp32 decode H={H} K={K} d={d}")
 
 
+@pytest.mark.parametrize("bs", [1, 4, 8, 32, 64, 256])
+def test_decode_paged_block_sizes(bs):
+    wl = W.WORKLOADS["paged_long_decode"].replace(B=3, ctx=("loguniform", 17, 1500), block_size=bs)
+    inp = W.make_decode(wl)
+    _decode_case(inp, f"paged bf16 decode, {bs}-token blocks")
+
+
 def test_decode_paged_small():
     wl = W.WORKLOADS["paged_long_decode"].replace(B=6, ctx=("loguniform", 17, 3000))
     inp = W.make_decode(wl)
     _decode_case(inp, "paged bf16 decode")
 
 
-@pytest.mark.parametrize("split", ["64", "256", "1024"])
-def test_decode_split_size_invariance(split, monkeypatch):
-    wl = W.WORKLOADS["llama2_70b_decode"].replace(B=2, ctx=("fixed", 2500))
+@pytest.mark.parametrize("B,ctx", [(1, 1), (1, 63), (1, 64), (1, 65), (2, 16448), (3, 200000 // 3), (300, 40)])
+def test_decode_slices_cut_items_anywhere(B, ctx):
+    """Rows shorter than a tile, exactly a tile, and long rows cut by many workgroup slices."""
+    wl = W.WORKLOADS["llama2_70b_decode"].replace(B=B, ctx=("fixed", ctx))
     inp = W.make_decode(wl)
-    base = from_dev(DecodeRun(inp).run())
-    monkeypatch.setenv("GQA_DECODE_SPLIT_TOKENS", split)
-    say("decode split", split)
-    other = from_dev(DecodeRun(inp).run())
-    check_close(as_f64(other, "bf16"), as_f64(base, "bf16"), BF16_TOL, f"split {split} vs default")
-    rows, want = oracle_decode_rows(inp)
-    check_close(gpu_rows(other, rows, "bf16"), want, BF16_TOL, f"split {split} vs oracle")
+    seqs = sorted({0, B - 1, B // 2})
+    _decode_case(inp, f"decode B={B} ctx={ctx}", seqs=seqs)
+
+
+def test_decode_more_rows_than_one_launch():
+    """B above the 512 rows one launch handles: the rows run in consecutive launches."""
+    wl = W.WORKLOADS["llama3_8b_decode"].replace(B=1100, ctx=("uniform", 1, 300))
+    inp = W.make_decode(wl)
+    _decode_case(inp, "decode B=1100", seqs=[0, 1, 511, 512, 513, 1023, 1024, 1099])
 
 
 def test_decode_workspace_reused_across_layouts():
