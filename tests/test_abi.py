@@ -50,12 +50,12 @@ def test_cache_elems_per_token(lib, K, d, expect):
 
 
 def test_workspace_plan(lib):
-    # tile prefix of one launch (513 int32) + two partial slots per workgroup (256)
+    # tile prefix of one launch (513 int32) + two partial slots per workgroup (512)
     align = lambda x: (x + 255) // 256 * 256
     for (B, H, K, d) in [(16, 64, 8, 128), (1, 8, 2, 64), (64, 64, 1, 128)]:
         G = H // K
         n = binding.gqa_decode_workspace_bytes(B, H, K, d, 8192)
-        assert n == align(513 * 4) + align(256 * 2 * G * d * 4) + align(256 * 2 * G * 2 * 4)
+        assert n == align(513 * 4) + align(512 * 2 * G * d * 4) + align(512 * 2 * G * 2 * 4)
     assert binding.gqa_decode_workspace_bytes(1, 8, 3, 64, 128) == 0   # H % K != 0 -> 0
     assert binding.gqa_decode_workspace_bytes(0, 8, 2, 64, 128) == 0
 
