@@ -13,11 +13,12 @@
 //    list and each of the W workgroups (two per CU) takes an equal contiguous
 //    slice of it.  Ragged and paged contexts are
 //    balanced exactly, and no workgroup starts just to find nothing to do.
-//  * Memory pipeline.  K, V (and the item's q rows) of the next three tiles
-//    are in flight as LDS-direct loads (global_load_lds_dwordx4: HBM -> LDS
-//    without registers) while the current tile is used; the loads of one
-//    tile are waited for with an explicit vmcnt, so the pipeline also runs
-//    across item boundaries.  Every K and V row is read from HBM once and
+//  * Memory pipeline.  K, V (and the item's q rows) of the next tiles are in
+//    flight as LDS-direct loads (global_load_lds_dwordx4: HBM -> LDS without
+//    registers) while the scores of one tile and the V sum of the previous
+//    one are computed, with one barrier per tile; the loads of a tile are
+//    waited for with an explicit vmcnt, so the pipeline also runs across
+//    item boundaries.  Every K and V row is read from HBM once and
 //    then serves all G heads of its group from LDS (the group broadcast).
 //  * Scores: thread (head r, key t) computes the full dot product of its
 //    register-resident q row with the K row from LDS (v_dot2_f32_bf16: two
@@ -131,9 +132,9 @@ struct Cfg {
     static constexpr int TPT = TT / TGL;               // keys per lane per tile
     // LDS
     static constexpr int P_BYTES = TT * GP * (BF16 ? 2 : 4);
-    static constexpr int OTHER = P_BYTES + 3 * GP * 4 + (2 * kStreamRows + 1) * 4 + NW * 4 + 256;
-    // two workgroups per CU when two stages fit in half the LDS, else one
-    static constexpr int LIMIT = (LDS_LIMIT - OTHER) / STAGE >= 2 ? LDS_LIMIT : 2 * LDS_LIMIT;
+    static constexpr int OTHER = 2 * P_BYTES + 6 * GP * 4 + (2 * kStreamRows + 1) * 4 + NW * 4 + 256;
+    // two workgroups per CU when three stages fit in half the LDS, else one
+    static constexpr int LIMIT = (LDS_LIMIT - OTHER) / STAGE >= 3 ? LDS_LIMIT : 2 * LDS_LIMIT;
     static constexpr int NBUF0 = (LIMIT - OTHER) / STAGE;
     static constexpr int NBUF = NBUF0 > 4 ? 4 : NBUF0;
     // vector-memory loads per wave per tile (waves below Q_EXTRA load one more q block)
@@ -145,7 +146,7 @@ struct Cfg {
     static_assert(TGL >= 1 && TGL * CPW * HG == kWave, "weighted-sum lanes");
     static_assert(!BF16 || TPT % 2 == 0, "key pairs need an even key count per lane");
     static_assert(NS * TPH == TT && S_THREADS <= NT, "score layout");
-    static_assert(NBUF >= 2 && NBUF <= 4, "stage count (the waits assume at most two tiles ahead)");
+    static_assert(NBUF >= 3 && NBUF <= 4, "stage count (the pipeline keeps NBUF-2 tiles in flight, waits assume <= 2)");
 };
 
 // ---------------------------------------------------------------------------
@@ -266,8 +267,8 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
 {
     using C = Cfg<D, GP, BF16>;
     __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE];
-    __shared__ __attribute__((aligned(16))) char lds_p[C::P_BYTES];
-    __shared__ float lds_alpha[GP], lds_m[GP], lds_l[GP];
+    __shared__ __attribute__((aligned(16))) char lds_p[2 * C::P_BYTES];   // double-buffered
+    __shared__ float lds_alpha[2][GP], lds_m[2][GP], lds_l[2][GP];
     __shared__ int32_t lds_prefix[kStreamRows + 1];
     __shared__ int32_t lds_nvis[kStreamRows];
     __shared__ int lds_waves[NW];
@@ -364,120 +365,141 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
     const int v_tg = v_rest / C::HG;
     const int v_c = wave * C::CPW + v_cl;             // column piece of the row
     float acc[C::HPT][C::CE];
+#pragma unroll
+    for (int i = 0; i < C::HPT; ++i)
+#pragma unroll
+        for (int e = 0; e < C::CE; ++e) acc[i][e] = 0.f;
 
-    // ---- prologue: the first NBUF-1 tiles -----------------------------------
+    // ---- software pipeline ---------------------------------------------------
+    // Iteration tau (one barrier each): the scores of tile tau and the V sum
+    // of tile tau-1 run back to back with no barrier between them (they touch
+    // different stages and different halves of the double-buffered P / alpha /
+    // (m, l) arrays), while tiles tau+1 .. tau+A are in flight.  Stage use:
+    // tau (K, q), tau-1 (V), tau+1 .. tau+A (loading) = NBUF.
+    constexpr int A = C::NBUF - 2;
     Cursor pc = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);
-    const int pre = min(C::NBUF - 1, tau1 - tau0);
+    const int pre = min(A, tau1 - tau0);
     for (int i = 0; i < pre; ++i) {
         issue(pc, i);
         cursor_next(lds_nvis, p.rows, cache.K, pc, C::TT);
     }
-    Cursor cc = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);
-    int piece0 = tau0;                                // first tile of the current piece
+    Cursor cs = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);   // tile of the score phase
+    Cursor cv = cs;                                                    // tile of the V phase
+    int piece0 = tau0;                                // first tile of the V phase's piece
 
-    for (int tau = tau0; tau < tau1; ++tau) {
-        const int stage = (tau - tau0) % C::NBUF;
-        const char *base = smem + stage * C::STAGE;
-        // tile tau's loads are the oldest in flight: wait for them, then let
-        // every wave see them (and be done with the stage refilled below)
-        const int n_after = min(C::NBUF - 2, tau1 - 1 - tau);
-        if (q_extra) wait_tiles<C::L0 + 1>(n_after);
-        else wait_tiles<C::L0>(n_after);
+    for (int tau = tau0; tau <= tau1; ++tau) {
+        const bool do_s = tau < tau1;
+        const bool do_v = tau > tau0;
+        if (do_s) {
+            // tile tau's loads are the oldest in flight
+            const int n_after = min(A - 1, tau1 - 1 - tau);
+            if (q_extra) wait_tiles<C::L0 + 1>(n_after);
+            else wait_tiles<C::L0>(n_after);
+        }
         barrier();
-        if (tau + C::NBUF - 1 < tau1) {
-            issue(pc, (tau - tau0 + C::NBUF - 1) % C::NBUF);
+        if (tau + A < tau1) {
+            issue(pc, (tau + A - tau0) % C::NBUF);
             cursor_next(lds_nvis, p.rows, cache.K, pc, C::TT);
         }
-        const uint4 *Ks = reinterpret_cast<const uint4 *>(base);
-        const uint4 *Vs = reinterpret_cast<const uint4 *>(base + C::K_BYTES);
-        const uint4 *Qs = reinterpret_cast<const uint4 *>(base + 2 * C::K_BYTES);
-        const int tile0 = cc.j * C::TT;
-        const int nvalid = min(C::TT, cc.n_vis - tile0);
-        const bool item_first = cc.j == 0 || tau == tau0;
-        const bool item_last = cc.j == cc.tiles - 1 || tau == tau1 - 1;
+        const int buf = tau & 1;                      // P / alpha / (m, l) half written by this S phase
 
-        if (item_first) {
-            if (s_thread) {
+        // ---- scores and online softmax of tile tau ----------------------------
+        if (do_s) {
+            const char *base = smem + ((tau - tau0) % C::NBUF) * C::STAGE;
+            const uint4 *Ks = reinterpret_cast<const uint4 *>(base);
+            const uint4 *Qs = reinterpret_cast<const uint4 *>(base + 2 * C::K_BYTES);
+            const int nvalid = min(C::TT, cs.n_vis - cs.j * C::TT);
+            const bool s_first = cs.j == 0 || tau == tau0;
+            const bool s_last = cs.j == cs.tiles - 1 || tau == tau1 - 1;
+            if (s_first) {
+                if (s_thread) {
 #pragma unroll
-                for (int w = 0; w < C::QW / 4; ++w) {
-                    const uint4 x = Qs[s_r * C::CPR + w];
-                    qw[4 * w + 0] = x.x; qw[4 * w + 1] = x.y; qw[4 * w + 2] = x.z; qw[4 * w + 3] = x.w;
-                }
-            }
-            m_ref = -INFINITY;
-            l_run = 0.f;
-#pragma unroll
-            for (int i = 0; i < C::HPT; ++i)
-#pragma unroll
-                for (int e = 0; e < C::CE; ++e) acc[i][e] = 0.f;
-            piece0 = tau;
-        }
-
-        // ---- scores and online softmax ---------------------------------------
-        if (s_thread) {
-            float s[C::NS];
-            float mt = -INFINITY;
-#pragma unroll
-            for (int k = 0; k < C::NS; ++k) {
-                const int t = s_j + k * C::TPH;
-                float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-                for (int pcs = 0; pcs < C::CPR; ++pcs) {
-                    const uint4 kv = Ks[t * C::CPR + (pcs ^ (t & C::SWZ))];
-                    if constexpr (BF16) {
-                        a0 = dot2_bf16(qw[4 * pcs + 0], kv.x, a0);
-                        a1 = dot2_bf16(qw[4 * pcs + 1], kv.y, a1);
-                        a0 = dot2_bf16(qw[4 * pcs + 2], kv.z, a0);
-                        a1 = dot2_bf16(qw[4 * pcs + 3], kv.w, a1);
-                    } else {
-                        a0 = fmaf(__uint_as_float(qw[4 * pcs + 0]), __uint_as_float(kv.x), a0);
-                        a1 = fmaf(__uint_as_float(qw[4 * pcs + 1]), __uint_as_float(kv.y), a1);
-                        a0 = fmaf(__uint_as_float(qw[4 * pcs + 2]), __uint_as_float(kv.z), a0);
-                        a1 = fmaf(__uint_as_float(qw[4 * pcs + 3]), __uint_as_float(kv.w), a1);
+                    for (int w = 0; w < C::QW / 4; ++w) {
+                        const uint4 x = Qs[s_r * C::CPR + w];
+                        qw[4 * w + 0] = x.x; qw[4 * w + 1] = x.y; qw[4 * w + 2] = x.z; qw[4 * w + 3] = x.w;
                     }
                 }
-                s[k] = (t < nvalid) ? (a0 + a1) * p.scale_log2 : -INFINITY;
-                mt = fmaxf(mt, s[k]);
+                m_ref = -INFINITY;
+                l_run = 0.f;
             }
-            mt = group_max<C::TPH>(mt);
-            float alpha = 1.f;
-            if (mt > m_ref + TAU) {
-                alpha = fast_exp2(m_ref - mt);   // 0 on an item's first tile
-                m_ref = mt;
-            }
-            float ps = 0.f;
+            if (s_thread) {
+                float sc[C::NS];
+                float mt = -INFINITY;
 #pragma unroll
-            for (int k = 0; k < C::NS; ++k) {
-                const int t = s_j + k * C::TPH;
-                const float pk = fast_exp2(s[k] - m_ref);
-                if constexpr (BF16) {
-                    const uint32_t pb = f32_to_bf16_rne(pk);
-                    ps += __uint_as_float(pb << 16);   // the sum of what the V product uses
-                    reinterpret_cast<uint16_t *>(lds_p)[((t >> 1) * GP + s_r) * 2 + (t & 1)] = (uint16_t)pb;
-                } else {
-                    ps += pk;
-                    reinterpret_cast<float *>(lds_p)[t * GP + s_r] = pk;
+                for (int k = 0; k < C::NS; ++k) {
+                    const int t = s_j + k * C::TPH;
+                    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+                    for (int pcs = 0; pcs < C::CPR; ++pcs) {
+                        const uint4 kv = Ks[t * C::CPR + (pcs ^ (t & C::SWZ))];
+                        if constexpr (BF16) {
+                            a0 = dot2_bf16(qw[4 * pcs + 0], kv.x, a0);
+                            a1 = dot2_bf16(qw[4 * pcs + 1], kv.y, a1);
+                            a2 = dot2_bf16(qw[4 * pcs + 2], kv.z, a2);
+                            a3 = dot2_bf16(qw[4 * pcs + 3], kv.w, a3);
+                        } else {
+                            a0 = fmaf(__uint_as_float(qw[4 * pcs + 0]), __uint_as_float(kv.x), a0);
+                            a1 = fmaf(__uint_as_float(qw[4 * pcs + 1]), __uint_as_float(kv.y), a1);
+                            a2 = fmaf(__uint_as_float(qw[4 * pcs + 2]), __uint_as_float(kv.z), a2);
+                            a3 = fmaf(__uint_as_float(qw[4 * pcs + 3]), __uint_as_float(kv.w), a3);
+                        }
+                    }
+                    sc[k] = (t < nvalid) ? ((a0 + a1) + (a2 + a3)) * p.scale_log2 : -INFINITY;
+                    mt = fmaxf(mt, sc[k]);
                 }
-            }
-            ps = group_sum<C::TPH>(ps);
-            l_run = l_run * alpha + ps;
-            if (s_j == 0) {
-                lds_alpha[s_r] = alpha;
-                if (item_last) {
-                    lds_m[s_r] = m_ref;
-                    lds_l[s_r] = l_run;
+                mt = group_max<C::TPH>(mt);
+                float alpha = 1.f;
+                if (mt > m_ref + TAU) {
+                    alpha = fast_exp2(m_ref - mt);   // 0 on an item's first tile
+                    m_ref = mt;
+                }
+                float ps = 0.f;
+                char *pbuf = lds_p + buf * C::P_BYTES;
+#pragma unroll
+                for (int k = 0; k < C::NS; ++k) {
+                    const int t = s_j + k * C::TPH;
+                    const float pk = fast_exp2(sc[k] - m_ref);
+                    if constexpr (BF16) {
+                        const uint32_t pb = f32_to_bf16_rne(pk);
+                        ps += __uint_as_float(pb << 16);   // the sum of what the V product uses
+                        reinterpret_cast<uint16_t *>(pbuf)[((t >> 1) * GP + s_r) * 2 + (t & 1)] = (uint16_t)pb;
+                    } else {
+                        ps += pk;
+                        reinterpret_cast<float *>(pbuf)[t * GP + s_r] = pk;
+                    }
+                }
+                ps = group_sum<C::TPH>(ps);
+                l_run = l_run * alpha + ps;
+                if (s_j == 0) {
+                    lds_alpha[buf][s_r] = alpha;
+                    if (s_last) {
+                        lds_m[buf][s_r] = m_ref;
+                        lds_l[buf][s_r] = l_run;
+                    }
                 }
             }
         }
-        barrier();
 
-        // ---- o = o * alpha + sum_t p_t v_t ------------------------------------
-        {
+        // ---- o = o * alpha + sum_t p_t v_t of tile tau-1 ----------------------
+        if (do_v) {
+            const int tv = tau - 1;
+            const int vb = buf ^ 1;
+            const char *base = smem + ((tv - tau0) % C::NBUF) * C::STAGE;
+            const uint4 *Vs = reinterpret_cast<const uint4 *>(base + C::K_BYTES);
+            const bool v_first = cv.j == 0 || tv == tau0;
+            const bool v_last = cv.j == cv.tiles - 1 || tv == tau1 - 1;
+            if (v_first) {
+#pragma unroll
+                for (int i = 0; i < C::HPT; ++i)
+#pragma unroll
+                    for (int e = 0; e < C::CE; ++e) acc[i][e] = 0.f;
+                piece0 = tv;
+            }
             float al[C::HPT];
             bool any = false;
 #pragma unroll
             for (int i = 0; i < C::HPT; ++i) {
-                al[i] = lds_alpha[v_hg * C::HPT + i];
+                al[i] = lds_alpha[vb][v_hg * C::HPT + i];
                 any |= (al[i] != 1.f);
             }
             if (any) {
@@ -486,8 +508,9 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
 #pragma unroll
                     for (int e = 0; e < C::CE; ++e) acc[i][e] *= al[i];
             }
+            const char *pbuf = lds_p + vb * C::P_BYTES;
             if constexpr (BF16) {
-                const uint32_t *P2 = reinterpret_cast<const uint32_t *>(lds_p);
+                const uint32_t *P2 = reinterpret_cast<const uint32_t *>(pbuf);
 #pragma unroll
                 for (int kp = 0; kp < C::TPT / 2; ++kp) {
                     const int t = v_tg * C::TPT + 2 * kp;
@@ -506,7 +529,7 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
                     }
                 }
             } else {
-                const float *Pf = reinterpret_cast<const float *>(lds_p);
+                const float *Pf = reinterpret_cast<const float *>(pbuf);
 #pragma unroll
                 for (int k = 0; k < C::TPT; ++k) {
                     const int t = v_tg * C::TPT + k;
@@ -521,63 +544,60 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
                     }
                 }
             }
-        }
 
-        // ---- end of a piece: reduce the key groups and store ------------------
-        if (item_last) {
+            // ---- end of a piece: reduce the key groups and store --------------
+            if (v_last) {
 #pragma unroll
-            for (int m = C::CPW * C::HG; m < kWave; m <<= 1)
+                for (int m = C::CPW * C::HG; m < kWave; m <<= 1)
 #pragma unroll
-                for (int i = 0; i < C::HPT; ++i)
+                    for (int i = 0; i < C::HPT; ++i)
 #pragma unroll
-                    for (int e = 0; e < C::CE; ++e) acc[i][e] += __shfl_xor(acc[i][e], m, kWave);
-            const bool whole = (piece0 == cc.item0) && (cc.j == cc.tiles - 1);
-            const int64_t head0 = ((int64_t)p.row0 + cc.row) * H + (int64_t)cc.g * G;
-            if (v_tg == 0) {
+                        for (int e = 0; e < C::CE; ++e) acc[i][e] += __shfl_xor(acc[i][e], m, kWave);
+                const bool whole = (piece0 == cv.item0) && (cv.j == cv.tiles - 1);
+                const int64_t head0 = ((int64_t)p.row0 + cv.row) * H + (int64_t)cv.g * G;
+                if (v_tg == 0) {
 #pragma unroll
-                for (int i = 0; i < C::HPT; ++i) {
-                    const int r = v_hg * C::HPT + i;
-                    if (r >= G) continue;
-                    const int col = v_c * C::CE;
-                    if (whole) {
-                        const float inv = 1.f / lds_l[r];
-                        const int64_t o = (head0 + r) * D + col;
-                        if constexpr (BF16) {
-                            uint4 w;
-                            w.x = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
-                            w.y = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
-                            w.z = pack_bf16x2(acc[i][4] * inv, acc[i][5] * inv);
-                            w.w = pack_bf16x2(acc[i][6] * inv, acc[i][7] * inv);
-                            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p.out) + o) = w;
+                    for (int i = 0; i < C::HPT; ++i) {
+                        const int r = v_hg * C::HPT + i;
+                        if (r >= G) continue;
+                        const int col = v_c * C::CE;
+                        if (whole) {
+                            const float inv = 1.f / lds_l[vb][r];
+                            const int64_t o = (head0 + r) * D + col;
+                            if constexpr (BF16) {
+                                uint4 w;
+                                w.x = pack_bf16x2(acc[i][0] * inv, acc[i][1] * inv);
+                                w.y = pack_bf16x2(acc[i][2] * inv, acc[i][3] * inv);
+                                w.z = pack_bf16x2(acc[i][4] * inv, acc[i][5] * inv);
+                                w.w = pack_bf16x2(acc[i][6] * inv, acc[i][7] * inv);
+                                *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(p.out) + o) = w;
+                            } else {
+                                *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.out) + o) =
+                                    make_float4(acc[i][0] * inv, acc[i][1] * inv, acc[i][2] * inv, acc[i][3] * inv);
+                            }
                         } else {
-                            *reinterpret_cast<float4 *>(reinterpret_cast<float *>(p.out) + o) =
-                                make_float4(acc[i][0] * inv, acc[i][1] * inv, acc[i][2] * inv, acc[i][3] * inv);
-                        }
-                    } else {
-                        const int slot = (tau0 < cc.item0) ? 1 : 0;
-                        float *dst = p.ws_o + (((int64_t)blockIdx.x * 2 + slot) * G + r) * D + col;
+                            const int slot = (tau0 < cv.item0) ? 1 : 0;
+                            float *dst = p.ws_o + (((int64_t)blockIdx.x * 2 + slot) * G + r) * D + col;
 #pragma unroll
-                        for (int e = 0; e < C::CE; e += 4)
-                            *reinterpret_cast<float4 *>(dst + e) =
-                                make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
-                        if (v_c == 0) {
-                            float *ml = p.ws_ml + (((int64_t)blockIdx.x * 2 + slot) * G + r) * 2;
-                            ml[0] = lds_m[r];
-                            ml[1] = lds_l[r];
+                            for (int e = 0; e < C::CE; e += 4)
+                                *reinterpret_cast<float4 *>(dst + e) =
+                                    make_float4(acc[i][e], acc[i][e + 1], acc[i][e + 2], acc[i][e + 3]);
+                            if (v_c == 0) {
+                                float *ml = p.ws_ml + (((int64_t)blockIdx.x * 2 + slot) * G + r) * 2;
+                                ml[0] = lds_m[vb][r];
+                                ml[1] = lds_l[vb][r];
+                            }
                         }
                     }
                 }
+                // These stores share the vector-memory counter with the loads in
+                // flight; they can only make the next waits longer, never shorter.
             }
-            // These stores share the vector-memory counter with the loads in
-            // flight; they can only make the next waits longer, never shorter.
+            cursor_next(lds_nvis, p.rows, cache.K, cv, C::TT);
         }
-        cursor_next(lds_nvis, p.rows, cache.K, cc, C::TT);
+        if (do_s) cursor_next(lds_nvis, p.rows, cache.K, cs, C::TT);
     }
 }
-
-// ---------------------------------------------------------------------------
-// planning (many rows) and merging
-// ---------------------------------------------------------------------------
 
 // Merge of the pieces of one (row, KV group) item with their global max and
 // sum: M = max_s m_s, L = sum_s l_s 2^(m_s - M), out = sum_s o_s 2^(m_s - M) / L
