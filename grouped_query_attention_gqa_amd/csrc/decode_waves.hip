@@ -1,0 +1,391 @@
+// decode_waves.hip -- the bf16 decode step for groups of up to 8 query heads
+// per KV head: the memory-bound hot path.
+//
+// What it computes ("Grouped-Query Attention" concept page, 技术原理 steps
+// 2-4): for every sequence b and KV group g, the G query heads g*G ..
+// g*G+G-1 of the single new query row attend to K/V head g of the cache,
+// softmax(q K_g^T * scale) V_g over the ctx[b] cached keys.
+//
+// How (designed for CDNA4; flash-decoding on the inference-optimisation page
+// §10.2-§10.3 is prior art, not the blueprint):
+//  * Work list.  The (sequence, KV group) items are cut into tiles of 8 KB of
+//    K (32 keys at d = 128); the flat tile list is cut into equal contiguous
+//    slices, one per workgroup (two per CU).  Inside a slice, the run of
+//    tiles that belongs to one item (a segment) is dealt round-robin to the
+//    four waves.
+//  * No barrier per tile.  Each wave streams its own tiles: the K and V rows
+//    of the next tile are loaded straight into registers (coalesced 16-byte
+//    loads, 1 KB per wave instruction) while the current tile is computed, so
+//    every wave keeps 16 KB in flight and no LDS stage limits the depth.
+//  * Scores: the wave copies its K tile into its own LDS buffer (rows
+//    XOR-swizzled) and lane (key t, head set) then reads the whole row t and
+//    the q rows of its heads (an LDS broadcast) and forms full dot products
+//    with v_dot2_f32_bf16.  One K row read from HBM serves all G heads.
+//  * Online softmax per wave (inference-optimisation page §9.2.1) in exp2
+//    units with a lazy reference maximum: it moves only when a score exceeds
+//    it by 2^8, checked with one wave vote per tile, so the accumulators are
+//    rarely rescaled (the final o / l cancels the reference).  P is rounded to
+//    bf16 and l sums the rounded values.
+//  * Weighted V sum straight from the V registers: lane (row group, 8-byte
+//    column chunk) pairs two keys per v_perm and adds p_t v_t + p_t' v_t' for
+//    all G heads with one v_dot2 per column; 4 columns x G heads of fp32
+//    accumulators per lane.
+//  * At the end of a segment the four waves' (m, l, o) are merged in LDS with
+//    their common maximum (page §10.2); an item that lies wholly in the
+//    segment is normalised and stored, a cut item leaves one partial per
+//    workgroup for the merge kernel.
+#include "common.h"
+#include "kernels.h"
+#include "worklist.h"
+
+namespace gqa {
+namespace {
+
+constexpr int NT = 256;            // threads per workgroup; two workgroups per CU
+constexpr int NW = NT / kWave;     // waves per workgroup
+constexpr float TAU = 8.0f;        // lazy-rescale threshold (log2 units)
+
+template <int D, int GP>
+struct WCfg {
+    static constexpr int RB = D * 2;            // bytes per cache row
+    static constexpr int CPR = RB / 16;         // 16-byte chunks per row
+    static constexpr int RPL = kWave / CPR;     // rows per 1 KB wave load
+    static constexpr int TT = 8192 / RB;        // keys per tile (8 KB of K)
+    static constexpr int NL = TT / RPL;         // 16-byte K loads per lane per tile
+    static constexpr int VCPR = RB / 8;         // 8-byte V chunks per row
+    static constexpr int VRPL = kWave / VCPR;   // V rows per 512 B wave load
+    static constexpr int VNL = TT / VRPL;       // 8-byte V loads per lane per tile
+    static constexpr int NP = VNL / 2;          // key pairs per lane per tile
+    static constexpr int NGR = TT / 16;         // 16-key groups per tile
+    static constexpr int SWZ = CPR - 1;
+    static constexpr int HS0 = kWave / TT;
+    static constexpr int HS = HS0 < GP ? HS0 : GP;    // head sets in the score phase
+    static constexpr int HPL = GP / HS;              // heads per score lane
+    static constexpr int K_WAVE = TT * RB;           // LDS K buffer per wave
+    static constexpr int P_WAVE = VRPL * NP * GP;    // P words per wave (bf16 pairs)
+    static constexpr int Q_BYTES = GP * RB;
+    static constexpr int CMB = NW * GP * D * 4;      // wave partials, in the K buffers
+    static_assert(NL == 8 && VNL == 16 && NP == 8, "tile shape");
+    static_assert(GP >= 1 && GP <= 8 && (GP & (GP - 1)) == 0, "heads per group");
+    static_assert(CMB <= NW * K_WAVE, "the merge area fits in the K buffers");
+};
+
+template <int N>
+__device__ __forceinline__ void read_p(const uint32_t *src, uint32_t (&pp)[N])
+{
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const uint4 x = *reinterpret_cast<const uint4 *>(src + i);
+            pp[i] = x.x; pp[i + 1] = x.y; pp[i + 2] = x.z; pp[i + 3] = x.w;
+        }
+    } else if constexpr (N == 2) {
+        const uint2 x = *reinterpret_cast<const uint2 *>(src);
+        pp[0] = x.x; pp[1] = x.y;
+    } else {
+        pp[0] = src[0];
+    }
+}
+
+template <int D, int GP>
+__global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
+{
+    using C = WCfg<D, GP>;
+    __shared__ __attribute__((aligned(16))) char lds_k[NW * C::K_WAVE];
+    __shared__ __attribute__((aligned(16))) char lds_q[C::Q_BYTES];
+    __shared__ __attribute__((aligned(16))) uint32_t lds_p[NW][C::P_WAVE];
+    __shared__ float lds_alpha[NW][GP];
+    __shared__ float lds_ml[NW][GP][2];
+    __shared__ int32_t lds_prefix[kStreamRows + 1];
+    __shared__ int32_t lds_nvis[kStreamRows];
+    __shared__ int lds_waves[NW];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const CacheView &cache = p.cache;
+    const int G = p.G, H = p.H;
+
+    // ---- the flat tile list and this workgroup's slice ---------------------
+    build_tables<NT>(p, C::TT, lds_prefix, lds_nvis, lds_waves);
+    if (blockIdx.x == 0 && p.prefix != nullptr)   // the merge kernel reads it from the workspace
+        for (int r = tid; r <= p.rows; r += NT) p.prefix[r] = lds_prefix[r];
+    const int T = lds_prefix[p.rows];
+    const int64_t W = gridDim.x;
+    const int tau0 = (int)slice_start(blockIdx.x, T, W), tau1 = (int)slice_start(blockIdx.x + 1, T, W);
+    if (tau0 >= tau1) return;
+
+    // K loads: lane = (row krow, 16-byte chunk kc); score phase: lane = (key
+    // st, head set sh); V phase: lane = (row vr, 8-byte chunk vc: columns 4 vc ..)
+    const int krow = lane / C::CPR, kc = lane % C::CPR;
+    const int st = lane % C::TT, sh = lane / C::TT;
+    const bool s_lane = sh < C::HS;
+    const int qh = s_lane ? sh : 0;
+    const int vr = lane / C::VCPR, vc = lane % C::VCPR;
+    char *kw = lds_k + wave * C::K_WAVE;
+    uint32_t *pw = lds_p[wave];
+    uint16_t *pw16 = reinterpret_cast<uint16_t *>(pw);
+    // where the score lane's probability goes: key st is V row st % VRPL of
+    // V load 2 kk + half, so it pairs with the key VRPL rows away
+    const int p_slot = (((st % C::VRPL) * C::NP + st / (2 * C::VRPL)) * GP + qh * C::HPL) * 2 + ((st / C::VRPL) & 1);
+
+    Cursor c = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);
+    int tau = tau0;
+    while (tau < tau1) {
+        const int seg_end = min(tau1, c.item0 + c.tiles);
+        const int n_seg = seg_end - tau;
+        const int j_first = c.j;
+        const int64_t row_g = p.row0 + c.row;
+        const int b = (int)(row_g / p.Sq);
+        const int n_vis = c.n_vis;
+        const int g = c.g;
+
+        // q rows of the item -> LDS (padded heads are zero)
+        if (tid < GP * C::CPR) {
+            const int r = tid / C::CPR, ch = tid % C::CPR;
+            uint4 x = make_uint4(0u, 0u, 0u, 0u);
+            if (r < G) x = ld16(p.q + ((row_g * H + (int64_t)g * G + r) * D) * 2 + ch * 16);
+            *reinterpret_cast<uint4 *>(lds_q + r * C::RB + ch * 16) = x;
+        }
+        __syncthreads();
+
+        // K and V rows of tile j of the item.  A wave load covers rows of one
+        // 16-key group, whose cache rows are consecutive (contiguous cache,
+        // or one block of >= 16 tokens): a wave-uniform 64-bit base plus a
+        // 32-bit lane offset.
+        const uint32_t k_off = (uint32_t)(krow * C::RB + kc * 16);
+        const uint32_t v_off = (uint32_t)(vr * C::RB + vc * 8);
+        auto load_tile = [&](int j, uint4 (&kr)[C::NL], uint2 (&vv)[C::VNL]) {
+            const int key0 = j * C::TT;
+            const int nvalid = min(C::TT, n_vis - key0);
+            int64_t gb[C::NGR];   // cache row of key key0 + 16 gi (wave-uniform), -1: none
+#pragma unroll
+            for (int gi = 0; gi < C::NGR; ++gi)
+                gb[gi] = 16 * gi < nvalid ? cache_row_wave(cache, b, g, key0 + 16 * gi) : -1;
+#pragma unroll
+            for (int i = 0; i < C::NL; ++i) {
+                const int r0 = i * C::RPL;                       // first tile row of the load
+                const int64_t base = gb[r0 / 16];
+                uint4 x = make_uint4(0u, 0u, 0u, 0u);
+                if (base >= 0 && r0 + krow < nvalid)
+                    x = ld16(cache.k + (base + r0 % 16) * C::RB + k_off);
+                kr[i] = x;
+            }
+#pragma unroll
+            for (int i = 0; i < C::VNL; ++i) {
+                const int r0 = i * C::VRPL;
+                const int64_t base = gb[r0 / 16];
+                uint2 y = make_uint2(0u, 0u);
+                if (base >= 0 && r0 + vr < nvalid)
+                    y = *reinterpret_cast<const uint2 *>(cache.v + (base + r0 % 16) * C::RB + v_off);
+                vv[i] = y;
+            }
+        };
+
+        // ---- this wave's tiles of the segment: j_first + wave + NW * i -------
+        const int n_w = n_seg > wave ? (n_seg - wave + NW - 1) / NW : 0;
+        float m_ref[C::HPL], l_run[C::HPL];
+#pragma unroll
+        for (int h = 0; h < C::HPL; ++h) { m_ref[h] = -INFINITY; l_run[h] = 0.f; }
+        float acc[GP][4];
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
+
+        uint4 kr[C::NL];
+        uint2 va[C::VNL], vb[C::VNL];
+        if (n_w > 0) load_tile(j_first + wave, kr, va);
+
+        auto step = [&](int i, uint2 (&vcur)[C::VNL], uint2 (&vnext)[C::VNL]) {
+            const int j = j_first + wave + NW * i;
+            const int nvalid = min(C::TT, n_vis - j * C::TT);
+            // K tile -> this wave's LDS buffer, row t's chunk x at slot x ^ (t & SWZ)
+#pragma unroll
+            for (int ii = 0; ii < C::NL; ++ii) {
+                const int rt = ii * C::RPL + krow;
+                *reinterpret_cast<uint4 *>(kw + rt * C::RB + ((kc ^ (rt & C::SWZ)) * 16)) = kr[ii];
+            }
+            if (i + 1 < n_w) load_tile(j + NW, kr, vnext);
+
+            // ---- scores --------------------------------------------------------
+            float sc[C::HPL];
+            {
+                float a0[C::HPL], a1[C::HPL];
+#pragma unroll
+                for (int h = 0; h < C::HPL; ++h) { a0[h] = 0.f; a1[h] = 0.f; }
+#pragma unroll
+                for (int ch = 0; ch < C::CPR; ++ch) {
+                    const uint4 kv = *reinterpret_cast<const uint4 *>(kw + st * C::RB + ((ch ^ (st & C::SWZ)) * 16));
+#pragma unroll
+                    for (int h = 0; h < C::HPL; ++h) {
+                        const uint4 qv = *reinterpret_cast<const uint4 *>(lds_q + (qh * C::HPL + h) * C::RB + ch * 16);
+                        a0[h] = dot2_bf16(qv.x, kv.x, a0[h]);
+                        a1[h] = dot2_bf16(qv.y, kv.y, a1[h]);
+                        a0[h] = dot2_bf16(qv.z, kv.z, a0[h]);
+                        a1[h] = dot2_bf16(qv.w, kv.w, a1[h]);
+                    }
+                }
+                const bool valid = s_lane && st < nvalid;
+#pragma unroll
+                for (int h = 0; h < C::HPL; ++h) sc[h] = valid ? (a0[h] + a1[h]) * p.scale_log2 : -INFINITY;
+            }
+
+            // ---- lazy reference maximum: one vote per tile ---------------------
+            bool need = false;
+#pragma unroll
+            for (int h = 0; h < C::HPL; ++h) need |= sc[h] > m_ref[h] + TAU;
+            const bool rescale = __ballot(need) != 0;
+            if (rescale) {
+#pragma unroll
+                for (int h = 0; h < C::HPL; ++h) {
+                    const float mt = group_max<C::TT>(sc[h]);
+                    const float mn = mt > m_ref[h] + TAU ? mt : m_ref[h];
+                    const float al = mn == m_ref[h] ? 1.f : fast_exp2(m_ref[h] - mn);   // 0 on the first tile
+                    l_run[h] *= al;
+                    m_ref[h] = mn;
+                    if (s_lane && st == 0) lds_alpha[wave][qh * C::HPL + h] = al;
+                }
+            }
+            // ---- P (bf16) for the V sum; l sums the rounded values -------------
+#pragma unroll
+            for (int h = 0; h < C::HPL; ++h) {
+                const float pk = fast_exp2(sc[h] - m_ref[h]);   // 0 for keys past the end
+                const uint32_t pb = f32_to_bf16_rne(pk);
+                l_run[h] += __uint_as_float(pb << 16);
+                if (s_lane) pw16[p_slot + 2 * h] = (uint16_t)pb;
+            }
+
+            // ---- o = o * alpha + sum_t p_t v_t ---------------------------------
+            if (rescale) {
+#pragma unroll
+                for (int h = 0; h < GP; ++h) {
+                    const float al = lds_alpha[wave][h];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[h][e] *= al;
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < C::NP; ++kk) {
+                const uint2 a = vcur[2 * kk], bb = vcur[2 * kk + 1];   // rows 2kk*VRPL + vr and VRPL later
+                uint32_t vv[4];
+                vv[0] = pair_lo(a.x, bb.x); vv[1] = pair_hi(a.x, bb.x);
+                vv[2] = pair_lo(a.y, bb.y); vv[3] = pair_hi(a.y, bb.y);
+                uint32_t pp[GP];
+                read_p<GP>(pw + (vr * C::NP + kk) * GP, pp);
+#pragma unroll
+                for (int h = 0; h < GP; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[h][e] = dot2_bf16(pp[h], vv[e], acc[h][e]);
+            }
+        };
+
+        for (int i = 0; i < n_w; i += 2) {
+            step(i, va, vb);
+            if (i + 1 < n_w) step(i + 1, vb, va);
+        }
+
+        // ---- merge the waves' pieces of the segment ---------------------------
+#pragma unroll
+        for (int m = C::VCPR; m < kWave; m <<= 1)
+#pragma unroll
+            for (int h = 0; h < GP; ++h)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[h][e] += __shfl_xor(acc[h][e], m, kWave);
+#pragma unroll
+        for (int h = 0; h < C::HPL; ++h) l_run[h] = group_sum<C::TT>(l_run[h]);
+        __syncthreads();   // every wave is done with its K buffer: it becomes the merge area
+        float *cmb = reinterpret_cast<float *>(lds_k);   // [NW][GP][D]
+        if (lane < C::VCPR) {
+#pragma unroll
+            for (int h = 0; h < GP; ++h)
+                *reinterpret_cast<float4 *>(cmb + (wave * GP + h) * D + lane * 4) =
+                    make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+        }
+        if (s_lane && st == 0) {
+#pragma unroll
+            for (int h = 0; h < C::HPL; ++h) {
+                lds_ml[wave][qh * C::HPL + h][0] = n_w > 0 ? m_ref[h] : -INFINITY;
+                lds_ml[wave][qh * C::HPL + h][1] = n_w > 0 ? l_run[h] : 0.f;
+            }
+        }
+        __syncthreads();
+        const bool whole = tau == c.item0 && seg_end == c.item0 + c.tiles;
+        const int slot = tau0 < c.item0 ? 1 : 0;
+        const int64_t head0 = row_g * H + (int64_t)g * G;
+        for (int idx = tid; idx < GP * D / 4; idx += NT) {
+            const int h = idx / (D / 4), col = (idx % (D / 4)) * 4;
+            if (h >= G) continue;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_ml[w][h][0]);
+            float L = 0.f;
+            float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = lds_ml[w][h][0];
+                if (mw == -INFINITY) continue;   // a wave without tiles in the segment
+                const float wt = fast_exp2(mw - M);
+                L += lds_ml[w][h][1] * wt;
+                const float4 o = *reinterpret_cast<const float4 *>(cmb + (w * GP + h) * D + col);
+                O.x += o.x * wt;
+                O.y += o.y * wt;
+                O.z += o.z * wt;
+                O.w += o.w * wt;
+            }
+            if (whole) {
+                const float inv = 1.f / L;
+                *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) + (head0 + h) * D + col) =
+                    make_uint2(pack_bf16x2(O.x * inv, O.y * inv), pack_bf16x2(O.z * inv, O.w * inv));
+            } else {
+                const int64_t sr = ((int64_t)blockIdx.x * 2 + slot) * G + h;
+                *reinterpret_cast<float4 *>(p.ws_o + sr * D + col) = O;
+                if (col == 0) {
+                    p.ws_ml[sr * 2] = M;
+                    p.ws_ml[sr * 2 + 1] = L;
+                }
+            }
+        }
+        __syncthreads();   // the merge area and q are free again
+
+        tau = seg_end;
+        if (tau < tau1) c = cursor_at(lds_prefix, lds_nvis, p.rows, tau, C::TT);
+    }
+}
+
+template <int D, int GP>
+hipError_t launch_w(const RowAttnParams &p, hipStream_t s)
+{
+    hipLaunchKernelGGL((decode_waves_kernel<D, GP>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_merge_pieces(p, WCfg<D, GP>::TT, p.num_wgs, s);
+}
+
+template <int D>
+hipError_t launch_wd(const RowAttnParams &p, int gp, hipStream_t s)
+{
+    switch (gp) {
+    case 1: return launch_w<D, 1>(p, s);
+    case 2: return launch_w<D, 2>(p, s);
+    case 4: return launch_w<D, 4>(p, s);
+    case 8: return launch_w<D, 8>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool decode_waves_supported(const RowAttnParams &p, int gp)
+{
+    // paged caches need blocks of at least 16 tokens (a wave load stays in one block)
+    return !p.prefill && !p.whole_items && p.cache.elem_bytes == 2 && gp <= 8 &&
+           (p.cache.d == 64 || p.cache.d == 128) && p.num_wgs <= kStreamWGs &&
+           (p.cache.block_table == nullptr || p.cache.log2_bs >= 4);
+}
+
+hipError_t launch_decode_waves(const RowAttnParams &p, int gp, hipStream_t stream)
+{
+    if (!decode_waves_supported(p, gp)) return hipErrorInvalidValue;
+    return p.cache.d == 128 ? launch_wd<128>(p, gp, stream) : launch_wd<64>(p, gp, stream);
+}
+
+}  // namespace gqa

@@ -84,23 +84,50 @@ __device__ __forceinline__ int64_t cache_row(const CacheView &c, int b, int g, i
     return (((int64_t)blk * c.K + g) << c.log2_bs) + (pos & ((1 << c.log2_bs) - 1));
 }
 
+// Wave-uniform 32-bit load through the scalar data cache (s_load_dword).  It
+// is counted by lgkmcnt, so waiting for it does not wait behind the wave's
+// vector-memory loads in flight (a vector load of the same word would need
+// vmcnt(0), which drains every load the wave has issued).
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t *p)
+{
+    // readfirstlane returns a signed int: go through uint32_t so that the
+    // low half is zero-extended, not sign-extended, into the 64-bit address
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const uint64_t ua = ((uint64_t)hi << 32) | (uint64_t)lo;
+    int32_t v;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ua) : "memory");
+#pragma clang diagnostic pop
+    return v;
+}
+
 // The same lookup for loads where all active lanes of a wave ask for
 // positions inside one 16-aligned group of 16 tokens.  With blocks of 16 or
-// more tokens that group lies in one block, so one wave-uniform table read (a
-// scalar load, which does not wait behind the wave's outstanding vector
-// loads) serves the whole wave.
+// more tokens that group lies in one block, so one wave-uniform scalar
+// table read serves the whole wave.
 __device__ __forceinline__ int64_t cache_row_wave(const CacheView &c, int b, int g, int pos)
 {
     if (c.block_table == nullptr) return ((int64_t)b * c.K + g) * c.S_max + pos;
     if (c.log2_bs < 4) return cache_row(c, b, g, pos);
-    const int lead = __builtin_amdgcn_readfirstlane(pos);
-    const int32_t blk = c.block_table[(int64_t)b * c.max_blocks + (lead >> c.log2_bs)];
+    // the column is checked so that the scalar load stays inside the table
+    // even if it ran for a wave with no active lane
+    const int col = __builtin_amdgcn_readfirstlane(pos) >> c.log2_bs;
+    if (col < 0 || col >= c.max_blocks) return -1;
+    const int32_t blk = scalar_load_i32(c.block_table + (int64_t)b * c.max_blocks + col);
     if (blk < 0 || blk >= c.num_blocks) return -1;
     return (((int64_t)blk * c.K + g) << c.log2_bs) + (pos & ((1 << c.log2_bs) - 1));
 }
 
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_row_attention(const RowAttnParams &p, int gp, hipStream_t stream);
+// bf16 decode for padded group sizes gp <= 8 (one launch of at most kStreamRows rows)
+bool decode_waves_supported(const RowAttnParams &p, int gp);
+hipError_t launch_decode_waves(const RowAttnParams &p, int gp, hipStream_t stream);
+// merge of the partial pieces that W workgroup slices of tt-key tiles left in the workspace
+hipError_t launch_merge_pieces(const RowAttnParams &p, int tt, int W, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams &p, hipStream_t stream);
 
 constexpr int kKeyTile = 64;   // prefill key tile

@@ -40,6 +40,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "worklist.h"
 
 namespace gqa {
 namespace {
@@ -78,17 +79,24 @@ __device__ __forceinline__ void wait_vm()
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
-// Wait until at most n_after tiles of L loads each are in flight.  Loads
-// return in issue order, so the tile issued before them has landed.
-template <int L>
-__device__ __forceinline__ void wait_tiles(int n_after)
+// s_waitcnt vmcnt(n) for a run-time n in [0, kMaxWait]: a branch tree over
+// the immediates (n is wave-uniform, so this is scalar code).
+constexpr int kMaxWait = 31;
+template <int LO, int HI>
+__device__ __forceinline__ void wait_vm_range(int n)
 {
-    switch (n_after) {
-    case 0: wait_vm<0>(); break;
-    case 1: wait_vm<L>(); break;
-    default: wait_vm<2 * L>(); break;
+    if constexpr (LO == HI) {
+        wait_vm<LO>();
+    } else {
+        constexpr int MID = (LO + HI) / 2;
+        if (n <= MID) wait_vm_range<LO, MID>(n);
+        else wait_vm_range<MID + 1, HI>(n);
     }
 }
+// Loads return in issue order, so "at most n loads in flight" means every
+// load issued before the last n has landed.  n above the range waits for
+// more than needed, which is always safe.
+__device__ __forceinline__ void wait_vm_dyn(int n) { wait_vm_range<0, kMaxWait>(n < kMaxWait ? n : kMaxWait); }
 __device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }   // lgkmcnt(0)
 
 // Workgroup barrier without the memory fence of __syncthreads() (that fence
@@ -136,134 +144,29 @@ struct Cfg {
     // two workgroups per CU when three stages fit in half the LDS, else one
     static constexpr int LIMIT = (LDS_LIMIT - OTHER) / STAGE >= 3 ? LDS_LIMIT : 2 * LDS_LIMIT;
     static constexpr int NBUF0 = (LIMIT - OTHER) / STAGE;
-    static constexpr int NBUF = NBUF0 > 4 ? 4 : NBUF0;
-    // vector-memory loads per wave per tile (waves below Q_EXTRA load one more q block)
-    static constexpr int L0 = 2 * LK + QN / NW;
+    static constexpr int NBUF = NBUF0 > 6 ? 6 : NBUF0;
+    static constexpr int A = NBUF - 1;                 // tiles in flight
+    // q loads per wave of a tile that needs q (waves below Q_EXTRA load one more block)
+    static constexpr int QL = QN / NW;
     static constexpr int Q_EXTRA = QN % NW;
+    // loads one wave issues per pipeline iteration (K and q of one tile, V of another)
+    static constexpr int MAX_ITER_LOADS = 2 * LK + QL + (Q_EXTRA ? 1 : 0);
 
     static_assert(LK >= 1 && LK * 1024 * NW == K_BYTES, "K tile does not split into 1 KB loads per wave");
     static_assert(CPW >= 1 && CPW * NW == CPR, "column pieces do not split over the waves");
     static_assert(TGL >= 1 && TGL * CPW * HG == kWave, "weighted-sum lanes");
     static_assert(!BF16 || TPT % 2 == 0, "key pairs need an even key count per lane");
     static_assert(NS * TPH == TT && S_THREADS <= NT, "score layout");
-    static_assert(NBUF >= 3 && NBUF <= 4, "stage count (the pipeline keeps NBUF-2 tiles in flight, waits assume <= 2)");
+    static_assert(NBUF >= 2, "stage count");
+    static_assert(MAX_ITER_LOADS < 32 && (A - 1) * MAX_ITER_LOADS <= kMaxWait, "load counts of the pipeline waits");
 };
-
-// ---------------------------------------------------------------------------
-// the flat tile list
-// ---------------------------------------------------------------------------
-
-// Visible keys of query row `row` (b * Sq + i), clamped to the cache capacity.
-__device__ __forceinline__ int row_visible(const RowAttnParams &p, int64_t row)
-{
-    const int b = (int)(row / p.Sq);
-    const int i = (int)(row % p.Sq);
-    int64_t n;
-    if (!p.prefill) {
-        n = p.ctx_lens[b];
-    } else {
-        const int64_t start = p.start_pos[b];
-        n = p.causal ? start + i + 1 : start + p.Sq;
-    }
-    if (n > p.cache.capacity) n = p.cache.capacity;
-    if (n < 0) n = 0;
-    return (int)n;
-}
-
-// For the rows of this launch (local rows 0 .. rows-1, at most kStreamRows):
-// nvis[r] = visible keys, prefix[r] = K * sum_{r' < r} tiles(r'),
-// prefix[rows] = the number of tiles T.  Every thread of the workgroup calls
-// it; thread i handles the consecutive rows i*per .. i*per+per-1, so any row
-// count up to kStreamRows is covered whatever the workgroup size.
-__device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, int32_t *nvis, int *lds_waves)
-{
-    static_assert(kStreamRows % NT == 0, "rows per thread");
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int rows = p.rows;
-    const int per = (rows + NT - 1) / NT;
-    const int r0 = tid * per;
-    int local = 0;
-    for (int k = 0; k < per; ++k) {
-        const int r = r0 + k;
-        if (r < rows) {
-            const int n = row_visible(p, p.row0 + r);
-            nvis[r] = n;
-            local += (n + tt - 1) / tt;
-        }
-    }
-    int x = local;   // inclusive scan over the wave, then over the waves
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) lds_waves[wave] = x;
-    __syncthreads();
-    int before = 0;
-    for (int w = 0; w < wave; ++w) before += lds_waves[w];
-    int run = before + x - local;
-    for (int k = 0; k < per; ++k) {
-        const int r = r0 + k;
-        if (r < rows) {
-            prefix[r] = run * p.cache.K;
-            run += (nvis[r] + tt - 1) / tt;
-        }
-    }
-    if (tid == NT - 1) prefix[rows] = (before + x) * p.cache.K;
-    __syncthreads();
-}
-
-struct Cursor {
-    int row;       // local query row
-    int g;         // KV group
-    int j;         // tile within the item
-    int tiles;     // tiles of the item
-    int n_vis;     // visible keys of the row
-    int item0;     // flat index of the item's first tile
-};
-
-__device__ __forceinline__ Cursor cursor_at(const int32_t *prefix, const int32_t *nvis, int rows, int tau, int tt)
-{
-    // last row whose prefix is <= tau (rows without tiles share their prefix)
-    int lo = 0, hi = rows - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (prefix[mid] <= tau) lo = mid; else hi = mid - 1;
-    }
-    Cursor c;
-    c.row = lo;
-    c.n_vis = nvis[lo];
-    c.tiles = (c.n_vis + tt - 1) / tt;
-    const int off = tau - prefix[lo];
-    c.g = off / c.tiles;
-    c.j = off % c.tiles;
-    c.item0 = prefix[lo] + c.g * c.tiles;
-    return c;
-}
-
-__device__ __forceinline__ void cursor_next(const int32_t *nvis, int rows, int K, Cursor &c, int tt)
-{
-    if (++c.j < c.tiles) return;
-    c.j = 0;
-    c.item0 += c.tiles;
-    if (++c.g < K) return;
-    c.g = 0;
-    do {
-        ++c.row;
-        if (c.row >= rows) return;
-        c.n_vis = nvis[c.row];
-        c.tiles = (c.n_vis + tt - 1) / tt;
-    } while (c.tiles == 0);
-}
-
-__device__ __forceinline__ int64_t slice_start(int64_t w, int64_t T, int64_t W) { return w * T / W; }
 
 // ---------------------------------------------------------------------------
 // main kernel
 // ---------------------------------------------------------------------------
 
 template <int D, int GP, bool BF16>
-__global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p)
+__global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) void stream_attention_kernel(RowAttnParams p)
 {
     using C = Cfg<D, GP, BF16>;
     __shared__ __attribute__((aligned(1024))) char smem[C::NBUF * C::STAGE];
@@ -278,7 +181,7 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
     const int G = p.G, H = p.H;
 
     // ---- the flat tile list and this workgroup's slice ---------------------
-    build_tables(p, C::TT, lds_prefix, lds_nvis, lds_waves);
+    build_tables<NT>(p, C::TT, lds_prefix, lds_nvis, lds_waves);
     if (blockIdx.x == 0 && p.prefix != nullptr)   // the merge kernel reads it from the workspace
         for (int r = tid; r <= p.rows; r += NT) p.prefix[r] = lds_prefix[r];
     const int T = lds_prefix[p.rows];
@@ -307,40 +210,40 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
     }
     if (tau0 >= tau1) return;
     const bool q_extra = wave < C::Q_EXTRA;
-    const int q_loads = C::QN / NW + (q_extra ? 1 : 0);
+    const int q_loads = C::QL + (q_extra ? 1 : 0);
 
-    // ---- LDS-direct loads of one tile into one stage ----------------------
-    auto issue = [&](const Cursor &c, int stage) {
-        char *base = smem + stage * C::STAGE;
+    // ---- LDS-direct loads of one tile's K (and q) or V into a stage ----------
+    // Source address of this lane's 16 bytes in 1 KB block `blk` of the tile
+    // (nullptr: the row is past the item's keys or its block id is invalid).
+    auto row_src = [&](const Cursor &c, int blk) -> int64_t {
         const int tile0 = c.j * C::TT;
         const int nvalid = min(C::TT, c.n_vis - tile0);
-        const int64_t row_g = (int64_t)p.row0 + c.row;
-        const int b = (int)(row_g / p.Sq);
+        const int t = blk * C::RPK + lane / C::CPR;
+        if (blk * C::RPK >= nvalid) return -1;
+        const int b = (int)(((int64_t)p.row0 + c.row) / p.Sq);
+        if (cache.block_table == nullptr || cache.log2_bs >= 4) {
+            // the block's RPK consecutive rows lie in one 16-row group,
+            // hence in one cache block: one lookup per wave
+            const int64_t r0 = cache_row_wave(cache, b, c.g, tile0 + blk * C::RPK);
+            return (r0 >= 0 && t < nvalid) ? r0 + (t - blk * C::RPK) : -1;
+        }
+        return t < nvalid ? cache_row(cache, b, c.g, tile0 + t) : -1;   // blocks shorter than 16 rows
+    };
+    // K rows are stored XOR-swizzled: piece x of row t lands in slot x ^ (t & SWZ).
+    auto issue_k = [&](const Cursor &c, bool with_q, int stage) -> int {
+        char *base = smem + stage * C::STAGE;
 #pragma unroll
         for (int k = 0; k < C::LK; ++k) {
-            const int blk = wave + NW * k;              // 1 KB block of the tile
-            const int t = blk * C::RPK + lane / C::CPR; // row of this lane
+            const int blk = wave + NW * k;
+            const int t = blk * C::RPK + lane / C::CPR;
             const int piece = lane % C::CPR;
-            const void *srck = &kZero16;
-            const void *srcv = &kZero16;
-            if (blk * C::RPK < nvalid) {
-                int64_t r = -1;
-                if (cache.block_table == nullptr || cache.log2_bs >= 4) {
-                    // the block's RPK consecutive rows lie in one 16-row group,
-                    // hence in one cache block: one lookup per wave
-                    const int64_t row0 = cache_row_wave(cache, b, c.g, tile0 + blk * C::RPK);
-                    if (row0 >= 0 && t < nvalid) r = row0 + (t - blk * C::RPK);
-                } else if (t < nvalid) {
-                    r = cache_row(cache, b, c.g, tile0 + t);   // blocks shorter than 16 rows
-                }
-                if (r >= 0) {
-                    srck = cache.k + r * C::RB + (piece ^ (t & C::SWZ)) * 16;
-                    srcv = cache.v + r * C::RB + piece * 16;
-                }
-            }
-            dma16(srck, base + blk * 1024);
-            dma16(srcv, base + C::K_BYTES + blk * 1024);
+            const int64_t r = row_src(c, blk);
+            const void *src = r >= 0 ? (const void *)(cache.k + r * C::RB + (piece ^ (t & C::SWZ)) * 16)
+                                     : (const void *)&kZero16;
+            dma16(src, base + blk * 1024);
         }
+        if (!with_q) return C::LK;
+        const int64_t row_g = (int64_t)p.row0 + c.row;
         for (int k = 0; k < q_loads; ++k) {
             const int qblk = wave + NW * k;
             const int off = qblk * 1024 + lane * 16;
@@ -350,6 +253,19 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
                 src = p.q + ((row_g * H + (int64_t)c.g * G + r) * D) * C::ES + (off % C::RB);
             dma16(src, base + 2 * C::K_BYTES + qblk * 1024);
         }
+        return C::LK + q_loads;
+    };
+    auto issue_v = [&](const Cursor &c, int stage) -> int {
+        char *base = smem + stage * C::STAGE + C::K_BYTES;
+#pragma unroll
+        for (int k = 0; k < C::LK; ++k) {
+            const int blk = wave + NW * k;
+            const int piece = lane % C::CPR;
+            const int64_t r = row_src(c, blk);
+            const void *src = r >= 0 ? (const void *)(cache.v + r * C::RB + piece * 16) : (const void *)&kZero16;
+            dma16(src, base + blk * 1024);
+        }
+        return C::LK;
     };
 
     // ---- per-thread state ---------------------------------------------------
@@ -371,36 +287,48 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
         for (int e = 0; e < C::CE; ++e) acc[i][e] = 0.f;
 
     // ---- software pipeline ---------------------------------------------------
-    // Iteration tau (one barrier each): the scores of tile tau and the V sum
-    // of tile tau-1 run back to back with no barrier between them (they touch
-    // different stages and different halves of the double-buffered P / alpha /
-    // (m, l) arrays), while tiles tau+1 .. tau+A are in flight.  Stage use:
-    // tau (K, q), tau-1 (V), tau+1 .. tau+A (loading) = NBUF.
-    constexpr int A = C::NBUF - 2;
-    Cursor pc = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);
-    const int pre = min(A, tau1 - tau0);
-    for (int i = 0; i < pre; ++i) {
-        issue(pc, i);
-        cursor_next(lds_nvis, p.rows, cache.K, pc, C::TT);
-    }
+    // Iteration tau (one barrier each) computes the scores of tile tau and the
+    // V sum of tile tau-1; they touch different halves of the double-buffered
+    // P / alpha / (m, l) arrays.  Tile t lives in stage (t - tau0) % NBUF.
+    // Its K (with q when it starts an item or the slice) is issued A = NBUF-1
+    // iterations ahead and its V one iteration later, because the V sum of a
+    // tile runs one iteration after its scores: A tiles are in flight while
+    // only one stage's K and one stage's V are being read.
+    // Virtual iteration i issues K(i + A) and V(i + A - 1); iterations
+    // tau0 - A .. tau0 - 1 form the prologue.
+    constexpr int A = C::A;
+    Cursor kc = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);   // next K to issue
+    Cursor vc = kc;                                                     // next V to issue
+    uint32_t hist = 0;   // loads of the last virtual iterations, 5 bits each (newest lowest)
+    auto issue_iter = [&](int i) {
+        int n = 0;
+        const int tk = i + A, tv = i + A - 1;
+        if (tk >= tau0 && tk < tau1) {
+            n += issue_k(kc, kc.j == 0 || tk == tau0, (tk - tau0) % C::NBUF);
+            cursor_next(lds_nvis, p.rows, cache.K, kc, C::TT);
+        }
+        if (tv >= tau0 && tv < tau1) {
+            n += issue_v(vc, (tv - tau0) % C::NBUF);
+            cursor_next(lds_nvis, p.rows, cache.K, vc, C::TT);
+        }
+        hist = (hist << 5) | (uint32_t)n;
+    };
+    for (int i = tau0 - A; i < tau0; ++i) issue_iter(i);
     Cursor cs = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);   // tile of the score phase
     Cursor cv = cs;                                                    // tile of the V phase
     int piece0 = tau0;                                // first tile of the V phase's piece
 
     for (int tau = tau0; tau <= tau1; ++tau) {
+        // K(tau) and V(tau-1) came from virtual iteration tau - A; the loads
+        // of the A - 1 iterations after it may stay in flight.
+        int after = 0;
+#pragma unroll
+        for (int k = 0; k < A - 1; ++k) after += (hist >> (5 * k)) & 31;
+        wait_vm_dyn(after);
+        barrier();
+        issue_iter(tau);
         const bool do_s = tau < tau1;
         const bool do_v = tau > tau0;
-        if (do_s) {
-            // tile tau's loads are the oldest in flight
-            const int n_after = min(A - 1, tau1 - 1 - tau);
-            if (q_extra) wait_tiles<C::L0 + 1>(n_after);
-            else wait_tiles<C::L0>(n_after);
-        }
-        barrier();
-        if (tau + A < tau1) {
-            issue(pc, (tau + A - tau0) % C::NBUF);
-            cursor_next(lds_nvis, p.rows, cache.K, pc, C::TT);
-        }
         const int buf = tau & 1;                      // P / alpha / (m, l) half written by this S phase
 
         // ---- scores and online softmax of tile tau ----------------------------
@@ -602,17 +530,26 @@ __global__ __launch_bounds__(NT, 2) void stream_attention_kernel(RowAttnParams p
 // Merge of the pieces of one (row, KV group) item with their global max and
 // sum: M = max_s m_s, L = sum_s l_s 2^(m_s - M), out = sum_s o_s 2^(m_s - M) / L
 // (m in log2 units).  Items held by one workgroup were stored by it; rows
-// without a visible key get zeros.
+// without a visible key get zeros.  Block (g, row, z) handles heads
+// z*kMergeHeads .. of the item; the workspace slots of its pieces are listed
+// once in LDS.
+constexpr int kMergeHeads = 8;
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_pieces_kernel(RowAttnParams p, int tt, int W)
 {
+    __shared__ int slots[kStreamWGs];
+    __shared__ int n_slots;
     const int g = blockIdx.x;
     const int row = blockIdx.y;                       // local row of this launch
     const int G = p.G;
-    const int64_t head0 = ((int64_t)p.row0 + row) * p.H + (int64_t)g * G;
+    const int h0 = blockIdx.z * kMergeHeads;
+    if (h0 >= G) return;
+    const int nh = min(kMergeHeads, G - h0);
+    const int64_t head0 = ((int64_t)p.row0 + row) * p.H + (int64_t)g * G + h0;
     const int n_vis = row_visible(p, (int64_t)p.row0 + row);
     if (n_vis <= 0) {
-        for (int idx = threadIdx.x; idx < G * D; idx += 256) {
+        for (int idx = threadIdx.x; idx < nh * D; idx += 256) {
             const int64_t o = head0 * D + idx;
             if constexpr (BF16) reinterpret_cast<uint16_t *>(p.out)[o] = 0;
             else reinterpret_cast<float *>(p.out)[o] = 0.f;
@@ -630,31 +567,36 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(RowAttnParams p, int 
     };
     const int64_t wa = owner(a), wb = owner(e);
     if (wa == wb) return;
-    for (int idx = threadIdx.x; idx < G * D / 4; idx += 256) {
-        const int r = (4 * idx) / D, col = (4 * idx) % D;
+    if (threadIdx.x == 0) {
         // workgroups whose slice is empty (fewer tiles than workgroups) hold nothing
-        float M = -INFINITY;
+        int n = 0;
         for (int64_t w = wa; w <= wb; ++w) {
-            if (slice_start(w, T, W) == slice_start(w + 1, T, W)) continue;
-            const int slot = slice_start(w, T, W) < a ? 1 : 0;
-            M = fmaxf(M, p.ws_ml[((w * 2 + slot) * G + r) * 2]);
+            const int64_t s0 = slice_start(w, T, W);
+            if (s0 == slice_start(w + 1, T, W)) continue;
+            slots[n++] = (int)(w * 2 + (s0 < a ? 1 : 0));
         }
+        n_slots = n;
+    }
+    __syncthreads();
+    const int ns = n_slots;
+    for (int idx = threadIdx.x; idx < nh * D / 4; idx += 256) {
+        const int r = h0 + (4 * idx) / D, col = (4 * idx) % D;
+        float M = -INFINITY;
+        for (int k = 0; k < ns; ++k) M = fmaxf(M, p.ws_ml[((int64_t)slots[k] * G + r) * 2]);
         float L = 0.f;
         float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int64_t w = wa; w <= wb; ++w) {
-            if (slice_start(w, T, W) == slice_start(w + 1, T, W)) continue;
-            const int slot = slice_start(w, T, W) < a ? 1 : 0;
-            const float *ml = p.ws_ml + ((w * 2 + slot) * G + r) * 2;
-            const float wt = fast_exp2(ml[0] - M);
-            L += ml[1] * wt;
-            const float4 os = *reinterpret_cast<const float4 *>(p.ws_o + ((w * 2 + slot) * G + r) * D + col);
+        for (int k = 0; k < ns; ++k) {
+            const int64_t sr = (int64_t)slots[k] * G + r;
+            const float wt = fast_exp2(p.ws_ml[sr * 2] - M);
+            L += p.ws_ml[sr * 2 + 1] * wt;
+            const float4 os = *reinterpret_cast<const float4 *>(p.ws_o + sr * D + col);
             O.x += os.x * wt;
             O.y += os.y * wt;
             O.z += os.z * wt;
             O.w += os.w * wt;
         }
         const float inv = 1.f / L;
-        const int64_t o = (head0 + r) * D + col;
+        const int64_t o = (head0 - h0 + r) * D + col;
         if constexpr (BF16) {
             *reinterpret_cast<uint2 *>(reinterpret_cast<uint16_t *>(p.out) + o) =
                 make_uint2(pack_bf16x2(O.x * inv, O.y * inv), pack_bf16x2(O.z * inv, O.w * inv));
@@ -665,42 +607,68 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(RowAttnParams p, int 
     }
 }
 
+// Workgroups per launch: the caller's count (two per CU) when two fit in a
+// CU's LDS, half of it when one workgroup needs more than half the LDS (a
+// second wave of slices would only run after the first).
+template <int D, int GP, bool BF16>
+hipError_t launch_g(const RowAttnParams &p0, hipStream_t s)
+{
+    using C = Cfg<D, GP, BF16>;
+    RowAttnParams p = p0;
+    if (C::LIMIT > LDS_LIMIT && p.num_wgs > 1) p.num_wgs /= 2;
+    hipLaunchKernelGGL((stream_attention_kernel<D, GP, BF16>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.whole_items) return e;
+    return launch_merge_pieces(p, C::TT, p.num_wgs, s);
+}
+
 template <int D, bool BF16>
 hipError_t launch_d(const RowAttnParams &p, int gp, hipStream_t s)
 {
-    const int tt = K_TILE_BYTES / (D * (BF16 ? 2 : 4));
-    const int W = p.num_wgs;
     switch (gp) {
-    case 1: hipLaunchKernelGGL((stream_attention_kernel<D, 1, BF16>), dim3(W), dim3(NT), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((stream_attention_kernel<D, 2, BF16>), dim3(W), dim3(NT), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((stream_attention_kernel<D, 4, BF16>), dim3(W), dim3(NT), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((stream_attention_kernel<D, 8, BF16>), dim3(W), dim3(NT), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((stream_attention_kernel<D, 16, BF16>), dim3(W), dim3(NT), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((stream_attention_kernel<D, 32, BF16>), dim3(W), dim3(NT), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((stream_attention_kernel<D, 64, BF16>), dim3(W), dim3(NT), 0, s, p); break;
+    case 1: return launch_g<D, 1, BF16>(p, s);
+    case 2: return launch_g<D, 2, BF16>(p, s);
+    case 4: return launch_g<D, 4, BF16>(p, s);
+    case 8: return launch_g<D, 8, BF16>(p, s);
+    case 16: return launch_g<D, 16, BF16>(p, s);
+    case 32: return launch_g<D, 32, BF16>(p, s);
+    case 64: return launch_g<D, 64, BF16>(p, s);
     default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.whole_items) return e;
-    hipLaunchKernelGGL((merge_pieces_kernel<D, BF16>), dim3(p.cache.K, p.rows), dim3(256), 0, s, p, tt, W);
-    return hipGetLastError();
 }
 
 }  // namespace
+
+hipError_t launch_merge_pieces(const RowAttnParams &p, int tt, int W, hipStream_t s)
+{
+    const dim3 grid(p.cache.K, p.rows, (p.G + kMergeHeads - 1) / kMergeHeads);
+    const bool bf16 = p.cache.elem_bytes == 2;
+    if (p.cache.d == 128) {
+        if (bf16) hipLaunchKernelGGL((merge_pieces_kernel<128, true>), grid, dim3(256), 0, s, p, tt, W);
+        else hipLaunchKernelGGL((merge_pieces_kernel<128, false>), grid, dim3(256), 0, s, p, tt, W);
+    } else if (p.cache.d == 64) {
+        if (bf16) hipLaunchKernelGGL((merge_pieces_kernel<64, true>), grid, dim3(256), 0, s, p, tt, W);
+        else hipLaunchKernelGGL((merge_pieces_kernel<64, false>), grid, dim3(256), 0, s, p, tt, W);
+    } else {
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 // Rows are processed in launches of at most kStreamRows rows (the row tables
 // live in LDS); launches on one stream run in order and share the workspace.
 hipError_t launch_row_attention(const RowAttnParams &p0, int gp, hipStream_t stream)
 {
     if (p0.total_rows <= 0) return hipSuccess;
-    if (p0.cache.K > 65535 || p0.num_wgs <= 0) return hipErrorInvalidValue;
+    if (p0.cache.K > 65535 || p0.num_wgs <= 0 || p0.num_wgs > kStreamWGs) return hipErrorInvalidValue;
     const bool bf16 = p0.cache.elem_bytes == 2;
     for (int64_t r0 = 0; r0 < p0.total_rows; r0 += kStreamRows) {
         RowAttnParams p = p0;
         p.row0 = r0;
         p.rows = (int32_t)(p0.total_rows - r0 < kStreamRows ? p0.total_rows - r0 : kStreamRows);
         hipError_t e = hipErrorInvalidValue;
-        if (p.cache.d == 128) e = bf16 ? launch_d<128, true>(p, gp, stream) : launch_d<128, false>(p, gp, stream);
+        if (decode_waves_supported(p, gp)) e = launch_decode_waves(p, gp, stream);
+        else if (p.cache.d == 128) e = bf16 ? launch_d<128, true>(p, gp, stream) : launch_d<128, false>(p, gp, stream);
         else if (p.cache.d == 64) e = bf16 ? launch_d<64, true>(p, gp, stream) : launch_d<64, false>(p, gp, stream);
         if (e != hipSuccess) return e;
     }

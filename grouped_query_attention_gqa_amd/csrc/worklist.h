@@ -1,0 +1,124 @@
+// worklist.h -- the flat tile list shared by the row-attention kernels
+// (internal).
+//
+// Every (query row, KV group) item is cut into tiles of `tt` keys; the tiles
+// of all items of one launch form one flat list, ordered by row, then KV
+// group, then key.  Workgroup w of W takes the contiguous slice
+// [w*T/W, (w+1)*T/W) of the T tiles, so ragged and paged contexts are
+// balanced exactly.  The per-row tables live in LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace gqa {
+
+// Visible keys of query row `row` (b * Sq + i), clamped to the cache capacity.
+__device__ __forceinline__ int row_visible(const RowAttnParams &p, int64_t row)
+{
+    const int b = (int)(row / p.Sq);
+    const int i = (int)(row % p.Sq);
+    int64_t n;
+    if (!p.prefill) {
+        n = p.ctx_lens[b];
+    } else {
+        const int64_t start = p.start_pos[b];
+        n = p.causal ? start + i + 1 : start + p.Sq;
+    }
+    if (n > p.cache.capacity) n = p.cache.capacity;
+    if (n < 0) n = 0;
+    return (int)n;
+}
+
+// For the rows of this launch (local rows 0 .. rows-1, at most kStreamRows):
+// nvis[r] = visible keys, prefix[r] = K * sum_{r' < r} tiles(r'),
+// prefix[rows] = the number of tiles T.  Every thread of the workgroup calls
+// it; thread i handles the consecutive rows i*per .. i*per+per-1, so any row
+// count up to kStreamRows is covered whatever the workgroup size.
+template <int NT>
+__device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, int32_t *nvis, int *lds_waves)
+{
+    static_assert(kStreamRows % NT == 0, "rows per thread");
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int rows = p.rows;
+    const int per = (rows + NT - 1) / NT;
+    const int r0 = tid * per;
+    int local = 0;
+    for (int k = 0; k < per; ++k) {
+        const int r = r0 + k;
+        if (r < rows) {
+            const int n = row_visible(p, p.row0 + r);
+            nvis[r] = n;
+            local += (n + tt - 1) / tt;
+        }
+    }
+    int x = local;   // inclusive scan over the wave, then over the waves
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) lds_waves[wave] = x;
+    __syncthreads();
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += lds_waves[w];
+    int run = before + x - local;
+    for (int k = 0; k < per; ++k) {
+        const int r = r0 + k;
+        if (r < rows) {
+            prefix[r] = run * p.cache.K;
+            run += (nvis[r] + tt - 1) / tt;
+        }
+    }
+    if (tid == NT - 1) prefix[rows] = (before + x) * p.cache.K;
+    __syncthreads();
+}
+
+struct Cursor {
+    int row;       // local query row
+    int g;         // KV group
+    int j;         // tile within the item
+    int tiles;     // tiles of the item
+    int n_vis;     // visible keys of the row
+    int item0;     // flat index of the item's first tile
+};
+
+__device__ __forceinline__ Cursor cursor_at(const int32_t *prefix, const int32_t *nvis, int rows, int tau, int tt)
+{
+    // last row whose prefix is <= tau (rows without tiles share their prefix)
+    int lo = 0, hi = rows - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (prefix[mid] <= tau) lo = mid; else hi = mid - 1;
+    }
+    Cursor c;
+    c.row = lo;
+    c.n_vis = nvis[lo];
+    c.tiles = (c.n_vis + tt - 1) / tt;
+    const int off = tau - prefix[lo];
+    c.g = off / c.tiles;
+    c.j = off % c.tiles;
+    c.item0 = prefix[lo] + c.g * c.tiles;
+    return c;
+}
+
+__device__ __forceinline__ void cursor_next(const int32_t *nvis, int rows, int K, Cursor &c, int tt)
+{
+    if (++c.j < c.tiles) return;
+    c.j = 0;
+    c.item0 += c.tiles;
+    if (++c.g < K) return;
+    c.g = 0;
+    do {
+        ++c.row;
+        if (c.row >= rows) return;
+        c.n_vis = nvis[c.row];
+        c.tiles = (c.n_vis + tt - 1) / tt;
+    } while (c.tiles == 0);
+}
+
+__device__ __forceinline__ int64_t slice_start(int64_t w, int64_t T, int64_t W) { return w * T / W; }
+
+}  // namespace gqa
