@@ -17,8 +17,8 @@
 //    of the next tile are loaded straight into registers (coalesced 16-byte
 //    loads, 1 KB per wave instruction) while the current tile is computed, so
 //    every wave keeps 16 KB in flight and no LDS stage limits the depth.
-//  * Scores: the wave copies its K tile into its own LDS buffer (rows
-//    XOR-swizzled) and lane (key t, head set) then reads the whole row t and
+//  * Scores: the wave copies its K tile into its own LDS buffer (rows padded
+//    by 16 bytes) and lane (key t, head set) then reads the whole row t and
 //    the q rows of its heads (an LDS broadcast) and forms full dot products
 //    with v_dot2_f32_bf16.  One K row read from HBM serves all G heads.
 //  * Online softmax per wave (inference-optimisation page §9.2.1) in exp2
@@ -57,11 +57,11 @@ struct WCfg {
     static constexpr int VNL = TT / VRPL;       // 8-byte V loads per lane per tile
     static constexpr int NP = VNL / 2;          // key pairs per lane per tile
     static constexpr int NGR = TT / 16;         // 16-key groups per tile
-    static constexpr int SWZ = CPR - 1;
+    static constexpr int KRS = RB + 16;         // LDS row stride of K: 16 lanes reading 16 rows hit distinct banks
     static constexpr int HS0 = kWave / TT;
     static constexpr int HS = HS0 < GP ? HS0 : GP;    // head sets in the score phase
     static constexpr int HPL = GP / HS;              // heads per score lane
-    static constexpr int K_WAVE = TT * RB;           // LDS K buffer per wave
+    static constexpr int K_WAVE = TT * KRS;          // LDS K buffer per wave
     static constexpr int P_WAVE = VRPL * NP * GP;    // P words per wave (bf16 pairs)
     static constexpr int Q_BYTES = GP * RB;
     static constexpr int CMB = NW * GP * D * 4;      // wave partials, in the K buffers
@@ -100,7 +100,8 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     __shared__ int32_t lds_nvis[kStreamRows];
     __shared__ int lds_waves[NW];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar registers
     const CacheView &cache = p.cache;
     const int G = p.G, H = p.H;
 
@@ -127,61 +128,117 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     // V load 2 kk + half, so it pairs with the key VRPL rows away
     const int p_slot = (((st % C::VRPL) * C::NP + st / (2 * C::VRPL)) * GP + qh * C::HPL) * 2 + ((st / C::VRPL) & 1);
 
-    Cursor c = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);
-    int tau = tau0;
-    while (tau < tau1) {
-        const int seg_end = min(tau1, c.item0 + c.tiles);
-        const int n_seg = seg_end - tau;
-        const int j_first = c.j;
-        const int64_t row_g = p.row0 + c.row;
-        const int b = (int)(row_g / p.Sq);
-        const int n_vis = c.n_vis;
-        const int g = c.g;
+    // One segment: the tiles [tau, end) of the slice that belong to one item.
+    struct Seg {
+        int64_t row_g;    // query row (sequence) of the item
+        int b, g;         // sequence and KV group
+        int n_vis;        // keys of the item
+        int j_first;      // tile of the item at tau
+        int tau, end;     // flat tile range
+        int item0, tiles; // the item's flat range
+        int n_w;          // tiles of this wave: j_first + wave + NW * i, i < n_w
+    };
+    auto make_seg = [&](int at) {
+        const Cursor c = cursor_at(lds_prefix, lds_nvis, p.rows, at, C::TT);
+        Seg sg;
+        sg.row_g = p.row0 + c.row;
+        sg.b = (int)(sg.row_g / p.Sq);
+        sg.g = c.g;
+        sg.n_vis = c.n_vis;
+        sg.j_first = c.j;
+        sg.tau = at;
+        sg.end = min(tau1, c.item0 + c.tiles);
+        sg.item0 = c.item0;
+        sg.tiles = c.tiles;
+        const int n_seg = sg.end - at;
+        sg.n_w = n_seg > wave ? (n_seg - wave + NW - 1) / NW : 0;
+        return sg;
+    };
 
-        // q rows of the item -> LDS (padded heads are zero)
-        if (tid < GP * C::CPR) {
-            const int r = tid / C::CPR, ch = tid % C::CPR;
+    // Where the rows of tile j of an item live.  A wave load covers rows of
+    // one 16-key group, whose cache rows are consecutive (contiguous cache, or
+    // one block of >= 16 tokens): a wave-uniform row base per group plus a
+    // 32-bit lane offset.
+    struct TileRows {
+        int64_t base[C::NGR];   // cache row of key 16 gi of the tile, -1: none
+        int nvalid;             // keys of the tile (<= 0: none)
+    };
+    auto tile_rows = [&](int lb, int lg, int l_nvis, int j) {
+        TileRows t;
+        const int key0 = j * C::TT;
+        t.nvalid = min(C::TT, l_nvis - key0);
+#pragma unroll
+        for (int gi = 0; gi < C::NGR; ++gi)
+            t.base[gi] = 16 * gi < t.nvalid ? cache_row_wave(cache, lb, lg, key0 + 16 * gi) : -1;
+        return t;
+    };
+    const uint32_t k_off = (uint32_t)(krow * C::RB + kc * 16);
+    const uint32_t v_off = (uint32_t)(vr * C::RB + vc * 8);
+    auto load_k = [&](const TileRows &t, uint4 (&kr)[C::NL]) {
+#pragma unroll
+        for (int i = 0; i < C::NL; ++i) {
+            const int r0 = i * C::RPL;                       // first tile row of the load
+            const int64_t base = t.base[r0 / 16];
             uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            if (r < G) x = ld16(p.q + ((row_g * H + (int64_t)g * G + r) * D) * 2 + ch * 16);
-            *reinterpret_cast<uint4 *>(lds_q + r * C::RB + ch * 16) = x;
+            if (base >= 0 && r0 + krow < t.nvalid) x = ld16(cache.k + (base + r0 % 16) * C::RB + k_off);
+            kr[i] = x;
         }
-        __syncthreads();
+    };
+    auto load_v = [&](const TileRows &t, uint2 (&vv)[C::VNL]) {
+#pragma unroll
+        for (int i = 0; i < C::VNL; ++i) {
+            const int r0 = i * C::VRPL;
+            const int64_t base = t.base[r0 / 16];
+            uint2 y = make_uint2(0u, 0u);
+            if (base >= 0 && r0 + vr < t.nvalid)
+                y = *reinterpret_cast<const uint2 *>(cache.v + (base + r0 % 16) * C::RB + v_off);
+            vv[i] = y;
+        }
+    };
+    // this thread's 16 bytes of the q rows of a segment's item (padded heads are zero)
+    const bool q_thread = tid < GP * C::CPR;
+    const int q_r = tid / C::CPR, q_ch = tid % C::CPR;
+    auto load_q = [&](const Seg &sg) {
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+        if (q_thread && q_r < G) x = ld16(p.q + ((sg.row_g * H + (int64_t)sg.g * G + q_r) * D) * 2 + q_ch * 16);
+        return x;
+    };
 
-        // K and V rows of tile j of the item.  A wave load covers rows of one
-        // 16-key group, whose cache rows are consecutive (contiguous cache,
-        // or one block of >= 16 tokens): a wave-uniform 64-bit base plus a
-        // 32-bit lane offset.
-        const uint32_t k_off = (uint32_t)(krow * C::RB + kc * 16);
-        const uint32_t v_off = (uint32_t)(vr * C::RB + vc * 8);
-        auto load_tile = [&](int j, uint4 (&kr)[C::NL], uint2 (&vv)[C::VNL]) {
-            const int key0 = j * C::TT;
-            const int nvalid = min(C::TT, n_vis - key0);
-            int64_t gb[C::NGR];   // cache row of key key0 + 16 gi (wave-uniform), -1: none
+    // This wave's next tile at or after flat tile `at`: the first tile of the
+    // first segment there in which the wave has one (none: no rows).
+    auto next_tile = [&](int at) {
+        while (at < tau1) {
+            const Seg sg = make_seg(at);
+            if (sg.n_w > 0) return tile_rows(sg.b, sg.g, sg.n_vis, sg.j_first + wave);
+            at = sg.end;
+        }
+        TileRows t;
 #pragma unroll
-            for (int gi = 0; gi < C::NGR; ++gi)
-                gb[gi] = 16 * gi < nvalid ? cache_row_wave(cache, b, g, key0 + 16 * gi) : -1;
-#pragma unroll
-            for (int i = 0; i < C::NL; ++i) {
-                const int r0 = i * C::RPL;                       // first tile row of the load
-                const int64_t base = gb[r0 / 16];
-                uint4 x = make_uint4(0u, 0u, 0u, 0u);
-                if (base >= 0 && r0 + krow < nvalid)
-                    x = ld16(cache.k + (base + r0 % 16) * C::RB + k_off);
-                kr[i] = x;
-            }
-#pragma unroll
-            for (int i = 0; i < C::VNL; ++i) {
-                const int r0 = i * C::VRPL;
-                const int64_t base = gb[r0 / 16];
-                uint2 y = make_uint2(0u, 0u);
-                if (base >= 0 && r0 + vr < nvalid)
-                    y = *reinterpret_cast<const uint2 *>(cache.v + (base + r0 % 16) * C::RB + v_off);
-                vv[i] = y;
-            }
-        };
+        for (int gi = 0; gi < C::NGR; ++gi) t.base[gi] = -1;
+        t.nvalid = 0;
+        return t;
+    };
+
+    // The wave's tiles form one stream across segments.  Step i: copy K(i)
+    // from registers to LDS and start K(i+1); add P(i-1) V(i-1) from the V
+    // registers; start V(i) into them; score tile i into P(i).  Every load
+    // has one step to arrive, and V needs a single register buffer.
+    uint4 kr[C::NL];
+    uint2 vbuf[C::VNL];
+    Seg cur = make_seg(tau0);
+    TileRows rows_next = next_tile(tau0);
+    {
+        const uint4 x = load_q(cur);
+        load_k(rows_next, kr);
+        if (q_thread) *reinterpret_cast<uint4 *>(lds_q + q_r * C::RB + q_ch * 16) = x;
+        __syncthreads();
+    }
+    for (;;) {
+        const bool has_next = cur.end < tau1;
+        const Seg nxt = has_next ? make_seg(cur.end) : cur;
+        const int n_w = cur.n_w;
 
         // ---- this wave's tiles of the segment: j_first + wave + NW * i -------
-        const int n_w = n_seg > wave ? (n_seg - wave + NW - 1) / NW : 0;
         float m_ref[C::HPL], l_run[C::HPL];
 #pragma unroll
         for (int h = 0; h < C::HPL; ++h) { m_ref[h] = -INFINITY; l_run[h] = 0.f; }
@@ -191,22 +248,46 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
 #pragma unroll
             for (int e = 0; e < 4; ++e) acc[h][e] = 0.f;
 
-        uint4 kr[C::NL];
-        uint2 va[C::VNL], vb[C::VNL];
-        if (n_w > 0) load_tile(j_first + wave, kr, va);
-
-        auto step = [&](int i, uint2 (&vcur)[C::VNL], uint2 (&vnext)[C::VNL]) {
-            const int j = j_first + wave + NW * i;
-            const int nvalid = min(C::TT, n_vis - j * C::TT);
-            // K tile -> this wave's LDS buffer, row t's chunk x at slot x ^ (t & SWZ)
+        // o = o * alpha + sum_t p_t v_t for the tile whose V is in vbuf
+        auto pv = [&](bool rescale) {
+            if (rescale) {
 #pragma unroll
-            for (int ii = 0; ii < C::NL; ++ii) {
-                const int rt = ii * C::RPL + krow;
-                *reinterpret_cast<uint4 *>(kw + rt * C::RB + ((kc ^ (rt & C::SWZ)) * 16)) = kr[ii];
+                for (int h = 0; h < GP; ++h) {
+                    const float al = lds_alpha[wave][h];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[h][e] *= al;
+                }
             }
-            if (i + 1 < n_w) load_tile(j + NW, kr, vnext);
+#pragma unroll
+            for (int kk = 0; kk < C::NP; ++kk) {
+                const uint2 a = vbuf[2 * kk], bb = vbuf[2 * kk + 1];   // rows 2kk*VRPL + vr and VRPL later
+                uint32_t vv[4];
+                vv[0] = pair_lo(a.x, bb.x); vv[1] = pair_hi(a.x, bb.x);
+                vv[2] = pair_lo(a.y, bb.y); vv[3] = pair_hi(a.y, bb.y);
+                uint32_t pp[GP];
+                read_p<GP>(pw + (vr * C::NP + kk) * GP, pp);
+#pragma unroll
+                for (int h = 0; h < GP; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[h][e] = dot2_bf16(pp[h], vv[e], acc[h][e]);
+            }
+        };
 
-            // ---- scores --------------------------------------------------------
+        bool pend_rescale = false;
+        for (int i = 0; i < n_w; ++i) {
+            const TileRows rows = rows_next;   // tile i
+            // K(i) -> this wave's LDS buffer (padded rows); start K(i+1)
+#pragma unroll
+            for (int ii = 0; ii < C::NL; ++ii)
+                *reinterpret_cast<uint4 *>(kw + (ii * C::RPL + krow) * C::KRS + kc * 16) = kr[ii];
+            rows_next = i + 1 < n_w ? tile_rows(cur.b, cur.g, cur.n_vis, cur.j_first + wave + NW * (i + 1))
+                                    : next_tile(cur.end);
+            load_k(rows_next, kr);
+            // P(i-1) V(i-1), then start V(i)
+            if (i > 0) pv(pend_rescale);
+            load_v(rows, vbuf);
+
+            // ---- scores of tile i ----------------------------------------------
             float sc[C::HPL];
             {
                 float a0[C::HPL], a1[C::HPL];
@@ -214,7 +295,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
                 for (int h = 0; h < C::HPL; ++h) { a0[h] = 0.f; a1[h] = 0.f; }
 #pragma unroll
                 for (int ch = 0; ch < C::CPR; ++ch) {
-                    const uint4 kv = *reinterpret_cast<const uint4 *>(kw + st * C::RB + ((ch ^ (st & C::SWZ)) * 16));
+                    const uint4 kv = *reinterpret_cast<const uint4 *>(kw + st * C::KRS + ch * 16);
 #pragma unroll
                     for (int h = 0; h < C::HPL; ++h) {
                         const uint4 qv = *reinterpret_cast<const uint4 *>(lds_q + (qh * C::HPL + h) * C::RB + ch * 16);
@@ -224,7 +305,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
                         a1[h] = dot2_bf16(qv.w, kv.w, a1[h]);
                     }
                 }
-                const bool valid = s_lane && st < nvalid;
+                const bool valid = s_lane && st < rows.nvalid;
 #pragma unroll
                 for (int h = 0; h < C::HPL; ++h) sc[h] = valid ? (a0[h] + a1[h]) * p.scale_log2 : -INFINITY;
             }
@@ -245,6 +326,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
                     if (s_lane && st == 0) lds_alpha[wave][qh * C::HPL + h] = al;
                 }
             }
+            pend_rescale = rescale;
             // ---- P (bf16) for the V sum; l sums the rounded values -------------
 #pragma unroll
             for (int h = 0; h < C::HPL; ++h) {
@@ -253,35 +335,11 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
                 l_run[h] += __uint_as_float(pb << 16);
                 if (s_lane) pw16[p_slot + 2 * h] = (uint16_t)pb;
             }
-
-            // ---- o = o * alpha + sum_t p_t v_t ---------------------------------
-            if (rescale) {
-#pragma unroll
-                for (int h = 0; h < GP; ++h) {
-                    const float al = lds_alpha[wave][h];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[h][e] *= al;
-                }
-            }
-#pragma unroll
-            for (int kk = 0; kk < C::NP; ++kk) {
-                const uint2 a = vcur[2 * kk], bb = vcur[2 * kk + 1];   // rows 2kk*VRPL + vr and VRPL later
-                uint32_t vv[4];
-                vv[0] = pair_lo(a.x, bb.x); vv[1] = pair_hi(a.x, bb.x);
-                vv[2] = pair_lo(a.y, bb.y); vv[3] = pair_hi(a.y, bb.y);
-                uint32_t pp[GP];
-                read_p<GP>(pw + (vr * C::NP + kk) * GP, pp);
-#pragma unroll
-                for (int h = 0; h < GP; ++h)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) acc[h][e] = dot2_bf16(pp[h], vv[e], acc[h][e]);
-            }
-        };
-
-        for (int i = 0; i < n_w; i += 2) {
-            step(i, va, vb);
-            if (i + 1 < n_w) step(i + 1, vb, va);
         }
+        if (n_w > 0) pv(pend_rescale);   // the last tile's V sum
+
+        // the next item's q rows are loaded while the pieces are merged
+        const uint4 q_next = has_next ? load_q(nxt) : make_uint4(0u, 0u, 0u, 0u);
 
         // ---- merge the waves' pieces of the segment ---------------------------
 #pragma unroll
@@ -292,7 +350,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
                 for (int e = 0; e < 4; ++e) acc[h][e] += __shfl_xor(acc[h][e], m, kWave);
 #pragma unroll
         for (int h = 0; h < C::HPL; ++h) l_run[h] = group_sum<C::TT>(l_run[h]);
-        __syncthreads();   // every wave is done with its K buffer: it becomes the merge area
+        __syncthreads();   // every wave is done with its K buffer and q: the K buffers become the merge area
         float *cmb = reinterpret_cast<float *>(lds_k);   // [NW][GP][D]
         if (lane < C::VCPR) {
 #pragma unroll
@@ -308,9 +366,9 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             }
         }
         __syncthreads();
-        const bool whole = tau == c.item0 && seg_end == c.item0 + c.tiles;
-        const int slot = tau0 < c.item0 ? 1 : 0;
-        const int64_t head0 = row_g * H + (int64_t)g * G;
+        const bool whole = cur.tau == cur.item0 && cur.end == cur.item0 + cur.tiles;
+        const int slot = tau0 < cur.item0 ? 1 : 0;
+        const int64_t head0 = cur.row_g * H + (int64_t)cur.g * G;
         for (int idx = tid; idx < GP * D / 4; idx += NT) {
             const int h = idx / (D / 4), col = (idx % (D / 4)) * 4;
             if (h >= G) continue;
@@ -344,10 +402,10 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
                 }
             }
         }
-        __syncthreads();   // the merge area and q are free again
-
-        tau = seg_end;
-        if (tau < tau1) c = cursor_at(lds_prefix, lds_nvis, p.rows, tau, C::TT);
+        if (!has_next) break;
+        if (q_thread) *reinterpret_cast<uint4 *>(lds_q + q_r * C::RB + q_ch * 16) = q_next;
+        __syncthreads();   // the merge area is free again and the next q is in place
+        cur = nxt;
     }
 }
 
