@@ -61,6 +61,7 @@ struct WCfg {
     static constexpr int HS0 = kWave / TT;
     static constexpr int HS = HS0 < GP ? HS0 : GP;    // head sets in the score phase
     static constexpr int HPL = GP / HS;              // heads per score lane
+    static constexpr int KD = GP >= 8 ? 1 : 2;       // K tiles in flight per wave (register budget)
     static constexpr int K_WAVE = TT * KRS;          // LDS K buffer per wave
     static constexpr int P_WAVE = VRPL * NP * GP;    // P words per wave (bf16 pairs)
     static constexpr int Q_BYTES = GP * RB;
@@ -204,32 +205,45 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         return x;
     };
 
-    // This wave's next tile at or after flat tile `at`: the first tile of the
-    // first segment there in which the wave has one (none: no rows).
-    auto next_tile = [&](int at) {
-        while (at < tau1) {
-            const Seg sg = make_seg(at);
-            if (sg.n_w > 0) return tile_rows(sg.b, sg.g, sg.n_vis, sg.j_first + wave);
-            at = sg.end;
-        }
+    // The first two tiles of this wave's stream at or after flat tile `at`:
+    // the wave's tiles of the segments from there on (none: no rows).
+    auto no_rows = [&]() {
         TileRows t;
 #pragma unroll
         for (int gi = 0; gi < C::NGR; ++gi) t.base[gi] = -1;
         t.nvalid = 0;
         return t;
     };
+    auto stream_from = [&](int at, TileRows &t1, TileRows &t2) {
+        t1 = no_rows();
+        t2 = no_rows();
+        int found = 0;
+        while (at < tau1 && found < C::KD) {
+            const Seg sg = make_seg(at);
+            for (int k = 0; k < sg.n_w && found < C::KD; ++k, ++found) {
+                const TileRows t = tile_rows(sg.b, sg.g, sg.n_vis, sg.j_first + wave + NW * k);
+                if (found == 0) t1 = t;
+                else t2 = t;
+            }
+            at = sg.end;
+        }
+    };
 
-    // The wave's tiles form one stream across segments.  Step i: copy K(i)
-    // from registers to LDS and start K(i+1); add P(i-1) V(i-1) from the V
-    // registers; start V(i) into them; score tile i into P(i).  Every load
-    // has one step to arrive, and V needs a single register buffer.
-    uint4 kr[C::NL];
+    // The wave's tiles form one stream across segments.  Step i (stream
+    // position gi): copy K(i) from its register buffer to LDS and start
+    // K(i + KD) into that buffer; add P(i-1) V(i-1) from the V registers;
+    // start V(i) into them; score tile i into P(i).  K has KD steps to
+    // arrive, V one, and V needs a single register buffer.
+    uint4 kA[C::NL], kB[C::NL];
     uint2 vbuf[C::VNL];
+    int gi = 0;
     Seg cur = make_seg(tau0);
-    TileRows rows_next = next_tile(tau0);
+    TileRows r1, r2;   // rows of the stream's next tiles (K already started)
+    stream_from(tau0, r1, r2);
     {
         const uint4 x = load_q(cur);
-        load_k(rows_next, kr);
+        load_k(r1, kA);
+        if constexpr (C::KD == 2) load_k(r2, kB);
         if (q_thread) *reinterpret_cast<uint4 *>(lds_q + q_r * C::RB + q_ch * 16) = x;
         __syncthreads();
     }
@@ -237,6 +251,8 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         const bool has_next = cur.end < tau1;
         const Seg nxt = has_next ? make_seg(cur.end) : cur;
         const int n_w = cur.n_w;
+        TileRows after1, after2;   // the stream's first tiles after this segment
+        stream_from(cur.end, after1, after2);
 
         // ---- this wave's tiles of the segment: j_first + wave + NW * i -------
         float m_ref[C::HPL], l_run[C::HPL];
@@ -274,15 +290,23 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         };
 
         bool pend_rescale = false;
-        for (int i = 0; i < n_w; ++i) {
-            const TileRows rows = rows_next;   // tile i
-            // K(i) -> this wave's LDS buffer (padded rows); start K(i+1)
+        for (int i = 0; i < n_w; ++i, ++gi) {
+            const TileRows rows = r1;   // tile i
+            // rows of the tile KD steps ahead in the stream
+            const int ia = i + C::KD;
+            const TileRows ra = ia < n_w ? tile_rows(cur.b, cur.g, cur.n_vis, cur.j_first + wave + NW * ia)
+                                         : (ia == n_w ? after1 : after2);
+            // K(i) -> this wave's LDS buffer (padded rows); start K(i + KD) in its place
+            auto k_step = [&](uint4 (&kx)[C::NL]) {
 #pragma unroll
-            for (int ii = 0; ii < C::NL; ++ii)
-                *reinterpret_cast<uint4 *>(kw + (ii * C::RPL + krow) * C::KRS + kc * 16) = kr[ii];
-            rows_next = i + 1 < n_w ? tile_rows(cur.b, cur.g, cur.n_vis, cur.j_first + wave + NW * (i + 1))
-                                    : next_tile(cur.end);
-            load_k(rows_next, kr);
+                for (int ii = 0; ii < C::NL; ++ii)
+                    *reinterpret_cast<uint4 *>(kw + (ii * C::RPL + krow) * C::KRS + kc * 16) = kx[ii];
+                load_k(ra, kx);
+            };
+            if (C::KD == 2 && (gi & 1)) k_step(kB);
+            else k_step(kA);
+            if constexpr (C::KD == 2) { r1 = r2; r2 = ra; }
+            else r1 = ra;
             // P(i-1) V(i-1), then start V(i)
             if (i > 0) pv(pend_rescale);
             load_v(rows, vbuf);
