@@ -37,9 +37,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# gqa_decode is the main kernel plus the small merge of cut items; events time both
+DECODE_KERNELS = "decode_waves_kernel<128, 4> + merge_pieces_kernel<128, true> (one gqa_decode call)"
+DECODE_SOURCES = ("decode_waves.hip", "stream_attention.hip", "worklist.h", "kernels.h", "common.h")
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "GQA decode HBM GB/s (% of peak) + causal prefill TFLOP/s (% MFMA peak), bf16"
 MALL_BYTES = 256 * 2**20
+COPY_BYTES = 512 * 2**20   # calibration copy for the HBM byte counters
 
 
 def log(*a):
@@ -53,7 +57,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
-    ap.add_argument("--only", default=None, help="profile one kernel: decode|prefill|decode70b|paged")
+    ap.add_argument("--only", default=None,
+                    help="profile one kernel: decode|prefill|decode70b|paged|mha|mqa|copy (a 512 MiB device copy)")
+    ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
     return ap.parse_args()
 
 
@@ -152,14 +158,17 @@ def time_decode_only(db: DecodeBench, iters: int, warmup: int):
 # traffic figures from the committed rocprofv3 counter summaries
 # ---------------------------------------------------------------------------
 
-def kernel_source_hash(name: str) -> str:
-    path = os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_source_hash(names=DECODE_SOURCES) -> str:
+    """Hash of the kernel sources the traffic counters were taken on."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def committed_traffic(key: str, source: str, launches_units: float):
-    """HBM bytes per launch from profiles/traffic.json, if taken on the current kernel source."""
+def committed_traffic(key: str):
+    """HBM bytes per launch from profiles/traffic.json, if taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -167,9 +176,61 @@ def committed_traffic(key: str, source: str, launches_units: float):
     except (OSError, ValueError):
         return None
     ent = table.get(key)
-    if not ent or ent.get("source_sha") != kernel_source_hash(source):
+    if not ent or ent.get("source_sha") != kernel_source_hash():
         return None
     return ent.get("bytes_per_launch")
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_trace(d: str):
+    """Per-kernel call count and average duration from a rocprofv3 --kernel-trace --stats run."""
+    rows = _csv_rows(os.path.join(d, "run_kernel_stats.csv"))
+    lines = [f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'total_%':>8}  kernel"]
+    for r in rows:
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} {float(r['MinNs']) / 1e3:10.2f} "
+                     f"{float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}  {r['Name'][:110]}")
+    return "\n".join(lines)
+
+
+def counter_means(d: str):
+    """Mean value per (kernel, counter) over the dispatches of a rocprofv3 --pmc run."""
+    acc = {}
+    for r in _csv_rows(os.path.join(d, "run_counter_collection.csv")):
+        k = (r["Kernel_Name"], r["Counter_Name"])
+        acc.setdefault(k, []).append(float(r["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v)) for k, v in acc.items()}
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str, copy_bytes: int):
+    """HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE (KiB), each scaled by what the same
+    counter reads for a device copy of `copy_bytes` bytes (reads copy_bytes, writes copy_bytes)."""
+    def find(means, pat, ctr):
+        for (k, c), (v, n) in means.items():
+            if pat in k and c == ctr:
+                return v, n
+        raise KeyError(pat)
+    cf = counter_means(copy_fetch_dir)
+    cw = counter_means(copy_write_dir)
+    f_copy, _ = find(cf, "copyBuffer", "FETCH_SIZE")
+    w_copy, _ = find(cw, "copyBuffer", "WRITE_SIZE")
+    f_scale = copy_bytes / (f_copy * 1024.0)
+    w_scale = copy_bytes / (w_copy * 1024.0)
+    kf = counter_means(fetch_dir)
+    kw = counter_means(write_dir)
+    out = {"copy_bytes": copy_bytes, "copy_FETCH_SIZE_KiB": f_copy, "copy_WRITE_SIZE_KiB": w_copy,
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+    for (k, c), (v, n) in kf.items():
+        if c != "FETCH_SIZE" or "copyBuffer" in k or "at::native" in k:
+            continue
+        w = next((vv for (kk, cc), (vv, nn) in kw.items() if kk == k and cc == "WRITE_SIZE"), 0.0)
+        out["kernels"][k[:110]] = {"dispatches": n, "FETCH_SIZE_KiB": round(v, 1), "WRITE_SIZE_KiB": round(w, 1),
+                                   "hbm_bytes": int(v * 1024 * f_scale + w * 1024 * w_scale)}
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -215,6 +276,9 @@ def cpu_baseline(db: DecodeBench, budget_s: float = 12.0):
 
 def main():
     args = parse()
+    if args.summarize:
+        print(summarize_trace(args.summarize))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus above 1 is not supported",
                           "n_gpus": args.gpus}))
@@ -253,7 +317,7 @@ def main():
     dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = db.alg_bytes / (dec_ms * 1e-3) / 1e9
-    traffic = committed_traffic("decode/llama3_8b_decode", "row_attention.hip", 1)
+    traffic = committed_traffic("decode/llama3_8b_decode")
     log(f"decode step {ms_step * 1e3:.1f} us ({value:.0f} GB/s); decode kernel {dec_ms * 1e3:.1f} us "
         f"({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of peak)")
 
@@ -273,7 +337,7 @@ def main():
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "K": wl.K, "d": wl.d,
                    "ctx": "U[1024,4096] per sequence", "sum_ctx": int(db.ctx.sum()),
                    "step": "gqa_kv_append (newest token) + gqa_decode", "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "kernel": "row_attention_kernel<128,4,bf16> (gqa_decode)",
+        "roofline": {"bound": "hbm", "kernel": DECODE_KERNELS,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": db.alg_bytes, "avg_launch_us": round(dec_ms * 1e3, 2)},
@@ -346,6 +410,15 @@ def profile_only(args):
     if args.only == "prefill":
         r = bench_prefill(W.WORKLOADS["causal_prefill_4k"], args.steps, args.warmup)
         print(json.dumps(r), flush=True)
+        return
+    if args.only == "copy":
+        # the calibration copy for the byte counters: reads and writes COPY_BYTES per dispatch
+        a = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "copies": args.steps}), flush=True)
         return
     name = {"decode": "llama3_8b_decode", "decode70b": "llama2_70b_decode", "paged": "paged_long_decode",
             "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa"}[args.only]
