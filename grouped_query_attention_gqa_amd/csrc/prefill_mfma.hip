@@ -4,32 +4,37 @@
 // What it computes ("Grouped-Query Attention" concept page, 技术原理 steps 2-4):
 // out[b,i,h] = softmax(q[b,i,h] K_g^T * scale) V_g, g = h / G, over the keys
 // visible to row i: keys 0 .. start_pos[b]+i when causal (a token attends to
-// itself and to every earlier token, inference-optimisation page §5.1), keys
-// 0 .. start_pos[b]+s-1 otherwise.  The new tokens' K/V are already in the
-// cache (the append kernel runs first on the same stream).
+// itself and to every earlier token), keys 0 .. start_pos[b]+s-1 otherwise.
+// The new tokens' K/V are already in the cache (the append kernel runs first
+// on the same stream).
 //
-// How (designed for gfx950, prior art only for the ideas):
-//  * One workgroup owns a block of QB consecutive query positions of one
-//    sequence and ALL G heads of one KV group g: 128*RBW rows (position,
-//    head) that share every K/V tile, so each K/V tile is fetched once per
-//    group (the group broadcast), and every row of the workgroup has the same
-//    causal key range.
-//  * Keys stream in 64-key tiles (the tile and the 16-token cache block
-//    align, inference-optimisation page §9.4) through LDS; the tile for the
-//    next step is loaded into registers while the current one is used.
-//  * Scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: K comes from LDS (rows XOR-swizzled over
-//    16-byte chunks, so 16 lanes reading 16 keys hit 16 bank groups), Q^T
-//    stays in registers for the whole key loop.  In the accumulator layout
-//    each lane then owns one query row, so the row max and sum need a single
-//    exchange with the lane 32 away.
-//  * Online softmax in fp32 (inference-optimisation page §9.2.1), with the
-//    running max only moved when a tile max exceeds it by 2^8 (exp2 units);
-//    the probabilities are rounded to bf16 and used directly as the B operand
-//    of O^T += V^T P^T -- the accumulator layout of S^T is already the operand
-//    layout of P^T once both MFMAs use the same order of keys, so P never
-//    leaves registers.  V is stored transposed in LDS (rows padded to 136 B so
-//    32 lanes reading one key column hit distinct banks).
+// How (designed for gfx950; FlashAttention on the inference-optimisation
+// page §9 is prior art for the tiling idea only):
+//  * A workgroup (8 waves, two per SIMD) owns 256 (position, head) rows of
+//    one sequence and one KV group: 256/G consecutive positions x the G heads.
+//    Every K/V tile it loads therefore serves all G heads of the group.  Each
+//    wave owns one 32-row block.
+//  * K/V tiles of 64 keys move HBM -> LDS with LDS-direct loads
+//    (global_load_lds_dwordx4, no registers), four stages deep, with explicit
+//    vmcnt waits; one barrier per tile.
+//  * Scores are formed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
+//    so a lane holds 32 scores of ONE query row: the row max is lane-local
+//    plus one exchange with the lane 32 away, and the row sum is kept per
+//    lane until the end.  Q^T stays in registers for the whole key loop.
+//  * The accumulator layout of S^T, rounded to bf16 (hardware RNE), is the
+//    B operand P^T of O^T += V^T P^T as it stands.  The matching V^T operand
+//    is read straight from the row-major V tile with the gfx950 transposing
+//    LDS read (ds_read_b64_tr_b16): sixteen lanes fetch four 4-key x
+//    4-column pieces and each lane receives four consecutive keys of one
+//    column.  K and V rows are XOR-swizzled in 16-byte chunks so that these
+//    reads hit distinct banks.
+//  * Online softmax in fp32 and exp2 units (inference-optimisation page
+//    §9.2.1): scale folded into one FMA, the running max only moved when a
+//    tile max exceeds it by 2^8 (checked with one wave vote), masking only on
+//    the tiles that cross the causal diagonal or the end of the keys.
+//  * The scores of tile j+1 are issued before the softmax and the V product
+//    of tile j, so the matrix cores have independent work while the vector
+//    units run the softmax.
 //  * Heaviest query blocks (largest causal key range) are launched first.
 #include "common.h"
 #include "kernels.h"
@@ -39,10 +44,20 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int NT = 256;
-constexpr int BN = kKeyTile;   // keys per tile
+constexpr int NT = 512;            // 8 waves, two per SIMD
+constexpr int NW = NT / kWave;
+constexpr int BN = kKeyTile;       // keys per tile (64)
+constexpr int ROWS = 256;          // (position, head) rows per workgroup
+constexpr int RPW = ROWS / NW;     // rows per wave (one 32-row block)
+constexpr int RBW = RPW / 32;      // 32-row blocks per wave
+constexpr int NS = 4;              // LDS stages
 constexpr float TAU = 8.0f;
+
+__device__ const uint4 kZero16P = {0u, 0u, 0u, 0u};
 
 __device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c)
 {
@@ -50,31 +65,72 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c)
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-template <int D, int GP, int RBW>
+// One LDS-direct 16-byte load per lane (lane i's bytes land at base + 16 i),
+// written as inline assembly so the compiler does not wait for it before LDS
+// reads; the kernel waits with explicit vmcnt.
+__device__ __forceinline__ void dma16(const void *src, void *lds_wave_base)
+{
+    const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t *)lds_wave_base;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS accesses are done
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// The transposing LDS read: 64 bits per lane, see the header comment.
+__device__ __forceinline__ uint2 lds_read_tr16(const char *p)
+{
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(lds_void_t *)p);
+    return __builtin_bit_cast(uint2, v);
+}
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
+{
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
+}
+
+template <int D, int GP>
 struct PCfg {
-    static constexpr int ROWS = 128 * RBW;        // (position, head) rows per workgroup
     static constexpr int QB = ROWS / GP;          // positions per workgroup
-    static constexpr int CPR = D * 2 / 16;        // 16-byte chunks per K row
-    static constexpr int SWZ = (CPR < 16 ? CPR : 16) - 1;
+    static constexpr int RB = D * 2;              // bytes per K/V row
+    static constexpr int CPR = RB / 16;           // 16-byte chunks per row
+    static constexpr int KSW = (CPR < 16 ? CPR : 16) - 1;   // K swizzle mask
     static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
     static constexpr int DB = D / 32;             // 32-row blocks of O^T
-    static constexpr int VT = BN + 4;             // V^T row stride (bf16 elements)
-    static constexpr int LPT_K = BN * CPR / NT;   // K chunks per thread per tile
-    static constexpr int NCK = D / 8;             // 8-element chunks per V row
-    static constexpr int KPT_V = BN * NCK / NT;   // consecutive keys per thread for V
-    static_assert(QB >= 1 && QB * GP == ROWS, "rows must split into positions x heads");
-    static_assert(LPT_K >= 1 && KPT_V >= 2 && KPT_V <= 4, "tile split");
+    static constexpr int TILE = BN * RB;          // bytes of K (or V) per tile
+    static constexpr int STAGE = 2 * TILE;        // K then V
+    static constexpr int RPK = 1024 / RB;         // rows per 1 KB load
+    static constexpr int LPW = TILE / 1024 / NW;  // 1 KB loads per wave per tile, each of K and V
+    static constexpr int LOADS = 2 * LPW;         // loads per wave per tile
+    static_assert(QB * GP == ROWS, "rows split into positions x heads");
+    static_assert(LPW >= 1 && LPW * NW * 1024 == TILE, "tile load split");
+    static_assert(NS * STAGE <= 160 * 1024, "LDS");
 };
 
-template <int D, int GP, int RBW>
+template <int D, int GP>
 __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
 {
-    using C = PCfg<D, GP, RBW>;
-    __shared__ uint4 Kl[BN * C::CPR];
-    __shared__ __attribute__((aligned(16))) uint16_t Vt[D * C::VT];
+    using C = PCfg<D, GP>;
+    __shared__ __attribute__((aligned(1024))) char smem[NS * C::STAGE];
 
     const CacheView &cache = p.cache;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nq = lane & 31, hh = lane >> 5;
     const int num_qb = (p.s + C::QB - 1) / C::QB;
     const int qb = num_qb - 1 - (int)blockIdx.x;   // heaviest first
@@ -84,17 +140,21 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     const int G = p.G, H = p.H;
     const int kv_len = (int)min((int64_t)start + p.s, (int64_t)cache.capacity);
     const int kv_end = p.causal ? (int)min((int64_t)start + q0 + C::QB, (int64_t)kv_len) : kv_len;
+    const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
+    // keys at or past this one may be masked for some row of the workgroup
+    const int mask_from = p.causal ? (int)min((int64_t)start + q0 + 1, (int64_t)kv_len) : kv_len;
 
-    // ---- this lane's query rows and their Q^T fragments ---------------------
-    int row_r[RBW], row_i[RBW];
+    // ---- this lane's two query rows and their Q^T fragments -------------------
+    int row_r[RBW], row_i[RBW], qpos[RBW];
     bool row_ok[RBW];
     uint4 qf[RBW][C::KS];
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-        const int rho = (wave * RBW + rb) * 32 + nq;
-        row_r[rb] = rho / C::QB;
-        row_i[rb] = q0 + rho % C::QB;
+        const int rho = wave * RPW + rb * 32 + nq;
+        row_r[rb] = rho % GP;
+        row_i[rb] = q0 + rho / GP;
         row_ok[rb] = row_r[rb] < G && row_i[rb] < p.s;
+        qpos[rb] = start + row_i[rb];
         const uint4 *qrow = reinterpret_cast<const uint4 *>(
             p.q + ((((int64_t)b * p.s + (row_ok[rb] ? row_i[rb] : 0)) * H + (int64_t)g * G +
                     (row_ok[rb] ? row_r[rb] : 0)) * D) * 2);
@@ -103,6 +163,38 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
             qf[rb][ks] = row_ok[rb] ? qrow[2 * ks + hh] : make_uint4(0, 0, 0, 0);
     }
 
+    // ---- LDS-direct loads of tile t into stage t % NS --------------------------
+    // K: row r's 16-byte chunk c lands in slot c ^ (r & KSW); V: slot c ^ 2 (r & 3).
+    auto issue = [&](int t) {
+        char *base = smem + (t % NS) * C::STAGE;
+        const int j0 = t * BN;
+#pragma unroll
+        for (int k = 0; k < C::LPW; ++k) {
+            const int blk = wave + NW * k;                // 1 KB block of the tile
+            const int r = blk * C::RPK + lane / C::CPR;   // tile row of this lane
+            const int slot = lane % C::CPR;
+            const void *srck = &kZero16P, *srcv = &kZero16P;
+            if (j0 + blk * C::RPK < kv_len) {
+                // the block's rows lie in one 16-row group, hence in one cache block
+                const int64_t row0 = cache_row_wave(cache, b, g, j0 + blk * C::RPK);
+                if (row0 >= 0 && j0 + r < kv_len) {
+                    const int64_t row = row0 + (r - blk * C::RPK);
+                    srck = cache.k + row * C::RB + (slot ^ (r & C::KSW)) * 16;
+                    srcv = cache.v + row * C::RB + (slot ^ (2 * (r & 3))) * 16;
+                }
+            }
+            dma16(srck, base + blk * 1024);
+            dma16(srcv, base + C::TILE + blk * 1024);
+        }
+    };
+    // wait until tile t's loads have landed, given how many tiles were issued after it
+    auto wait_tile = [&](int after) {
+        if (after <= 0) wait_vm<0>();
+        else if (after == 1) wait_vm<C::LOADS>();
+        else wait_vm<2 * C::LOADS>();
+    };
+
+    // ---- per-lane softmax state and accumulators --------------------------------
     float m_ref[RBW], l_run[RBW];
     f32x16_t acc[RBW][C::DB];
 #pragma unroll
@@ -115,151 +207,146 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
             for (int i = 0; i < 16; ++i) acc[rb][db][i] = 0.f;
     }
 
-    // ---- tile loads: global -> registers -----------------------------------
-    uint4 kreg[C::LPT_K], vreg[C::KPT_V];
-    const int v_c = tid % C::NCK, v_kq = tid / C::NCK;
-    auto load_tile = [&](int j0) {
+    // S^T of tile t for both row blocks
+    auto scores = [&](int t, f32x16_t (&s)[RBW][2]) {
+        const char *kt = smem + (t % NS) * C::STAGE;
 #pragma unroll
-        for (int li = 0; li < C::LPT_K; ++li) {
-            const int pidx = tid + li * NT;
-            const int key = pidx / C::CPR, ch = pidx % C::CPR;
-            kreg[li] = make_uint4(0, 0, 0, 0);
-            if (j0 + key < kv_len) {
-                // a wave's 64 / CPR keys lie in one 16-key group of the tile
-                const int64_t row = cache_row_wave(cache, b, g, j0 + key);
-                if (row >= 0) kreg[li] = ld16(cache.k + row * (D * 2) + ch * 16);
-            }
-        }
+        for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-        for (int k = 0; k < C::KPT_V; ++k) {
-            const int key = v_kq * C::KPT_V + k;
-            vreg[k] = make_uint4(0, 0, 0, 0);
-            if (j0 + key < kv_len) {
-                // a wave covers keys 16w .. 16w+15 of the tile
-                const int64_t row = cache_row_wave(cache, b, g, j0 + key);
-                if (row >= 0) vreg[k] = ld16(cache.v + row * (D * 2) + v_c * 16);
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s[rb][kb][i] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int key = kb * 32 + nq;
+                const uint4 a = *reinterpret_cast<const uint4 *>(
+                    kt + key * C::RB + (((2 * ks + hh) ^ (key & C::KSW)) * 16));
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb) s[rb][kb] = mfma32x32x16(a, qf[rb][ks], s[rb][kb]);
             }
-        }
     };
 
-    if (kv_end > 0) load_tile(0);
-    for (int j0 = 0; j0 < kv_end; j0 += BN) {
-        __syncthreads();   // everyone is done with the previous tile
-#pragma unroll
-        for (int li = 0; li < C::LPT_K; ++li) {
-            const int pidx = tid + li * NT;
-            const int key = pidx / C::CPR, ch = pidx % C::CPR;
-            Kl[key * C::CPR + (ch ^ (key & C::SWZ))] = kreg[li];
-        }
-        {
-            // V^T[d][key]: this thread holds keys v_kq*KPT_V .. +KPT_V-1 of columns 8*v_c .. 8*v_c+7
-            const uint32_t *w[4];
-#pragma unroll
-            for (int k = 0; k < C::KPT_V; ++k) w[k] = reinterpret_cast<const uint32_t *>(&vreg[k]);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                uint16_t *dst = Vt + (8 * v_c + e) * C::VT + v_kq * C::KPT_V;
-                if constexpr (C::KPT_V == 4) {
-                    const uint32_t w0 = (e & 1) ? pair_hi(w[0][e >> 1], w[1][e >> 1]) : pair_lo(w[0][e >> 1], w[1][e >> 1]);
-                    const uint32_t w1 = (e & 1) ? pair_hi(w[2][e >> 1], w[3][e >> 1]) : pair_lo(w[2][e >> 1], w[3][e >> 1]);
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(w0, w1);
-                } else {
-                    const uint32_t w0 = (e & 1) ? pair_hi(w[0][e >> 1], w[1][e >> 1]) : pair_lo(w[0][e >> 1], w[1][e >> 1]);
-                    *reinterpret_cast<uint32_t *>(dst) = w0;
-                }
-            }
-        }
-        __syncthreads();
-        if (j0 + BN < kv_end) load_tile(j0 + BN);
-
-        const bool need_mask = (j0 + BN > kv_len) || (p.causal && j0 + BN - 1 > start + q0);
+    // softmax of tile t -> bf16 P^T operands, and the rescale of the accumulators
+    auto softmax = [&](int t, f32x16_t (&s)[RBW][2], uint4 (&pb)[RBW][2][2]) {
+        const int j0 = t * BN;
+        const bool masked = j0 + BN > mask_from;
+        float mt[RBW];
+        bool need = false;
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
-            // S^T = K Q^T for the two 32-key halves of the tile
-            f32x16_t sacc[2];
+            if (masked) {
+                const int lim = p.causal ? min(qpos[rb] + 1, kv_len) : kv_len;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) sacc[kb][i] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < C::KS; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int key = kb * 32 + nq;
-                    const uint4 a = Kl[key * C::CPR + ((2 * ks + hh) ^ (key & C::SWZ))];
-                    sacc[kb] = mfma32x32x16(a, qf[rb][ks], sacc[kb]);
-                }
-            }
-            // scale, mask, row max (lane pairs l, l^32 share a query row)
-            const int qpos = start + row_i[rb];
-            float mt = -INFINITY;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float x = sacc[kb][i] * p.scale_log2;
-                    if (need_mask) {
+                    for (int i = 0; i < 16; ++i) {
                         const int key = j0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-                        if (key >= kv_len || (p.causal && key > qpos)) x = -INFINITY;
+                        if (key >= lim) s[rb][kb][i] = -INFINITY;
                     }
-                    sacc[kb][i] = x;
-                    mt = fmaxf(mt, x);
-                }
-            mt = fmaxf(mt, __shfl_xor(mt, 32, kWave));
-            float alpha = 1.f;
-            if (mt > m_ref[rb] + TAU) {
-                alpha = fast_exp2(m_ref[rb] - mt);
-                m_ref[rb] = mt;
             }
-            const float m_use = (m_ref[rb] == -INFINITY) ? 0.f : m_ref[rb];
-            // probabilities -> bf16 operand pairs; the sum uses the rounded values
-            uint4 pb[2][2];
+            float m = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m = fmaxf(m, s[rb][kb][i]);
+            m = fmaxf(m, __shfl_xor(m, 32, kWave));
+            mt[rb] = m * p.scale_log2;   // scale > 0, so the max commutes with it
+            need |= mt[rb] > m_ref[rb] + TAU;
+        }
+        if (__ballot(need) != 0) {
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                if (mt[rb] > m_ref[rb] + TAU) {
+                    const float alpha = fast_exp2(m_ref[rb] - mt[rb]);   // 0 on the first tile
+                    m_ref[rb] = mt[rb];
+                    l_run[rb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) acc[rb][db][i] *= alpha;
+                }
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            const float mu = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
             float ps = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
-                    uint32_t wv[4];
+                    uint32_t w[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float p0 = fast_exp2(sacc[kb][half * 8 + 2 * j] - m_use);
-                        const float p1 = fast_exp2(sacc[kb][half * 8 + 2 * j + 1] - m_use);
-                        const uint32_t u = pack_bf16x2(p0, p1);
-                        ps += __uint_as_float(u << 16) + __uint_as_float(u & 0xffff0000u);
-                        wv[j] = u;
+                        const float p0 = fast_exp2(fmaf(s[rb][kb][half * 8 + 2 * j], p.scale_log2, -mu));
+                        const float p1 = fast_exp2(fmaf(s[rb][kb][half * 8 + 2 * j + 1], p.scale_log2, -mu));
+                        ps += p0 + p1;
+                        w[j] = cvt_pk_bf16(p0, p1);
                     }
-                    pb[kb][half] = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                    pb[rb][kb][half] = make_uint4(w[0], w[1], w[2], w[3]);
                 }
-            ps += __shfl_xor(ps, 32, kWave);
-            l_run[rb] = l_run[rb] * alpha + ps;
-            if (alpha != 1.f) {
-#pragma unroll
-                for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) acc[rb][db][i] *= alpha;
-            }
-            // O^T += V^T P^T
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                const uint16_t *vrow = Vt + (db * 32 + nq) * C::VT;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const int k0 = kb * 32 + half * 16 + hh * 4;
-                        const uint2 lo = *reinterpret_cast<const uint2 *>(vrow + k0);
-                        const uint2 hi = *reinterpret_cast<const uint2 *>(vrow + k0 + 8);
-                        acc[rb][db] = mfma32x32x16(make_uint4(lo.x, lo.y, hi.x, hi.y), pb[kb][half], acc[rb][db]);
-                    }
-            }
+            l_run[rb] += ps;
         }
+    };
+
+    // O^T += V^T P^T for tile t: the V^T operand of (key step, 32 columns) via
+    // two transposing reads (keys +0..3 and +8..11 of this lane's 16-key step)
+    const int tr_g = lane >> 4, tr_j = lane & 15;
+    auto pv = [&](int t, const uint4 (&pb)[RBW][2][2]) {
+        const char *vt = smem + (t % NS) * C::STAGE + C::TILE;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    uint2 part[2];
+#pragma unroll
+                    for (int rd = 0; rd < 2; ++rd) {
+                        const int row = kb * 32 + half * 16 + 4 * (tr_g >> 1) + 8 * rd + (tr_j >> 2);
+                        const int col = db * 32 + 16 * (tr_g & 1) + 4 * (tr_j & 3);
+                        const int chunk = (col >> 3) ^ (2 * (row & 3));
+                        part[rd] = lds_read_tr16(vt + row * C::RB + chunk * 16 + (col & 7) * 2);
+                    }
+                    const uint4 a = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
+#pragma unroll
+                    for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = mfma32x32x16(a, pb[rb][kb][half], acc[rb][db]);
+                }
+    };
+
+    // ---- the pipeline -----------------------------------------------------------
+    // Iteration t: wait for tile t+1, barrier (everyone is past iteration
+    // t-1, so tile t-1's stage is free), start tile t+NS-1 into it, issue the
+    // scores of tile t+1, then the softmax and the V product of tile t.
+    for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t);
+    f32x16_t sa[RBW][2], sb[RBW][2];
+    uint4 pbuf[RBW][2][2];
+    if (ntiles > 0) {
+        wait_tile(min(NS - 2, ntiles - 1));
+        barrier();
+        scores(0, sa);
+    }
+    auto iter = [&](int t, f32x16_t (&scur)[RBW][2], f32x16_t (&snext)[RBW][2]) {
+        if (t + 1 < ntiles) wait_tile(min(NS - 3, ntiles - 2 - t));
+        barrier();
+        if (t + NS - 1 < ntiles) issue(t + NS - 1);
+        if (t + 1 < ntiles) scores(t + 1, snext);
+        softmax(t, scur, pbuf);
+        pv(t, pbuf);
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+        iter(t, sa, sb);
+        if (t + 1 < ntiles) iter(t + 1, sb, sa);
     }
 
-    // ---- normalise and store: lane owns 16 columns per 32-column block -----
+    // ---- normalise and store: lane owns 16 columns per 32-column block ----------
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
+        const float l = l_run[rb] + __shfl_xor(l_run[rb], 32, kWave);
         if (!row_ok[rb]) continue;
-        const float inv = l_run[rb] > 0.f ? 1.f / l_run[rb] : 0.f;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
         uint16_t *orow = reinterpret_cast<uint16_t *>(p.out) +
                          (((int64_t)b * p.s + row_i[rb]) * H + (int64_t)g * G + row_r[rb]) * D;
 #pragma unroll
@@ -267,29 +354,28 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int d0 = db * 32 + i4 * 8 + hh * 4;
-                const uint2 v = make_uint2(pack_bf16x2(acc[rb][db][4 * i4 + 0] * inv, acc[rb][db][4 * i4 + 1] * inv),
-                                           pack_bf16x2(acc[rb][db][4 * i4 + 2] * inv, acc[rb][db][4 * i4 + 3] * inv));
+                const uint2 v = make_uint2(cvt_pk_bf16(acc[rb][db][4 * i4 + 0] * inv, acc[rb][db][4 * i4 + 1] * inv),
+                                           cvt_pk_bf16(acc[rb][db][4 * i4 + 2] * inv, acc[rb][db][4 * i4 + 3] * inv));
                 *reinterpret_cast<uint2 *>(orow + d0) = v;
             }
     }
 }
 
-template <int D, int RBW>
-hipError_t launch_gp(const PrefillParams &p, int gp, hipStream_t s)
+template <int D>
+hipError_t launch_d(const PrefillParams &p, int gp, hipStream_t s)
 {
-    const int64_t rows = 128 * RBW;
-    const int64_t qb_pos = rows / gp;
+    const int64_t qb_pos = ROWS / gp;
     const int64_t nqb = (p.s + qb_pos - 1) / qb_pos;
     if (nqb > 0x7fffffffLL || p.cache.K > 65535 || p.B > 65535) return hipErrorInvalidValue;
     const dim3 grid((unsigned)nqb, (unsigned)p.cache.K, (unsigned)p.B);
     switch (gp) {
-    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, 1, RBW>), grid, dim3(NT), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, 2, RBW>), grid, dim3(NT), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, 4, RBW>), grid, dim3(NT), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((prefill_mfma_kernel<D, 8, RBW>), grid, dim3(NT), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((prefill_mfma_kernel<D, 16, RBW>), grid, dim3(NT), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32, RBW>), grid, dim3(NT), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((prefill_mfma_kernel<D, 64, RBW>), grid, dim3(NT), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, 1>), grid, dim3(NT), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, 2>), grid, dim3(NT), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, 4>), grid, dim3(NT), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((prefill_mfma_kernel<D, 8>), grid, dim3(NT), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((prefill_mfma_kernel<D, 16>), grid, dim3(NT), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32>), grid, dim3(NT), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((prefill_mfma_kernel<D, 64>), grid, dim3(NT), 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -301,8 +387,8 @@ hipError_t launch_prefill_mfma(const PrefillParams &p, hipStream_t stream)
 {
     const int gp = pow2_at_least(p.G);
     if (p.cache.elem_bytes != 2) return hipErrorInvalidValue;
-    if (p.cache.d == 128) return launch_gp<128, 1>(p, gp, stream);
-    if (p.cache.d == 64) return launch_gp<64, 1>(p, gp, stream);
+    if (p.cache.d == 128) return launch_d<128>(p, gp, stream);
+    if (p.cache.d == 64) return launch_d<64>(p, gp, stream);
     return hipErrorInvalidValue;
 }
 
