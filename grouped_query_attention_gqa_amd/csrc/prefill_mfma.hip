@@ -32,10 +32,13 @@
 //    §9.2.1): scale folded into one FMA, the running max only moved when a
 //    tile max exceeds it by 2^8 (checked with one wave vote), masking only on
 //    the tiles that cross the causal diagonal or the end of the keys.
-//  * The scores of tile j+1 are issued before the softmax and the V product
-//    of tile j, so the matrix cores have independent work while the vector
-//    units run the softmax.
+//  * The two waves of each SIMD run the tile loop half a phase apart (one
+//    scores tile t while the other finishes tile t-1), so one wave's softmax
+//    overlaps the other's matrix work; the K and V^T fragments are read from
+//    LDS a few matrix instructions ahead of their use.
 //  * Heaviest query blocks (largest causal key range) are launched first.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
 
     // ---- LDS-direct loads of tile t into stage t % NS --------------------------
     // K: row r's 16-byte chunk c lands in slot c ^ (r & KSW); V: slot c ^ 2 (r & 3).
-    auto issue = [&](int t) {
+    auto issue = [&](int t) __attribute__((always_inline)) {
         char *base = smem + (t % NS) * C::STAGE;
         const int j0 = t * BN;
 #pragma unroll
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
         }
     };
     // wait until tile t's loads have landed, given how many tiles were issued after it
-    auto wait_tile = [&](int after) {
+    auto wait_tile = [&](int after) __attribute__((always_inline)) {
         if (after <= 0) wait_vm<0>();
         else if (after == 1) wait_vm<C::LOADS>();
         else wait_vm<2 * C::LOADS>();
@@ -208,8 +211,20 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     }
 
     // S^T of tile t for both row blocks
-    auto scores = [&](int t, f32x16_t (&s)[RBW][2]) {
+    // S^T of tile t.  The K fragments are read KPF steps ahead of their
+    // matrix instruction so that LDS latency overlaps the matrix pipeline.
+    constexpr int SSTEPS = C::KS * 2;   // (k-step, 32-key block) pairs
+    constexpr int KPF = 4;
+    auto k_frag = [&](const char *kt, int st) __attribute__((always_inline)) {
+        const int ks = st / 2, kb = st % 2;
+        const int key = kb * 32 + nq;
+        return *reinterpret_cast<const uint4 *>(kt + key * C::RB + (((2 * ks + hh) ^ (key & C::KSW)) * 16));
+    };
+    auto scores = [&](int t, f32x16_t (&s)[RBW][2]) __attribute__((always_inline)) {
         const char *kt = smem + (t % NS) * C::STAGE;
+        uint4 kf[KPF];
+#pragma unroll
+        for (int st = 0; st < KPF; ++st) kf[st] = k_frag(kt, st);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
@@ -217,19 +232,17 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) s[rb][kb][i] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
+        for (int st = 0; st < SSTEPS; ++st) {
+            const uint4 a = kf[st % KPF];
+            if (st + KPF < SSTEPS) kf[st % KPF] = k_frag(kt, st + KPF);
+            const int ks = st / 2, kb = st % 2;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int key = kb * 32 + nq;
-                const uint4 a = *reinterpret_cast<const uint4 *>(
-                    kt + key * C::RB + (((2 * ks + hh) ^ (key & C::KSW)) * 16));
-#pragma unroll
-                for (int rb = 0; rb < RBW; ++rb) s[rb][kb] = mfma32x32x16(a, qf[rb][ks], s[rb][kb]);
-            }
+            for (int rb = 0; rb < RBW; ++rb) s[rb][kb] = mfma32x32x16(a, qf[rb][ks], s[rb][kb]);
+        }
     };
 
     // softmax of tile t -> bf16 P^T operands, and the rescale of the accumulators
-    auto softmax = [&](int t, f32x16_t (&s)[RBW][2], uint4 (&pb)[RBW][2][2]) {
+    auto softmax = [&](int t, f32x16_t (&s)[RBW][2], uint4 (&pb)[RBW][2][2]) __attribute__((always_inline)) {
         const int j0 = t * BN;
         const bool masked = j0 + BN > mask_from;
         float mt[RBW];
@@ -294,52 +307,74 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     // O^T += V^T P^T for tile t: the V^T operand of (key step, 32 columns) via
     // two transposing reads (keys +0..3 and +8..11 of this lane's 16-key step)
     const int tr_g = lane >> 4, tr_j = lane & 15;
-    auto pv = [&](int t, const uint4 (&pb)[RBW][2][2]) {
+    constexpr int PSTEPS = C::DB * 4;   // (32-column block, 16-key step) pairs
+    constexpr int VPF = 2;
+    auto v_frag = [&](const char *vt, int st) __attribute__((always_inline)) {
+        const int db = st / 4, kb = (st / 2) % 2, half = st % 2;
+        uint2 part[2];
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            const int row = kb * 32 + half * 16 + 4 * (tr_g >> 1) + 8 * rd + (tr_j >> 2);
+            const int col = db * 32 + 16 * (tr_g & 1) + 4 * (tr_j & 3);
+            const int chunk = (col >> 3) ^ (2 * (row & 3));
+            part[rd] = lds_read_tr16(vt + row * C::RB + chunk * 16 + (col & 7) * 2);
+        }
+        return make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
+    };
+    auto pv = [&](int t, const uint4 (&pb)[RBW][2][2]) __attribute__((always_inline)) {
         const char *vt = smem + (t % NS) * C::STAGE + C::TILE;
+        uint4 vf[VPF];
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+        for (int st = 0; st < VPF; ++st) vf[st] = v_frag(vt, st);
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int st = 0; st < PSTEPS; ++st) {
+            const uint4 a = vf[st % VPF];
+            if (st + VPF < PSTEPS) vf[st % VPF] = v_frag(vt, st + VPF);
+            const int db = st / 4, kb = (st / 2) % 2, half = st % 2;
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    uint2 part[2];
-#pragma unroll
-                    for (int rd = 0; rd < 2; ++rd) {
-                        const int row = kb * 32 + half * 16 + 4 * (tr_g >> 1) + 8 * rd + (tr_j >> 2);
-                        const int col = db * 32 + 16 * (tr_g & 1) + 4 * (tr_j & 3);
-                        const int chunk = (col >> 3) ^ (2 * (row & 3));
-                        part[rd] = lds_read_tr16(vt + row * C::RB + chunk * 16 + (col & 7) * 2);
-                    }
-                    const uint4 a = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
-#pragma unroll
-                    for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = mfma32x32x16(a, pb[rb][kb][half], acc[rb][db]);
-                }
+            for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = mfma32x32x16(a, pb[rb][kb][half], acc[rb][db]);
+        }
     };
 
     // ---- the pipeline -----------------------------------------------------------
-    // Iteration t: wait for tile t+1, barrier (everyone is past iteration
-    // t-1, so tile t-1's stage is free), start tile t+NS-1 into it, issue the
-    // scores of tile t+1, then the softmax and the V product of tile t.
-    for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t);
-    f32x16_t sa[RBW][2], sb[RBW][2];
+    // Iteration t: wait for tile t, barrier (everyone is past iteration t-1,
+    // so tile t-2's stage is free), start tile t+NS-2 into it.  Then the two
+    // waves of each SIMD run opposite phases: waves 0-3 score tile t, run its
+    // softmax and its V product; waves 4-7 first finish tile t-1 (softmax, V
+    // product) and then score tile t.  While one wave runs its softmax on the
+    // vector units, the other keeps the matrix core busy.
+    for (int t = 0; t < NS - 2 && t < ntiles; ++t) issue(t);
+    f32x16_t sc[RBW][2];
     uint4 pbuf[RBW][2][2];
-    if (ntiles > 0) {
-        wait_tile(min(NS - 2, ntiles - 1));
-        barrier();
-        scores(0, sa);
-    }
-    auto iter = [&](int t, f32x16_t (&scur)[RBW][2], f32x16_t (&snext)[RBW][2]) {
-        if (t + 1 < ntiles) wait_tile(min(NS - 3, ntiles - 2 - t));
-        barrier();
-        if (t + NS - 1 < ntiles) issue(t + NS - 1);
-        if (t + 1 < ntiles) scores(t + 1, snext);
-        softmax(t, scur, pbuf);
-        pv(t, pbuf);
+    // the whole loop is written out once per phase order, so each copy gets
+    // its own register allocation (both copies pass the same barriers)
+    auto run = [&](auto lag_tag) __attribute__((always_inline)) {
+        constexpr bool LAG = decltype(lag_tag)::value;
+        for (int t = 0; t < ntiles; ++t) {
+            wait_tile(min(NS - 3, ntiles - 1 - t));
+            barrier();
+            if (t + NS - 2 < ntiles) issue(t + NS - 2);
+            if constexpr (!LAG) {
+                scores(t, sc);
+                softmax(t, sc, pbuf);
+                pv(t, pbuf);
+            } else {
+                if (t > 0) {
+                    softmax(t - 1, sc, pbuf);
+                    pv(t - 1, pbuf);
+                }
+                scores(t, sc);
+            }
+        }
+        if constexpr (LAG) {
+            if (ntiles > 0) {
+                softmax(ntiles - 1, sc, pbuf);
+                pv(ntiles - 1, pbuf);
+            }
+        }
     };
-    for (int t = 0; t < ntiles; t += 2) {
-        iter(t, sa, sb);
-        if (t + 1 < ntiles) iter(t + 1, sb, sa);
-    }
+    if (wave >= NW / 2) run(std::true_type{});
+    else run(std::false_type{});
 
     // ---- normalise and store: lane owns 16 columns per 32-column block ----------
 #pragma unroll
