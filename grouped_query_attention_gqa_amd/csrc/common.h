@@ -52,13 +52,40 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // 64); every lane of a group ends with the group's result.  Within a 16-lane
 // row the steps are DPP lane permutations fused into the max/add (quad swaps,
 // half-row mirror, row mirror: after each step the value is uniform over the
-// lanes combined so far, so a mirror pairs complete sub-groups); only the
-// steps across rows go through ds_bpermute.
+// lanes combined so far, so a mirror pairs complete sub-groups); the steps
+// across rows use the permlane swaps above.
 template <int ctrl>
 __device__ __forceinline__ float dpp_f32(float x)
 {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false));
 }
+// Cross-row steps of a reduction without LDS traffic (a ds_bpermute would
+// share the LDS counter with the loads a kernel keeps in flight).
+// v_permlane32_swap (v_permlane16_swap) of a register with itself leaves each
+// lane holding its own value and the value of the lane 32 (16) away; which
+// of the two results is which depends on the lane, so they are combined with
+// a symmetric operation.
+__device__ __forceinline__ float2 swap_pair32(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 swap_pair16(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) { const float2 r = swap_pair32(x); return fmaxf(r.x, r.y); }
+__device__ __forceinline__ float sum_xor32(float x) { const float2 r = swap_pair32(x); return r.x + r.y; }
+// x + (x of the lane M away), for M = 16 or 32 through the swaps, else ds_bpermute
+template <int M>
+__device__ __forceinline__ float sum_xor(float x)
+{
+    if constexpr (M == 32) return sum_xor32(x);
+    else if constexpr (M == 16) { const float2 r = swap_pair16(x); return r.x + r.y; }
+    else return x + __shfl_xor(x, M, kWave);
+}
+
 template <int width, bool is_max>
 __device__ __forceinline__ float group_reduce(float x)
 {
@@ -67,8 +94,8 @@ __device__ __forceinline__ float group_reduce(float x)
     if constexpr (width >= 4) x = op(x, dpp_f32<0x4E>(x));    // quad_perm [2,3,0,1]
     if constexpr (width >= 8) x = op(x, dpp_f32<0x141>(x));   // row_half_mirror
     if constexpr (width >= 16) x = op(x, dpp_f32<0x140>(x));  // row_mirror
-    if constexpr (width >= 32) x = op(x, __shfl_xor(x, 16, kWave));
-    if constexpr (width >= 64) x = op(x, __shfl_xor(x, 32, kWave));
+    if constexpr (width >= 32) { const float2 r = swap_pair16(x); x = op(r.x, r.y); }
+    if constexpr (width >= 64) { const float2 r = swap_pair32(x); x = op(r.x, r.y); }
     return x;
 }
 template <int width>

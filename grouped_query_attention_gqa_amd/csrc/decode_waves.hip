@@ -367,11 +367,12 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
 
         // ---- merge the waves' pieces of the segment ---------------------------
 #pragma unroll
-        for (int m = C::VCPR; m < kWave; m <<= 1)
+        for (int h = 0; h < GP; ++h)
 #pragma unroll
-            for (int h = 0; h < GP; ++h)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[h][e] += __shfl_xor(acc[h][e], m, kWave);
+            for (int e = 0; e < 4; ++e) {
+                if constexpr (C::VCPR <= 16) acc[h][e] = sum_xor<16>(acc[h][e]);
+                acc[h][e] = sum_xor<32>(acc[h][e]);
+            }
 #pragma unroll
         for (int h = 0; h < C::HPL; ++h) l_run[h] = group_sum<C::TT>(l_run[h]);
         __syncthreads();   // every wave is done with its K buffer and q: the K buffers become the merge area

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) m = fmaxf(m, s[rb][kb][i]);
-            m = fmaxf(m, __shfl_xor(m, 32, kWave));
+            m = max_xor32(m);
             mt[rb] = m * p.scale_log2;   // scale > 0, so the max commutes with it
             need |= mt[rb] > m_ref[rb] + TAU;
         }
@@ -295,8 +295,8 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
                     for (int j = 0; j < 4; ++j) {
                         const float p0 = fast_exp2(fmaf(s[rb][kb][half * 8 + 2 * j], p.scale_log2, -mu));
                         const float p1 = fast_exp2(fmaf(s[rb][kb][half * 8 + 2 * j + 1], p.scale_log2, -mu));
-                        ps += p0 + p1;
                         w[j] = cvt_pk_bf16(p0, p1);
+                        ps = dot2_bf16(w[j], 0x3F803F80u, ps);   // + both rounded probabilities
                     }
                     pb[rb][kb][half] = make_uint4(w[0], w[1], w[2], w[3]);
                 }
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     // ---- normalise and store: lane owns 16 columns per 32-column block ----------
 #pragma unroll
     for (int rb = 0; rb < RBW; ++rb) {
-        const float l = l_run[rb] + __shfl_xor(l_run[rb], 32, kWave);
+        const float l = sum_xor32(l_run[rb]);
         if (!row_ok[rb]) continue;
         const float inv = l > 0.f ? 1.f / l : 0.f;
         uint16_t *orow = reinterpret_cast<uint16_t *>(p.out) +
