@@ -23,9 +23,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
     return u >> 16;
 }
 
+// Two floats to a bf16 pair (lo in the low half), round to nearest even, in
+// one v_cvt_pk_bf16_f32.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
 }
 
 // Two bf16 products summed into an fp32 accumulator (v_dot2_f32_bf16).

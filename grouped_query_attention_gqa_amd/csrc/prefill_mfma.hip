@@ -101,11 +101,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char *p)
     return __builtin_bit_cast(uint2, v);
 }
 
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi)
-{
-    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)hi) << 16);
-}
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
 template <int D, int GP>
 struct PCfg {
@@ -268,7 +264,10 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
             mt[rb] = m * p.scale_log2;   // scale > 0, so the max commutes with it
             need |= mt[rb] > m_ref[rb] + TAU;
         }
-        if (__ballot(need) != 0) {
+        if (__builtin_expect(__ballot(need) != 0, 0)) {
+            // rare: kept as a branch (the empty volatile asm stops the compiler
+            // from flattening it into multiplies on every tile)
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 if (mt[rb] > m_ref[rb] + TAU) {
