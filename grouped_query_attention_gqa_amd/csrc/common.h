@@ -110,6 +110,23 @@ __device__ __forceinline__ float group_sum(float x) { return group_reduce<width,
 
 // 16-byte global load / store helpers.
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// Pointers tagged as global memory.  A pointer picked between two objects
+// (a cache row or a zero page) would otherwise be a generic one, and a
+// generic (flat) load is also counted by the LDS counter: every wait for an
+// LDS read would then wait for the HBM loads in flight as well.
+typedef const __attribute__((address_space(1))) char gmem_t;
+__device__ __forceinline__ gmem_t *gmem(const void *p) { return (gmem_t *)p; }
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 gld16(gmem_t *p)
+{
+    return __builtin_bit_cast(uint4, *(const __attribute__((address_space(1))) u32x4_t *)p);
+}
+__device__ __forceinline__ uint2 gld8(gmem_t *p)
+{
+    return __builtin_bit_cast(uint2, *(const __attribute__((address_space(1))) u32x2_t *)p);
+}
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
 }  // namespace gqa

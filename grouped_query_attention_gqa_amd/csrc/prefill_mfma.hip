@@ -342,6 +342,11 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     // softmax and its V product; waves 4-7 first finish tile t-1 (softmax, V
     // product) and then score tile t.  While one wave runs its softmax on the
     // vector units, the other keeps the matrix core busy.
+    // The Q^T fragments must have landed before the first tile is issued:
+    // otherwise the wait the compiler places before their first use (inside
+    // the loop, so it runs on every iteration) also waits for every tile
+    // load in flight.
+    wait_vm<0>();
     for (int t = 0; t < NS - 2 && t < ntiles; ++t) issue(t);
     f32x16_t sc[RBW][2];
     uint4 pbuf[RBW][2][2];
