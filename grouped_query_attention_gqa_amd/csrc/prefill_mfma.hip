@@ -80,6 +80,18 @@ __device__ __forceinline__ void dma16(const void *src, void *lds_wave_base)
                  :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 #pragma clang diagnostic pop
 }
+// The same with a wave-uniform 64-bit base and a 32-bit lane offset.
+__device__ __forceinline__ void dma16_s(uint32_t off, const void *base, uint32_t lds)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint64_t ua = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32) |
+                        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :: "v"(off), "s"(ua), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+#pragma clang diagnostic pop
+}
 template <int N>
 __device__ __forceinline__ void wait_vm()
 {
@@ -132,8 +144,15 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int nq = lane & 31, hh = lane >> 5;
     const int num_qb = (p.s + C::QB - 1) / C::QB;
-    const int qb = num_qb - 1 - (int)blockIdx.x;   // heaviest first
-    const int g = blockIdx.y, b = blockIdx.z;
+    // Workgroups are dispatched in index order: the heaviest query blocks
+    // (longest causal key range) of every (sequence, group) come first, and
+    // the K (x B) workgroups of one query block follow each other.  The
+    // blocks of one (sequence, group) are K x B indices apart, so with K x B
+    // a multiple of 8 they share an XCD and its L2.
+    const int kb_pairs = p.cache.K * p.B;
+    const int qb = num_qb - 1 - (int)(blockIdx.x / kb_pairs);
+    const int g = (int)(blockIdx.x % kb_pairs) % p.cache.K;
+    const int b = (int)(blockIdx.x % kb_pairs) / p.cache.K;
     const int q0 = qb * C::QB;
     const int start = p.start_pos[b];
     const int G = p.G, H = p.H;
@@ -164,9 +183,33 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
 
     // ---- LDS-direct loads of tile t into stage t % NS --------------------------
     // K: row r's 16-byte chunk c lands in slot c ^ (r & KSW); V: slot c ^ 2 (r & 3).
+    // Lane offsets of the full-tile path (contiguous cache): tile row r_k of
+    // this lane's k-th load and its swizzled 16-byte slot, for K and for V.
+    uint32_t koff[C::LPW], voff[C::LPW];
+#pragma unroll
+    for (int k = 0; k < C::LPW; ++k) {
+        const int r = (wave + NW * k) * C::RPK + lane / C::CPR;
+        const int slot = lane % C::CPR;
+        koff[k] = (uint32_t)(r * C::RB + (slot ^ (r & C::KSW)) * 16);
+        voff[k] = (uint32_t)(r * C::RB + (slot ^ (2 * (r & 3))) * 16);
+    }
+    const bool contiguous = cache.block_table == nullptr;
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;   // LDS address of the stages
+    const char *kseq = cache.k + ((int64_t)b * cache.K + g) * cache.S_max * C::RB;
+    const char *vseq = cache.v + ((int64_t)b * cache.K + g) * cache.S_max * C::RB;
     auto issue = [&](int t) __attribute__((always_inline)) {
         char *base = smem + (t % NS) * C::STAGE;
         const int j0 = t * BN;
+        if (contiguous && j0 + BN <= kv_len) {
+            // every row of the tile is in the cache: a uniform base and lane offsets
+#pragma unroll
+            for (int k = 0; k < C::LPW; ++k) {
+                const uint32_t at = lds0 + (uint32_t)((t % NS) * C::STAGE + (wave + NW * k) * 1024);
+                dma16_s(koff[k], kseq + (int64_t)j0 * C::RB, at);
+                dma16_s(voff[k], vseq + (int64_t)j0 * C::RB, at + C::TILE);
+            }
+            return;
+        }
 #pragma unroll
         for (int k = 0; k < C::LPW; ++k) {
             const int blk = wave + NW * k;                // 1 KB block of the tile
@@ -237,11 +280,11 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
         }
     };
 
-    // softmax of tile t -> bf16 P^T operands, and the rescale of the accumulators
-    auto softmax = [&](int t, f32x16_t (&s)[RBW][2], uint4 (&pb)[RBW][2][2]) __attribute__((always_inline)) {
+    // Softmax of tile t in three parts: the tile maximum (with the causal
+    // mask on the tiles that need it) and the vote on a rescale; the rare
+    // rescale of the accumulators; the bf16 probabilities P^T and their sum.
+    auto tile_max = [&](int t, f32x16_t (&s)[RBW][2], bool masked, float (&mt)[RBW]) __attribute__((always_inline)) {
         const int j0 = t * BN;
-        const bool masked = j0 + BN > mask_from;
-        float mt[RBW];
         bool need = false;
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
@@ -264,23 +307,23 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
             mt[rb] = m * p.scale_log2;   // scale > 0, so the max commutes with it
             need |= mt[rb] > m_ref[rb] + TAU;
         }
-        if (__builtin_expect(__ballot(need) != 0, 0)) {
-            // rare: kept as a branch (the empty volatile asm stops the compiler
-            // from flattening it into multiplies on every tile)
-            asm volatile("" ::: "memory");
+        return __ballot(need) != 0;
+    };
+    auto rescale = [&](const float (&mt)[RBW]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-                if (mt[rb] > m_ref[rb] + TAU) {
-                    const float alpha = fast_exp2(m_ref[rb] - mt[rb]);   // 0 on the first tile
-                    m_ref[rb] = mt[rb];
-                    l_run[rb] *= alpha;
+        for (int rb = 0; rb < RBW; ++rb) {
+            if (mt[rb] > m_ref[rb] + TAU) {
+                const float alpha = fast_exp2(m_ref[rb] - mt[rb]);   // 0 on the first tile
+                m_ref[rb] = mt[rb];
+                l_run[rb] *= alpha;
 #pragma unroll
-                    for (int db = 0; db < C::DB; ++db)
+                for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-                        for (int i = 0; i < 16; ++i) acc[rb][db][i] *= alpha;
-                }
+                    for (int i = 0; i < 16; ++i) acc[rb][db][i] *= alpha;
             }
         }
+    };
+    auto probs = [&](const f32x16_t (&s)[RBW][2], uint4 (&pb)[RBW][2][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
             const float mu = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
@@ -308,8 +351,10 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     const int tr_g = lane >> 4, tr_j = lane & 15;
     constexpr int PSTEPS = C::DB * 4;   // (32-column block, 16-key step) pairs
     constexpr int VPF = 2;
+    // step st: key step st / DB (kb, half), column block st % DB, so that the
+    // first matrix instructions need only the first probabilities
     auto v_frag = [&](const char *vt, int st) __attribute__((always_inline)) {
-        const int db = st / 4, kb = (st / 2) % 2, half = st % 2;
+        const int db = st % C::DB, kb = st / C::DB / 2, half = (st / C::DB) % 2;
         uint2 part[2];
 #pragma unroll
         for (int rd = 0; rd < 2; ++rd) {
@@ -329,56 +374,155 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
         for (int st = 0; st < PSTEPS; ++st) {
             const uint4 a = vf[st % VPF];
             if (st + VPF < PSTEPS) vf[st % VPF] = v_frag(vt, st + VPF);
-            const int db = st / 4, kb = (st / 2) % 2, half = st % 2;
+            const int db = st % C::DB, kb = st / C::DB / 2, half = (st / C::DB) % 2;
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = mfma32x32x16(a, pb[rb][kb][half], acc[rb][db]);
         }
     };
 
     // ---- the pipeline -----------------------------------------------------------
-    // Iteration t: wait for tile t, barrier (everyone is past iteration t-1,
-    // so tile t-2's stage is free), start tile t+NS-2 into it.  Then the two
-    // waves of each SIMD run opposite phases: waves 0-3 score tile t, run its
-    // softmax and its V product; waves 4-7 first finish tile t-1 (softmax, V
-    // product) and then score tile t.  While one wave runs its softmax on the
-    // vector units, the other keeps the matrix core busy.
-    // The Q^T fragments must have landed before the first tile is issued:
-    // otherwise the wait the compiler places before their first use (inside
-    // the loop, so it runs on every iteration) also waits for every tile
-    // load in flight.
-    wait_vm<0>();
-    for (int t = 0; t < NS - 2 && t < ntiles; ++t) issue(t);
-    f32x16_t sc[RBW][2];
+    // Iteration t: wait for tile t+1, barrier (every wave is past iteration
+    // t-1, so the stage of tile t-1 is free), start tile t+NS-1 into it.
+    // Then, in one wave: the scores of tile t+1 on the matrix cores while the
+    // vector units take the maximum of tile t; the rare rescale; the V product
+    // of tile t on the matrix cores while the vector units form the
+    // probabilities of tile t.  The instruction groups are interleaved
+    // explicitly (one matrix instruction, then a few LDS reads and vector
+    // instructions) so that one wave keeps both units busy.
+    for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t);
+    if (ntiles > 0) {
+        wait_tile(min(NS - 2, ntiles - 1));
+        barrier();
+    }
+    f32x16_t sA[RBW][2], sB[RBW][2];
     uint4 pbuf[RBW][2][2];
-    // the whole loop is written out once per phase order, so each copy gets
-    // its own register allocation (both copies pass the same barriers)
-    auto run = [&](auto lag_tag) __attribute__((always_inline)) {
-        constexpr bool LAG = decltype(lag_tag)::value;
-        for (int t = 0; t < ntiles; ++t) {
-            wait_tile(min(NS - 3, ntiles - 1 - t));
-            barrier();
-            if (t + NS - 2 < ntiles) issue(t + NS - 2);
-            if constexpr (!LAG) {
-                scores(t, sc);
-                softmax(t, sc, pbuf);
-                pv(t, pbuf);
-            } else {
-                if (t > 0) {
-                    softmax(t - 1, sc, pbuf);
-                    pv(t - 1, pbuf);
-                }
-                scores(t, sc);
-            }
-        }
-        if constexpr (LAG) {
-            if (ntiles > 0) {
-                softmax(ntiles - 1, sc, pbuf);
-                pv(ntiles - 1, pbuf);
-            }
-        }
+    if (ntiles > 0) scores(0, sA);
+    // tiles below t_mask need no mask; the steady loop runs while a next
+    // tile exists and the current one is unmasked
+    const int t_mask = min(ntiles, mask_from / BN);
+    const int t_steady = min(t_mask, ntiles - 1);
+    // One probability pair of tile t: k-step ksp (keys kb*32 + half*16 ..),
+    // pair j of its four, into pw and the running sum.
+    auto prob_pair = [&](int rb, const f32x16_t (&s)[RBW][2], float mu, int ksp, int j, uint32_t (&pw)[RBW][4][4],
+                         float &ps) __attribute__((always_inline)) {
+        const int kb = ksp / 2, half = ksp % 2;
+        const float p0 = fast_exp2(fmaf(s[rb][kb][half * 8 + 2 * j], p.scale_log2, -mu));
+        const float p1 = fast_exp2(fmaf(s[rb][kb][half * 8 + 2 * j + 1], p.scale_log2, -mu));
+        pw[rb][ksp][j] = cvt_pk_bf16(p0, p1);
+        ps = dot2_bf16(pw[rb][ksp][j], 0x3F803F80u, ps);   // + both rounded probabilities
     };
-    if (wave >= NW / 2) run(std::true_type{});
-    else run(std::false_type{});
+    // The steady iteration, written as a sequence of small groups fenced from
+    // each other: each group holds one matrix instruction, the LDS reads a
+    // few matrix instructions ahead, and a share of the softmax of tile t.
+    auto steady = [&](int t, f32x16_t (&sc)[RBW][2], f32x16_t (&sn)[RBW][2]) __attribute__((always_inline)) {
+        wait_tile(min(1, ntiles - 2 - t));   // tile t+1 landed (t+2 may be in flight)
+        barrier();
+        if (t + NS - 1 < ntiles) issue(t + NS - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        // -- S(t+1) = K(t+1) Q^T, with the maximum of S(t) alongside
+        const char *kt = smem + ((t + 1) % NS) * C::STAGE;
+        uint4 kf[KPF];
+#pragma unroll
+        for (int st = 0; st < KPF; ++st) kf[st] = k_frag(kt, st);
+        float m[RBW];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            m[rb] = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) sn[rb][kb][i] = 0.f;
+        }
+#pragma unroll
+        for (int st = 0; st < SSTEPS; ++st) {
+            const uint4 a = kf[st % KPF];
+            if (st + KPF < SSTEPS) kf[st % KPF] = k_frag(kt, st + KPF);
+            const int ks = st / 2, kb = st % 2;
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) sn[rb][kb] = mfma32x32x16(a, qf[rb][ks], sn[rb][kb]);
+            // 32 scores per lane over 16 steps: two per step
+            const int e = 2 * st;
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+                m[rb] = fmaxf(fmaxf(m[rb], sc[rb][e / 16][e % 16]), sc[rb][e / 16][e % 16 + 1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        float mt[RBW];
+        bool need = false;
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            mt[rb] = max_xor32(m[rb]) * p.scale_log2;   // scale > 0, so the max commutes with it
+            need |= mt[rb] > m_ref[rb] + TAU;
+        }
+        if (__builtin_expect(__ballot(need) != 0, 0)) {
+            // rare: kept as a branch (the empty volatile asm stops the compiler
+            // from flattening it into multiplies on every tile)
+            asm volatile("" ::: "memory");
+            rescale(mt);
+        }
+        // -- O^T += V^T(t) P^T(t), forming the probabilities one k-step ahead
+        const char *vt = smem + (t % NS) * C::STAGE + C::TILE;
+        uint4 vf[VPF];
+#pragma unroll
+        for (int st = 0; st < VPF; ++st) vf[st] = v_frag(vt, st);
+        uint32_t pw[RBW][4][4];
+        float mu[RBW], ps[RBW][2];   // two partial row sums: shorter dependency chains
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            mu[rb] = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
+            ps[rb][0] = 0.f;
+            ps[rb][1] = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) prob_pair(rb, sc, mu[rb], 0, j, pw, ps[rb][j & 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        constexpr int PPS = 4 / C::DB;   // probability pairs per matrix instruction
+#pragma unroll
+        for (int st = 0; st < PSTEPS; ++st) {
+            const uint4 a = vf[st % VPF];
+            if (st + VPF < PSTEPS) vf[st % VPF] = v_frag(vt, st + VPF);
+            const int db = st % C::DB, ksp = st / C::DB;
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+                acc[rb][db] = mfma32x32x16(a, make_uint4(pw[rb][ksp][0], pw[rb][ksp][1], pw[rb][ksp][2], pw[rb][ksp][3]),
+                                           acc[rb][db]);
+            if (ksp + 1 < 4) {
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                    for (int q = 0; q < PPS; ++q)
+                        prob_pair(rb, sc, mu[rb], ksp + 1, db * PPS + q, pw, ps[rb][(db * PPS + q) & 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) l_run[rb] += ps[rb][0] + ps[rb][1];
+    };
+    int t = 0;
+    for (; t + 1 < t_steady; t += 2) {
+        steady(t, sA, sB);
+        steady(t + 1, sB, sA);
+    }
+    if (t < t_steady) {
+        steady(t, sA, sB);
+        ++t;
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) { sA[rb][0] = sB[rb][0]; sA[rb][1] = sB[rb][1]; }
+    }
+    // the rest: tiles that need the mask, and the last tile
+    for (; t < ntiles; ++t) {
+        const bool has_next = t + 1 < ntiles;
+        if (has_next) wait_tile(min(1, ntiles - 2 - t));
+        barrier();
+        if (t + NS - 1 < ntiles) issue(t + NS - 1);
+        if (has_next) scores(t + 1, sB);
+        float mt[RBW];
+        if (tile_max(t, sA, t >= t_mask, mt)) rescale(mt);
+        probs(sA, pbuf);
+        pv(t, pbuf);
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) { sA[rb][0] = sB[rb][0]; sA[rb][1] = sB[rb][1]; }
+    }
 
     // ---- normalise and store: lane owns 16 columns per 32-column block ----------
 #pragma unroll
@@ -405,8 +549,8 @@ hipError_t launch_d(const PrefillParams &p, int gp, hipStream_t s)
 {
     const int64_t qb_pos = ROWS / gp;
     const int64_t nqb = (p.s + qb_pos - 1) / qb_pos;
-    if (nqb > 0x7fffffffLL || p.cache.K > 65535 || p.B > 65535) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)nqb, (unsigned)p.cache.K, (unsigned)p.B);
+    if (nqb * p.cache.K * p.B > 0x7fffffffLL) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(nqb * p.cache.K * p.B));
     switch (gp) {
     case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, 1>), grid, dim3(NT), 0, s, p); break;
     case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, 2>), grid, dim3(NT), 0, s, p); break;
