@@ -120,7 +120,12 @@ struct PCfg {
     static constexpr int QB = ROWS / GP;          // positions per workgroup
     static constexpr int RB = D * 2;              // bytes per K/V row
     static constexpr int CPR = RB / 16;           // 16-byte chunks per row
-    static constexpr int KSW = (CPR < 16 ? CPR : 16) - 1;   // K swizzle mask
+    // 16-byte slot swizzles, chosen so that the LDS reads of the scores (16
+    // lanes read 16 bytes of 16 consecutive keys) and of V^T (32 lanes read 8
+    // bytes of 4 consecutive keys) spread over all 64 LDS banks: K row r keeps
+    // chunk c in slot c ^ ksw(r), V row r in slot c ^ vsw(r).
+    __device__ static constexpr int ksw(int r) { return CPR >= 16 ? (r & 15) : ((r >> 1) & (CPR - 1)); }
+    __device__ static constexpr int vsw(int r) { return CPR >= 16 ? 4 * (r & 3) : 2 * (r & 3); }
     static constexpr int KS = D / 16;             // k-steps of S^T = K Q^T
     static constexpr int DB = D / 32;             // 32-row blocks of O^T
     static constexpr int TILE = BN * RB;          // bytes of K (or V) per tile
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     }
 
     // ---- LDS-direct loads of tile t into stage t % NS --------------------------
-    // K: row r's 16-byte chunk c lands in slot c ^ (r & KSW); V: slot c ^ 2 (r & 3).
+    // K: row r's 16-byte chunk c lands in slot c ^ ksw(r); V: slot c ^ vsw(r).
     // Lane offsets of the full-tile path (contiguous cache): tile row r_k of
     // this lane's k-th load and its swizzled 16-byte slot, for K and for V.
     uint32_t koff[C::LPW], voff[C::LPW];
@@ -190,8 +195,8 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     for (int k = 0; k < C::LPW; ++k) {
         const int r = (wave + NW * k) * C::RPK + lane / C::CPR;
         const int slot = lane % C::CPR;
-        koff[k] = (uint32_t)(r * C::RB + (slot ^ (r & C::KSW)) * 16);
-        voff[k] = (uint32_t)(r * C::RB + (slot ^ (2 * (r & 3))) * 16);
+        koff[k] = (uint32_t)(r * C::RB + (slot ^ C::ksw(r)) * 16);
+        voff[k] = (uint32_t)(r * C::RB + (slot ^ C::vsw(r)) * 16);
     }
     const bool contiguous = cache.block_table == nullptr;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;   // LDS address of the stages
@@ -221,8 +226,8 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
                 const int64_t row0 = cache_row_wave(cache, b, g, j0 + blk * C::RPK);
                 if (row0 >= 0 && j0 + r < kv_len) {
                     const int64_t row = row0 + (r - blk * C::RPK);
-                    srck = cache.k + row * C::RB + (slot ^ (r & C::KSW)) * 16;
-                    srcv = cache.v + row * C::RB + (slot ^ (2 * (r & 3))) * 16;
+                    srck = cache.k + row * C::RB + (slot ^ C::ksw(r)) * 16;
+                    srcv = cache.v + row * C::RB + (slot ^ C::vsw(r)) * 16;
                 }
             }
             dma16(srck, base + blk * 1024);
@@ -257,7 +262,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     auto k_frag = [&](const char *kt, int st) __attribute__((always_inline)) {
         const int ks = st / 2, kb = st % 2;
         const int key = kb * 32 + nq;
-        return *reinterpret_cast<const uint4 *>(kt + key * C::RB + (((2 * ks + hh) ^ (key & C::KSW)) * 16));
+        return *reinterpret_cast<const uint4 *>(kt + key * C::RB + (((2 * ks + hh) ^ C::ksw(key)) * 16));
     };
     auto scores = [&](int t, f32x16_t (&s)[RBW][2]) __attribute__((always_inline)) {
         const char *kt = smem + (t % NS) * C::STAGE;
@@ -360,7 +365,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
         for (int rd = 0; rd < 2; ++rd) {
             const int row = kb * 32 + half * 16 + 4 * (tr_g >> 1) + 8 * rd + (tr_j >> 2);
             const int col = db * 32 + 16 * (tr_g & 1) + 4 * (tr_j & 3);
-            const int chunk = (col >> 3) ^ (2 * (row & 3));
+            const int chunk = (col >> 3) ^ C::vsw(row);
             part[rd] = lds_read_tr16(vt + row * C::RB + chunk * 16 + (col & 7) * 2);
         }
         return make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
