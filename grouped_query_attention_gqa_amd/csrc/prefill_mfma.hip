@@ -71,25 +71,12 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(uint4 a, uint4 b, f32x16_t c)
 // One LDS-direct 16-byte load per lane (lane i's bytes land at base + 16 i),
 // written as inline assembly so the compiler does not wait for it before LDS
 // reads; the kernel waits with explicit vmcnt.
-__device__ __forceinline__ void dma16(const void *src, void *lds_wave_base)
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds)
 {
-    const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t *)lds_wave_base;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
                  :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
-#pragma clang diagnostic pop
-}
-// The same with a wave-uniform 64-bit base and a 32-bit lane offset.
-__device__ __forceinline__ void dma16_s(uint32_t off, const void *base, uint32_t lds)
-{
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    const uint64_t ua = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32) |
-                        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-                 :: "v"(off), "s"(ua), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 #pragma clang diagnostic pop
 }
 template <int N>
@@ -202,16 +189,17 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;   // LDS address of the stages
     const char *kseq = cache.k + ((int64_t)b * cache.K + g) * cache.S_max * C::RB;
     const char *vseq = cache.v + ((int64_t)b * cache.K + g) * cache.S_max * C::RB;
-    auto issue = [&](int t) __attribute__((always_inline)) {
-        char *base = smem + (t % NS) * C::STAGE;
+    // Lane source pointers of tile t's loads (K then V for each of this
+    // wave's 1 KB blocks); rows outside the keys, and tiles past the last,
+    // read a zero constant.
+    auto plan = [&](int t, const char *(&src)[2 * C::LPW]) __attribute__((always_inline)) {
         const int j0 = t * BN;
-        if (contiguous && j0 + BN <= kv_len) {
+        if (t < ntiles && contiguous && j0 + BN <= kv_len) {
             // every row of the tile is in the cache: a uniform base and lane offsets
 #pragma unroll
             for (int k = 0; k < C::LPW; ++k) {
-                const uint32_t at = lds0 + (uint32_t)((t % NS) * C::STAGE + (wave + NW * k) * 1024);
-                dma16_s(koff[k], kseq + (int64_t)j0 * C::RB, at);
-                dma16_s(voff[k], vseq + (int64_t)j0 * C::RB, at + C::TILE);
+                src[2 * k] = kseq + (int64_t)j0 * C::RB + koff[k];
+                src[2 * k + 1] = vseq + (int64_t)j0 * C::RB + voff[k];
             }
             return;
         }
@@ -220,8 +208,8 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
             const int blk = wave + NW * k;                // 1 KB block of the tile
             const int r = blk * C::RPK + lane / C::CPR;   // tile row of this lane
             const int slot = lane % C::CPR;
-            const void *srck = &kZero16P, *srcv = &kZero16P;
-            if (j0 + blk * C::RPK < kv_len) {
+            const char *srck = reinterpret_cast<const char *>(&kZero16P), *srcv = srck;
+            if (t < ntiles && j0 + blk * C::RPK < kv_len) {
                 // the block's rows lie in one 16-row group, hence in one cache block
                 const int64_t row0 = cache_row_wave(cache, b, g, j0 + blk * C::RPK);
                 if (row0 >= 0 && j0 + r < kv_len) {
@@ -230,9 +218,19 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
                     srcv = cache.v + row * C::RB + (slot ^ C::vsw(r)) * 16;
                 }
             }
-            dma16(srck, base + blk * 1024);
-            dma16(srcv, base + C::TILE + blk * 1024);
+            src[2 * k] = srck;
+            src[2 * k + 1] = srcv;
         }
+    };
+    // LDS address of load i (K or V of block k = i / 2) of tile t
+    auto lds_at = [&](int t, int i) __attribute__((always_inline)) {
+        return lds0 + (uint32_t)((t % NS) * C::STAGE + (i & 1) * C::TILE + (wave + NW * (i / 2)) * 1024);
+    };
+    auto issue = [&](int t) __attribute__((always_inline)) {
+        const char *src[2 * C::LPW];
+        plan(t, src);
+#pragma unroll
+        for (int i = 0; i < 2 * C::LPW; ++i) dma16(src[i], lds_at(t, i));
     };
     // wait until tile t's loads have landed, given how many tiles were issued after it
     auto wait_tile = [&](int after) __attribute__((always_inline)) {
@@ -422,7 +420,12 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     auto steady = [&](int t, f32x16_t (&sc)[RBW][2], f32x16_t (&sn)[RBW][2]) __attribute__((always_inline)) {
         wait_tile(min(1, ntiles - 2 - t));   // tile t+1 landed (t+2 may be in flight)
         barrier();
-        if (t + NS - 1 < ntiles) issue(t + NS - 1);
+        // tile t+NS-1 goes into the stage of tile t-1; its loads are spread
+        // over the score steps (issued together, they would stall the wave
+        // on the full memory queue)
+        const int tn = t + NS - 1;
+        const char *src[2 * C::LPW];
+        plan(tn, src);
         __builtin_amdgcn_sched_barrier(0);
         // -- S(t+1) = K(t+1) Q^T, with the maximum of S(t) alongside
         const char *kt = smem + ((t + 1) % NS) * C::STAGE;
@@ -450,6 +453,8 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb)
                 m[rb] = fmaxf(fmaxf(m[rb], sc[rb][e / 16][e % 16]), sc[rb][e / 16][e % 16 + 1]);
+            constexpr int EVERY = SSTEPS / (2 * C::LPW);
+            if (st % EVERY == EVERY / 2) dma16(src[st / EVERY], lds_at(tn, st / EVERY));
             __builtin_amdgcn_sched_barrier(0);
         }
         float mt[RBW];
