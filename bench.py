@@ -347,7 +347,7 @@ def main():
 
     if not args.no_extra:
         # ---- causal prefill ------------------------------------------------
-        result["prefill"] = bench_prefill(W.WORKLOADS["causal_prefill_4k"], max(3, args.steps // 5), 2)
+        result["prefill"] = bench_prefill(W.WORKLOADS["causal_prefill_4k"], max(10, args.steps // 2), 5)
         torch.cuda.empty_cache()
         # ---- the other decode shapes --------------------------------------
         extra = {}
