@@ -51,13 +51,9 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
-constexpr int NT = 512;            // 8 waves, two per SIMD
-constexpr int NW = NT / kWave;
 constexpr int BN = kKeyTile;       // keys per tile (64)
 constexpr int ROWS = 256;          // (position, head) rows per workgroup
-constexpr int RPW = ROWS / NW;     // rows per wave (one 32-row block)
-constexpr int RBW = RPW / 32;      // 32-row blocks per wave
-constexpr int NS = 4;              // LDS stages
+constexpr int NS = 5;              // LDS stages (160 KB)
 constexpr float TAU = 8.0f;
 
 __device__ const uint4 kZero16P = {0u, 0u, 0u, 0u};
@@ -102,8 +98,15 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char *p)
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
-template <int D, int GP>
+// NT_ = 512: 8 waves (two per SIMD), one 32-row block each; NT_ = 256: 4
+// waves (one per SIMD), two 32-row blocks each, so every K and V^T fragment
+// read from LDS feeds two matrix instructions.
+template <int D, int GP, int NT_>
 struct PCfg {
+    static constexpr int NT = NT_;
+    static constexpr int NW = NT / kWave;
+    static constexpr int RPW = ROWS / NW;         // rows per wave
+    static constexpr int RBW = RPW / 32;          // 32-row blocks per wave
     static constexpr int QB = ROWS / GP;          // positions per workgroup
     static constexpr int RB = D * 2;              // bytes per K/V row
     static constexpr int CPR = RB / 16;           // 16-byte chunks per row
@@ -125,10 +128,11 @@ struct PCfg {
     static_assert(NS * STAGE <= 160 * 1024, "LDS");
 };
 
-template <int D, int GP>
-__global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
+template <int D, int GP, int NT_>
+__global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
 {
-    using C = PCfg<D, GP>;
+    using C = PCfg<D, GP, NT_>;
+    constexpr int NW = C::NW, RPW = C::RPW, RBW = C::RBW;
     __shared__ __attribute__((aligned(1024))) char smem[NS * C::STAGE];
 
     const CacheView &cache = p.cache;
@@ -392,18 +396,24 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     // probabilities of tile t.  The instruction groups are interleaved
     // explicitly (one matrix instruction, then a few LDS reads and vector
     // instructions) so that one wave keeps both units busy.
-    for (int t = 0; t < NS - 1 && t < ntiles; ++t) issue(t);
+    // Tiles start PD iterations ahead.  Eight waves: the barrier is taken
+    // every second iteration, so the stage a load fills must have been free
+    // since the barrier before the previous iteration: PD = NS - 2.  Four
+    // waves take a barrier every tile: PD = NS - 1.
+    constexpr int PD = RBW == 1 ? NS - 2 : NS - 1;
+    for (int t = 0; t < PD && t < ntiles; ++t) issue(t);
     if (ntiles > 0) {
-        wait_tile(min(NS - 2, ntiles - 1));
+        wait_vm<0>();
         barrier();
     }
-    f32x16_t sA[RBW][2], sB[RBW][2];
-    uint4 pbuf[RBW][2][2];
-    if (ntiles > 0) scores(0, sA);
     // tiles below t_mask need no mask; the steady loop runs while a next
     // tile exists and the current one is unmasked
     const int t_mask = min(ntiles, mask_from / BN);
     const int t_steady = min(t_mask, ntiles - 1);
+    if constexpr (RBW == 1) {
+    f32x16_t sA[RBW][2], sB[RBW][2];
+    uint4 pbuf[RBW][2][2];
+    if (ntiles > 0) scores(0, sA);
     // One probability pair of tile t: k-step ksp (keys kb*32 + half*16 ..),
     // pair j of its four, into pw and the running sum.
     auto prob_pair = [&](int rb, const f32x16_t (&s)[RBW][2], float mu, int ksp, int j, uint32_t (&pw)[RBW][4][4],
@@ -417,13 +427,17 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     // The steady iteration, written as a sequence of small groups fenced from
     // each other: each group holds one matrix instruction, the LDS reads a
     // few matrix instructions ahead, and a share of the softmax of tile t.
-    auto steady = [&](int t, f32x16_t (&sc)[RBW][2], f32x16_t (&sn)[RBW][2]) __attribute__((always_inline)) {
-        wait_tile(min(1, ntiles - 2 - t));   // tile t+1 landed (t+2 may be in flight)
-        barrier();
-        // tile t+NS-1 goes into the stage of tile t-1; its loads are spread
-        // over the score steps (issued together, they would stall the wave
-        // on the full memory queue)
-        const int tn = t + NS - 1;
+    // bar: iteration t takes the barrier (every second one); before it, the
+    // tiles t+1 and t+2 (the latest issued) must have landed.
+    auto steady = [&](int t, f32x16_t (&sc)[RBW][2], f32x16_t (&sn)[RBW][2], bool bar) __attribute__((always_inline)) {
+        if (bar) {
+            wait_vm<0>();
+            barrier();
+        }
+        // tile t+PD goes into the stage of tile t-2 (free since the last
+        // barrier); its loads are spread over the score steps (issued
+        // together, they would stall the wave on the full memory queue)
+        const int tn = t + PD;
         const char *src[2 * C::LPW];
         plan(tn, src);
         __builtin_amdgcn_sched_barrier(0);
@@ -510,11 +524,11 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     };
     int t = 0;
     for (; t + 1 < t_steady; t += 2) {
-        steady(t, sA, sB);
-        steady(t + 1, sB, sA);
+        steady(t, sA, sB, true);
+        steady(t + 1, sB, sA, false);
     }
     if (t < t_steady) {
-        steady(t, sA, sB);
+        steady(t, sA, sB, true);
         ++t;
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) { sA[rb][0] = sB[rb][0]; sA[rb][1] = sB[rb][1]; }
@@ -522,9 +536,9 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     // the rest: tiles that need the mask, and the last tile
     for (; t < ntiles; ++t) {
         const bool has_next = t + 1 < ntiles;
-        if (has_next) wait_tile(min(1, ntiles - 2 - t));
+        wait_vm<0>();
         barrier();
-        if (t + NS - 1 < ntiles) issue(t + NS - 1);
+        if (t + PD < ntiles) issue(t + PD);
         if (has_next) scores(t + 1, sB);
         float mt[RBW];
         if (tile_max(t, sA, t >= t_mask, mt)) rescale(mt);
@@ -532,6 +546,184 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
         pv(t, pbuf);
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) { sA[rb][0] = sB[rb][0]; sA[rb][1] = sB[rb][1]; }
+    }
+    } else {
+        // ---- four waves of 64 rows: the pipeline runs in 32-key halves --------
+        // Half (t, kb) covers keys t*64 + kb*32 ...  Step (t, kb): the scores of
+        // the next half on the matrix cores (each K fragment feeds both row
+        // blocks) while the vector units take the maximum of (t, kb); the rare
+        // rescale; the V product of (t, kb) (each V^T fragment feeds both row
+        // blocks) while the probabilities are formed one k-step ahead.  The
+        // barrier and the start of tile t+NS-1 sit at step (t, 1), whose next
+        // half needs tile t+1.
+        f32x16_t hA[RBW], hB[RBW];
+        constexpr int HSTEPS = C::KS;        // k-steps of one half's scores
+        constexpr int HPSTEPS = 2 * C::DB;   // (16-key step, column block) pairs of one half's V product
+        auto scores_half = [&](int t, int kb, f32x16_t (&h)[RBW]) __attribute__((always_inline)) {
+            const char *kt = smem + (t % NS) * C::STAGE;
+            uint4 kf[KPF];
+#pragma unroll
+            for (int i = 0; i < KPF; ++i) kf[i] = k_frag(kt, 2 * i + kb);
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) h[rb][i] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < HSTEPS; ++ks) {
+                const uint4 a = kf[ks % KPF];
+                if (ks + KPF < HSTEPS) kf[ks % KPF] = k_frag(kt, 2 * (ks + KPF) + kb);
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb) h[rb] = mfma32x32x16(a, qf[rb][ks], h[rb]);
+            }
+        };
+        auto half_max = [&](int t, int kb, f32x16_t (&h)[RBW], bool masked, float (&mt)[RBW]) __attribute__((always_inline)) {
+            bool need = false;
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                if (masked) {
+                    const int lim = p.causal ? min(qpos[rb] + 1, kv_len) : kv_len;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = t * BN + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
+                        if (key >= lim) h[rb][i] = -INFINITY;
+                    }
+                }
+                float m = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) m = fmaxf(m, h[rb][i]);
+                mt[rb] = max_xor32(m) * p.scale_log2;
+                need |= mt[rb] > m_ref[rb] + TAU;
+            }
+            return __ballot(need) != 0;
+        };
+        auto prob_pair_h = [&](int rb, const f32x16_t (&h)[RBW], float mu, int half, int j, uint32_t (&pw)[RBW][2][4],
+                               float &ps) __attribute__((always_inline)) {
+            const float p0 = fast_exp2(fmaf(h[rb][half * 8 + 2 * j], p.scale_log2, -mu));
+            const float p1 = fast_exp2(fmaf(h[rb][half * 8 + 2 * j + 1], p.scale_log2, -mu));
+            pw[rb][half][j] = cvt_pk_bf16(p0, p1);
+            ps = dot2_bf16(pw[rb][half][j], 0x3F803F80u, ps);   // + both rounded probabilities
+        };
+        // O^T += V^T P^T of half (t, kb); the probabilities of the second
+        // 16-key step are formed during the matrix work of the first.
+        auto pv_half = [&](int t, int kb, const f32x16_t (&h)[RBW], bool fenced) __attribute__((always_inline)) {
+            const char *vt = smem + (t % NS) * C::STAGE + C::TILE;
+            uint4 vf[VPF];
+#pragma unroll
+            for (int i = 0; i < VPF; ++i) vf[i] = v_frag(vt, kb * HPSTEPS + i);
+            uint32_t pw[RBW][2][4];
+            float mu[RBW], ps[RBW][2];
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                mu[rb] = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
+                ps[rb][0] = 0.f;
+                ps[rb][1] = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) prob_pair_h(rb, h, mu[rb], 0, j, pw, ps[rb][j & 1]);
+            }
+            if (fenced) __builtin_amdgcn_sched_barrier(0);
+            constexpr int PPS = 4 / C::DB;   // probability pairs per row block and step
+#pragma unroll
+            for (int i = 0; i < HPSTEPS; ++i) {
+                const uint4 a = vf[i % VPF];
+                if (i + VPF < HPSTEPS) vf[i % VPF] = v_frag(vt, kb * HPSTEPS + i + VPF);
+                const int db = i % C::DB, half = i / C::DB;
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+                    acc[rb][db] = mfma32x32x16(a, make_uint4(pw[rb][half][0], pw[rb][half][1], pw[rb][half][2], pw[rb][half][3]),
+                                               acc[rb][db]);
+                if (half == 0) {
+#pragma unroll
+                    for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                        for (int q = 0; q < PPS; ++q)
+                            prob_pair_h(rb, h, mu[rb], 1, db * PPS + q, pw, ps[rb][(db * PPS + q) & 1]);
+                }
+                if (fenced) __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) l_run[rb] += ps[rb][0] + ps[rb][1];
+        };
+        // the fenced steady step (t, kb) with the scores of the next half into hn
+        auto steady_half = [&](int t, int kb, f32x16_t (&hc)[RBW], f32x16_t (&hn)[RBW]) __attribute__((always_inline)) {
+            const int tn = t + kb, kbn = 1 - kb;
+            const int tl = t + PD;   // tile started at step (t, 1)
+            const char *src[2 * C::LPW];
+            if (kb == 1) {
+                wait_tile(min(2, ntiles - 2 - t));   // tile t+1 landed (t+2, t+3 may be in flight)
+                barrier();
+                plan(tl, src);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const char *kt = smem + (tn % NS) * C::STAGE;
+            uint4 kf[KPF];
+#pragma unroll
+            for (int i = 0; i < KPF; ++i) kf[i] = k_frag(kt, 2 * i + kbn);
+            float m[RBW];
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                m[rb] = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) hn[rb][i] = 0.f;
+            }
+#pragma unroll
+            for (int ks = 0; ks < HSTEPS; ++ks) {
+                const uint4 a = kf[ks % KPF];
+                if (ks + KPF < HSTEPS) kf[ks % KPF] = k_frag(kt, 2 * (ks + KPF) + kbn);
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb) hn[rb] = mfma32x32x16(a, qf[rb][ks], hn[rb]);
+                // 16 scores per row block over HSTEPS steps
+                constexpr int PER = 16 / HSTEPS;
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) m[rb] = fmaxf(m[rb], hc[rb][ks * PER + e]);
+                if (kb == 1) {
+                    constexpr int EVERY = HSTEPS / (2 * C::LPW) > 0 ? HSTEPS / (2 * C::LPW) : 1;
+                    constexpr int PERSTEP = (2 * C::LPW + HSTEPS - 1) / HSTEPS;
+                    if (ks % EVERY == 0) {
+#pragma unroll
+                        for (int q = 0; q < PERSTEP; ++q) {
+                            const int i = (ks / EVERY) * PERSTEP + q;
+                            if (i < 2 * C::LPW) dma16(src[i], lds_at(tl, i));
+                        }
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            float mt[RBW];
+            bool need = false;
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                mt[rb] = max_xor32(m[rb]) * p.scale_log2;
+                need |= mt[rb] > m_ref[rb] + TAU;
+            }
+            if (__builtin_expect(__ballot(need) != 0, 0)) {
+                asm volatile("" ::: "memory");
+                rescale(mt);
+            }
+            pv_half(t, kb, hc, true);
+        };
+        if (ntiles > 0) scores_half(0, 0, hA);
+        int t = 0;
+        for (; t < t_steady; ++t) {
+            steady_half(t, 0, hA, hB);
+            steady_half(t, 1, hB, hA);
+        }
+        // the rest: tiles that need the mask, and the last tile
+        for (; t < ntiles; ++t) {
+            const bool masked = t >= t_mask;
+            float mt[RBW];
+            scores_half(t, 1, hB);
+            if (half_max(t, 0, hA, masked, mt)) rescale(mt);
+            pv_half(t, 0, hA, false);
+            const bool has_next = t + 1 < ntiles;
+            if (has_next) wait_tile(min(2, ntiles - 2 - t));
+            barrier();
+            if (t + PD < ntiles) issue(t + PD);
+            if (has_next) scores_half(t + 1, 0, hA);
+            if (half_max(t, 1, hB, masked, mt)) rescale(mt);
+            pv_half(t, 1, hB, false);
+        }
     }
 
     // ---- normalise and store: lane owns 16 columns per 32-column block ----------
@@ -554,7 +746,7 @@ __global__ __launch_bounds__(NT) void prefill_mfma_kernel(PrefillParams p)
     }
 }
 
-template <int D>
+template <int D, int NT_>
 hipError_t launch_d(const PrefillParams &p, int gp, hipStream_t s)
 {
     const int64_t qb_pos = ROWS / gp;
@@ -562,17 +754,19 @@ hipError_t launch_d(const PrefillParams &p, int gp, hipStream_t s)
     if (nqb * p.cache.K * p.B > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(nqb * p.cache.K * p.B));
     switch (gp) {
-    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, 1>), grid, dim3(NT), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, 2>), grid, dim3(NT), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, 4>), grid, dim3(NT), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((prefill_mfma_kernel<D, 8>), grid, dim3(NT), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((prefill_mfma_kernel<D, 16>), grid, dim3(NT), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32>), grid, dim3(NT), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((prefill_mfma_kernel<D, 64>), grid, dim3(NT), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, 1, NT_>), grid, dim3(NT_), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, 2, NT_>), grid, dim3(NT_), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, 4, NT_>), grid, dim3(NT_), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((prefill_mfma_kernel<D, 8, NT_>), grid, dim3(NT_), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((prefill_mfma_kernel<D, 16, NT_>), grid, dim3(NT_), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32, NT_>), grid, dim3(NT_), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((prefill_mfma_kernel<D, 64, NT_>), grid, dim3(NT_), 0, s, p); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
+
+constexpr int kPrefillThreads = 512;   // workgroup shape of the prefill kernel
 
 }  // namespace
 
@@ -580,8 +774,8 @@ hipError_t launch_prefill_mfma(const PrefillParams &p, hipStream_t stream)
 {
     const int gp = pow2_at_least(p.G);
     if (p.cache.elem_bytes != 2) return hipErrorInvalidValue;
-    if (p.cache.d == 128) return launch_d<128>(p, gp, stream);
-    if (p.cache.d == 64) return launch_d<64>(p, gp, stream);
+    if (p.cache.d == 128) return launch_d<128, kPrefillThreads>(p, gp, stream);
+    if (p.cache.d == 64) return launch_d<64, kPrefillThreads>(p, gp, stream);
     return hipErrorInvalidValue;
 }
 
