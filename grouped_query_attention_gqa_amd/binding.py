@@ -26,6 +26,7 @@ GQA_F32, GQA_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
     "gqa_abi_version", "gqa_status_string", "gqa_cache_elems_per_token",
     "gqa_kv_append", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_prefill",
+    "gqa_decode_window", "gqa_prefill_window",
 )
 
 
@@ -81,6 +82,10 @@ def load_library():
         lib.gqa_decode.argtypes = [vp, cp, vp, i32, i32, i32, ctypes.c_float, vp, vp, sz, vp]
         lib.gqa_prefill.restype = i32
         lib.gqa_prefill.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp]
+        lib.gqa_decode_window.restype = i32
+        lib.gqa_decode_window.argtypes = [vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
+        lib.gqa_prefill_window.restype = i32
+        lib.gqa_prefill_window.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
         if lib.gqa_abi_version() != 1:
             raise RuntimeError("libgqa.so ABI version mismatch")
         _lib = lib
@@ -210,8 +215,9 @@ def gqa_kv_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, star
 
 def gqa_decode(q: torch.Tensor, cache: KVCache, ctx_lens: torch.Tensor, max_ctx: int,
                out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
-               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """One decode step: q [B,1,H,d] against the first ctx_lens[b] cached tokens."""
+               workspace: Optional[torch.Tensor] = None, stream=None, window: int = 0) -> torch.Tensor:
+    """One decode step: q [B,1,H,d] against the first ctx_lens[b] cached tokens
+    (with window > 0, only against the last `window` of them)."""
     _need(q, "q", dtype=cache.dtype, dim=4)
     _need(ctx_lens, "ctx_lens", dtype=torch.int32, dim=1)
     B, one, H, d = q.shape
@@ -229,16 +235,21 @@ def gqa_decode(q: torch.Tensor, cache: KVCache, ctx_lens: torch.Tensor, max_ctx:
     if workspace is None and nbytes > 0:
         workspace = _default_workspace(q.device, hs.value or 0, nbytes)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.gqa_decode(_ptr(q), cache.struct, _ptr(ctx_lens), int(max_ctx), B, H, ctypes.c_float(scale),
-                        _ptr(out), _ptr(workspace), ws_bytes, hs)
+    if window > 0:
+        st = lib.gqa_decode_window(_ptr(q), cache.struct, _ptr(ctx_lens), int(max_ctx), B, H, ctypes.c_float(scale),
+                                   int(window), _ptr(out), _ptr(workspace), ws_bytes, hs)
+    else:
+        st = lib.gqa_decode(_ptr(q), cache.struct, _ptr(ctx_lens), int(max_ctx), B, H, ctypes.c_float(scale),
+                            _ptr(out), _ptr(workspace), ws_bytes, hs)
     _check(st, "gqa_decode")
     return out
 
 
 def gqa_prefill(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: KVCache,
                 start_pos: torch.Tensor, causal: bool = True, out: Optional[torch.Tensor] = None,
-                scale: Optional[float] = None, stream=None) -> torch.Tensor:
-    """Append k_new/v_new [B,s,K,d] and attend q [B,s,H,d] (causal by default)."""
+                scale: Optional[float] = None, stream=None, window: int = 0) -> torch.Tensor:
+    """Append k_new/v_new [B,s,K,d] and attend q [B,s,H,d] (causal by default;
+    with window > 0 each row sees only its `window` most recent positions)."""
     _need(q, "q", dtype=cache.dtype, dim=4)
     _need(k_new, "k_new", dtype=cache.dtype, dim=4)
     _need(v_new, "v_new", dtype=cache.dtype, dim=4)
@@ -252,7 +263,12 @@ def gqa_prefill(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache
     if out.shape != q.shape:
         raise ValueError("out must have the shape of q")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    st = load_library().gqa_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), cache.struct, _ptr(start_pos), B, s, H,
-                                    ctypes.c_float(scale), int(bool(causal)), _ptr(out), _stream(stream))
+    if window > 0:
+        st = load_library().gqa_prefill_window(_ptr(q), _ptr(k_new), _ptr(v_new), cache.struct, _ptr(start_pos), B,
+                                               s, H, ctypes.c_float(scale), int(bool(causal)), int(window), _ptr(out),
+                                               _stream(stream))
+    else:
+        st = load_library().gqa_prefill(_ptr(q), _ptr(k_new), _ptr(v_new), cache.struct, _ptr(start_pos), B, s, H,
+                                        ctypes.c_float(scale), int(bool(causal)), _ptr(out), _stream(stream))
     _check(st, "gqa_prefill")
     return out

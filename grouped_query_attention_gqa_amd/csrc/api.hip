@@ -211,6 +211,14 @@ gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *c
                       int32_t max_ctx, int32_t B, int32_t num_heads, float scale, void *out,
                       void *workspace, size_t workspace_bytes, void *stream)
 {
+    return gqa_decode_window(q, cache, ctx_lens, max_ctx, B, num_heads, scale, 0, out, workspace, workspace_bytes,
+                             stream);
+}
+
+gqa_status gqa_decode_window(const void *q, const gqa_kv_cache *cache, const int32_t *ctx_lens,
+                             int32_t max_ctx, int32_t B, int32_t num_heads, float scale, int32_t window,
+                             void *out, void *workspace, size_t workspace_bytes, void *stream)
+{
     CacheView v;
     gqa_status st = make_view(cache, &v);
     if (st != GQA_OK) return st;
@@ -249,6 +257,7 @@ gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *c
     p.prefill = 0;
     p.causal = 0;
     p.whole_items = 0;
+    p.window = window > 0 ? window : 0;
     p.num_wgs = kStreamWGs;
     p.scale_log2 = scale * 1.4426950408889634f;
     return launch_status(launch_row_attention(p, pow2_at_least(p.G), static_cast<hipStream_t>(stream)),
@@ -258,6 +267,14 @@ gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *c
 gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
                        const gqa_kv_cache *cache, const int32_t *start_pos, int32_t B, int32_t s,
                        int32_t num_heads, float scale, int32_t causal, void *out, void *stream)
+{
+    return gqa_prefill_window(q, k_new, v_new, cache, start_pos, B, s, num_heads, scale, causal, 0, out, stream);
+}
+
+gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_new,
+                              const gqa_kv_cache *cache, const int32_t *start_pos, int32_t B, int32_t s,
+                              int32_t num_heads, float scale, int32_t causal, int32_t window, void *out,
+                              void *stream)
 {
     CacheView v;
     gqa_status st = make_view(cache, &v);
@@ -300,6 +317,7 @@ gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
         pp.H = num_heads;
         pp.G = num_heads / v.K;
         pp.causal = causal != 0;
+        pp.window = window > 0 ? window : 0;
         pp.scale_log2 = scale_log2;
         return launch_status(launch_prefill_mfma(pp, hs), "prefill");
     }
@@ -316,6 +334,7 @@ gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
     p.prefill = 1;
     p.causal = causal != 0;
     p.whole_items = 1;   // no workspace here: every item stays in one workgroup
+    p.window = window > 0 ? window : 0;
     p.num_wgs = kStreamWGs;
     p.scale_log2 = scale_log2;
     return launch_status(launch_row_attention(p, pow2_at_least(p.G), hs), "prefill (fp32)");

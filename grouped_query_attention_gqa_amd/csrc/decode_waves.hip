@@ -99,6 +99,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     __shared__ float lds_ml[NW][GP][2];
     __shared__ int32_t lds_prefix[kStreamRows + 1];
     __shared__ int32_t lds_nvis[kStreamRows];
+    __shared__ int32_t lds_first[kStreamRows];
     __shared__ int lds_waves[NW];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     const int G = p.G, H = p.H;
 
     // ---- the flat tile list and this workgroup's slice ---------------------
-    build_tables<NT>(p, C::TT, lds_prefix, lds_nvis, lds_waves);
+    build_tables<NT>(p, C::TT, lds_prefix, lds_nvis, lds_first, lds_waves);
     if (blockIdx.x == 0 && p.prefix != nullptr)   // the merge kernel reads it from the workspace
         for (int r = tid; r <= p.rows; r += NT) p.prefix[r] = lds_prefix[r];
     const int T = lds_prefix[p.rows];
@@ -133,19 +134,22 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     struct Seg {
         int64_t row_g;    // query row (sequence) of the item
         int b, g;         // sequence and KV group
-        int n_vis;        // keys of the item
+        int n_vis;        // end of the item's visible keys
+        int lo, jlo;      // first visible key; its tile (the item's tile 0)
         int j_first;      // tile of the item at tau
         int tau, end;     // flat tile range
         int item0, tiles; // the item's flat range
         int n_w;          // tiles of this wave: j_first + wave + NW * i, i < n_w
     };
     auto make_seg = [&](int at) {
-        const Cursor c = cursor_at(lds_prefix, lds_nvis, p.rows, at, C::TT);
+        const Cursor c = cursor_at(lds_prefix, lds_nvis, lds_first, p.rows, at, C::TT);
         Seg sg;
         sg.row_g = p.row0 + c.row;
         sg.b = (int)(sg.row_g / p.Sq);
         sg.g = c.g;
         sg.n_vis = c.n_vis;
+        sg.lo = c.lo;
+        sg.jlo = c.jlo;
         sg.j_first = c.j;
         sg.tau = at;
         sg.end = min(tau1, c.item0 + c.tiles);
@@ -160,17 +164,22 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     // one 16-key group, whose cache rows are consecutive (contiguous cache, or
     // one block of >= 16 tokens): a wave-uniform row base per group plus a
     // 32-bit lane offset.
+    // A sliding window can leave the first keys of the item's first tile
+    // outside: those keys are masked, and a 16-key group wholly outside is
+    // not read at all (its block may have been recycled).
     struct TileRows {
         int64_t base[C::NGR];   // cache row of key 16 gi of the tile, -1: none
-        int nvalid;             // keys of the tile (<= 0: none)
+        int nvalid;             // keys of the tile below the end (<= 0: none)
+        int first;              // first visible key of the tile
     };
-    auto tile_rows = [&](int lb, int lg, int l_nvis, int j) {
+    auto tile_rows = [&](int lb, int lg, int l_lo, int l_nvis, int j) {
         TileRows t;
-        const int key0 = j * C::TT;
+        const int key0 = j * C::TT;   // j: tile of the row
         t.nvalid = min(C::TT, l_nvis - key0);
+        t.first = max(0, l_lo - key0);
 #pragma unroll
         for (int gi = 0; gi < C::NGR; ++gi)
-            t.base[gi] = 16 * gi < t.nvalid ? cache_row_wave(cache, lb, lg, key0 + 16 * gi) : -1;
+            t.base[gi] = 16 * gi < t.nvalid && 16 * gi + 16 > t.first ? cache_row_wave(cache, lb, lg, key0 + 16 * gi) : -1;
         return t;
     };
     const uint32_t k_off = (uint32_t)(krow * C::RB + kc * 16);
@@ -212,6 +221,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
 #pragma unroll
         for (int gi = 0; gi < C::NGR; ++gi) t.base[gi] = -1;
         t.nvalid = 0;
+        t.first = 0;
         return t;
     };
     auto stream_from = [&](int at, TileRows &t1, TileRows &t2) {
@@ -221,7 +231,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         while (at < tau1 && found < C::KD) {
             const Seg sg = make_seg(at);
             for (int k = 0; k < sg.n_w && found < C::KD; ++k, ++found) {
-                const TileRows t = tile_rows(sg.b, sg.g, sg.n_vis, sg.j_first + wave + NW * k);
+                const TileRows t = tile_rows(sg.b, sg.g, sg.lo, sg.n_vis, sg.jlo + sg.j_first + wave + NW * k);
                 if (found == 0) t1 = t;
                 else t2 = t;
             }
@@ -294,7 +304,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             const TileRows rows = r1;   // tile i
             // rows of the tile KD steps ahead in the stream
             const int ia = i + C::KD;
-            const TileRows ra = ia < n_w ? tile_rows(cur.b, cur.g, cur.n_vis, cur.j_first + wave + NW * ia)
+            const TileRows ra = ia < n_w ? tile_rows(cur.b, cur.g, cur.lo, cur.n_vis, cur.jlo + cur.j_first + wave + NW * ia)
                                          : (ia == n_w ? after1 : after2);
             // K(i) -> this wave's LDS buffer (padded rows); start K(i + KD) in its place
             auto k_step = [&](uint4 (&kx)[C::NL]) {
@@ -329,7 +339,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
                         a1[h] = dot2_bf16(qv.w, kv.w, a1[h]);
                     }
                 }
-                const bool valid = s_lane && st < rows.nvalid;
+                const bool valid = s_lane && st < rows.nvalid && st >= rows.first;
 #pragma unroll
                 for (int h = 0; h < C::HPL; ++h) sc[h] = valid ? (a0[h] + a1[h]) * p.scale_log2 : -INFINITY;
             }

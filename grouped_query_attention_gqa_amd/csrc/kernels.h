@@ -56,6 +56,7 @@ struct RowAttnParams {
     int32_t prefill;            // 0: decode rows; 1: prefill rows
     int32_t causal;
     int32_t whole_items;        // 1: slices snap to item starts (no partial pieces, no workspace)
+    int32_t window;             // > 0: a row sees only its `window` most recent positions
     int32_t num_wgs;            // W
     float scale_log2;           // softmax scale * log2(e)
 };
@@ -71,6 +72,7 @@ struct PrefillParams {
     int32_t H;
     int32_t G;
     int32_t causal;
+    int32_t window;             // > 0: a row sees only its `window` most recent positions
     float scale_log2;
 };
 

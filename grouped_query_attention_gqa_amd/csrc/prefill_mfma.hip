@@ -98,9 +98,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const char *p)
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) { return pack_bf16x2(lo, hi); }
 
-// NT_ = 512: 8 waves (two per SIMD), one 32-row block each; NT_ = 256: 4
-// waves (one per SIMD), two 32-row blocks each, so every K and V^T fragment
-// read from LDS feeds two matrix instructions.
+// NT_ = 512: 8 waves (two per SIMD), one 32-row block each.
 template <int D, int GP, int NT_>
 struct PCfg {
     static constexpr int NT = NT_;
@@ -157,9 +155,17 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
     const int ntiles = kv_end > 0 ? (kv_end + BN - 1) / BN : 0;
     // keys at or past this one may be masked for some row of the workgroup
     const int mask_from = p.causal ? (int)min((int64_t)start + q0 + 1, (int64_t)kv_len) : kv_len;
+    // Sliding window of W positions (inference-optimisation page §6.4.1): row
+    // i sees keys from qpos + 1 - W on.  The workgroup's first row sets the
+    // first tile; tiles below the last row's first key need the mask.
+    const int win = p.window;
+    const int kv_begin = win > 0 ? (int)min(max((int64_t)0, (int64_t)start + q0 + 1 - win), (int64_t)kv_len) : 0;
+    const int t_first = kv_begin / BN;
+    const int lo_last = win > 0 ? (int)min(max((int64_t)0, (int64_t)start + q0 + C::QB - win), (int64_t)kv_len) : 0;
+    const int t_lo_end = (lo_last + BN - 1) / BN;   // tiles below this one need the window mask
 
     // ---- this lane's two query rows and their Q^T fragments -------------------
-    int row_r[RBW], row_i[RBW], qpos[RBW];
+    int row_r[RBW], row_i[RBW], qpos[RBW], row_lo[RBW];
     bool row_ok[RBW];
     uint4 qf[RBW][C::KS];
 #pragma unroll
@@ -169,6 +175,7 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
         row_i[rb] = q0 + rho / GP;
         row_ok[rb] = row_r[rb] < G && row_i[rb] < p.s;
         qpos[rb] = start + row_i[rb];
+        row_lo[rb] = win > 0 ? max(0, qpos[rb] + 1 - win) : 0;
         const uint4 *qrow = reinterpret_cast<const uint4 *>(
             p.q + ((((int64_t)b * p.s + (row_ok[rb] ? row_i[rb] : 0)) * H + (int64_t)g * G +
                     (row_ok[rb] ? row_r[rb] : 0)) * D) * 2);
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
     // read a zero constant.
     auto plan = [&](int t, const char *(&src)[2 * C::LPW]) __attribute__((always_inline)) {
         const int j0 = t * BN;
-        if (t < ntiles && contiguous && j0 + BN <= kv_len) {
+        if (t < ntiles && contiguous && j0 >= kv_begin && j0 + BN <= kv_len) {
             // every row of the tile is in the cache: a uniform base and lane offsets
 #pragma unroll
             for (int k = 0; k < C::LPW; ++k) {
@@ -213,10 +220,11 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
             const int r = blk * C::RPK + lane / C::CPR;   // tile row of this lane
             const int slot = lane % C::CPR;
             const char *srck = reinterpret_cast<const char *>(&kZero16P), *srcv = srck;
-            if (t < ntiles && j0 + blk * C::RPK < kv_len) {
+            // rows below kv_begin are outside every row's window: not read
+            if (t < ntiles && j0 + blk * C::RPK < kv_len && j0 + blk * C::RPK + C::RPK > kv_begin) {
                 // the block's rows lie in one 16-row group, hence in one cache block
                 const int64_t row0 = cache_row_wave(cache, b, g, j0 + blk * C::RPK);
-                if (row0 >= 0 && j0 + r < kv_len) {
+                if (row0 >= 0 && j0 + r < kv_len && j0 + r >= kv_begin) {
                     const int64_t row = row0 + (r - blk * C::RPK);
                     srck = cache.k + row * C::RB + (slot ^ C::ksw(r)) * 16;
                     srcv = cache.v + row * C::RB + (slot ^ C::vsw(r)) * 16;
@@ -302,7 +310,7 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = j0 + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-                        if (key >= lim) s[rb][kb][i] = -INFINITY;
+                        if (key >= lim || key < row_lo[rb]) s[rb][kb][i] = -INFINITY;
                     }
             }
             float m = -INFINITY;
@@ -396,24 +404,22 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
     // probabilities of tile t.  The instruction groups are interleaved
     // explicitly (one matrix instruction, then a few LDS reads and vector
     // instructions) so that one wave keeps both units busy.
-    // Tiles start PD iterations ahead.  Eight waves: the barrier is taken
-    // every second iteration, so the stage a load fills must have been free
-    // since the barrier before the previous iteration: PD = NS - 2.  Four
-    // waves take a barrier every tile: PD = NS - 1.
-    constexpr int PD = RBW == 1 ? NS - 2 : NS - 1;
-    for (int t = 0; t < PD && t < ntiles; ++t) issue(t);
-    if (ntiles > 0) {
+    // Tiles start PD iterations ahead.  The barrier is taken every second
+    // iteration, so the stage a load fills must have been free since the
+    // barrier before the previous iteration: PD = NS - 2.
+    constexpr int PD = NS - 2;
+    for (int t = t_first; t < t_first + PD && t < ntiles; ++t) issue(t);
+    if (ntiles > t_first) {
         wait_vm<0>();
         barrier();
     }
-    // tiles below t_mask need no mask; the steady loop runs while a next
-    // tile exists and the current one is unmasked
+    // tiles in [t_lo_end, t_mask) need no mask; the steady loop runs over
+    // them while a next tile exists
     const int t_mask = min(ntiles, mask_from / BN);
     const int t_steady = min(t_mask, ntiles - 1);
-    if constexpr (RBW == 1) {
     f32x16_t sA[RBW][2], sB[RBW][2];
     uint4 pbuf[RBW][2][2];
-    if (ntiles > 0) scores(0, sA);
+    if (ntiles > t_first) scores(t_first, sA);
     // One probability pair of tile t: k-step ksp (keys kb*32 + half*16 ..),
     // pair j of its four, into pw and the running sum.
     auto prob_pair = [&](int rb, const f32x16_t (&s)[RBW][2], float mu, int ksp, int j, uint32_t (&pw)[RBW][4][4],
@@ -522,7 +528,24 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) l_run[rb] += ps[rb][0] + ps[rb][1];
     };
-    int t = 0;
+    // One iteration with a barrier of its own and the mask where the tile
+    // needs it: the tiles below the window's edge, the tiles at the causal
+    // diagonal or the end of the keys, and the last tile.
+    auto general = [&](int t) __attribute__((always_inline)) {
+        const bool has_next = t + 1 < ntiles;
+        wait_vm<0>();
+        barrier();
+        if (t + PD < ntiles) issue(t + PD);
+        if (has_next) scores(t + 1, sB);
+        float mt[RBW];
+        if (tile_max(t, sA, t >= t_mask || t < t_lo_end, mt)) rescale(mt);
+        probs(sA, pbuf);
+        pv(t, pbuf);
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) { sA[rb][0] = sB[rb][0]; sA[rb][1] = sB[rb][1]; }
+    };
+    int t = t_first;
+    for (; t < t_lo_end && t < ntiles; ++t) general(t);
     for (; t + 1 < t_steady; t += 2) {
         steady(t, sA, sB, true);
         steady(t + 1, sB, sA, false);
@@ -534,197 +557,7 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
         for (int rb = 0; rb < RBW; ++rb) { sA[rb][0] = sB[rb][0]; sA[rb][1] = sB[rb][1]; }
     }
     // the rest: tiles that need the mask, and the last tile
-    for (; t < ntiles; ++t) {
-        const bool has_next = t + 1 < ntiles;
-        wait_vm<0>();
-        barrier();
-        if (t + PD < ntiles) issue(t + PD);
-        if (has_next) scores(t + 1, sB);
-        float mt[RBW];
-        if (tile_max(t, sA, t >= t_mask, mt)) rescale(mt);
-        probs(sA, pbuf);
-        pv(t, pbuf);
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) { sA[rb][0] = sB[rb][0]; sA[rb][1] = sB[rb][1]; }
-    }
-    } else {
-        // ---- four waves of 64 rows: the pipeline runs in 32-key halves --------
-        // Half (t, kb) covers keys t*64 + kb*32 ...  Step (t, kb): the scores of
-        // the next half on the matrix cores (each K fragment feeds both row
-        // blocks) while the vector units take the maximum of (t, kb); the rare
-        // rescale; the V product of (t, kb) (each V^T fragment feeds both row
-        // blocks) while the probabilities are formed one k-step ahead.  The
-        // barrier and the start of tile t+NS-1 sit at step (t, 1), whose next
-        // half needs tile t+1.
-        f32x16_t hA[RBW], hB[RBW];
-        constexpr int HSTEPS = C::KS;        // k-steps of one half's scores
-        constexpr int HPSTEPS = 2 * C::DB;   // (16-key step, column block) pairs of one half's V product
-        auto scores_half = [&](int t, int kb, f32x16_t (&h)[RBW]) __attribute__((always_inline)) {
-            const char *kt = smem + (t % NS) * C::STAGE;
-            uint4 kf[KPF];
-#pragma unroll
-            for (int i = 0; i < KPF; ++i) kf[i] = k_frag(kt, 2 * i + kb);
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) h[rb][i] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < HSTEPS; ++ks) {
-                const uint4 a = kf[ks % KPF];
-                if (ks + KPF < HSTEPS) kf[ks % KPF] = k_frag(kt, 2 * (ks + KPF) + kb);
-#pragma unroll
-                for (int rb = 0; rb < RBW; ++rb) h[rb] = mfma32x32x16(a, qf[rb][ks], h[rb]);
-            }
-        };
-        auto half_max = [&](int t, int kb, f32x16_t (&h)[RBW], bool masked, float (&mt)[RBW]) __attribute__((always_inline)) {
-            bool need = false;
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-                if (masked) {
-                    const int lim = p.causal ? min(qpos[rb] + 1, kv_len) : kv_len;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const int key = t * BN + kb * 32 + (i >> 2) * 8 + hh * 4 + (i & 3);
-                        if (key >= lim) h[rb][i] = -INFINITY;
-                    }
-                }
-                float m = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) m = fmaxf(m, h[rb][i]);
-                mt[rb] = max_xor32(m) * p.scale_log2;
-                need |= mt[rb] > m_ref[rb] + TAU;
-            }
-            return __ballot(need) != 0;
-        };
-        auto prob_pair_h = [&](int rb, const f32x16_t (&h)[RBW], float mu, int half, int j, uint32_t (&pw)[RBW][2][4],
-                               float &ps) __attribute__((always_inline)) {
-            const float p0 = fast_exp2(fmaf(h[rb][half * 8 + 2 * j], p.scale_log2, -mu));
-            const float p1 = fast_exp2(fmaf(h[rb][half * 8 + 2 * j + 1], p.scale_log2, -mu));
-            pw[rb][half][j] = cvt_pk_bf16(p0, p1);
-            ps = dot2_bf16(pw[rb][half][j], 0x3F803F80u, ps);   // + both rounded probabilities
-        };
-        // O^T += V^T P^T of half (t, kb); the probabilities of the second
-        // 16-key step are formed during the matrix work of the first.
-        auto pv_half = [&](int t, int kb, const f32x16_t (&h)[RBW], bool fenced) __attribute__((always_inline)) {
-            const char *vt = smem + (t % NS) * C::STAGE + C::TILE;
-            uint4 vf[VPF];
-#pragma unroll
-            for (int i = 0; i < VPF; ++i) vf[i] = v_frag(vt, kb * HPSTEPS + i);
-            uint32_t pw[RBW][2][4];
-            float mu[RBW], ps[RBW][2];
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-                mu[rb] = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
-                ps[rb][0] = 0.f;
-                ps[rb][1] = 0.f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) prob_pair_h(rb, h, mu[rb], 0, j, pw, ps[rb][j & 1]);
-            }
-            if (fenced) __builtin_amdgcn_sched_barrier(0);
-            constexpr int PPS = 4 / C::DB;   // probability pairs per row block and step
-#pragma unroll
-            for (int i = 0; i < HPSTEPS; ++i) {
-                const uint4 a = vf[i % VPF];
-                if (i + VPF < HPSTEPS) vf[i % VPF] = v_frag(vt, kb * HPSTEPS + i + VPF);
-                const int db = i % C::DB, half = i / C::DB;
-#pragma unroll
-                for (int rb = 0; rb < RBW; ++rb)
-                    acc[rb][db] = mfma32x32x16(a, make_uint4(pw[rb][half][0], pw[rb][half][1], pw[rb][half][2], pw[rb][half][3]),
-                                               acc[rb][db]);
-                if (half == 0) {
-#pragma unroll
-                    for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-                        for (int q = 0; q < PPS; ++q)
-                            prob_pair_h(rb, h, mu[rb], 1, db * PPS + q, pw, ps[rb][(db * PPS + q) & 1]);
-                }
-                if (fenced) __builtin_amdgcn_sched_barrier(0);
-            }
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) l_run[rb] += ps[rb][0] + ps[rb][1];
-        };
-        // the fenced steady step (t, kb) with the scores of the next half into hn
-        auto steady_half = [&](int t, int kb, f32x16_t (&hc)[RBW], f32x16_t (&hn)[RBW]) __attribute__((always_inline)) {
-            const int tn = t + kb, kbn = 1 - kb;
-            const int tl = t + PD;   // tile started at step (t, 1)
-            const char *src[2 * C::LPW];
-            if (kb == 1) {
-                wait_tile(min(2, ntiles - 2 - t));   // tile t+1 landed (t+2, t+3 may be in flight)
-                barrier();
-                plan(tl, src);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            const char *kt = smem + (tn % NS) * C::STAGE;
-            uint4 kf[KPF];
-#pragma unroll
-            for (int i = 0; i < KPF; ++i) kf[i] = k_frag(kt, 2 * i + kbn);
-            float m[RBW];
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-                m[rb] = -INFINITY;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) hn[rb][i] = 0.f;
-            }
-#pragma unroll
-            for (int ks = 0; ks < HSTEPS; ++ks) {
-                const uint4 a = kf[ks % KPF];
-                if (ks + KPF < HSTEPS) kf[ks % KPF] = k_frag(kt, 2 * (ks + KPF) + kbn);
-#pragma unroll
-                for (int rb = 0; rb < RBW; ++rb) hn[rb] = mfma32x32x16(a, qf[rb][ks], hn[rb]);
-                // 16 scores per row block over HSTEPS steps
-                constexpr int PER = 16 / HSTEPS;
-#pragma unroll
-                for (int rb = 0; rb < RBW; ++rb)
-#pragma unroll
-                    for (int e = 0; e < PER; ++e) m[rb] = fmaxf(m[rb], hc[rb][ks * PER + e]);
-                if (kb == 1) {
-                    constexpr int EVERY = HSTEPS / (2 * C::LPW) > 0 ? HSTEPS / (2 * C::LPW) : 1;
-                    constexpr int PERSTEP = (2 * C::LPW + HSTEPS - 1) / HSTEPS;
-                    if (ks % EVERY == 0) {
-#pragma unroll
-                        for (int q = 0; q < PERSTEP; ++q) {
-                            const int i = (ks / EVERY) * PERSTEP + q;
-                            if (i < 2 * C::LPW) dma16(src[i], lds_at(tl, i));
-                        }
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            float mt[RBW];
-            bool need = false;
-#pragma unroll
-            for (int rb = 0; rb < RBW; ++rb) {
-                mt[rb] = max_xor32(m[rb]) * p.scale_log2;
-                need |= mt[rb] > m_ref[rb] + TAU;
-            }
-            if (__builtin_expect(__ballot(need) != 0, 0)) {
-                asm volatile("" ::: "memory");
-                rescale(mt);
-            }
-            pv_half(t, kb, hc, true);
-        };
-        if (ntiles > 0) scores_half(0, 0, hA);
-        int t = 0;
-        for (; t < t_steady; ++t) {
-            steady_half(t, 0, hA, hB);
-            steady_half(t, 1, hB, hA);
-        }
-        // the rest: tiles that need the mask, and the last tile
-        for (; t < ntiles; ++t) {
-            const bool masked = t >= t_mask;
-            float mt[RBW];
-            scores_half(t, 1, hB);
-            if (half_max(t, 0, hA, masked, mt)) rescale(mt);
-            pv_half(t, 0, hA, false);
-            const bool has_next = t + 1 < ntiles;
-            if (has_next) wait_tile(min(2, ntiles - 2 - t));
-            barrier();
-            if (t + PD < ntiles) issue(t + PD);
-            if (has_next) scores_half(t + 1, 0, hA);
-            if (half_max(t, 1, hB, masked, mt)) rescale(mt);
-            pv_half(t, 1, hB, false);
-        }
-    }
+    for (; t < ntiles; ++t) general(t);
 
     // ---- normalise and store: lane owns 16 columns per 32-column block ----------
 #pragma unroll

@@ -174,6 +174,7 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
     __shared__ float lds_alpha[2][GP], lds_m[2][GP], lds_l[2][GP];
     __shared__ int32_t lds_prefix[kStreamRows + 1];
     __shared__ int32_t lds_nvis[kStreamRows];
+    __shared__ int32_t lds_first[kStreamRows];
     __shared__ int lds_waves[NW];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
     const int G = p.G, H = p.H;
 
     // ---- the flat tile list and this workgroup's slice ---------------------
-    build_tables<NT>(p, C::TT, lds_prefix, lds_nvis, lds_waves);
+    build_tables<NT>(p, C::TT, lds_prefix, lds_nvis, lds_first, lds_waves);
     if (blockIdx.x == 0 && p.prefix != nullptr)   // the merge kernel reads it from the workspace
         for (int r = tid; r <= p.rows; r += NT) p.prefix[r] = lds_prefix[r];
     const int T = lds_prefix[p.rows];
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
         // slices start at item starts, so no item is cut (no partial pieces)
         auto snap = [&](int tau) {
             if (tau >= T) return T;
-            const Cursor c = cursor_at(lds_prefix, lds_nvis, p.rows, tau, C::TT);
+            const Cursor c = cursor_at(lds_prefix, lds_nvis, lds_first, p.rows, tau, C::TT);
             return c.j == 0 ? tau : c.item0 + c.tiles;
         };
         tau0 = snap(tau0);
@@ -216,18 +217,19 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
     // Source address of this lane's 16 bytes in 1 KB block `blk` of the tile
     // (nullptr: the row is past the item's keys or its block id is invalid).
     auto row_src = [&](const Cursor &c, int blk) -> int64_t {
-        const int tile0 = c.j * C::TT;
+        const int tile0 = (c.jlo + c.j) * C::TT;
         const int nvalid = min(C::TT, c.n_vis - tile0);
+        const int first = c.lo - tile0;   // keys of the tile before it are outside a sliding window
         const int t = blk * C::RPK + lane / C::CPR;
-        if (blk * C::RPK >= nvalid) return -1;
+        if (blk * C::RPK >= nvalid || blk * C::RPK + C::RPK <= first) return -1;
         const int b = (int)(((int64_t)p.row0 + c.row) / p.Sq);
         if (cache.block_table == nullptr || cache.log2_bs >= 4) {
             // the block's RPK consecutive rows lie in one 16-row group,
             // hence in one cache block: one lookup per wave
             const int64_t r0 = cache_row_wave(cache, b, c.g, tile0 + blk * C::RPK);
-            return (r0 >= 0 && t < nvalid) ? r0 + (t - blk * C::RPK) : -1;
+            return (r0 >= 0 && t < nvalid && t >= first) ? r0 + (t - blk * C::RPK) : -1;
         }
-        return t < nvalid ? cache_row(cache, b, c.g, tile0 + t) : -1;   // blocks shorter than 16 rows
+        return t < nvalid && t >= first ? cache_row(cache, b, c.g, tile0 + t) : -1;   // blocks shorter than 16 rows
     };
     // K rows are stored XOR-swizzled: piece x of row t lands in slot x ^ (t & SWZ).
     auto issue_k = [&](const Cursor &c, bool with_q, int stage) -> int {
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
     // Virtual iteration i issues K(i + A) and V(i + A - 1); iterations
     // tau0 - A .. tau0 - 1 form the prologue.
     constexpr int A = C::A;
-    Cursor kc = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);   // next K to issue
+    Cursor kc = cursor_at(lds_prefix, lds_nvis, lds_first, p.rows, tau0, C::TT);   // next K to issue
     Cursor vc = kc;                                                     // next V to issue
     uint32_t hist = 0;   // loads of the last virtual iterations, 5 bits each (newest lowest)
     auto issue_iter = [&](int i) {
@@ -305,16 +307,16 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
         const int tk = i + A, tv = i + A - 1;
         if (tk >= tau0 && tk < tau1) {
             n += issue_k(kc, kc.j == 0 || tk == tau0, (tk - tau0) % C::NBUF);
-            cursor_next(lds_nvis, p.rows, cache.K, kc, C::TT);
+            cursor_next(lds_nvis, lds_first, p.rows, cache.K, kc, C::TT);
         }
         if (tv >= tau0 && tv < tau1) {
             n += issue_v(vc, (tv - tau0) % C::NBUF);
-            cursor_next(lds_nvis, p.rows, cache.K, vc, C::TT);
+            cursor_next(lds_nvis, lds_first, p.rows, cache.K, vc, C::TT);
         }
         hist = (hist << 5) | (uint32_t)n;
     };
     for (int i = tau0 - A; i < tau0; ++i) issue_iter(i);
-    Cursor cs = cursor_at(lds_prefix, lds_nvis, p.rows, tau0, C::TT);   // tile of the score phase
+    Cursor cs = cursor_at(lds_prefix, lds_nvis, lds_first, p.rows, tau0, C::TT);   // tile of the score phase
     Cursor cv = cs;                                                    // tile of the V phase
     int piece0 = tau0;                                // first tile of the V phase's piece
 
@@ -336,7 +338,8 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
             const char *base = smem + ((tau - tau0) % C::NBUF) * C::STAGE;
             const uint4 *Ks = reinterpret_cast<const uint4 *>(base);
             const uint4 *Qs = reinterpret_cast<const uint4 *>(base + 2 * C::K_BYTES);
-            const int nvalid = min(C::TT, cs.n_vis - cs.j * C::TT);
+            const int nvalid = min(C::TT, cs.n_vis - (cs.jlo + cs.j) * C::TT);
+            const int vfirst = cs.lo - (cs.jlo + cs.j) * C::TT;   // first key inside a sliding window
             const bool s_first = cs.j == 0 || tau == tau0;
             const bool s_last = cs.j == cs.tiles - 1 || tau == tau1 - 1;
             if (s_first) {
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
                             a3 = fmaf(__uint_as_float(qw[4 * pcs + 3]), __uint_as_float(kv.w), a3);
                         }
                     }
-                    sc[k] = (t < nvalid) ? ((a0 + a1) + (a2 + a3)) * p.scale_log2 : -INFINITY;
+                    sc[k] = (t < nvalid && t >= vfirst) ? ((a0 + a1) + (a2 + a3)) * p.scale_log2 : -INFINITY;
                     mt = fmaxf(mt, sc[k]);
                 }
                 mt = group_max<C::TPH>(mt);
@@ -521,9 +524,9 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
                 // These stores share the vector-memory counter with the loads in
                 // flight; they can only make the next waits longer, never shorter.
             }
-            cursor_next(lds_nvis, p.rows, cache.K, cv, C::TT);
+            cursor_next(lds_nvis, lds_first, p.rows, cache.K, cv, C::TT);
         }
-        if (do_s) cursor_next(lds_nvis, p.rows, cache.K, cs, C::TT);
+        if (do_s) cursor_next(lds_nvis, lds_first, p.rows, cache.K, cs, C::TT);
     }
 }
 
@@ -557,7 +560,7 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(RowAttnParams p, int 
         return;
     }
     const int64_t T = p.prefix[p.rows];
-    const int64_t tiles = (n_vis + tt - 1) / tt;
+    const int64_t tiles = item_tiles(row_first(p, (int64_t)p.row0 + row, n_vis), n_vis, tt);
     const int64_t a = p.prefix[row] + (int64_t)g * tiles, e = a + tiles - 1;
     auto owner = [&](int64_t x) {
         int64_t w = x * W / T;

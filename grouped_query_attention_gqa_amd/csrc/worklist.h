@@ -15,7 +15,8 @@
 
 namespace gqa {
 
-// Visible keys of query row `row` (b * Sq + i), clamped to the cache capacity.
+// End of the visible keys of query row `row` (b * Sq + i): keys below it
+// may be seen; clamped to the cache capacity.
 __device__ __forceinline__ int row_visible(const RowAttnParams &p, int64_t row)
 {
     const int b = (int)(row / p.Sq);
@@ -32,13 +33,33 @@ __device__ __forceinline__ int row_visible(const RowAttnParams &p, int64_t row)
     return (int)n;
 }
 
+// First visible key of the row: 0, or with a sliding window of W positions
+// (inference-optimisation page §6.4.1) the oldest of the W most recent
+// positions up to the row's own, qpos + 1 - W.
+__device__ __forceinline__ int row_first(const RowAttnParams &p, int64_t row, int n_end)
+{
+    if (p.window <= 0) return 0;
+    const int b = (int)(row / p.Sq);
+    const int i = (int)(row % p.Sq);
+    const int64_t qpos = p.prefill ? (int64_t)p.start_pos[b] + i : (int64_t)p.ctx_lens[b] - 1;
+    int64_t lo = qpos + 1 - p.window;
+    if (lo < 0) lo = 0;
+    if (lo > n_end) lo = n_end;
+    return (int)lo;
+}
+
+// Tiles of `tt` keys an item with visible keys [lo, n) covers: tiles lo/tt
+// .. ceil(n/tt)-1 of the row.
+__device__ __forceinline__ int item_tiles(int lo, int n, int tt) { return n > lo ? (n + tt - 1) / tt - lo / tt : 0; }
+
 // For the rows of this launch (local rows 0 .. rows-1, at most kStreamRows):
-// nvis[r] = visible keys, prefix[r] = K * sum_{r' < r} tiles(r'),
+// keys first[r] .. nvis[r]-1 are visible, prefix[r] = K * sum_{r' < r} tiles(r'),
 // prefix[rows] = the number of tiles T.  Every thread of the workgroup calls
 // it; thread i handles the consecutive rows i*per .. i*per+per-1, so any row
 // count up to kStreamRows is covered whatever the workgroup size.
 template <int NT>
-__device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, int32_t *nvis, int *lds_waves)
+__device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, int32_t *nvis, int32_t *first,
+                             int *lds_waves)
 {
     static_assert(kStreamRows % NT == 0, "rows per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -50,8 +71,10 @@ __device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, in
         const int r = r0 + k;
         if (r < rows) {
             const int n = row_visible(p, p.row0 + r);
+            const int lo = row_first(p, p.row0 + r, n);
             nvis[r] = n;
-            local += (n + tt - 1) / tt;
+            first[r] = lo;
+            local += item_tiles(lo, n, tt);
         }
     }
     int x = local;   // inclusive scan over the wave, then over the waves
@@ -69,7 +92,7 @@ __device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, in
         const int r = r0 + k;
         if (r < rows) {
             prefix[r] = run * p.cache.K;
-            run += (nvis[r] + tt - 1) / tt;
+            run += item_tiles(first[r], nvis[r], tt);
         }
     }
     if (tid == NT - 1) prefix[rows] = (before + x) * p.cache.K;
@@ -79,13 +102,16 @@ __device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, in
 struct Cursor {
     int row;       // local query row
     int g;         // KV group
-    int j;         // tile within the item
+    int j;         // tile within the item (the item's tile 0 is tile jlo of the row)
     int tiles;     // tiles of the item
-    int n_vis;     // visible keys of the row
+    int n_vis;     // end of the visible keys of the row
+    int lo;        // first visible key of the row
+    int jlo;       // row tile of the item's first tile (lo / tt)
     int item0;     // flat index of the item's first tile
 };
 
-__device__ __forceinline__ Cursor cursor_at(const int32_t *prefix, const int32_t *nvis, int rows, int tau, int tt)
+__device__ __forceinline__ Cursor cursor_at(const int32_t *prefix, const int32_t *nvis, const int32_t *first, int rows,
+                                            int tau, int tt)
 {
     // last row whose prefix is <= tau (rows without tiles share their prefix)
     int lo = 0, hi = rows - 1;
@@ -96,7 +122,9 @@ __device__ __forceinline__ Cursor cursor_at(const int32_t *prefix, const int32_t
     Cursor c;
     c.row = lo;
     c.n_vis = nvis[lo];
-    c.tiles = (c.n_vis + tt - 1) / tt;
+    c.lo = first[lo];
+    c.jlo = c.lo / tt;
+    c.tiles = item_tiles(c.lo, c.n_vis, tt);
     const int off = tau - prefix[lo];
     c.g = off / c.tiles;
     c.j = off % c.tiles;
@@ -104,7 +132,8 @@ __device__ __forceinline__ Cursor cursor_at(const int32_t *prefix, const int32_t
     return c;
 }
 
-__device__ __forceinline__ void cursor_next(const int32_t *nvis, int rows, int K, Cursor &c, int tt)
+__device__ __forceinline__ void cursor_next(const int32_t *nvis, const int32_t *first, int rows, int K, Cursor &c,
+                                            int tt)
 {
     if (++c.j < c.tiles) return;
     c.j = 0;
@@ -115,7 +144,9 @@ __device__ __forceinline__ void cursor_next(const int32_t *nvis, int rows, int K
         ++c.row;
         if (c.row >= rows) return;
         c.n_vis = nvis[c.row];
-        c.tiles = (c.n_vis + tt - 1) / tt;
+        c.lo = first[c.row];
+        c.jlo = c.lo / tt;
+        c.tiles = item_tiles(c.lo, c.n_vis, tt);
     } while (c.tiles == 0);
 }
 

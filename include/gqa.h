@@ -159,6 +159,29 @@ gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
                        const gqa_kv_cache *cache, const int32_t *start_pos, int32_t B, int32_t s,
                        int32_t num_heads, float scale, int32_t causal, void *out, void *stream);
 
+/*
+ * Sliding-window attention (the inference-optimisation page §6.4.1: a model
+ * such as Mistral 7B keeps only the most recent N tokens, N = 4096, in its
+ * attention window).  With window > 0, the query at position qpos sees only
+ * the keys qpos - window + 1 .. qpos (those that exist and that the causal
+ * rule or ctx_lens allow); window <= 0 is no window, the same call as
+ * gqa_decode / gqa_prefill.  Keys outside the window are not read: whole
+ * tiles below it are skipped and a 16-token cache block that lies wholly
+ * below it is never touched, so its block-table entry may be stale.
+ *   gqa_decode_window: the decode row's position is ctx_lens[b] - 1, so it
+ *     sees keys max(0, ctx_lens[b] - window) .. ctx_lens[b] - 1.
+ *   gqa_prefill_window: row i is at position start_pos[b] + i.
+ * All other arguments, layouts, ownership and errors are those of
+ * gqa_decode and gqa_prefill.
+ */
+gqa_status gqa_decode_window(const void *q, const gqa_kv_cache *cache, const int32_t *ctx_lens,
+                             int32_t max_ctx, int32_t B, int32_t num_heads, float scale, int32_t window,
+                             void *out, void *workspace, size_t workspace_bytes, void *stream);
+gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_new,
+                              const gqa_kv_cache *cache, const int32_t *start_pos, int32_t B, int32_t s,
+                              int32_t num_heads, float scale, int32_t causal, int32_t window, void *out,
+                              void *stream);
+
 #ifdef __cplusplus
 }
 #endif

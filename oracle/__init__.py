@@ -65,6 +65,9 @@ def _load():
         lib.oracle_gqa_attention_rows.restype = i64
         lib.oracle_gqa_attention_rows.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                                   vp, vp, i32, dbl, i64, vp, vp]
+        lib.oracle_gqa_attention_rows_window.restype = i64
+        lib.oracle_gqa_attention_rows_window.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                         vp, vp, i32, dbl, i32, i64, vp, vp]
         lib.oracle_kv_append.restype = i64
         lib.oracle_kv_append.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32]
         lib.oracle_kv_append_paged.restype = i64
@@ -143,8 +146,9 @@ def attention(q, k, v, q_start, kv_len, causal: bool, scale: float) -> np.ndarra
     return out
 
 
-def attention_rows(q, k, v, q_start, kv_len, causal: bool, scale: float, rows) -> np.ndarray:
-    """Listed rows only; rows is an int array [n, 3] of (b, i, h); returns [n, d]."""
+def attention_rows(q, k, v, q_start, kv_len, causal: bool, scale: float, rows, window: int = 0) -> np.ndarray:
+    """Listed rows only; rows is an int array [n, 3] of (b, i, h); returns [n, d].
+    window > 0: each row sees only its `window` most recent positions."""
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
     v = np.ascontiguousarray(v, dtype=np.float64)
@@ -153,9 +157,9 @@ def attention_rows(q, k, v, q_start, kv_len, causal: bool, scale: float, rows) -
     rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int32).reshape(-1, 3))
     qs, kl = _i32(q_start, B), _i32(kv_len, B)
     out = np.empty((rows.shape[0], d), dtype=np.float64)
-    rc = _load().oracle_gqa_attention_rows(_ptr(q), _ptr(k), _ptr(v), B, Sq, H, K, d, Sk,
-                                           _ptr(qs), _ptr(kl), int(bool(causal)), float(scale),
-                                           rows.shape[0], _ptr(rows), _ptr(out))
+    rc = _load().oracle_gqa_attention_rows_window(_ptr(q), _ptr(k), _ptr(v), B, Sq, H, K, d, Sk,
+                                                  _ptr(qs), _ptr(kl), int(bool(causal)), float(scale), int(window),
+                                                  rows.shape[0], _ptr(rows), _ptr(out))
     if rc < 0:
         raise ValueError("oracle rejected the shapes")
     return out
@@ -229,7 +233,7 @@ def gather_paged_raw(pool: np.ndarray, block_table, ctx_lens, S_out: int, fill) 
 
 
 def paged_attention_rows(q, pool_k, pool_v, block_table, ctx_lens, scale, rows_per_seq=None,
-                         seqs=None) -> tuple[np.ndarray, np.ndarray]:
+                         seqs=None, window: int = 0) -> tuple[np.ndarray, np.ndarray]:
     """Decode rows over a paged cache: gather each listed sequence, then attend.
 
     q is [B,1,H,d] fp64; pool_k/pool_v [N,K,bs,d] fp64.  ``seqs`` lists the
@@ -246,7 +250,7 @@ def paged_attention_rows(q, pool_k, pool_v, block_table, ctx_lens, scale, rows_p
         kc = gather_paged(pool_k, bt[b:b + 1], cl[b:b + 1], S)
         vc = gather_paged(pool_v, bt[b:b + 1], cl[b:b + 1], S)
         r = np.array([[0, 0, h] for h in range(H)], dtype=np.int32)
-        o = attention_rows(q[b:b + 1], kc, vc, [S - 1], [S], False, scale, r)
+        o = attention_rows(q[b:b + 1], kc, vc, [S - 1], [S], False, scale, r, window)
         outs.append(o)
         rows.append(np.array([[b, 0, h] for h in range(H)], dtype=np.int32))
     return np.concatenate(rows), np.concatenate(outs)

@@ -154,11 +154,33 @@ int64_t oracle_gqa_attention(const double *q, const double *k, const double *v,
  * workload can be checked on a sample.  rows[3*r + 0..2] = (b, i, h);
  * out is [n_rows, d].
  */
+/*
+ * The rows variant with a sliding window (inference-optimisation page
+ * §6.4.1: attention kept to the most recent N tokens).  window > 0: the row
+ * at position qpos sees only the keys from qpos + 1 - window on (and, as
+ * without a window, below its visible end); window <= 0: no window.
+ */
+int64_t oracle_gqa_attention_rows_window(const double *q, const double *k, const double *v,
+                                         int B, int Sq, int H, int K, int d, int Sk,
+                                         const int32_t *q_start, const int32_t *kv_len,
+                                         int causal, double scale, int window,
+                                         int64_t n_rows, const int32_t *rows, double *out);
+
 int64_t oracle_gqa_attention_rows(const double *q, const double *k, const double *v,
                                   int B, int Sq, int H, int K, int d, int Sk,
                                   const int32_t *q_start, const int32_t *kv_len,
                                   int causal, double scale,
                                   int64_t n_rows, const int32_t *rows, double *out)
+{
+    return oracle_gqa_attention_rows_window(q, k, v, B, Sq, H, K, d, Sk, q_start, kv_len, causal, scale, 0,
+                                            n_rows, rows, out);
+}
+
+int64_t oracle_gqa_attention_rows_window(const double *q, const double *k, const double *v,
+                                         int B, int Sq, int H, int K, int d, int Sk,
+                                         const int32_t *q_start, const int32_t *kv_len,
+                                         int causal, double scale, int window,
+                                         int64_t n_rows, const int32_t *rows, double *out)
 {
     if (B <= 0 || Sq <= 0 || H <= 0 || K <= 0 || d <= 0 || Sk < 0 || H % K != 0) return -1;
     const int G = H / K;
@@ -176,11 +198,16 @@ int64_t oracle_gqa_attention_rows(const double *q, const double *k, const double
             }
             const int g = h / G;
             int64_t len = kv_len[b] < Sk ? kv_len[b] : Sk;
-            const int64_t n_vis = visible_keys((int64_t)q_start[b] + i, len, causal);
+            const int64_t qpos = (int64_t)q_start[b] + i;
+            const int64_t n_vis = visible_keys(qpos, len, causal);
+            /* with a window: keys lo .. n_vis-1 */
+            int64_t lo = window > 0 ? qpos + 1 - window : 0;
+            if (lo < 0) lo = 0;
+            if (lo > n_vis) lo = n_vis;
             const double *q_row = q + (((int64_t)b * Sq + i) * H + h) * d;
-            const double *k_head = k + ((int64_t)b * K + g) * Sk * d;
-            const double *v_head = v + ((int64_t)b * K + g) * Sk * d;
-            empty += attend_row(q_row, k_head, v_head, n_vis, d, scale, scores, out + r * d);
+            const double *k_head = k + (((int64_t)b * K + g) * Sk + lo) * d;
+            const double *v_head = v + (((int64_t)b * K + g) * Sk + lo) * d;
+            empty += attend_row(q_row, k_head, v_head, n_vis - lo, d, scale, scores, out + r * d);
         }
         free(scores);
     }

@@ -35,8 +35,10 @@ def visible_count(qpos: int, kv_len: int, causal: bool) -> int:
     return max(n, 0)
 
 
-def gqa_reference(q, k, v, q_start, kv_len, causal: bool, scale: float) -> np.ndarray:
-    """q [B,Sq,H,d], k/v [B,K,Sk,d] fp64 -> out [B,Sq,H,d] fp64."""
+def gqa_reference(q, k, v, q_start, kv_len, causal: bool, scale: float, window: int = 0) -> np.ndarray:
+    """q [B,Sq,H,d], k/v [B,K,Sk,d] fp64 -> out [B,Sq,H,d] fp64.
+    window > 0: a row at position qpos sees keys from qpos + 1 - window on
+    (sliding window, inference-optimisation page §6.4.1)."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -50,15 +52,17 @@ def gqa_reference(q, k, v, q_start, kv_len, causal: bool, scale: float) -> np.nd
     out = np.full((B, Sq, K, G, d), np.nan)
     for b in range(B):
         for i in range(Sq):
-            n = visible_count(int(q_start[b]) + i, min(int(kv_len[b]), k.shape[2]), causal)
-            if n == 0:
+            qpos = int(q_start[b]) + i
+            n = visible_count(qpos, min(int(kv_len[b]), k.shape[2]), causal)
+            lo = min(max(qpos + 1 - window, 0), n) if window > 0 else 0
+            if n - lo <= 0:
                 continue
             for g in range(K):
                 # step 3: scores of the G heads of group g against K_g
-                s = scale * (qg[b, i, g] @ k[b, g, :n].T)          # [G, n]
+                s = scale * (qg[b, i, g] @ k[b, g, lo:n].T)       # [G, n - lo]
                 m = s.max(axis=1, keepdims=True)                  # pass 1
                 p = np.exp(s - m)                                 # pass 2
-                out[b, i, g] = (p @ v[b, g, :n]) / p.sum(axis=1, keepdims=True)  # pass 3
+                out[b, i, g] = (p @ v[b, g, lo:n]) / p.sum(axis=1, keepdims=True)  # pass 3
     # step 4: back to [B, Sq, H, d]
     return out.reshape(B, Sq, H, d)
 

@@ -75,14 +75,14 @@ class DecodeRun:
         self.cache = binding.KVCache(self.k, self.v, self.bt)
         self.max_ctx = int(inp.ctx.max())
 
-    def run(self, out=None, workspace=None) -> torch.Tensor:
+    def run(self, out=None, workspace=None, window=0) -> torch.Tensor:
         out = binding.gqa_decode(self.q, self.cache, self.ctx, self.max_ctx, out=out, scale=self.inp.wl.scale,
-                                 workspace=workspace)
+                                 workspace=workspace, window=window)
         torch.cuda.synchronize()
         return out
 
 
-def oracle_decode_rows(inp: W.DecodeInputs, seqs=None, heads=None):
+def oracle_decode_rows(inp: W.DecodeInputs, seqs=None, heads=None, window=0):
     """Oracle outputs (fp64) for the listed sequences and heads; returns (rows, out)."""
     wl = inp.wl
     seqs = range(wl.B) if seqs is None else seqs
@@ -99,7 +99,7 @@ def oracle_decode_rows(inp: W.DecodeInputs, seqs=None, heads=None):
             vb = oracle.gather_paged_raw(inp.v, inp.block_table[b:b + 1], inp.ctx[b:b + 1], n, fill)
         rows = np.array([[0, 0, h] for h in heads], dtype=np.int32)
         o = oracle.attention_rows(as_f64(inp.q[b:b + 1], wl.dtype), as_f64(kb, wl.dtype), as_f64(vb, wl.dtype),
-                                  [n - 1], [n], False, wl.scale, rows)
+                                  [n - 1], [n], False, wl.scale, rows, window)
         rows[:, 0] = b
         rows_all.append(rows)
         outs.append(o)
@@ -146,14 +146,14 @@ class PrefillRun:
             zero = torch.zeros(wl.B, dtype=torch.int32, device=DEV)
             binding.gqa_kv_append(self.cache, to_dev(kp), to_dev(vp), zero)
 
-    def run(self, causal=True) -> torch.Tensor:
+    def run(self, causal=True, window=0) -> torch.Tensor:
         out = binding.gqa_prefill(self.q, self.kn, self.vn, self.cache, self.start, causal=causal,
-                                  scale=self.inp.wl.scale)
+                                  scale=self.inp.wl.scale, window=window)
         torch.cuda.synchronize()
         return out
 
 
-def oracle_prefill_rows(inp: W.PrefillInputs, rows, causal=True, prior=None):
+def oracle_prefill_rows(inp: W.PrefillInputs, rows, causal=True, prior=None, window=0):
     """Oracle rows (b, i, h) of a prefill whose cache holds prior rows then the new ones."""
     wl = inp.wl
     if prior is None:
@@ -170,4 +170,5 @@ def oracle_prefill_rows(inp: W.PrefillInputs, rows, causal=True, prior=None):
     oracle.kv_append(vc, v_all, zero)
     kc, vc = as_f64(kc, wl.dtype), as_f64(vc, wl.dtype)
     kv_len = inp.start_pos + wl.s
-    return oracle.attention_rows(as_f64(inp.q, wl.dtype), kc, vc, inp.start_pos, kv_len, causal, wl.scale, rows)
+    return oracle.attention_rows(as_f64(inp.q, wl.dtype), kc, vc, inp.start_pos, kv_len, causal, wl.scale, rows,
+                                 window)

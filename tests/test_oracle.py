@@ -26,10 +26,11 @@ def rand(rng, *shape):
     return rng.standard_normal(shape)
 
 
-def sdpa_ref(q, k, v, q_start, kv_len, causal, scale):
+def sdpa_ref(q, k, v, q_start, kv_len, causal, scale, window=0):
     """PyTorch fp64 SDPA (CPU, math path) row by row with an explicit mask.
 
-    q [B,Sq,H,d], k/v [B,K,Sk,d]; enable_gqa broadcasts KV head h // G."""
+    q [B,Sq,H,d], k/v [B,K,Sk,d]; enable_gqa broadcasts KV head h // G.
+    window > 0 adds the band j > qpos - window to the mask."""
     B, Sq, H, d = q.shape
     K, Sk = k.shape[1], k.shape[2]
     out = np.full(q.shape, np.nan)
@@ -42,6 +43,8 @@ def sdpa_ref(q, k, v, q_start, kv_len, causal, scale):
         allowed = j < min(kv_len[b], Sk)
         if causal:
             allowed = allowed & (j <= pos)
+        if window > 0:
+            allowed = allowed & (j > pos - window)
         mask = torch.from_numpy(np.broadcast_to(allowed, (Sq, Sk)).copy())
         o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale,
                                            enable_gqa=(H != K))
@@ -234,6 +237,71 @@ def test_causal_row_equals_decode_over_prefix(oracle_lib):
         assert np.array_equal(pre[0, i], dec[0, 0])
 
 
+# ---------------------------------------------------------------------------
+# sliding window (inference-optimisation page §6.4.1): a row sees only its
+# `window` most recent positions
+# ---------------------------------------------------------------------------
+
+def _rows_all(B, Sq, H):
+    return np.array([[b, i, h] for b in range(B) for i in range(Sq) for h in range(H)], np.int32)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("window", [1, 3, 7, 40])
+def test_window_matches_sdpa_band_mask(oracle_lib, causal, window):
+    """Against PyTorch's fp64 SDPA with the band j > qpos - window in its mask."""
+    rng = np.random.default_rng(31)
+    B, Sq, H, K, d, Sk = 2, 6, 4, 2, 8, 21
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    qs, kl = [5, 12], [Sk, 17]
+    want = sdpa_ref(q, k, v, qs, kl, causal, 0.31, window)
+    got = oracle.attention_rows(q, k, v, qs, kl, causal, 0.31, _rows_all(B, Sq, H), window)
+    np.testing.assert_allclose(got, want.reshape(-1, d), rtol=0, atol=1e-12)
+
+
+def test_window_one_returns_own_value(oracle_lib):
+    """window = 1 leaves one key, the row's own position: out = v[qpos] exactly."""
+    rng = np.random.default_rng(32)
+    B, Sq, H, K, d, Sk = 1, 4, 4, 2, 8, 10
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    got = oracle.attention_rows(q, k, v, [3], [Sk], True, 0.5, _rows_all(B, Sq, H), 1).reshape(Sq, H, d)
+    for i in range(Sq):
+        for h in range(H):
+            assert np.array_equal(got[i, h], v[0, h // 2, 3 + i])
+
+
+def test_window_covering_every_key_is_no_window(oracle_lib):
+    rng = np.random.default_rng(33)
+    B, Sq, H, K, d, Sk = 2, 3, 4, 1, 8, 12
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    rows = _rows_all(B, Sq, H)
+    full = oracle.attention_rows(q, k, v, [4, 9], [Sk, Sk], True, 0.4, rows)
+    wide = oracle.attention_rows(q, k, v, [4, 9], [Sk, Sk], True, 0.4, rows, Sk)
+    assert np.array_equal(full, wide)
+
+
+def test_window_equals_attention_over_the_key_slice(oracle_lib):
+    """A decode row with window W equals a plain decode over keys ctx-W .. ctx-1."""
+    rng = np.random.default_rng(34)
+    H, K, d, ctx, W = 4, 2, 8, 30, 11
+    q, k, v = rand(rng, 1, 1, H, d), rand(rng, 1, K, ctx, d), rand(rng, 1, K, ctx, d)
+    rows = _rows_all(1, 1, H)
+    got = oracle.attention_rows(q, k, v, [ctx - 1], [ctx], False, 0.3, rows, W)
+    lo = ctx - W
+    want = oracle.attention_rows(q, k[:, :, lo:].copy(), v[:, :, lo:].copy(), [W - 1], [W], False, 0.3, rows)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("window", [2, 9])
+def test_window_numpy_oracle_agrees(oracle_lib, window):
+    rng = np.random.default_rng(35)
+    B, Sq, H, K, d, Sk = 2, 5, 6, 3, 8, 16
+    q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
+    c = oracle.attention_rows(q, k, v, [2, 7], [Sk, 12], True, 0.35, _rows_all(B, Sq, H), window)
+    n = np_oracle.gqa_reference(q, k, v, [2, 7], [Sk, 12], True, 0.35, window)
+    np.testing.assert_allclose(c, n.reshape(-1, d), rtol=0, atol=1e-12)
+
+
 def test_no_visible_key_is_reported(oracle_lib):
     q, k, v = np.ones((1, 1, 2, 4)), np.ones((1, 1, 3, 4)), np.ones((1, 1, 3, 4))
     out = oracle.attention(q, k, v, [0], [0], False, 1.0)
@@ -347,7 +415,7 @@ def test_paged_attention_equals_contiguous(oracle_lib):
 # ---------------------------------------------------------------------------
 
 def _mutant(kind):
-    def ref(q, k, v, q_start, kv_len, causal, scale):
+    def ref(q, k, v, q_start, kv_len, causal, scale, window=0):
         B, Sq, H, d = q.shape
         K = k.shape[1]
         G = H // K
@@ -358,18 +426,21 @@ def _mutant(kind):
                 n = min(kv_len[b], k.shape[2])
                 if causal:
                     n = min(n, qpos + (0 if kind == "causal_excludes_self" else 1))
-                if n <= 0:
+                lo = 0
+                if window > 0:
+                    lo = max(0, qpos + (0 if kind == "window_off_by_one" else 1) - window)
+                if n - lo <= 0:
                     continue
                 for h in range(H):
                     g = h % K if kind == "strided_group_map" else h // G
                     sc = 1.0 if kind == "dropped_scale" else scale
-                    kk = k[b, g, :n]
+                    kk = k[b, g, lo:n]
                     if kind == "transposed_k":
-                        kk = k[b, g, :n][:, ::-1]
+                        kk = k[b, g, lo:n][:, ::-1]
                     s = sc * (kk @ q[b, i, h])
                     p = np.exp(s - s.max())
                     l = p.sum() if kind != "unnormalised" else 1.0
-                    out[b, i, h] = (p @ v[b, g, :n]) / l
+                    out[b, i, h] = (p @ v[b, g, lo:n]) / l
         return out
     return ref
 
@@ -379,16 +450,19 @@ def _pins_pass(ref):
     B, Sq, H, K, d, Sk = 2, 3, 8, 2, 8, 9
     q, k, v = rand(rng, B, Sq, H, d), rand(rng, B, K, Sk, d), rand(rng, B, K, Sk, d)
     qs, kl = np.array([3, 6], np.int32), np.array([9, 9], np.int32)
-    got = ref(q, k, v, qs, kl, True, 0.35)
-    want = sdpa_ref(q, k, v, qs, kl, True, 0.35)
-    ok = ~np.isnan(want)
-    if not np.array_equal(ok, ~np.isnan(got)):
-        return False
-    return bool(np.max(np.abs(got[ok] - want[ok])) < 1e-12)
+    for window in (0, 3):
+        got = ref(q, k, v, qs, kl, True, 0.35, window)
+        want = sdpa_ref(q, k, v, qs, kl, True, 0.35, window)
+        ok = ~np.isnan(want)
+        if not np.array_equal(ok, ~np.isnan(got)):
+            return False
+        if not np.max(np.abs(got[ok] - want[ok])) < 1e-12:
+            return False
+    return True
 
 
 @pytest.mark.parametrize("kind", ["strided_group_map", "dropped_scale", "causal_excludes_self",
-                                  "transposed_k", "unnormalised"])
+                                  "transposed_k", "unnormalised", "window_off_by_one"])
 def test_planted_mistakes_are_caught(kind):
     assert _pins_pass(_mutant("none"))
     assert not _pins_pass(_mutant(kind))

@@ -77,11 +77,11 @@ def test_append_paged_bit_exact(s_new):
 # decode
 # ---------------------------------------------------------------------------
 
-def _decode_case(inp, what, seqs=None, heads=None):
-    say("decode", what, inp.wl.B, inp.wl.H, inp.wl.K, inp.wl.d, "ctx max", int(inp.ctx.max()))
+def _decode_case(inp, what, seqs=None, heads=None, window=0):
+    say("decode", what, inp.wl.B, inp.wl.H, inp.wl.K, inp.wl.d, "ctx max", int(inp.ctx.max()), "window", window)
     run = DecodeRun(inp)
-    out = from_dev(run.run())
-    rows, want = oracle_decode_rows(inp, seqs, heads)
+    out = from_dev(run.run(window=window))
+    rows, want = oracle_decode_rows(inp, seqs, heads, window)
     got = gpu_rows(out, rows, inp.wl.dtype)
     return check_close(got, want, _tol(inp.wl.dtype), what)
 
@@ -176,13 +176,13 @@ def _all_rows(B, s, H):
     return np.array([[b, i, h] for b in range(B) for i in range(s) for h in range(H)], np.int32)
 
 
-def _prefill_case(inp, what, rows=None, causal=True, **kw):
+def _prefill_case(inp, what, rows=None, causal=True, window=0, **kw):
     wl = inp.wl
-    say("prefill", what, wl.B, wl.s, wl.H, wl.K, wl.d, "causal", causal)
+    say("prefill", what, wl.B, wl.s, wl.H, wl.K, wl.d, "causal", causal, "window", window)
     run = PrefillRun(inp, **kw)
-    out = from_dev(run.run(causal=causal))
+    out = from_dev(run.run(causal=causal, window=window))
     rows = _all_rows(wl.B, wl.s, wl.H) if rows is None else rows
-    want = oracle_prefill_rows(inp, rows, causal=causal, prior=kw.get("prior"))
+    want = oracle_prefill_rows(inp, rows, causal=causal, prior=kw.get("prior"), window=window)
     return check_close(gpu_rows(out, rows, wl.dtype), want, _tol(wl.dtype), what), run
 
 

@@ -1,0 +1,144 @@
+"""GPU parity of the sliding-window calls (gqa_decode_window,
+gqa_prefill_window) against the fp64 CPU oracle on the same seeded bits.
+
+A row at position qpos sees only keys qpos - window + 1 .. qpos (the
+inference-optimisation page §6.4.1).  Random-input parity at the usual
+tolerances covers the decode kernels (groups of up to 8 heads, larger groups
+and fp32), paged caches and the prefill kernels; two structured cases pin the
+lower edge of the window exactly, and one checks that cache blocks wholly
+below the window are never read."""
+import numpy as np
+import pytest
+import torch
+
+from grouped_query_attention_gqa_amd import binding
+from grouped_query_attention_gqa_amd import workloads as W
+from gpu_common import (BF16_TOL, F32_TOL, DecodeRun, PrefillRun, check_close, from_dev, gpu_rows,
+                        oracle_decode_rows, oracle_prefill_rows, requires_gpu, say, to_dev)
+
+pytestmark = [pytest.mark.gpu, requires_gpu]
+
+
+def _tol(dtype):
+    return BF16_TOL if dtype == "bf16" else F32_TOL
+
+
+def _decode(inp, what, window):
+    say("decode window", what, inp.wl.B, inp.wl.H, inp.wl.K, inp.wl.d, "window", window)
+    out = from_dev(DecodeRun(inp).run(window=window))
+    rows, want = oracle_decode_rows(inp, window=window)
+    return check_close(gpu_rows(out, rows, inp.wl.dtype), want, _tol(inp.wl.dtype), what)
+
+
+CTX = [1, 63, 700, 1500, 129, 2000]
+
+
+@pytest.mark.parametrize("H,K", [(32, 8), (64, 8), (16, 16), (64, 1)])
+@pytest.mark.parametrize("window", [1, 17, 100, 1000])
+def test_decode_window_bf16(H, K, window):
+    wl = W.WORKLOADS["llama3_8b_decode"].replace(B=len(CTX), H=H, K=K, ctx=("uniform", 1, 2000))
+    _decode(W.make_decode(wl, ctx_override=CTX), f"bf16 H={H} K={K}", window)
+
+
+@pytest.mark.parametrize("window", [1, 33, 600])
+def test_decode_window_f32(window):
+    wl = W.WORKLOADS["tiny_decode_f32"].replace(B=4, H=8, K=2, d=64, ctx=("uniform", 1, 1500))
+    _decode(W.make_decode(wl, ctx_override=[1, 90, 1500, 700]), "fp32", window)
+
+
+@pytest.mark.parametrize("bs", [16, 4])
+def test_decode_window_paged(bs):
+    wl = W.WORKLOADS["paged_long_decode"].replace(B=4, ctx=("loguniform", 17, 3000), block_size=bs)
+    _decode(W.make_decode(wl), f"paged, {bs}-token blocks", 300)
+
+
+def test_decode_window_skips_blocks_below_it():
+    """Table entries of blocks wholly below every window point at an extra
+    pool block full of NaN: the output stays finite and equal to the
+    oracle's (computed with the true table), so those blocks are not read."""
+    wl = W.WORKLOADS["paged_long_decode"].replace(B=3, ctx=("loguniform", 600, 3000))
+    inp = W.make_decode(wl)
+    window = 200
+    bs = wl.block_size
+    n_pool = inp.k.shape[0]
+    nan = W.sentinel(wl.dtype, "nan")
+    pad = np.full((1,) + inp.k.shape[1:], nan, dtype=inp.k.dtype)
+    stale = W.DecodeInputs(inp.wl, inp.ctx, inp.q, np.concatenate([inp.k, pad]), np.concatenate([inp.v, pad]),
+                           inp.block_table.copy(), inp.n_blocks)
+    for b in range(wl.B):
+        lo = max(0, int(inp.ctx[b]) - window)
+        stale.block_table[b, :lo // bs] = n_pool
+    say("decode window, stale blocks below it", wl.B, "window", window)
+    out = from_dev(DecodeRun(stale).run(window=window))
+    rows, want = oracle_decode_rows(inp, window=window)
+    check_close(gpu_rows(out, rows, wl.dtype), want, BF16_TOL, "stale blocks below the window")
+
+
+@pytest.mark.parametrize("H,K", [(32, 8), (64, 8), (16, 16)])
+def test_decode_window_lower_edge_exact(H, K):
+    """V is 1 at keys inside the window and 0 below it: the output is exactly
+    1.0 in every column if and only if no key below the window contributes."""
+    ctx = [700, 129, 2000, 64]
+    window = 100
+    wl = W.WORKLOADS["llama3_8b_decode"].replace(B=len(ctx), H=H, K=K, ctx=("uniform", 1, 2000))
+    inp = W.make_decode(wl, ctx_override=ctx)
+    v = inp.v.copy()
+    one, zero = W.f32_to_bf16_bits(np.float32(1.0)), W.f32_to_bf16_bits(np.float32(0.0))
+    for b, n in enumerate(ctx):
+        lo = max(0, n - window)
+        v[b, :, :lo] = zero
+        v[b, :, lo:n] = one
+    inp = W.DecodeInputs(inp.wl, inp.ctx, inp.q, inp.k, v, inp.block_table)
+    say("decode window lower edge", H, K)
+    out = from_dev(DecodeRun(inp).run(window=window))
+    assert (out == one).all()
+
+
+@pytest.mark.parametrize("window", [1, 50, 64, 100, 257])
+@pytest.mark.parametrize("H,K,d", [(32, 8, 128), (16, 2, 64)])
+def test_prefill_window_bf16(window, H, K, d):
+    wl = W.WORKLOADS["causal_prefill_4k"].replace(B=2, s=300, H=H, K=K, d=d)
+    inp = W.make_prefill(wl)
+    say("prefill window", H, K, d, window)
+    run = PrefillRun(inp)
+    out = from_dev(run.run(window=window))
+    rows = np.array([[b, i, h] for b in range(wl.B) for i in range(wl.s) for h in range(wl.H)], np.int32)
+    want = oracle_prefill_rows(inp, rows, window=window)
+    check_close(gpu_rows(out, rows, "bf16"), want, BF16_TOL, f"bf16 prefill window {window}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_window_after_prefix(dtype):
+    """start_pos > 0 with a window shorter than the cached prefix."""
+    base = W.WORKLOADS["causal_prefill_4k"] if dtype == "bf16" else W.WORKLOADS["tiny_prefill_f32"]
+    wl = base.replace(B=2, s=96, H=16, K=4, d=128 if dtype == "bf16" else 64)
+    inp = W.make_prefill(wl)
+    P = 173
+    rng = np.random.default_rng(5)
+
+    def rows_of(shape):
+        if dtype == "bf16":
+            return W.f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
+        return rng.standard_normal(shape, dtype=np.float32)
+
+    prior = (rows_of((wl.B, P, wl.K, wl.d)), rows_of((wl.B, P, wl.K, wl.d)))
+    inp = W.PrefillInputs(wl, np.full(wl.B, P, np.int32), inp.q, inp.k_new, inp.v_new)
+    say("prefill window after a prefix", dtype)
+    run = PrefillRun(inp, prior=prior)
+    out = from_dev(run.run(window=120))
+    rows = np.array([[b, i, h] for b in range(wl.B) for i in range(wl.s) for h in range(wl.H)], np.int32)
+    want = oracle_prefill_rows(inp, rows, prior=prior, window=120)
+    check_close(gpu_rows(out, rows, dtype), want, _tol(dtype), f"{dtype} prefill window after prefix")
+
+
+def test_prefill_window_paged():
+    wl = W.WORKLOADS["causal_prefill_4k"].replace(B=3, s=130, H=32, K=8)
+    rng = np.random.default_rng(12)
+    table, n_pool = W.deal_blocks(rng, np.full(wl.B, wl.s, np.int32), wl.block_size, slack_blocks=5)
+    inp = W.make_prefill(wl)
+    say("prefill window paged")
+    run = PrefillRun(inp, paged_blocks=(table, n_pool))
+    out = from_dev(run.run(window=45))
+    rows = np.array([[b, i, h] for b in range(wl.B) for i in range(wl.s) for h in range(wl.H)], np.int32)
+    want = oracle_prefill_rows(inp, rows, window=45)
+    check_close(gpu_rows(out, rows, "bf16"), want, BF16_TOL, "paged prefill window")
