@@ -14,7 +14,10 @@ The same JSON line also carries
     bf16, append included) in TFLOP/s against the 2.5 PFLOP/s dense bf16
     matrix-core peak;
   * decode_workloads: the other decode shapes (Llama-2-70B contiguous and its
-    MHA / MQA variants, paged long-context) in GB/s;
+    MHA / MQA variants, paged long-context, and a Mistral-7B-shaped
+    sliding-window decode whose bytes count only the window) in GB/s;
+  * prefill_workloads: a chunked prefill (512 new tokens after a 3584-token
+    cached prefix, paged cache) in TFLOP/s;
   * cpu_baseline: the CPU oracle on the host cores, on the same step.
 
 The K/V caches are rotated over several copies so that the ~256 MB
@@ -58,7 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel: decode|prefill|decode70b|paged|mha|mqa|copy (a 512 MiB device copy)")
+                    help="profile one kernel: decode|prefill|decode70b|paged|mha|mqa|window|chunked|"
+                         "copy (a 512 MiB device copy)")
     ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
     return ap.parse_args()
 
@@ -76,9 +80,11 @@ def up(x: np.ndarray):
 
 
 def decode_bytes(wl, ctx):
-    """Algorithmic bytes of one decode: each valid K and V row once, Q read, O written."""
+    """Algorithmic bytes of one decode: each visible K and V row once (with a
+    sliding window only the window's rows), Q read, O written."""
     es = 2 if wl.dtype == "bf16" else 4
-    kv = 2 * wl.K * wl.d * es * int(np.sum(ctx, dtype=np.int64))
+    rows = np.minimum(ctx, wl.window) if wl.window > 0 else ctx
+    kv = 2 * wl.K * wl.d * es * int(np.sum(rows, dtype=np.int64))
     qo = 2 * wl.B * wl.H * wl.d * es
     return kv + qo
 
@@ -89,8 +95,9 @@ def append_bytes(wl, s_new):
 
 
 def causal_flops(wl):
-    """4 * B * H * d * sum_{i<s} (i+1): QK^T and PV over the visible (lower-triangle) keys."""
-    return 4 * wl.B * wl.H * wl.d * (wl.s * (wl.s + 1) // 2)
+    """4 * B * H * d * sum_{i<s} (start+i+1): QK^T and PV over the visible keys (the
+    cached prefix and the lower triangle of the new tokens)."""
+    return 4 * wl.B * wl.H * wl.d * (wl.s * wl.start + wl.s * (wl.s + 1) // 2)
 
 
 class DecodeBench:
@@ -135,7 +142,7 @@ class DecodeBench:
     def decode(self, i):
         from grouped_query_attention_gqa_amd import binding
         binding.gqa_decode(self.q, self.caches[i % len(self.caches)], self.ctx_d, self.max_ctx, out=self.out,
-                           scale=self.wl.scale, workspace=self.ws)
+                           scale=self.wl.scale, workspace=self.ws, window=self.wl.window)
 
 
 def time_decode_only(db: DecodeBench, iters: int, warmup: int):
@@ -351,7 +358,8 @@ def main():
         torch.cuda.empty_cache()
         # ---- the other decode shapes --------------------------------------
         extra = {}
-        for name in ("llama2_70b_decode", "paged_long_decode", "llama2_70b_decode_mha", "llama2_70b_decode_mqa"):
+        for name in ("llama2_70b_decode", "paged_long_decode", "llama2_70b_decode_mha", "llama2_70b_decode_mqa",
+                     "mistral_7b_window_decode"):
             w = W.WORKLOADS[name]
             d2 = DecodeBench(w)
             mean_ms, med_ms = time_decode_only(d2, max(5, args.steps // 2), 3)
@@ -362,6 +370,10 @@ def main():
             del d2
             torch.cuda.empty_cache()
         result["decode_workloads"] = extra
+        # ---- chunked prefill: new tokens after a cached prefix, paged ----
+        result["prefill_workloads"] = {
+            "chunked_prefill_paged": bench_prefill(W.WORKLOADS["chunked_prefill_paged"], max(10, args.steps // 2), 5)}
+        torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:
         wl = W.WORKLOADS["llama3_8b_decode"]
@@ -378,17 +390,27 @@ def bench_prefill(wl, iters, warmup):
     from grouped_query_attention_gqa_amd import workloads as W
     inp = W.make_prefill(wl)
     q, kn, vn, start = up(inp.q), up(inp.k_new), up(inp.v_new), up(inp.start_pos)
-    kc = torch.zeros(wl.B, wl.K, wl.s, wl.d, dtype=torch.bfloat16, device="cuda")
-    vc = torch.zeros_like(kc)
-    cache = binding.KVCache(kc, vc)
+    S = wl.start + wl.s
+    if wl.paged:
+        # a shuffled block table over a pool just large enough; the cached
+        # prefix holds zeros (its values do not change the work)
+        rng = np.random.default_rng(wl.seed)
+        table, n_pool = W.deal_blocks(rng, np.full(wl.B, S, np.int32), wl.block_size)
+        kc = torch.zeros(n_pool, wl.K, wl.block_size, wl.d, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        cache = binding.KVCache(kc, vc, up(table))
+    else:
+        kc = torch.zeros(wl.B, wl.K, S, wl.d, dtype=torch.bfloat16, device="cuda")
+        vc = torch.zeros_like(kc)
+        cache = binding.KVCache(kc, vc)
     out = torch.empty_like(q)
     for _ in range(warmup):
-        binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale)
+        binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale, window=wl.window)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for a, b in evs:
         a.record()
-        binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale)
+        binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale, window=wl.window)
         b.record()
     torch.cuda.synchronize()
     ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
@@ -396,8 +418,8 @@ def bench_prefill(wl, iters, warmup):
     tf = flops / (ms * 1e-3) / 1e12
     log(f"prefill {wl.name}: {ms * 1e3:.1f} us (append + attention), {tf:.1f} TFLOP/s "
         f"({100 * tf / BF16_MFMA_PEAK_TFLOPS:.1f}% of bf16 MFMA peak)")
-    return {"workload": wl.name, "B": wl.B, "s": wl.s, "H": wl.H, "K": wl.K, "d": wl.d,
-            "us_per_call": round(ms * 1e3, 2), "flops": flops, "TFLOP/s": round(tf, 2),
+    return {"workload": wl.name, "B": wl.B, "s": wl.s, "start": wl.start, "H": wl.H, "K": wl.K, "d": wl.d,
+            "paged": wl.paged, "us_per_call": round(ms * 1e3, 2), "flops": flops, "TFLOP/s": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                          "note": "time covers the append and the attention kernel"}}
@@ -407,8 +429,9 @@ def profile_only(args):
     """A short run of one kernel, for rocprofv3 (no JSON contract)."""
     import torch
     from grouped_query_attention_gqa_amd import workloads as W
-    if args.only == "prefill":
-        r = bench_prefill(W.WORKLOADS["causal_prefill_4k"], args.steps, args.warmup)
+    if args.only in ("prefill", "chunked"):
+        name = "causal_prefill_4k" if args.only == "prefill" else "chunked_prefill_paged"
+        r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup)
         print(json.dumps(r), flush=True)
         return
     if args.only == "copy":
@@ -421,7 +444,8 @@ def profile_only(args):
         print(json.dumps({"copy_bytes": COPY_BYTES, "copies": args.steps}), flush=True)
         return
     name = {"decode": "llama3_8b_decode", "decode70b": "llama2_70b_decode", "paged": "paged_long_decode",
-            "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa"}[args.only]
+            "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa",
+            "window": "mistral_7b_window_decode"}[args.only]
     db = DecodeBench(W.WORKLOADS[name])
     mean_ms, med_ms = time_decode_only(db, args.steps, args.warmup)
     print(json.dumps({"workload": name, "decode_us": round(mean_ms * 1e3, 2),

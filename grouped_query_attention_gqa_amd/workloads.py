@@ -51,6 +51,8 @@ class Workload:
     value_scale: float = 1.0
     paged: bool = False
     block_size: int = BLOCK_SIZE
+    window: int = 0         # > 0: sliding-window attention over the last `window` positions
+    start: int = 0          # prefill: tokens already in the cache before the new ones
     description: str = ""
 
     @property
@@ -65,7 +67,7 @@ class Workload:
     def S_max(self) -> int:
         """Cache capacity per sequence (the largest context the workload allows)."""
         if self.kind == "prefill":
-            return self.s
+            return self.start + self.s
         return int(self.ctx[-1])
 
     def replace(self, **kw) -> "Workload":
@@ -104,6 +106,20 @@ WORKLOADS = {
         ctx=("loguniform", 512, 32768), paged=True,
         description="paged decode, bf16, B=64 H=64 K=8 d=128, ctx log-uniform in "
                     "[512,32768], 16-token blocks, shuffled block table"),
+    # the two steps beside the hot path: a sliding-window decode with the
+    # window the inference-optimisation page (§6.4.1) gives for Mistral 7B,
+    # and a chunk of new tokens prefilled after a cached prefix into a paged
+    # cache (§11.7's chunked prefill)
+    "mistral_7b_window_decode": Workload(
+        "mistral_7b_window_decode", "decode", "bf16", B=32, H=32, K=8, d=128, seed=1006,
+        ctx=("fixed", 16384), window=4096,
+        description="Mistral-7B-shaped sliding-window decode, bf16, B=32 H=32 K=8 d=128, ctx = 16384, "
+                    "window 4096"),
+    "chunked_prefill_paged": Workload(
+        "chunked_prefill_paged", "prefill", "bf16", B=4, H=32, K=8, d=128, seed=1007, s=512, start=3584,
+        value_scale=0.5, paged=True,
+        description="chunked prefill, bf16, B=4 H=32 K=8 d=128: 512 new tokens after a 3584-token cached "
+                    "prefix, 16-token paged cache"),
 }
 
 
@@ -288,7 +304,7 @@ def make_prefill(wl: Workload) -> PrefillInputs:
     if wl.kind != "prefill":
         raise ValueError("not a prefill workload")
     rng = np.random.Generator(np.random.PCG64(wl.seed))
-    start = np.zeros(wl.B, dtype=np.int32)
+    start = np.full(wl.B, wl.start, dtype=np.int32)
     q = _normal(rng, (wl.B, wl.s, wl.H, wl.d), wl.dtype, wl.value_scale)
     kn = _normal(rng, (wl.B, wl.s, wl.K, wl.d), wl.dtype, wl.value_scale)
     vn = _normal(rng, (wl.B, wl.s, wl.K, wl.d), wl.dtype, wl.value_scale)
