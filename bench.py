@@ -148,8 +148,14 @@ class DecodeBench:
 def time_decode_only(db: DecodeBench, iters: int, warmup: int):
     """Average decode kernel time (ms) from HIP events on the launch stream."""
     import torch
-    for i in range(warmup):
+    # warm-up: at least `warmup` calls and ~0.2 s of work (see bench_prefill)
+    t_end = time.perf_counter() + 0.2
+    i = 0
+    while i < warmup or time.perf_counter() < t_end:
         db.decode(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for i, (a, b) in enumerate(evs):
@@ -404,8 +410,15 @@ def bench_prefill(wl, iters, warmup):
         vc = torch.zeros_like(kc)
         cache = binding.KVCache(kc, vc)
     out = torch.empty_like(q)
-    for _ in range(warmup):
+    # warm-up: at least `warmup` calls and ~0.3 s of work, so that the
+    # clocks have left the idle state the host-side input generation leaves
+    t_end = time.perf_counter() + 0.3
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
         binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale, window=wl.window)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for a, b in evs:
