@@ -2,14 +2,16 @@
 """Benchmark of the grouped-query attention hot path on one MI355X.
 
 A step is one decode step of the Llama-3-8B-shaped workload (B=32, H=32,
-K=8, d=128, bf16, contexts drawn from U[1024, 4096]): gqa_kv_append of every
-sequence's newest token, then gqa_decode over the whole cache.  `value` is
-the step's algorithmic bytes (the K/V rows every query must read once, plus
-Q, O and the appended rows) divided by the step time, in GB/s.
+K=8, d=128, bf16, contexts drawn from U[1024, 4096]): gqa_decode_step, which
+appends every sequence's newest token and attends over the whole cache in
+one call.  `value` is the step's algorithmic bytes (the K/V rows every query
+must read once, plus Q, O and the appended rows) divided by the step time,
+in GB/s.
 
 The same JSON line also carries
-  * roofline: the decode kernel alone (HBM bound), timed with HIP events on
-    the stream it runs on, against MI355X's 8 TB/s;
+  * roofline: the decode step's kernels (HBM bound), timed with HIP events on
+    the stream they run on, against MI355X's 8 TB/s; two_call_step: the same
+    step as gqa_kv_append followed by gqa_decode, for comparison;
   * prefill: the causal prefill workload (B=4, s=4096, H=32, K=8, d=128,
     bf16, append included) in TFLOP/s against the 2.5 PFLOP/s dense bf16
     matrix-core peak;
@@ -41,7 +43,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 # gqa_decode is the main kernel plus the small merge of cut items; events time both
-DECODE_KERNELS = "decode_waves_kernel<128, 4> + merge_pieces_kernel<128, true> (one gqa_decode call)"
+DECODE_KERNELS = ("decode_waves_kernel<128, 4> (with the append of the newest token) + merge_pieces_kernel<128, true> "
+                  "(one gqa_decode_step call)")
 DECODE_SOURCES = ("decode_waves.hip", "stream_attention.hip", "worklist.h", "kernels.h", "common.h")
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "GQA decode HBM GB/s (% of peak) + causal prefill TFLOP/s (% MFMA peak), bf16"
@@ -61,7 +64,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel: decode|prefill|decode70b|paged|mha|mqa|window|chunked|"
+                    help="profile one kernel: decode|step|prefill|decode70b|paged|mha|mqa|window|chunked|"
                          "copy (a 512 MiB device copy)")
     ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
     return ap.parse_args()
@@ -139,20 +142,28 @@ class DecodeBench:
         from grouped_query_attention_gqa_amd import binding
         binding.gqa_kv_append(self.caches[i % len(self.caches)], self.k_new, self.v_new, self.start)
 
+    def step(self, i):
+        from grouped_query_attention_gqa_amd import binding
+        binding.gqa_decode_step(self.q, self.k_new, self.v_new, self.caches[i % len(self.caches)], self.ctx_d,
+                                self.max_ctx, out=self.out, scale=self.wl.scale, workspace=self.ws,
+                                window=self.wl.window)
+
     def decode(self, i):
         from grouped_query_attention_gqa_amd import binding
         binding.gqa_decode(self.q, self.caches[i % len(self.caches)], self.ctx_d, self.max_ctx, out=self.out,
                            scale=self.wl.scale, workspace=self.ws, window=self.wl.window)
 
 
-def time_decode_only(db: DecodeBench, iters: int, warmup: int):
-    """Average decode kernel time (ms) from HIP events on the launch stream."""
+def time_decode_only(db: DecodeBench, iters: int, warmup: int, call=None):
+    """Average decode kernel time (ms) from HIP events on the launch stream
+    (`call`: DecodeBench.decode by default, or DecodeBench.step)."""
     import torch
+    call = db.decode if call is None else call
     # warm-up: at least `warmup` calls and ~0.2 s of work (see bench_prefill)
     t_end = time.perf_counter() + 0.2
     i = 0
     while i < warmup or time.perf_counter() < t_end:
-        db.decode(i)
+        call(i)
         i += 1
         if i % 8 == 0:
             torch.cuda.synchronize()
@@ -160,7 +171,7 @@ def time_decode_only(db: DecodeBench, iters: int, warmup: int):
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
     for i, (a, b) in enumerate(evs):
         a.record()
-        db.decode(i)
+        call(i)
         b.record()
     torch.cuda.synchronize()
     ts = [a.elapsed_time(b) for a, b in evs]
@@ -313,26 +324,42 @@ def main():
     wl = W.WORKLOADS["llama3_8b_decode"]
     db = DecodeBench(wl)
     step_bytes = db.alg_bytes + append_bytes(wl, 1)
-    for i in range(args.warmup):
-        db.append(i)
-        db.decode(i)
+    # warm-up: at least `warmup` steps and ~0.2 s of work (see bench_prefill)
+    t_end = time.perf_counter() + 0.2
+    i = 0
+    while i < args.warmup or time.perf_counter() < t_end:
+        db.step(i)
+        i += 1
+        if i % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    # the timed steps: wall clock over exactly `steps` calls
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        db.step(i)
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    # the kernels' own time: HIP events around each call on its stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for i in range(args.steps):
+        ev[i][0].record()
+        db.step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = step_bytes / (dec_ms * 1e-3) / 1e9
+    traffic = committed_traffic("decode/llama3_8b_decode")
+    log(f"decode step {ms_step * 1e3:.1f} us ({value:.0f} GB/s); step kernels {dec_ms * 1e3:.1f} us "
+        f"({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of peak)")
+    # the same step as two calls (append, then decode), timed the same way
     t0 = time.perf_counter()
     for i in range(args.steps):
         db.append(i)
-        ev[i][0].record()
         db.decode(i)
-        ev[i][1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-    achieved = db.alg_bytes / (dec_ms * 1e-3) / 1e9
-    traffic = committed_traffic("decode/llama3_8b_decode")
-    log(f"decode step {ms_step * 1e3:.1f} us ({value:.0f} GB/s); decode kernel {dec_ms * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s, {100 * achieved / HBM_PEAK_GBS:.1f}% of peak)")
+    two_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    log(f"two-call step (append, then decode) {two_ms * 1e3:.1f} us")
 
     result = {
         "metric": METRIC,
@@ -349,11 +376,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "K": wl.K, "d": wl.d,
                    "ctx": "U[1024,4096] per sequence", "sum_ctx": int(db.ctx.sum()),
-                   "step": "gqa_kv_append (newest token) + gqa_decode", "parallelism": "single GPU"},
+                   "step": "gqa_decode_step (append of the newest token + decode, one call)",
+                   "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": DECODE_KERNELS,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": db.alg_bytes, "avg_launch_us": round(dec_ms * 1e3, 2)},
+                     "bytes_per_launch": step_bytes, "avg_launch_us": round(dec_ms * 1e3, 2)},
+        "two_call_step": {"us": round(two_ms * 1e3, 2), "GB/s": round(step_bytes / (two_ms * 1e-3) / 1e9, 1),
+                          "calls": "gqa_kv_append + gqa_decode"},
     }
     del db
     torch.cuda.empty_cache()
@@ -456,11 +486,11 @@ def profile_only(args):
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": COPY_BYTES, "copies": args.steps}), flush=True)
         return
-    name = {"decode": "llama3_8b_decode", "decode70b": "llama2_70b_decode", "paged": "paged_long_decode",
-            "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa",
+    name = {"decode": "llama3_8b_decode", "step": "llama3_8b_decode", "decode70b": "llama2_70b_decode",
+            "paged": "paged_long_decode", "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa",
             "window": "mistral_7b_window_decode"}[args.only]
     db = DecodeBench(W.WORKLOADS[name])
-    mean_ms, med_ms = time_decode_only(db, args.steps, args.warmup)
+    mean_ms, med_ms = time_decode_only(db, args.steps, args.warmup, db.step if args.only == "step" else None)
     print(json.dumps({"workload": name, "decode_us": round(mean_ms * 1e3, 2),
                       "GB/s": round(db.alg_bytes / (mean_ms * 1e-3) / 1e9, 1), "bytes": db.alg_bytes}), flush=True)
 

@@ -26,7 +26,7 @@ GQA_F32, GQA_BF16 = 0, 1
 EXPORTED_SYMBOLS = (
     "gqa_abi_version", "gqa_status_string", "gqa_cache_elems_per_token",
     "gqa_kv_append", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_prefill",
-    "gqa_decode_window", "gqa_prefill_window",
+    "gqa_decode_window", "gqa_prefill_window", "gqa_decode_step",
 )
 
 
@@ -84,6 +84,8 @@ def load_library():
         lib.gqa_prefill.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp]
         lib.gqa_decode_window.restype = i32
         lib.gqa_decode_window.argtypes = [vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
+        lib.gqa_decode_step.restype = i32
+        lib.gqa_decode_step.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
         lib.gqa_prefill_window.restype = i32
         lib.gqa_prefill_window.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
         if lib.gqa_abi_version() != 1:
@@ -242,6 +244,39 @@ def gqa_decode(q: torch.Tensor, cache: KVCache, ctx_lens: torch.Tensor, max_ctx:
         st = lib.gqa_decode(_ptr(q), cache.struct, _ptr(ctx_lens), int(max_ctx), B, H, ctypes.c_float(scale),
                             _ptr(out), _ptr(workspace), ws_bytes, hs)
     _check(st, "gqa_decode")
+    return out
+
+
+def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: KVCache,
+                    ctx_lens: torch.Tensor, max_ctx: int, out: Optional[torch.Tensor] = None,
+                    scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None, stream=None,
+                    window: int = 0) -> torch.Tensor:
+    """Append the newest token k_new/v_new [B,1,K,d] at position ctx_lens[b] - 1 and
+    decode q [B,1,H,d] against the first ctx_lens[b] cached tokens, in one call."""
+    _need(q, "q", dtype=cache.dtype, dim=4)
+    _need(k_new, "k_new", dtype=cache.dtype, dim=4)
+    _need(v_new, "v_new", dtype=cache.dtype, dim=4)
+    _need(ctx_lens, "ctx_lens", dtype=torch.int32, dim=1)
+    B, one, H, d = q.shape
+    if one != 1 or d != cache.head_dim or ctx_lens.shape[0] != B:
+        raise ValueError("decode shapes disagree with the cache")
+    if k_new.shape != (B, 1, cache.num_kv_heads, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new / v_new must be [B, 1, K, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, dim=4)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    nbytes = int(lib.gqa_decode_workspace_bytes(B, H, cache.num_kv_heads, d, int(max_ctx)))
+    hs = _stream(stream)
+    if workspace is None and nbytes > 0:
+        workspace = _default_workspace(q.device, hs.value or 0, nbytes)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gqa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), cache.struct, _ptr(ctx_lens), int(max_ctx), B, H,
+                             ctypes.c_float(scale), int(window), _ptr(out), _ptr(workspace), ws_bytes, hs)
+    _check(st, "gqa_decode_step")
     return out
 
 

@@ -219,6 +219,16 @@ gqa_status gqa_decode_window(const void *q, const gqa_kv_cache *cache, const int
                              int32_t max_ctx, int32_t B, int32_t num_heads, float scale, int32_t window,
                              void *out, void *workspace, size_t workspace_bytes, void *stream)
 {
+    return gqa_decode_step(q, nullptr, nullptr, cache, ctx_lens, max_ctx, B, num_heads, scale, window, out,
+                           workspace, workspace_bytes, stream);
+}
+
+gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, const gqa_kv_cache *cache,
+                           const int32_t *ctx_lens, int32_t max_ctx, int32_t B, int32_t num_heads, float scale,
+                           int32_t window, void *out, void *workspace, size_t workspace_bytes, void *stream)
+{
+    // k_new == v_new == nullptr: the plain decode (gqa_decode_window)
+    const bool step = k_new != nullptr || v_new != nullptr;
     CacheView v;
     gqa_status st = make_view(cache, &v);
     if (st != GQA_OK) return st;
@@ -226,6 +236,7 @@ gqa_status gqa_decode_window(const void *q, const gqa_kv_cache *cache, const int
     if (B < 0) return fail(GQA_ERR_INVALID_ARG, "B negative");
     if (B == 0) return GQA_OK;
     if (!q || !out || !ctx_lens) return fail(GQA_ERR_INVALID_ARG, "NULL q/out/ctx_lens");
+    if (step && (!k_new || !v_new)) return fail(GQA_ERR_INVALID_ARG, "NULL k_new or v_new");
     if (max_ctx <= 0) return fail(GQA_ERR_INVALID_ARG, "max_ctx <= 0");
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
     DecodeLayout L;
@@ -260,8 +271,25 @@ gqa_status gqa_decode_window(const void *q, const gqa_kv_cache *cache, const int
     p.window = window > 0 ? window : 0;
     p.num_wgs = kStreamWGs;
     p.scale_log2 = scale * 1.4426950408889634f;
-    return launch_status(launch_row_attention(p, pow2_at_least(p.G), static_cast<hipStream_t>(stream)),
-                         "decode");
+    const hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (step) {
+        // the fused kernel writes the new rows itself and reads them from
+        // k_new / v_new; every other path appends first
+        p.k_new = static_cast<const char *>(k_new);
+        p.v_new = static_cast<const char *>(v_new);
+        if (!decode_waves_supported(p, pow2_at_least(p.G))) {
+            AppendParams ap{};
+            ap.cache = v;
+            ap.k_new = p.k_new;
+            ap.v_new = p.v_new;
+            ap.ctx_lens = ctx_lens;
+            ap.B = B;
+            ap.s_new = 1;
+            if ((st = launch_status(launch_kv_append(ap, hs), "decode step append")) != GQA_OK) return st;
+            p.k_new = p.v_new = nullptr;
+        }
+    }
+    return launch_status(launch_row_attention(p, pow2_at_least(p.G), hs), "decode");
 }
 
 gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,

@@ -100,6 +100,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     __shared__ int32_t lds_prefix[kStreamRows + 1];
     __shared__ int32_t lds_nvis[kStreamRows];
     __shared__ int32_t lds_first[kStreamRows];
+    __shared__ int32_t lds_newest[kStreamRows];
     __shared__ int lds_waves[NW];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -107,14 +108,53 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     const CacheView &cache = p.cache;
     const int G = p.G, H = p.H;
 
+    // ---- decode step: the newest token's K/V rows into the cache ----------
+    // The same bytes and the same skips as the append kernel.  This launch
+    // never reads those cache rows (it takes the token from k_new / v_new),
+    // so the copy only has to be done somewhere in it: thread (item, K or V,
+    // 16-byte piece) loads its piece now and stores it once the first tiles
+    // are on their way; further items, if any, are copied at the end.
+    constexpr int IPW = NT / (2 * C::CPR);   // items per workgroup pass
+    const int64_t cp_items = p.k_new != nullptr ? (int64_t)p.rows * cache.K : 0;
+    const int64_t cp_stride = (int64_t)gridDim.x * IPW;
+    const int64_t cp_first = (int64_t)blockIdx.x * IPW + tid / (2 * C::CPR);
+    auto copy_dst = [&](int64_t it, int64_t &src) -> char * {
+        const int which = (tid / C::CPR) & 1, piece = tid % C::CPR;
+        const int b = (int)(p.row0 + it / cache.K), g = (int)(it % cache.K);
+        const int pos = p.ctx_lens[b] - 1;
+        if (pos < 0 || pos >= cache.capacity) return nullptr;
+        const int64_t row = cache_row(cache, b, g, pos);
+        if (row < 0) return nullptr;
+        src = ((int64_t)b * cache.K + g) * C::RB + piece * 16 + (which ? p.v_new - p.k_new : 0);
+        return (which ? cache.v : cache.k) + row * C::RB + piece * 16;
+    };
+    auto copy_rest = [&]() {
+        for (int64_t it = cp_first + cp_stride; it < cp_items; it += cp_stride) {
+            int64_t src = 0;
+            char *dst = copy_dst(it, src);
+            if (dst != nullptr) st16(dst, ld16(p.k_new + src));
+        }
+    };
+    char *cp_to = nullptr;
+    uint4 cp_val = make_uint4(0u, 0u, 0u, 0u);
+    if (cp_first < cp_items) {
+        int64_t src = 0;
+        cp_to = copy_dst(cp_first, src);
+        if (cp_to != nullptr) cp_val = ld16(p.k_new + src);
+    }
+
     // ---- the flat tile list and this workgroup's slice ---------------------
-    build_tables<NT>(p, C::TT, lds_prefix, lds_nvis, lds_first, lds_waves);
+    build_tables<NT>(p, C::TT, lds_prefix, lds_nvis, lds_first, lds_waves, p.k_new != nullptr ? lds_newest : nullptr);
     if (blockIdx.x == 0 && p.prefix != nullptr)   // the merge kernel reads it from the workspace
         for (int r = tid; r <= p.rows; r += NT) p.prefix[r] = lds_prefix[r];
     const int T = lds_prefix[p.rows];
     const int64_t W = gridDim.x;
     const int tau0 = (int)slice_start(blockIdx.x, T, W), tau1 = (int)slice_start(blockIdx.x + 1, T, W);
-    if (tau0 >= tau1) return;
+    if (tau0 >= tau1) {   // an empty slice (fewer tiles than workgroups)
+        if (cp_to != nullptr) st16(cp_to, cp_val);
+        copy_rest();
+        return;
+    }
 
     // K loads: lane = (row krow, 16-byte chunk kc); score phase: lane = (key
     // st, head set sh); V phase: lane = (row vr, 8-byte chunk vc: columns 4 vc ..)
@@ -135,6 +175,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         int64_t row_g;    // query row (sequence) of the item
         int b, g;         // sequence and KV group
         int n_vis;        // end of the item's visible keys
+        int new_key;      // decode step: the key read from k_new / v_new (-1: none)
         int lo, jlo;      // first visible key; its tile (the item's tile 0)
         int j_first;      // tile of the item at tau
         int tau, end;     // flat tile range
@@ -148,6 +189,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         sg.b = (int)(sg.row_g / p.Sq);
         sg.g = c.g;
         sg.n_vis = c.n_vis;
+        sg.new_key = p.k_new != nullptr ? lds_newest[c.row] : -1;
         sg.lo = c.lo;
         sg.jlo = c.jlo;
         sg.j_first = c.j;
@@ -171,12 +213,16 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         int64_t base[C::NGR];   // cache row of key 16 gi of the tile, -1: none
         int nvalid;             // keys of the tile below the end (<= 0: none)
         int first;              // first visible key of the tile
+        int new_row;            // tile row read from k_new / v_new (-1: none)
+        int64_t new_off;        // byte offset of that row in k_new / v_new
     };
-    auto tile_rows = [&](int lb, int lg, int l_lo, int l_nvis, int j) {
+    auto tile_rows = [&](int lb, int lg, int l_lo, int l_nvis, int l_new, int j) {
         TileRows t;
         const int key0 = j * C::TT;   // j: tile of the row
         t.nvalid = min(C::TT, l_nvis - key0);
         t.first = max(0, l_lo - key0);
+        t.new_row = l_new >= key0 && l_new < key0 + C::TT ? l_new - key0 : -1;
+        t.new_off = ((int64_t)lb * cache.K + lg) * C::RB;
 #pragma unroll
         for (int gi = 0; gi < C::NGR; ++gi)
             t.base[gi] = 16 * gi < t.nvalid && 16 * gi + 16 > t.first ? cache_row_wave(cache, lb, lg, key0 + 16 * gi) : -1;
@@ -190,7 +236,8 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             const int r0 = i * C::RPL;                       // first tile row of the load
             const int64_t base = t.base[r0 / 16];
             uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            if (base >= 0 && r0 + krow < t.nvalid) x = ld16(cache.k + (base + r0 % 16) * C::RB + k_off);
+            if (base >= 0 && r0 + krow < t.nvalid)
+                x = ld16(r0 + krow == t.new_row ? p.k_new + t.new_off + kc * 16 : cache.k + (base + r0 % 16) * C::RB + k_off);
             kr[i] = x;
         }
     };
@@ -201,7 +248,8 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             const int64_t base = t.base[r0 / 16];
             uint2 y = make_uint2(0u, 0u);
             if (base >= 0 && r0 + vr < t.nvalid)
-                y = *reinterpret_cast<const uint2 *>(cache.v + (base + r0 % 16) * C::RB + v_off);
+                y = *reinterpret_cast<const uint2 *>(r0 + vr == t.new_row ? p.v_new + t.new_off + vc * 8
+                                                                          : cache.v + (base + r0 % 16) * C::RB + v_off);
             vv[i] = y;
         }
     };
@@ -222,6 +270,8 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         for (int gi = 0; gi < C::NGR; ++gi) t.base[gi] = -1;
         t.nvalid = 0;
         t.first = 0;
+        t.new_row = -1;
+        t.new_off = 0;
         return t;
     };
     auto stream_from = [&](int at, TileRows &t1, TileRows &t2) {
@@ -231,7 +281,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         while (at < tau1 && found < C::KD) {
             const Seg sg = make_seg(at);
             for (int k = 0; k < sg.n_w && found < C::KD; ++k, ++found) {
-                const TileRows t = tile_rows(sg.b, sg.g, sg.lo, sg.n_vis, sg.jlo + sg.j_first + wave + NW * k);
+                const TileRows t = tile_rows(sg.b, sg.g, sg.lo, sg.n_vis, sg.new_key, sg.jlo + sg.j_first + wave + NW * k);
                 if (found == 0) t1 = t;
                 else t2 = t;
             }
@@ -255,6 +305,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         load_k(r1, kA);
         if constexpr (C::KD == 2) load_k(r2, kB);
         if (q_thread) *reinterpret_cast<uint4 *>(lds_q + q_r * C::RB + q_ch * 16) = x;
+        if (cp_to != nullptr) st16(cp_to, cp_val);
         __syncthreads();
     }
     for (;;) {
@@ -304,7 +355,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             const TileRows rows = r1;   // tile i
             // rows of the tile KD steps ahead in the stream
             const int ia = i + C::KD;
-            const TileRows ra = ia < n_w ? tile_rows(cur.b, cur.g, cur.lo, cur.n_vis, cur.jlo + cur.j_first + wave + NW * ia)
+            const TileRows ra = ia < n_w ? tile_rows(cur.b, cur.g, cur.lo, cur.n_vis, cur.new_key, cur.jlo + cur.j_first + wave + NW * ia)
                                          : (ia == n_w ? after1 : after2);
             // K(i) -> this wave's LDS buffer (padded rows); start K(i + KD) in its place
             auto k_step = [&](uint4 (&kx)[C::NL]) {
@@ -442,6 +493,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         __syncthreads();   // the merge area is free again and the next q is in place
         cur = nxt;
     }
+    copy_rest();
 }
 
 template <int D, int GP>

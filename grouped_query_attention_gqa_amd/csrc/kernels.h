@@ -28,6 +28,7 @@ struct AppendParams {
     const char *k_new;          // [B, s_new, K, d]
     const char *v_new;
     const int32_t *start_pos;   // [B]
+    const int32_t *ctx_lens;    // non-null: one token per sequence at position ctx_lens[b] - 1 (start_pos unused)
     int32_t B;
     int32_t s_new;
 };
@@ -43,6 +44,8 @@ struct RowAttnParams {
     char *out;                  // [B, Sq, H, d]
     const int32_t *ctx_lens;    // decode: [B] keys per sequence
     const int32_t *start_pos;   // prefill: [B] position of query row 0
+    const char *k_new;          // decode step: [B, 1, K, d] newest token, at position ctx_lens[b] - 1 (or null)
+    const char *v_new;
     int32_t *prefix;            // workspace: [kStreamRows + 1] tile prefix of the launch
     float *ws_o;                // workspace: [W, 2, G, d] partial outputs (unnormalised)
     float *ws_ml;               // workspace: [W, 2, G, 2] partial (max, sum), log2 units

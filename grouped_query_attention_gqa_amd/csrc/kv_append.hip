@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p)
     const int t = (int)(r % p.s_new);
     const int b = (int)(r / p.s_new);
 
-    const int64_t pos = (int64_t)p.start_pos[b] + t;
+    const int64_t pos = p.ctx_lens != nullptr ? (int64_t)p.ctx_lens[b] - 1 : (int64_t)p.start_pos[b] + t;
     if (pos < 0 || pos >= c.capacity) return;
     int64_t dst_row;
     if (c.block_table == nullptr) {

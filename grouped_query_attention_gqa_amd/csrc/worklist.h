@@ -57,9 +57,11 @@ __device__ __forceinline__ int item_tiles(int lo, int n, int tt) { return n > lo
 // prefix[rows] = the number of tiles T.  Every thread of the workgroup calls
 // it; thread i handles the consecutive rows i*per .. i*per+per-1, so any row
 // count up to kStreamRows is covered whatever the workgroup size.
+// With `newest` (decode step only), newest[r] is the key of the row's newest
+// token, ctx - 1, or -1 when it lies past the cache capacity.
 template <int NT>
 __device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, int32_t *nvis, int32_t *first,
-                             int *lds_waves)
+                             int *lds_waves, int32_t *newest = nullptr)
 {
     static_assert(kStreamRows % NT == 0, "rows per thread");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -74,6 +76,10 @@ __device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, in
             const int lo = row_first(p, p.row0 + r, n);
             nvis[r] = n;
             first[r] = lo;
+            if (newest != nullptr) {
+                const int raw = p.ctx_lens[p.row0 + r];
+                newest[r] = raw >= 1 && raw <= p.cache.capacity ? raw - 1 : -1;
+            }
             local += item_tiles(lo, n, tt);
         }
     }

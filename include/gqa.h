@@ -182,6 +182,27 @@ gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_ne
                               int32_t num_heads, float scale, int32_t causal, int32_t window, void *out,
                               void *stream);
 
+/*
+ * One whole decode step: append the newest token's K/V and attend to the
+ * cache including it.  The result and the cache bytes are exactly those of
+ * gqa_kv_append(cache, k_new, v_new, start_pos = ctx_lens - 1, B, 1) followed
+ * by gqa_decode_window(...) (the concept page, 技术原理: each new token's
+ * K/V joins the cache, then its query attends to all cached keys).
+ *   k_new, v_new: device [B, 1, K, d] (cache dtype), the token at position
+ *                 ctx_lens[b] - 1 of sequence b
+ *   window: as for gqa_decode_window (<= 0: no window)
+ * For bf16 with G <= 8 one kernel does both: it reads the new token from
+ * k_new / v_new and writes it into the cache in the same launch; the other
+ * cases launch the append first.  A position at or past the cache capacity,
+ * or whose block id is outside the pool, is not written (as in
+ * gqa_kv_append).  All other arguments, layouts, ownership and errors are
+ * those of gqa_decode; k_new and v_new must both be given
+ * (GQA_ERR_INVALID_ARG otherwise).
+ */
+gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, const gqa_kv_cache *cache,
+                           const int32_t *ctx_lens, int32_t max_ctx, int32_t B, int32_t num_heads, float scale,
+                           int32_t window, void *out, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -131,3 +131,14 @@ def test_append_and_prefill_reject_bad_args(lib):
     assert pf(_cache(), s=0) == binding.GQA_OK
     assert lib.gqa_prefill(FAKE, FAKE, None, ctypes.byref(_cache()), FAKE, 1, 4, 8, ctypes.c_float(0.1), 1, FAKE,
                            None) == binding.GQA_ERR_INVALID_ARG
+
+
+def test_decode_step_rejects_bad_args(lib):
+    c = _cache()
+    step = lambda kn, vn, B=1, H=8: lib.gqa_decode_step(FAKE, kn, vn, ctypes.byref(c), FAKE, 128, B, H,
+                                                        ctypes.c_float(0.125), 0, FAKE, None, 0, None)
+    assert step(FAKE, None) == binding.GQA_ERR_INVALID_ARG      # both new rows or neither
+    assert step(None, FAKE) == binding.GQA_ERR_INVALID_ARG
+    assert step(FAKE, FAKE, H=7) == binding.GQA_ERR_INVALID_ARG
+    assert step(FAKE, FAKE) == binding.GQA_ERR_WORKSPACE          # checked before any launch
+    assert step(FAKE, FAKE, B=0) == binding.GQA_OK
