@@ -76,6 +76,14 @@ def _load():
         lib.oracle_gather_paged_raw.argtypes = [vp, i32, vp, i32, i32, i32, vp, i32, i32, i32, i32, vp]
         lib.oracle_gather_paged.restype = i64
         lib.oracle_gather_paged.argtypes = [vp, vp, i32, i32, i32, vp, i32, i32, i32, i32, vp]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_from_float.restype = ctypes.c_uint8
+        lib.oracle_e4m3_from_float.argtypes = [ctypes.c_float]
+        lib.oracle_quantize_e4m3_rows.restype = None
+        lib.oracle_quantize_e4m3_rows.argtypes = [vp, i64, i32, vp, vp]
+        lib.oracle_dequantize_e4m3_rows.restype = None
+        lib.oracle_dequantize_e4m3_rows.argtypes = [vp, vp, i64, i32, vp]
         _lib = lib
         return lib
 
@@ -254,3 +262,43 @@ def paged_attention_rows(q, pool_k, pool_v, block_table, ctx_lens, scale, rows_p
         outs.append(o)
         rows.append(np.array([[b, 0, h] for h in range(H)], dtype=np.int32))
     return np.concatenate(rows), np.concatenate(outs)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV cache, one fp32 scale per cached row (inference-optimisation
+# page §15.5.1: per-token / per-head scales, FP8 E4M3)
+# ---------------------------------------------------------------------------
+
+def e4m3_value(code: int) -> float:
+    """The value of one E4M3 code (NaN for the two NaN codes)."""
+    return float(_load().oracle_e4m3_value(int(code) & 0xFF))
+
+
+def e4m3_from_float(x: float) -> int:
+    """The E4M3 code nearest to the fp32 value x (ties to even, saturating)."""
+    return int(_load().oracle_e4m3_from_float(ctypes.c_float(float(x))))
+
+
+def quantize_e4m3_rows(x: np.ndarray):
+    """Rows x[..., d] (fp32 values; bf16 bits may be given as uint16) -> (codes
+    uint8 [..., d], scales float32 [...]): scale = amax / 448 and codes the
+    nearest E4M3 values of x / scale, both decided in fp32."""
+    if x.dtype == np.uint16:
+        x = (x.astype(np.uint32) << 16).view(np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    rows = x.size // d if d else 0
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    _load().oracle_quantize_e4m3_rows(_ptr(x), rows, d, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequantize_e4m3_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """scale[r] * E4M3(codes[r, i]) in fp64 (exact)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    d = codes.shape[-1]
+    out = np.empty(codes.shape, dtype=np.float64)
+    _load().oracle_dequantize_e4m3_rows(_ptr(codes), _ptr(scales), codes.size // d if d else 0, d, _ptr(out))
+    return out

@@ -329,3 +329,89 @@ int64_t oracle_gather_paged(const double *pool, const int32_t *block_table, int 
             }
     return bad;
 }
+
+/* ---------------------------------------------------------------------- */
+/* FP8 (E4M3) KV cache with one scale per cached row                      */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * The inference-optimisation page, §15.5-§15.5.1, lists for K/V quantisation
+ * a scale computed for every token (per-token) or every head (per-head), and
+ * FP8 E4M3 as the format whose exponent copes with the long-tailed K/V
+ * values.  Reading: one fp32 scale per cached row (one token of one KV head),
+ * scale = amax / 448 with 448 the largest finite E4M3 value, and every
+ * element stored as the E4M3 value nearest to x / scale (ties to the even
+ * code).  The decisions are taken in fp32 (the scale and each quotient are
+ * IEEE fp32 divisions), the precision the device takes them in, so codes
+ * and scales can be compared bit for bit.  A row that is all zero has
+ * scale 0 and all-zero codes.
+ *
+ * E4M3 here is the OCP 8-bit format: 1 sign bit, 4 exponent bits with bias
+ * 7, 3 mantissa bits; exponent field 0 holds the subnormals m * 2^-9;
+ * there are no infinities and S.1111.111 is NaN, so the largest finite
+ * magnitude is 1.75 * 2^8 = 448.
+ */
+double oracle_e4m3_value(uint8_t code)
+{
+    const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const double mag = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -mag : mag;
+}
+
+/* The E4M3 code nearest to x (ties to even), saturating at +-448. */
+uint8_t oracle_e4m3_from_float(float x)
+{
+    const uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs((double)x);
+    if (isnan(x)) return 0x7F;
+    if (a >= 448.0) return sign | 0x7E;   /* satfinite */
+    /* the spacing of E4M3 values around a: 2^-9 below 2^-6 (subnormals),
+     * else 2^(floor(log2 a) - 3) */
+    int ex = 0;
+    if (a > 0) frexp(a, &ex);             /* a = f * 2^ex, f in [0.5, 1) */
+    const int e_unb = ex - 1;             /* floor(log2 a) */
+    const int step_exp = e_unb < -6 ? -9 : e_unb - 3;
+    const double n = rint(ldexp(a, -step_exp));   /* round half to even (default mode) */
+    double v = ldexp(n, step_exp);
+    if (v > 448.0) v = 448.0;
+    if (v == 0.0) return sign;
+    /* encode v exactly */
+    if (v < ldexp(1.0, -6)) return sign | (uint8_t)ldexp(v, 9);
+    frexp(v, &ex);
+    const int e = ex - 1;                 /* v = (1 + m/8) * 2^e */
+    const int m = (int)(ldexp(v, -e) * 8.0) - 8;
+    return sign | (uint8_t)(((e + 7) << 3) | m);
+}
+
+/*
+ * Quantise rows of d fp32 values (bf16 values are exact in fp32):
+ * codes[r, i] = E4M3(x[r, i] / scale[r]), scale[r] = amax_r / 448 (fp32).
+ */
+void oracle_quantize_e4m3_rows(const float *x, int64_t rows, int d, uint8_t *codes, float *scales)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = x + r * d;
+        float amax = 0.0f;
+        for (int i = 0; i < d; ++i) {
+            const float a = fabsf(xr[i]);
+            if (a > amax) amax = a;
+        }
+        const float scale = amax / 448.0f;
+        scales[r] = scale;
+        for (int i = 0; i < d; ++i) {
+            if (amax == 0.0f) { codes[r * d + i] = 0; continue; }
+            const float q = xr[i] / scale;
+            codes[r * d + i] = oracle_e4m3_from_float(q);
+        }
+    }
+}
+
+/* The values a quantised row stands for: scale[r] * E4M3(codes[r, i]),
+ * exact in fp64. */
+void oracle_dequantize_e4m3_rows(const uint8_t *codes, const float *scales, int64_t rows, int d, double *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int i = 0; i < d; ++i)
+            out[r * d + i] = (double)scales[r] * oracle_e4m3_value(codes[r * d + i]);
+}

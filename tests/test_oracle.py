@@ -466,3 +466,98 @@ def _pins_pass(ref):
 def test_planted_mistakes_are_caught(kind):
     assert _pins_pass(_mutant("none"))
     assert not _pins_pass(_mutant(kind))
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) KV cache: one fp32 scale per cached row (inference-optimisation
+# page §15.5.1: per-token and per-head scales, FP8 E4M3)
+# ---------------------------------------------------------------------------
+
+def _torch_e4m3_values() -> np.ndarray:
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_code_values_match_torch(oracle_lib):
+    """Every one of the 256 codes decodes as torch's float8_e4m3fn does."""
+    want = _torch_e4m3_values()
+    got = np.array([oracle.e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = np.isfinite(want)
+    assert np.array_equal(got[fin], want[fin])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_e4m3_rounding_matches_torch(oracle_lib):
+    """Nearest value, ties to even: the same codes as torch's fp32 -> float8_e4m3fn cast
+    on random values of every magnitude, on every midpoint and on every code value."""
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * s for s in (1e-3, 0.05, 1.0, 40.0, 300.0)])
+    x = x[np.abs(x) < 448]
+    vals = _torch_e4m3_values()
+    vals = np.unique(vals[np.isfinite(vals) & (vals >= 0)])
+    mids = ((vals[1:] + vals[:-1]) / 2).astype(np.float32)     # exact in fp32: the ties
+    x = np.concatenate([x, mids, -mids, vals.astype(np.float32), -vals.astype(np.float32)])
+    want = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.e4m3_from_float(v) for v in x], dtype=np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_saturates_at_448(oracle_lib):
+    assert oracle.e4m3_from_float(448.0) == 0x7E
+    assert oracle.e4m3_from_float(1000.0) == 0x7E
+    assert oracle.e4m3_from_float(-1e30) == 0xFE
+
+
+def _bf16_rows(rng, shape, scale=1.0):
+    x = (rng.standard_normal(shape).astype(np.float32) * scale)
+    return (((x.view(np.uint32) + 0x7FFF + ((x.view(np.uint32) >> 16) & 1)) >> 16) << 16).view(np.float32)
+
+
+def test_quantized_row_max_maps_to_448_and_error_is_bounded(oracle_lib):
+    """Per row: the largest magnitude becomes +-448, and every element comes back
+    within half an E4M3 step (relative 2^-4, or 2^-10 of the scale in the
+    subnormal range) of its value."""
+    rng = np.random.default_rng(6)
+    x = _bf16_rows(rng, (300, 128), 1.0) * rng.lognormal(0, 2, (300, 1)).astype(np.float32)
+    codes, scales = oracle.quantize_e4m3_rows(x)
+    assert codes.shape == x.shape and scales.shape == (300,)
+    amax = np.abs(x).max(axis=1)
+    assert np.array_equal(scales, (amax / np.float32(448)).astype(np.float32))
+    arg = np.abs(x).argmax(axis=1)
+    assert np.all((codes[np.arange(300), arg] & 0x7F) == 0x7E)
+    deq = oracle.dequantize_e4m3_rows(codes, scales)
+    err = np.abs(deq - x.astype(np.float64))
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, scales[:, None].astype(np.float64) * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(err <= bound)
+
+
+def test_quantization_is_per_row(oracle_lib):
+    """Scaling one row by a power of two scales only that row's scale and keeps
+    every code (the quotients x / scale do not change)."""
+    rng = np.random.default_rng(7)
+    x = _bf16_rows(rng, (6, 64))
+    c0, s0 = oracle.quantize_e4m3_rows(x)
+    y = x.copy()
+    y[2] *= np.float32(2.0 ** 5)
+    c1, s1 = oracle.quantize_e4m3_rows(y)
+    assert np.array_equal(c0, c1)
+    assert s1[2] == s0[2] * 2.0 ** 5
+    assert np.array_equal(np.delete(s1, 2), np.delete(s0, 2))
+
+
+def test_zero_row_has_zero_scale_and_codes(oracle_lib):
+    x = np.zeros((2, 64), dtype=np.float32)
+    x[1, 5] = 3.0
+    codes, scales = oracle.quantize_e4m3_rows(x)
+    assert scales[0] == 0 and not codes[0].any()
+    # the max comes back as 448 * fl32(3 / 448): within one fp32 rounding of 3
+    assert abs(oracle.dequantize_e4m3_rows(codes, scales)[1, 5] - 3.0) <= 3.0 * 2.0 ** -24
+
+
+def test_bf16_bits_input_is_the_same_as_fp32_values(oracle_lib):
+    rng = np.random.default_rng(8)
+    x = _bf16_rows(rng, (4, 128))
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    a = oracle.quantize_e4m3_rows(x)
+    b = oracle.quantize_e4m3_rows(bits)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
