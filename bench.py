@@ -16,8 +16,10 @@ The same JSON line also carries
     bf16, append included) in TFLOP/s against the 2.5 PFLOP/s dense bf16
     matrix-core peak;
   * decode_workloads: the other decode shapes (Llama-2-70B contiguous and its
-    MHA / MQA variants, paged long-context, and a Mistral-7B-shaped
-    sliding-window decode whose bytes count only the window) in GB/s;
+    MHA / MQA variants, paged long-context, a Mistral-7B-shaped
+    sliding-window decode whose bytes count only the window, and the
+    Llama-3-8B decode on an FP8 E4M3 cache with a scale per row, whose bytes
+    are the codes and scales) in GB/s;
   * prefill_workloads: a chunked prefill (512 new tokens after a 3584-token
     cached prefix, paged cache) in TFLOP/s;
   * cpu_baseline: the CPU oracle on the host cores, on the same step.
@@ -64,7 +66,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel: decode|step|prefill|decode70b|paged|mha|mqa|window|chunked|"
+                    help="profile one kernel: decode|step|fp8|prefill|decode70b|paged|mha|mqa|window|chunked|"
                          "copy (a 512 MiB device copy)")
     ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
     return ap.parse_args()
@@ -82,12 +84,14 @@ def up(x: np.ndarray):
     return torch.from_numpy(x).cuda()
 
 
-def decode_bytes(wl, ctx):
+def decode_bytes(wl, ctx, fp8=False):
     """Algorithmic bytes of one decode: each visible K and V row once (with a
-    sliding window only the window's rows), Q read, O written."""
+    sliding window only the window's rows), Q read, O written.  An FP8 cache
+    row is d one-byte codes plus its 4-byte scale; Q and O stay bf16."""
     es = 2 if wl.dtype == "bf16" else 4
     rows = np.minimum(ctx, wl.window) if wl.window > 0 else ctx
-    kv = 2 * wl.K * wl.d * es * int(np.sum(rows, dtype=np.int64))
+    row_bytes = wl.d + 4 if fp8 else wl.d * es
+    kv = 2 * wl.K * row_bytes * int(np.sum(rows, dtype=np.int64))
     qo = 2 * wl.B * wl.H * wl.d * es
     return kv + qo
 
@@ -106,7 +110,7 @@ def causal_flops(wl):
 class DecodeBench:
     """Device-resident copies of one decode workload, rotated per call."""
 
-    def __init__(self, wl, copies=None):
+    def __init__(self, wl, copies=None, fp8=False):
         import torch
         from grouped_query_attention_gqa_amd import binding
         from grouped_query_attention_gqa_amd import workloads as W
@@ -116,7 +120,7 @@ class DecodeBench:
         self.inp = inp
         self.ctx = inp.ctx
         self.max_ctx = int(inp.ctx.max())
-        self.alg_bytes = decode_bytes(wl, inp.ctx)
+        self.alg_bytes = decode_bytes(wl, inp.ctx, fp8)
         valid = self.alg_bytes
         n = copies if copies is not None else max(1, min(4, math.ceil(3 * MALL_BYTES / max(valid, 1))))
         self.q = up(inp.q)
@@ -127,7 +131,24 @@ class DecodeBench:
         self.caches = []
         k0, v0 = up(inp.k), up(inp.v)
         bt = None if inp.block_table is None else up(inp.block_table)
-        for i in range(n):
+        if fp8:
+            # the FP8 cache is filled by the library's quantising append of
+            # every cached position (contiguous caches)
+            assert bt is None, "the FP8 bench leg uses a contiguous cache"
+            B, K, S, d = k0.shape
+            kt, vt = k0.permute(0, 2, 1, 3).contiguous(), v0.permute(0, 2, 1, 3).contiguous()
+            zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+            del k0, v0
+            for i in range(n):
+                kq = torch.empty((B, K, S, d), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+                vq = torch.empty_like(kq)
+                ks = torch.empty((B, K, S), dtype=torch.float32, device="cuda")
+                vs = torch.empty_like(ks)
+                c = binding.KVCache(kq, vq, None, k_scale=ks, v_scale=vs)
+                binding.gqa_kv_append(c, kt, vt, zero)
+                self.caches.append(c)
+            del kt, vt
+        for i in range(0 if fp8 else n):
             k = k0 if i == 0 else k0.clone()
             v = v0 if i == 0 else v0.clone()
             self.caches.append(binding.KVCache(k, v, bt))
@@ -405,6 +426,17 @@ def main():
             log(f"{name}: {mean_ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
             del d2
             torch.cuda.empty_cache()
+        # ---- the Llama-3-8B decode on an FP8 (E4M3, scale per row) cache ----
+        w = W.WORKLOADS["llama3_8b_decode"]
+        d2 = DecodeBench(w, fp8=True)
+        mean_ms, med_ms = time_decode_only(d2, max(5, args.steps // 2), 3)
+        gbs = d2.alg_bytes / (mean_ms * 1e-3) / 1e9
+        extra["llama3_8b_decode_fp8_cache"] = {
+            "us": round(mean_ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": d2.alg_bytes, "cache": "FP8 E4M3 codes + one fp32 scale per row; q/out bf16"}
+        log(f"llama3_8b_decode_fp8_cache: {mean_ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+        del d2
+        torch.cuda.empty_cache()
         result["decode_workloads"] = extra
         # ---- chunked prefill: new tokens after a cached prefix, paged ----
         result["prefill_workloads"] = {
@@ -488,8 +520,8 @@ def profile_only(args):
         return
     name = {"decode": "llama3_8b_decode", "step": "llama3_8b_decode", "decode70b": "llama2_70b_decode",
             "paged": "paged_long_decode", "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa",
-            "window": "mistral_7b_window_decode"}[args.only]
-    db = DecodeBench(W.WORKLOADS[name])
+            "window": "mistral_7b_window_decode", "fp8": "llama3_8b_decode"}[args.only]
+    db = DecodeBench(W.WORKLOADS[name], fp8=args.only == "fp8")
     mean_ms, med_ms = time_decode_only(db, args.steps, args.warmup, db.step if args.only == "step" else None)
     print(json.dumps({"workload": name, "decode_us": round(mean_ms * 1e3, 2),
                       "GB/s": round(db.alg_bytes / (mean_ms * 1e-3) / 1e9, 1), "bytes": db.alg_bytes}), flush=True)

@@ -21,7 +21,7 @@ _lib = None
 _lock = threading.Lock()
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_LAUNCH, GQA_ERR_DEVICE_ARG = range(6)
-GQA_F32, GQA_BF16 = 0, 1
+GQA_F32, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
 
 EXPORTED_SYMBOLS = (
     "gqa_abi_version", "gqa_status_string", "gqa_cache_elems_per_token",
@@ -48,6 +48,8 @@ class _CacheStruct(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p),
     ]
 
 
@@ -88,7 +90,7 @@ def load_library():
         lib.gqa_decode_step.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
         lib.gqa_prefill_window.restype = i32
         lib.gqa_prefill_window.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
-        if lib.gqa_abi_version() != 1:
+        if lib.gqa_abi_version() != 2:
             raise RuntimeError("libgqa.so ABI version mismatch")
         _lib = lib
         return lib
@@ -111,6 +113,8 @@ def _dtype_code(t: torch.dtype) -> int:
         return GQA_BF16
     if t == torch.float32:
         return GQA_F32
+    if t == torch.float8_e4m3fn:
+        return GQA_FP8_E4M3
     raise TypeError(f"unsupported dtype {t}")
 
 
@@ -138,21 +142,34 @@ def _need(t: torch.Tensor, name: str, dtype=None, dim=None):
 
 
 class KVCache:
-    """One layer's cache: contiguous [B,K,S_max,d] or paged [N,K,bs,d] + block table."""
+    """One layer's cache: contiguous [B,K,S_max,d] or paged [N,K,bs,d] + block table.
 
-    def __init__(self, k: torch.Tensor, v: torch.Tensor, block_table: Optional[torch.Tensor] = None):
+    An FP8 cache (k, v of torch.float8_e4m3fn) also takes k_scale / v_scale:
+    float32 [B,K,S_max] or [N,K,bs], one scale per cached row; its queries,
+    new rows and outputs are bf16."""
+
+    def __init__(self, k: torch.Tensor, v: torch.Tensor, block_table: Optional[torch.Tensor] = None,
+                 k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None):
         _need(k, "cache k", dim=4)
         _need(v, "cache v", dtype=k.dtype, dim=4)
         if k.shape != v.shape:
             raise ValueError("cache k and v must have the same shape")
         self.k, self.v, self.block_table = k, v, block_table
+        self.k_scale, self.v_scale = k_scale, v_scale
         self.dtype = k.dtype
+        self.act_dtype = torch.bfloat16 if k.dtype == torch.float8_e4m3fn else k.dtype
         self.num_kv_heads = int(k.shape[1])
         self.head_dim = int(k.shape[3])
         self.paged = block_table is not None
         s = _CacheStruct()
         s.k, s.v = k.data_ptr(), v.data_ptr()
         s.num_kv_heads, s.head_dim, s.dtype = self.num_kv_heads, self.head_dim, _dtype_code(k.dtype)
+        if k.dtype == torch.float8_e4m3fn:
+            for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
+                _need(sc, name, dtype=torch.float32, dim=3)
+                if tuple(sc.shape) != tuple(k.shape[:3]):
+                    raise ValueError(f"{name} must be {tuple(k.shape[:3])}")
+            s.k_scale, s.v_scale = k_scale.data_ptr(), v_scale.data_ptr()
         if self.paged:
             _need(block_table, "block_table", dtype=torch.int32, dim=2)
             s.block_table = block_table.data_ptr()
@@ -204,8 +221,8 @@ def _default_workspace(device: torch.device, stream_handle: int, nbytes: int) ->
 def gqa_kv_append(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, start_pos: torch.Tensor,
                   stream=None) -> None:
     """Write k_new/v_new [B,s_new,K,d] at positions start_pos[b] + t."""
-    _need(k_new, "k_new", dtype=cache.dtype, dim=4)
-    _need(v_new, "v_new", dtype=cache.dtype, dim=4)
+    _need(k_new, "k_new", dtype=cache.act_dtype, dim=4)
+    _need(v_new, "v_new", dtype=cache.act_dtype, dim=4)
     _need(start_pos, "start_pos", dtype=torch.int32, dim=1)
     B, s_new, K, d = k_new.shape
     if v_new.shape != k_new.shape or K != cache.num_kv_heads or d != cache.head_dim or start_pos.shape[0] != B:
@@ -220,7 +237,7 @@ def gqa_decode(q: torch.Tensor, cache: KVCache, ctx_lens: torch.Tensor, max_ctx:
                workspace: Optional[torch.Tensor] = None, stream=None, window: int = 0) -> torch.Tensor:
     """One decode step: q [B,1,H,d] against the first ctx_lens[b] cached tokens
     (with window > 0, only against the last `window` of them)."""
-    _need(q, "q", dtype=cache.dtype, dim=4)
+    _need(q, "q", dtype=cache.act_dtype, dim=4)
     _need(ctx_lens, "ctx_lens", dtype=torch.int32, dim=1)
     B, one, H, d = q.shape
     if one != 1 or d != cache.head_dim or ctx_lens.shape[0] != B:
@@ -253,9 +270,9 @@ def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, c
                     window: int = 0) -> torch.Tensor:
     """Append the newest token k_new/v_new [B,1,K,d] at position ctx_lens[b] - 1 and
     decode q [B,1,H,d] against the first ctx_lens[b] cached tokens, in one call."""
-    _need(q, "q", dtype=cache.dtype, dim=4)
-    _need(k_new, "k_new", dtype=cache.dtype, dim=4)
-    _need(v_new, "v_new", dtype=cache.dtype, dim=4)
+    _need(q, "q", dtype=cache.act_dtype, dim=4)
+    _need(k_new, "k_new", dtype=cache.act_dtype, dim=4)
+    _need(v_new, "v_new", dtype=cache.act_dtype, dim=4)
     _need(ctx_lens, "ctx_lens", dtype=torch.int32, dim=1)
     B, one, H, d = q.shape
     if one != 1 or d != cache.head_dim or ctx_lens.shape[0] != B:
@@ -285,9 +302,9 @@ def gqa_prefill(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache
                 scale: Optional[float] = None, stream=None, window: int = 0) -> torch.Tensor:
     """Append k_new/v_new [B,s,K,d] and attend q [B,s,H,d] (causal by default;
     with window > 0 each row sees only its `window` most recent positions)."""
-    _need(q, "q", dtype=cache.dtype, dim=4)
-    _need(k_new, "k_new", dtype=cache.dtype, dim=4)
-    _need(v_new, "v_new", dtype=cache.dtype, dim=4)
+    _need(q, "q", dtype=cache.act_dtype, dim=4)
+    _need(k_new, "k_new", dtype=cache.act_dtype, dim=4)
+    _need(v_new, "v_new", dtype=cache.act_dtype, dim=4)
     _need(start_pos, "start_pos", dtype=torch.int32, dim=1)
     B, s, H, d = q.shape
     if k_new.shape != (B, s, cache.num_kv_heads, d) or v_new.shape != k_new.shape or start_pos.shape[0] != B:

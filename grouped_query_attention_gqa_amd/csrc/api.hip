@@ -53,14 +53,21 @@ gqa_status make_view(const gqa_kv_cache *c, CacheView *out)
     if (c->num_kv_heads <= 0) return fail(GQA_ERR_INVALID_ARG, "num_kv_heads <= 0");
     if (c->head_dim <= 0) return fail(GQA_ERR_INVALID_ARG, "head_dim <= 0");
     if (c->head_dim != 64 && c->head_dim != 128) return fail(GQA_ERR_UNSUPPORTED, "head_dim not 64 or 128");
-    if (c->dtype != GQA_F32 && c->dtype != GQA_BF16) return fail(GQA_ERR_UNSUPPORTED, "unknown dtype");
+    if (c->dtype != GQA_F32 && c->dtype != GQA_BF16 && c->dtype != GQA_FP8_E4M3)
+        return fail(GQA_ERR_UNSUPPORTED, "unknown dtype");
+    if (c->dtype == GQA_FP8_E4M3) {
+        if (!c->k_scale || !c->v_scale) return fail(GQA_ERR_INVALID_ARG, "FP8 cache without scales");
+        if (c->head_dim != 128) return fail(GQA_ERR_UNSUPPORTED, "FP8 cache needs head_dim 128");
+    }
     CacheView v{};
     v.k = static_cast<char *>(c->k);
     v.v = static_cast<char *>(c->v);
     v.block_table = c->block_table;
     v.K = c->num_kv_heads;
     v.d = c->head_dim;
-    v.elem_bytes = c->dtype == GQA_BF16 ? 2 : 4;
+    v.elem_bytes = c->dtype == GQA_FP8_E4M3 ? 1 : c->dtype == GQA_BF16 ? 2 : 4;
+    v.k_scale = c->dtype == GQA_FP8_E4M3 ? c->k_scale : nullptr;
+    v.v_scale = c->dtype == GQA_FP8_E4M3 ? c->v_scale : nullptr;
     if (c->block_table == nullptr) {
         if (c->S_max <= 0) return fail(GQA_ERR_INVALID_ARG, "S_max <= 0");
         v.S_max = c->S_max;
@@ -237,6 +244,10 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
     if (B == 0) return GQA_OK;
     if (!q || !out || !ctx_lens) return fail(GQA_ERR_INVALID_ARG, "NULL q/out/ctx_lens");
     if (step && (!k_new || !v_new)) return fail(GQA_ERR_INVALID_ARG, "NULL k_new or v_new");
+    if (v.elem_bytes == 1) {
+        if (pow2_at_least(num_heads / v.K) > 8) return fail(GQA_ERR_UNSUPPORTED, "FP8 cache with G > 8");
+        if (v.block_table && v.log2_bs < 4) return fail(GQA_ERR_UNSUPPORTED, "FP8 cache with blocks below 16 tokens");
+    }
     if (max_ctx <= 0) return fail(GQA_ERR_INVALID_ARG, "max_ctx <= 0");
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
     DecodeLayout L;
@@ -277,7 +288,8 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
         // k_new / v_new; every other path appends first
         p.k_new = static_cast<const char *>(k_new);
         p.v_new = static_cast<const char *>(v_new);
-        if (!decode_waves_supported(p, pow2_at_least(p.G))) {
+        // an FP8 cache is written by the quantising append kernel
+        if (v.elem_bytes == 1 || !decode_waves_supported(p, pow2_at_least(p.G))) {
             AppendParams ap{};
             ap.cache = v;
             ap.k_new = p.k_new;
@@ -312,6 +324,7 @@ gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_ne
     if (B == 0 || s == 0) return GQA_OK;
     if (!q || !k_new || !v_new || !start_pos || !out) return fail(GQA_ERR_INVALID_ARG, "NULL pointer");
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
+    if (v.elem_bytes == 1) return fail(GQA_ERR_UNSUPPORTED, "prefill on an FP8 cache");
     const bool bf16 = v.elem_bytes == 2;
     if (check_mode()) {
         std::vector<int32_t> sp;

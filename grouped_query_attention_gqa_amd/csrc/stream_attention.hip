@@ -645,7 +645,7 @@ hipError_t launch_d(const RowAttnParams &p, int gp, hipStream_t s)
 hipError_t launch_merge_pieces(const RowAttnParams &p, int tt, int W, hipStream_t s)
 {
     const dim3 grid(p.cache.K, p.rows, (p.G + kMergeHeads - 1) / kMergeHeads);
-    const bool bf16 = p.cache.elem_bytes == 2;
+    const bool bf16 = p.cache.elem_bytes != 4;   // an FP8 cache has bf16 outputs
     if (p.cache.d == 128) {
         if (bf16) hipLaunchKernelGGL((merge_pieces_kernel<128, true>), grid, dim3(256), 0, s, p, tt, W);
         else hipLaunchKernelGGL((merge_pieces_kernel<128, false>), grid, dim3(256), 0, s, p, tt, W);
@@ -671,6 +671,7 @@ hipError_t launch_row_attention(const RowAttnParams &p0, int gp, hipStream_t str
         p.rows = (int32_t)(p0.total_rows - r0 < kStreamRows ? p0.total_rows - r0 : kStreamRows);
         hipError_t e = hipErrorInvalidValue;
         if (decode_waves_supported(p, gp)) e = launch_decode_waves(p, gp, stream);
+        else if (p.cache.elem_bytes == 1) return hipErrorInvalidValue;   // FP8: the decode kernel only
         else if (p.cache.d == 128) e = bf16 ? launch_d<128, true>(p, gp, stream) : launch_d<128, false>(p, gp, stream);
         else if (p.cache.d == 64) e = bf16 ? launch_d<64, true>(p, gp, stream) : launch_d<64, false>(p, gp, stream);
         if (e != hipSuccess) return e;

@@ -46,6 +46,13 @@
  *   - Supported: dtype GQA_BF16 or GQA_F32, head_dim 64 or 128,
  *     1 <= K <= H, H % K == 0, G = H / K <= 64, block_size a power of two in
  *     [1, 1024].
+ *   - Quantised cache (GQA_FP8_E4M3): K/V rows stored as FP8 E4M3 with one
+ *     fp32 scale per cached row (token x KV head), written by gqa_kv_append
+ *     and gqa_decode_step and read by the decode calls (inference-
+ *     optimisation page §15.5-§15.5.1: per-token / per-head scales, FP8
+ *     E4M3).  Queries, new K/V rows and outputs are then bf16.  Supported
+ *     for head_dim 128 and G <= 8; the prefill calls and larger groups return
+ *     GQA_ERR_UNSUPPORTED.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -57,7 +64,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 1
+#define GQA_ABI_VERSION 2
 
 typedef enum {
     GQA_OK = 0,
@@ -70,7 +77,9 @@ typedef enum {
 
 typedef enum {
     GQA_F32 = 0,               /* IEEE binary32 */
-    GQA_BF16 = 1               /* bfloat16 (upper half of a binary32), stored as 16-bit words */
+    GQA_BF16 = 1,              /* bfloat16 (upper half of a binary32), stored as 16-bit words */
+    GQA_FP8_E4M3 = 2           /* cache only: OCP FP8 E4M3 codes (bias 7, largest finite 448, no
+                                * infinities) with one fp32 scale per row: value = scale * E4M3(code) */
 } gqa_dtype;
 
 /* One layer's KV cache for K KV heads of width head_dim. */
@@ -85,6 +94,9 @@ typedef struct {
     int32_t num_kv_heads;         /* K */
     int32_t head_dim;             /* d */
     int32_t dtype;                /* gqa_dtype */
+    float *k_scale;               /* GQA_FP8_E4M3 only (else ignored): one scale per cached row,
+                                     contiguous [B, K, S_max], paged [num_blocks, K, block_size] */
+    float *v_scale;               /* the same for V */
 } gqa_kv_cache;
 
 /* ABI version of the loaded library (GQA_ABI_VERSION). */
@@ -101,6 +113,10 @@ const char *gqa_status_string(int32_t status);
 int32_t gqa_cache_elems_per_token(int32_t num_kv_heads, int32_t head_dim);
 
 /*
+ * FP8 cache: a row x of d bf16 values is stored as scale = amax(|x|) / 448
+ * and codes E4M3(x_i / scale), nearest value with ties to the even code,
+ * both divisions in IEEE fp32; an all-zero row has scale 0 and zero codes.
+ *
  * Append s_new tokens to every sequence of the cache:
  *     pos = start_pos[b] + t,  cache row (b, g, pos) <- new row (b, t, g)
  * for t < s_new, g < K (through the block table when the cache is paged).
