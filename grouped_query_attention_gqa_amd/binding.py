@@ -27,6 +27,7 @@ EXPORTED_SYMBOLS = (
     "gqa_abi_version", "gqa_status_string", "gqa_cache_elems_per_token",
     "gqa_kv_append", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_prefill",
     "gqa_decode_window", "gqa_prefill_window", "gqa_decode_step",
+    "gqa_decode_multi_workspace_bytes", "gqa_decode_multi",
 )
 
 
@@ -86,6 +87,10 @@ def load_library():
         lib.gqa_prefill.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp]
         lib.gqa_decode_window.restype = i32
         lib.gqa_decode_window.argtypes = [vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
+        lib.gqa_decode_multi_workspace_bytes.restype = sz
+        lib.gqa_decode_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+        lib.gqa_decode_multi.restype = i32
+        lib.gqa_decode_multi.argtypes = [vp, cp, vp, i32, i32, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
         lib.gqa_decode_step.restype = i32
         lib.gqa_decode_step.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
         lib.gqa_prefill_window.restype = i32
@@ -294,6 +299,40 @@ def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, c
     st = lib.gqa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), cache.struct, _ptr(ctx_lens), int(max_ctx), B, H,
                              ctypes.c_float(scale), int(window), _ptr(out), _ptr(workspace), ws_bytes, hs)
     _check(st, "gqa_decode_step")
+    return out
+
+
+def gqa_decode_multi_workspace_bytes(B: int, num_heads: int, num_kv_heads: int, head_dim: int, s: int,
+                                     max_ctx: int) -> int:
+    return int(load_library().gqa_decode_multi_workspace_bytes(B, num_heads, num_kv_heads, head_dim, s, max_ctx))
+
+
+def gqa_decode_multi(q: torch.Tensor, cache: KVCache, ctx_lens: torch.Tensor, max_ctx: int,
+                     out: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None, window: int = 0) -> torch.Tensor:
+    """Decode of the s newest positions of every sequence at once: q [B,s,H,d]; row i of
+    sequence b sits at position ctx_lens[b] - s + i and attends causally (the s tokens'
+    K/V already in the cache)."""
+    _need(q, "q", dtype=cache.act_dtype, dim=4)
+    _need(ctx_lens, "ctx_lens", dtype=torch.int32, dim=1)
+    B, s, H, d = q.shape
+    if d != cache.head_dim or ctx_lens.shape[0] != B:
+        raise ValueError("decode shapes disagree with the cache")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, dim=4)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    nbytes = int(lib.gqa_decode_multi_workspace_bytes(B, H, cache.num_kv_heads, d, s, int(max_ctx)))
+    hs = _stream(stream)
+    if workspace is None and nbytes > 0:
+        workspace = _default_workspace(q.device, hs.value or 0, nbytes)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.gqa_decode_multi(_ptr(q), cache.struct, _ptr(ctx_lens), int(max_ctx), B, s, H, ctypes.c_float(scale),
+                              int(window), _ptr(out), _ptr(workspace), ws_bytes, hs)
+    _check(st, "gqa_decode_multi")
     return out
 
 

@@ -304,6 +304,72 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
     return launch_status(launch_row_attention(p, pow2_at_least(p.G), hs), "decode");
 }
 
+size_t gqa_decode_multi_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t s, int32_t max_ctx)
+{
+    if (B <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_ctx <= 0 || s <= 0) return 0;
+    if (num_heads % num_kv_heads != 0) return 0;
+    const int64_t rows = (int64_t)s * (num_heads / num_kv_heads);
+    if (rows > 0x7fffffffLL) return 0;
+    DecodeLayout L;
+    decode_layout((int32_t)rows, head_dim, &L);
+    return L.total;
+}
+
+gqa_status gqa_decode_multi(const void *q, const gqa_kv_cache *cache, const int32_t *ctx_lens, int32_t max_ctx,
+                            int32_t B, int32_t s, int32_t num_heads, float scale, int32_t window, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (s == 1)
+        return gqa_decode_window(q, cache, ctx_lens, max_ctx, B, num_heads, scale, window, out, workspace,
+                                 workspace_bytes, stream);
+    CacheView v;
+    gqa_status st = make_view(cache, &v);
+    if (st != GQA_OK) return st;
+    if ((st = check_heads(num_heads, v.K)) != GQA_OK) return st;
+    if (B < 0 || s < 0) return fail(GQA_ERR_INVALID_ARG, "B or s negative");
+    if (B == 0 || s == 0) return GQA_OK;
+    if (!q || !out || !ctx_lens) return fail(GQA_ERR_INVALID_ARG, "NULL q/out/ctx_lens");
+    if (max_ctx <= 0) return fail(GQA_ERR_INVALID_ARG, "max_ctx <= 0");
+    if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
+    const int32_t G = num_heads / v.K;
+    if ((int64_t)s * G > 64) return fail(GQA_ERR_UNSUPPORTED, "s * G above 64");
+    if (v.elem_bytes != 2 || v.d != 128) return fail(GQA_ERR_UNSUPPORTED, "several positions need bf16, d = 128");
+    if (v.block_table && v.log2_bs < 4) return fail(GQA_ERR_UNSUPPORTED, "blocks below 16 tokens");
+    DecodeLayout L;
+    decode_layout(s * G, v.d, &L);
+    if (!workspace || workspace_bytes < L.total)
+        return fail(GQA_ERR_WORKSPACE, "workspace smaller than gqa_decode_multi_workspace_bytes()");
+    if (check_mode()) {
+        std::vector<int32_t> cl;
+        if (!fetch_i32(ctx_lens, B, cl)) return fail(GQA_ERR_LAUNCH, "ctx_lens copy failed");
+        for (int b = 0; b < B; ++b)
+            if (cl[b] < s || cl[b] > max_ctx) return fail(GQA_ERR_DEVICE_ARG, "ctx_lens outside [s, max_ctx]");
+        std::vector<int32_t> lo(B, 0);
+        if ((st = check_positions(v, lo, cl)) != GQA_OK) return st;
+    }
+    RowAttnParams p{};
+    p.cache = v;
+    p.q = static_cast<const char *>(q);
+    p.out = static_cast<char *>(out);
+    p.ctx_lens = ctx_lens;
+    char *ws = static_cast<char *>(workspace);
+    p.prefix = reinterpret_cast<int32_t *>(ws);
+    p.ws_o = reinterpret_cast<float *>(ws + L.prefix_bytes);
+    p.ws_ml = reinterpret_cast<float *>(ws + L.prefix_bytes + L.o_bytes);
+    p.total_rows = B;
+    p.B = B;
+    p.Sq = 1;
+    p.mq = s;
+    p.H = num_heads;
+    p.G = G;
+    p.window = window > 0 ? window : 0;
+    p.num_wgs = kStreamWGs;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    return launch_status(launch_row_attention(p, pow2_at_least(p.G), static_cast<hipStream_t>(stream)),
+                         "decode (several positions)");
+}
+
 gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
                        const gqa_kv_cache *cache, const int32_t *start_pos, int32_t B, int32_t s,
                        int32_t num_heads, float scale, int32_t causal, void *out, void *stream)

@@ -1,0 +1,423 @@
+// decode_mfma.hip -- bf16 decode on the matrix cores for many query rows per
+// KV head: large groups (up to G = 64, the multi-query end) and a block of
+// several newest query positions per sequence (speculative-verify shaped).
+//
+// What it computes ("Grouped-Query Attention" concept page, 技术原理 steps
+// 2-4): for sequence b and KV group g, the R = mq * G rows -- query position i
+// of the sequence's mq newest tokens, head g*G + j -- attend to K/V head g.
+// Row i sits at position ctx[b] - mq + i and sees the keys up to and including
+// its own position (the causal rule, so the block is causal among itself),
+// from 0 or, with a sliding window of W positions (inference-optimisation
+// page §6.4.1), from its position + 1 - W.
+//
+// How (flash-decoding on the inference-optimisation page §10.2 is prior art
+// for the split; the tiling is for CDNA4):
+//  * Work list and slices as in the vector decode: the (sequence, KV group)
+//    items are cut into 16-key tiles, the flat tile list into one slice per
+//    workgroup, and the tiles of one item in a slice (a segment) are dealt
+//    round-robin to the 4 waves, which need no barrier per tile.
+//  * Scores transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16: the A
+//    operand is K as it lies in memory (lane: key l%16, 16 contiguous bytes
+//    of each 32-dimension step), the B operand Q^T stays in registers for the
+//    whole item.  A lane then holds 4 keys of one row.
+//  * Those 4 scores, as bf16 probabilities, are the B operand P^T of
+//    O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 exactly as they lie.  V^T
+//    comes from the wave's V tile in LDS through the transposing read
+//    (ds_read_b64_tr_b16): each lane receives 4 consecutive keys of one
+//    column.
+//  * Online softmax per row in exp2 units (inference-optimisation page
+//    §9.2.1) with a lazy maximum that moves only by >= 2^8; the 4 lanes of a
+//    row combine through permlane swaps.
+//  * At the end of a segment the 4 waves' (m, l, O) are merged in LDS in wave
+//    order (deterministic); a whole item is normalised and stored, a cut item
+//    leaves one partial per workgroup that merge_rows_kernel combines with
+//    their global max and sum (page §10.2).
+#include "common.h"
+#include "kernels.h"
+#include "worklist.h"
+
+namespace gqa {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+constexpr int NT = 256;            // threads per workgroup; two workgroups per CU
+constexpr int NW = NT / kWave;     // waves
+constexpr int D = 128;             // head dim
+constexpr int RB = D * 2;          // bytes per K/V row
+constexpr int TT = 16;             // keys per tile
+constexpr int KS = D / 32;         // 32-dimension steps of S^T = K Q^T
+constexpr int DB = D / 16;         // 16-dimension blocks of O^T
+constexpr float TAU = 8.0f;        // lazy-rescale threshold (log2 units)
+constexpr int MAX_ROWS = 64;       // R = mq * G
+
+__device__ __forceinline__ f32x4_t mfma_s(uint4 a, uint4 b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_o(uint2 a, uint2 b, f32x4_t c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a), __builtin_bit_cast(i16x4_t, b),
+                                                     c, 0, 0, 0);
+}
+// V row r keeps its 16-byte chunk c in slot c ^ vsw(r): the transposing reads
+// (16 lanes, 4 rows x 4 pieces of 4 columns) then spread over the banks
+__device__ __forceinline__ constexpr int vsw(int r) { return 4 * (r & 3); }
+__device__ __forceinline__ uint2 lds_read_tr16(const char *p)
+{
+    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(lds_void_t *)p);
+    return __builtin_bit_cast(uint2, v);
+}
+// the sum / max over the 4 lanes of a row (lanes l, l^16, l^32, l^48)
+__device__ __forceinline__ float row_sum(float x)
+{
+    const float2 a = swap_pair16(x);
+    x = a.x + a.y;
+    const float2 b = swap_pair32(x);
+    return b.x + b.y;
+}
+__device__ __forceinline__ float row_max(float x)
+{
+    const float2 a = swap_pair16(x);
+    x = fmaxf(a.x, a.y);
+    const float2 b = swap_pair32(x);
+    return fmaxf(b.x, b.y);
+}
+
+// RBW: 16-row blocks (R <= 16 * RBW); KD: tiles in flight per wave; OCC:
+// workgroups per CU (one for the larger row counts, whose accumulators need
+// more than half of a SIMD's registers)
+template <int RBW, int KD, int OCC>
+__global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
+{
+    constexpr int RP = 16 * RBW;
+    __shared__ __attribute__((aligned(16))) char lds_v[NW][TT * RB];
+    __shared__ __attribute__((aligned(16))) float lds_o[RP][D];
+    __shared__ float lds_ml[NW][RP][2];
+    __shared__ int32_t lds_prefix[kStreamRows + 1];
+    __shared__ int32_t lds_nvis[kStreamRows];
+    __shared__ int32_t lds_first[kStreamRows];
+    __shared__ int lds_waves[NW];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const CacheView &cache = p.cache;
+    const int G = p.G, H = p.H, mq = p.mq > 1 ? p.mq : 1;
+    const int R = mq * G;
+    const int nr = lane & 15, lg = lane >> 4;   // row within a 16-row block; lane group
+
+    build_tables<NT>(p, TT, lds_prefix, lds_nvis, lds_first, lds_waves);
+    if (blockIdx.x == 0 && p.prefix != nullptr)   // the merge kernel reads it from the workspace
+        for (int r = tid; r <= p.rows; r += NT) p.prefix[r] = lds_prefix[r];
+    const int T = lds_prefix[p.rows];
+    const int64_t W = gridDim.x;
+    const int tau0 = (int)slice_start(blockIdx.x, T, W), tau1 = (int)slice_start(blockIdx.x + 1, T, W);
+    if (tau0 >= tau1) return;
+
+    char *vw = lds_v[wave];
+    // V loads: lane (row 4 i + lg of the tile, chunk nr); LDS slot nr ^ vsw(row)
+    // transposing reads: lane (group lg, index nr) addresses row 4 lg + nr / 4,
+    // columns 16 db + 4 (nr % 4) .. +3
+    const int tr_row = 4 * lg + (nr >> 2);
+
+    int at = tau0;
+    while (at < tau1) {
+        const Cursor c = cursor_at(lds_prefix, lds_nvis, lds_first, p.rows, at, TT);
+        const int64_t seq = p.row0 + c.row;
+        const int b = (int)seq, g = c.g;
+        const int n_vis = c.n_vis, lo = c.lo;
+        const int end = min(tau1, c.item0 + c.tiles);
+        const int n_seg = end - at;
+        const int n_w = n_seg > wave ? (n_seg - wave + NW - 1) / NW : 0;
+        const int ctx_b = p.ctx_lens[b];
+        // this lane's rows: rho = 16 rb + nr -> query position i = rho / G, head j = rho % G
+        uint4 qf[RBW][KS];
+        int lim[RBW], rlo[RBW];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            const int rho = 16 * rb + nr;
+            const bool ok = rho < R;
+            const int i = ok ? rho / G : 0, j = ok ? rho % G : 0;
+            const int64_t qpos = (int64_t)ctx_b - mq + i;
+            lim[rb] = ok ? (int)min(max(qpos + 1, (int64_t)0), (int64_t)n_vis) : 0;
+            rlo[rb] = p.window > 0 ? (int)max((int64_t)0, qpos + 1 - p.window) : 0;
+            const char *qrow = p.q + (((seq * mq + i) * H + (int64_t)g * G + j) * D) * 2;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                qf[rb][ks] = ok ? *reinterpret_cast<const uint4 *>(qrow + ks * 64 + lg * 16) : make_uint4(0, 0, 0, 0);
+        }
+
+        // tile k of this wave in the segment: row tile c.jlo + (at - item0) + wave + NW k
+        const int j_first = at - c.item0;
+        auto tile_key0 = [&](int k) { return (c.jlo + j_first + wave + NW * k) * TT; };
+        // K fragments (A operand) and V rows of tile k; keys outside [lo, n_vis) read as zero
+        auto load_tile = [&](int k, uint4 (&kf)[KS], uint4 (&vr)[4]) {
+            const int key0 = tile_key0(k);
+            const bool live = k < n_w;
+            const int64_t base = live ? cache_row_wave(cache, b, g, key0) : -1;   // 16 keys: one cache block
+            const int kk = key0 + nr;
+            const bool kok = base >= 0 && kk < n_vis && kk >= lo;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kf[ks] = kok ? ld16(cache.k + (base + nr) * RB + ks * 64 + lg * 16) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * i + lg;
+                const bool vok = base >= 0 && key0 + r < n_vis && key0 + r >= lo;
+                vr[i] = vok ? ld16(cache.v + (base + r) * RB + nr * 16) : make_uint4(0, 0, 0, 0);
+            }
+        };
+
+        float m_ref[RBW], l_run[RBW];
+        f32x4_t acc[RBW][DB];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            m_ref[rb] = -INFINITY;
+            l_run[rb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+
+        uint4 kA[KS], vA[4], kB[KS], vB[4];
+        load_tile(0, kA, vA);
+        if constexpr (KD == 2) load_tile(1, kB, vB);
+        auto step = [&](int k, uint4 (&kf)[KS], uint4 (&vr)[4]) {
+            const int key0 = tile_key0(k);
+            // V rows of tile k into the wave's LDS tile
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * i + lg;
+                *reinterpret_cast<uint4 *>(vw + r * RB + ((nr ^ vsw(r)) * 16)) = vr[i];
+            }
+            // S^T = K Q^T: lane holds keys key0 + 4 lg + e of row 16 rb + nr
+            f32x4_t s[RBW];
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                s[rb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) s[rb] = mfma_s(kf[ks], qf[rb][ks], s[rb]);
+            }
+            // tile k + KD starts into the registers just read
+            load_tile(k + KD, kf, vr);
+            // mask, tile maximum, lazy rescale
+            bool need = false;
+            float mt[RBW];
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                float m = -INFINITY;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int key = key0 + 4 * lg + e;
+                    if (key >= lim[rb] || key < rlo[rb]) s[rb][e] = -INFINITY;
+                    m = fmaxf(m, s[rb][e]);
+                }
+                mt[rb] = row_max(m) * p.scale_log2;   // scale > 0: the max commutes with it
+                need |= mt[rb] > m_ref[rb] + TAU;
+            }
+            if (__ballot(need) != 0) {
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb) {
+                    if (mt[rb] > m_ref[rb] + TAU) {
+                        const float al = fast_exp2(m_ref[rb] - mt[rb]);   // 0 on the first tile
+                        m_ref[rb] = mt[rb];
+                        l_run[rb] *= al;
+#pragma unroll
+                        for (int db = 0; db < DB; ++db) acc[rb][db] *= al;
+                    }
+                }
+            }
+            // P^T (bf16, rounded) and the running sum of the rounded values
+            uint2 pw[RBW];
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                const float mu = m_ref[rb] == -INFINITY ? 0.f : m_ref[rb];
+                const float p0 = fast_exp2(fmaf(s[rb][0], p.scale_log2, -mu));
+                const float p1 = fast_exp2(fmaf(s[rb][1], p.scale_log2, -mu));
+                const float p2 = fast_exp2(fmaf(s[rb][2], p.scale_log2, -mu));
+                const float p3 = fast_exp2(fmaf(s[rb][3], p.scale_log2, -mu));
+                pw[rb] = make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
+                l_run[rb] = dot2_bf16(pw[rb].x, 0x3F803F80u, l_run[rb]);
+                l_run[rb] = dot2_bf16(pw[rb].y, 0x3F803F80u, l_run[rb]);
+            }
+            // O^T += V^T P^T, one 16-column block of V^T per transposing read
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const int col = 16 * db + 4 * (nr & 3);
+                const int chunk = (col >> 3) ^ vsw(tr_row);
+                const uint2 vt = lds_read_tr16(vw + tr_row * RB + chunk * 16 + (col & 7) * 2);
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = mfma_o(vt, pw[rb], acc[rb][db]);
+            }
+        };
+        for (int k = 0; k < n_w; ++k) {
+            if (KD == 2 && (k & 1)) step(k, kB, vB);
+            else step(k, kA, vA);
+        }
+
+        // ---- merge the 4 waves' pieces in LDS, in wave order ------------------
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            l_run[rb] = row_sum(l_run[rb]);
+            if (lg == 0) {
+                lds_ml[wave][16 * rb + nr][0] = n_w > 0 ? m_ref[rb] : -INFINITY;
+                lds_ml[wave][16 * rb + nr][1] = n_w > 0 ? l_run[rb] : 0.f;
+            }
+        }
+        __syncthreads();
+        float wt[RBW];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            const int row = 16 * rb + nr;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_ml[w][row][0]);
+            wt[rb] = (n_w > 0 && m_ref[rb] != -INFINITY) ? fast_exp2(m_ref[rb] - M) : 0.f;
+        }
+        for (int w = 0; w < NW; ++w) {
+            if (wave == w) {
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                    for (int db = 0; db < DB; ++db)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float *o = &lds_o[16 * rb + nr][16 * db + 4 * lg + e];
+                            const float x = acc[rb][db][e] * wt[rb];
+                            *o = w == 0 ? x : *o + x;
+                        }
+            }
+            __syncthreads();
+        }
+        const bool whole = at == c.item0 && end == c.item0 + c.tiles;
+        const int slot = tau0 < c.item0 ? 1 : 0;
+        for (int idx = tid; idx < R * (D / 4); idx += NT) {
+            const int rho = idx / (D / 4), col = (idx % (D / 4)) * 4;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_ml[w][rho][0]);
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = lds_ml[w][rho][0];
+                if (mw != -INFINITY) L += lds_ml[w][rho][1] * fast_exp2(mw - M);
+            }
+            const float4 O = *reinterpret_cast<const float4 *>(&lds_o[rho][col]);
+            if (whole) {
+                const int i = rho / G, j = rho % G;
+                const float inv = L > 0.f ? 1.f / L : 0.f;   // a row with no visible key is zero
+                *reinterpret_cast<uint2 *>(p.out + (((seq * mq + i) * H + (int64_t)g * G + j) * D + col) * 2) =
+                    make_uint2(pack_bf16x2(O.x * inv, O.y * inv), pack_bf16x2(O.z * inv, O.w * inv));
+            } else {
+                const int64_t sr = ((int64_t)blockIdx.x * 2 + slot) * R + rho;
+                *reinterpret_cast<float4 *>(p.ws_o + sr * D + col) = O;
+                if (col == 0) {
+                    p.ws_ml[sr * 2] = M;
+                    p.ws_ml[sr * 2 + 1] = L;
+                }
+            }
+        }
+        __syncthreads();   // lds_o and lds_ml are free again
+        at = end;
+    }
+}
+
+// The pieces of the items cut by slice boundaries: workgroup (g, row, z)
+// merges rows 8 z .. 8 z + 7 of item (sequence row0 + row, group g) with
+// their global max and sum, one float4 of a row per thread; an item with no
+// visible key gets zero rows.
+constexpr int kMergeRows = 8;
+__global__ __launch_bounds__(256) void merge_rows_kernel(RowAttnParams p, int W)
+{
+    __shared__ int slots[kStreamWGs];
+    __shared__ int n_slots;
+    const int g = blockIdx.x, row = blockIdx.y;
+    const int G = p.G, H = p.H, mq = p.mq > 1 ? p.mq : 1;
+    const int R = mq * G;
+    const int rho = blockIdx.z * kMergeRows + (int)threadIdx.x / (D / 4), col = ((int)threadIdx.x % (D / 4)) * 4;
+    const int64_t seq = p.row0 + row;
+    const int n_vis = row_visible(p, seq);
+    const int lo = row_first(p, seq, n_vis);
+    uint16_t *dst = reinterpret_cast<uint16_t *>(p.out) +
+                    ((seq * mq + rho / G) * H + (int64_t)g * G + rho % G) * D + col;
+    if (n_vis <= lo) {
+        if (rho < R) *reinterpret_cast<uint2 *>(dst) = make_uint2(0u, 0u);
+        return;
+    }
+    const int64_t T = p.prefix[p.rows];
+    const int64_t tiles = item_tiles(lo, n_vis, TT);
+    const int64_t a = p.prefix[row] + (int64_t)g * tiles, e = a + tiles - 1;
+    const int64_t wa = slice_owner(a, T, W), wb = slice_owner(e, T, W);
+    if (wa == wb) return;
+    if (threadIdx.x == 0) {
+        int n = 0;
+        for (int64_t w = wa; w <= wb; ++w) {
+            const int64_t s0 = slice_start(w, T, W);
+            if (s0 == slice_start(w + 1, T, W)) continue;   // an empty slice holds nothing
+            slots[n++] = (int)(w * 2 + (s0 < a ? 1 : 0));
+        }
+        n_slots = n;
+    }
+    __syncthreads();
+    if (rho >= R) return;
+    const int ns = n_slots;
+    // one pass in slot order: the running maximum rescales what is summed so far
+    float M = -INFINITY, L = 0.f;
+    float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < ns; ++k) {
+        const int64_t sr = (int64_t)slots[k] * R + rho;
+        const float mw = p.ws_ml[sr * 2];
+        if (mw == -INFINITY) continue;
+        const float lw = p.ws_ml[sr * 2 + 1];
+        const float4 os = *reinterpret_cast<const float4 *>(p.ws_o + sr * D + col);
+        const float Mn = fmaxf(M, mw);
+        const float a_old = M == -INFINITY ? 0.f : fast_exp2(M - Mn), a_new = fast_exp2(mw - Mn);
+        L = L * a_old + lw * a_new;
+        O.x = O.x * a_old + os.x * a_new;
+        O.y = O.y * a_old + os.y * a_new;
+        O.z = O.z * a_old + os.z * a_new;
+        O.w = O.w * a_old + os.w * a_new;
+        M = Mn;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(O.x * inv, O.y * inv), pack_bf16x2(O.z * inv, O.w * inv));
+}
+
+template <int RBW, int KD, int OCC>
+hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
+{
+    RowAttnParams p = p0;
+    p.num_wgs = p0.num_wgs * OCC / 2;   // slices resident at once: OCC per CU
+    hipLaunchKernelGGL((decode_mfma_kernel<RBW, KD, OCC>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int R = (p.mq > 1 ? p.mq : 1) * p.G;
+    hipLaunchKernelGGL(merge_rows_kernel, dim3(p.cache.K, p.rows, (R + kMergeRows - 1) / kMergeRows), dim3(256), 0, s,
+                       p, p.num_wgs);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool decode_mfma_supported(const RowAttnParams &p)
+{
+    const int mq = p.mq > 1 ? p.mq : 1;
+    // paged caches need blocks of at least 16 tokens (a tile stays in one block)
+    return !p.prefill && !p.whole_items && p.cache.elem_bytes == 2 && p.cache.d == D && p.k_new == nullptr &&
+           mq * p.G <= MAX_ROWS && p.num_wgs <= kStreamWGs && (p.cache.block_table == nullptr || p.cache.log2_bs >= 4);
+}
+
+hipError_t launch_decode_mfma(const RowAttnParams &p, hipStream_t stream)
+{
+    if (!decode_mfma_supported(p)) return hipErrorInvalidValue;
+    const int R = (p.mq > 1 ? p.mq : 1) * p.G;
+    if (R <= 16) return launch_m<1, 1, 2>(p, stream);
+    if (R <= 32) return launch_m<2, 1, 1>(p, stream);
+    return launch_m<4, 1, 1>(p, stream);
+}
+
+}  // namespace gqa

@@ -62,6 +62,7 @@ struct RowAttnParams {
     int32_t causal;
     int32_t whole_items;        // 1: slices snap to item starts (no partial pieces, no workspace)
     int32_t window;             // > 0: a row sees only its `window` most recent positions
+    int32_t mq;                 // decode: query positions per sequence, the newest mq (0 or 1: one)
     int32_t num_wgs;            // W
     float scale_log2;           // softmax scale * log2(e)
 };
@@ -133,6 +134,9 @@ hipError_t launch_row_attention(const RowAttnParams &p, int gp, hipStream_t stre
 // bf16 decode for padded group sizes gp <= 8 (one launch of at most kStreamRows rows)
 bool decode_waves_supported(const RowAttnParams &p, int gp);
 hipError_t launch_decode_waves(const RowAttnParams &p, int gp, hipStream_t stream);
+// bf16 decode on the matrix cores: mq query positions x G heads per (sequence, KV head), up to 64 rows
+bool decode_mfma_supported(const RowAttnParams &p);
+hipError_t launch_decode_mfma(const RowAttnParams &p, hipStream_t stream);
 // merge of the partial pieces that W workgroup slices of tt-key tiles left in the workspace
 hipError_t launch_merge_pieces(const RowAttnParams &p, int tt, int W, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams &p, hipStream_t stream);

@@ -35,13 +35,14 @@ __device__ __forceinline__ int row_visible(const RowAttnParams &p, int64_t row)
 
 // First visible key of the row: 0, or with a sliding window of W positions
 // (inference-optimisation page §6.4.1) the oldest of the W most recent
-// positions up to the row's own, qpos + 1 - W.
+// positions up to the row's own, qpos + 1 - W.  A decode row that carries mq
+// query positions (the newest mq tokens) takes the window of the oldest.
 __device__ __forceinline__ int row_first(const RowAttnParams &p, int64_t row, int n_end)
 {
     if (p.window <= 0) return 0;
     const int b = (int)(row / p.Sq);
     const int i = (int)(row % p.Sq);
-    const int64_t qpos = p.prefill ? (int64_t)p.start_pos[b] + i : (int64_t)p.ctx_lens[b] - 1;
+    const int64_t qpos = p.prefill ? (int64_t)p.start_pos[b] + i : (int64_t)p.ctx_lens[b] - (p.mq > 1 ? p.mq : 1);
     int64_t lo = qpos + 1 - p.window;
     if (lo < 0) lo = 0;
     if (lo > n_end) lo = n_end;
@@ -157,5 +158,15 @@ __device__ __forceinline__ void cursor_next(const int32_t *nvis, const int32_t *
 }
 
 __device__ __forceinline__ int64_t slice_start(int64_t w, int64_t T, int64_t W) { return w * T / W; }
+
+// The workgroup whose slice holds flat tile x (slices may be empty when there
+// are fewer tiles than workgroups; the one returned is never empty).
+__device__ __forceinline__ int64_t slice_owner(int64_t x, int64_t T, int64_t W)
+{
+    int64_t w = x * W / T;
+    while (w + 1 < W && slice_start(w + 1, T, W) <= x) ++w;
+    while (w > 0 && slice_start(w, T, W) > x) --w;
+    return w;
+}
 
 }  // namespace gqa

@@ -219,6 +219,30 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
                            const int32_t *ctx_lens, int32_t max_ctx, int32_t B, int32_t num_heads, float scale,
                            int32_t window, void *out, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Decode of several new positions per sequence at once (a block of s
+ * speculative tokens verified in one step, inference-optimisation page §14.2;
+ * the concept page's rows are [B, s, H, d] for any s): row i of sequence b is
+ * at position ctx_lens[b] - s + i and attends, causally, to the keys up to and
+ * including its own position (from its position + 1 - window on when
+ * window > 0).  The s tokens' K/V must already be in the cache (gqa_kv_append
+ * at start_pos = ctx_lens - s), so ctx_lens[b] >= s.
+ *   q, out: device [B, s, H, d];  ctx_lens: device int32 [B]
+ *   workspace: at least gqa_decode_multi_workspace_bytes(B, H, K, d, s, max_ctx)
+ * Each (sequence, KV head) item carries s * G query rows, so every K/V row
+ * read from memory serves all of them; the products run on the matrix cores
+ * (bf16 in, fp32 accumulate), the keys split over the workgroups as in
+ * gqa_decode.  s == 1 is gqa_decode_window.  Supported for s > 1: bf16,
+ * head_dim 128, s * G <= 64, paged blocks of at least 16 tokens
+ * (GQA_ERR_UNSUPPORTED otherwise).  Other arguments, ownership and errors as
+ * for gqa_decode.
+ */
+size_t gqa_decode_multi_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t s, int32_t max_ctx);
+gqa_status gqa_decode_multi(const void *q, const gqa_kv_cache *cache, const int32_t *ctx_lens, int32_t max_ctx,
+                            int32_t B, int32_t s, int32_t num_heads, float scale, int32_t window, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
