@@ -16,10 +16,15 @@
 //    items are cut into 16-key tiles, the flat tile list into one slice per
 //    workgroup, and the tiles of one item in a slice (a segment) are dealt
 //    round-robin to the 4 waves, which need no barrier per tile.
+//  * Each wave streams its tiles through a ring of NSTG stages of its own in
+//    LDS (8 KB: the 16 K rows and the 16 V rows), filled NSTG - 1 tiles ahead
+//    by LDS-direct loads (global_load_lds_dwordx4: no registers hold data in
+//    flight) with explicit vmcnt waits.  Rows are XOR-swizzled in 16-byte
+//    slots so that the fragment reads below hit distinct banks.
 //  * Scores transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_bf16: the A
-//    operand is K as it lies in memory (lane: key l%16, 16 contiguous bytes
-//    of each 32-dimension step), the B operand Q^T stays in registers for the
-//    whole item.  A lane then holds 4 keys of one row.
+//    operand is K (lane: key l%16, 16 bytes of each 32-dimension step), the B
+//    operand Q^T stays in registers for the whole item.  A lane then holds 4
+//    keys of one row.
 //  * Those 4 scores, as bf16 probabilities, are the B operand P^T of
 //    O^T += V^T P^T on v_mfma_f32_16x16x16_bf16 exactly as they lie.  V^T
 //    comes from the wave's V tile in LDS through the transposing read
@@ -54,6 +59,32 @@ constexpr int KS = D / 32;         // 32-dimension steps of S^T = K Q^T
 constexpr int DB = D / 16;         // 16-dimension blocks of O^T
 constexpr float TAU = 8.0f;        // lazy-rescale threshold (log2 units)
 constexpr int MAX_ROWS = 64;       // R = mq * G
+constexpr int NSTG = 4;            // LDS stages per wave
+constexpr int STG = 2 * TT * RB;   // bytes per stage: K rows, then V rows
+constexpr int DMA_PER_TILE = 2 * TT * RB / 1024;   // 1 KB LDS-direct loads per tile (K and V)
+
+__device__ const uint4 kZero16M = {0u, 0u, 0u, 0u};
+
+// One LDS-direct 16-byte load per lane: lane i's bytes land at lds + 16 i.
+// Inline assembly, so that the compiler does not wait for these loads before
+// LDS reads; the kernel waits with explicit vmcnt.
+__device__ __forceinline__ void dma16(const void *src, uint32_t lds)
+{
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// K row r keeps its 16-byte chunk c in slot c ^ (r & 15): the 16 lanes of an
+// A-operand read (16 keys, one chunk) then hit 16 different slots
+__device__ __forceinline__ constexpr int ksw(int r) { return r & 15; }
 
 __device__ __forceinline__ f32x4_t mfma_s(uint4 a, uint4 b, f32x4_t c)
 {
@@ -89,19 +120,29 @@ __device__ __forceinline__ float row_max(float x)
     return fmaxf(b.x, b.y);
 }
 
-// RBW: 16-row blocks (R <= 16 * RBW); KD: tiles in flight per wave; OCC:
-// workgroups per CU (one for the larger row counts, whose accumulators need
-// more than half of a SIMD's registers)
-template <int RBW, int KD, int OCC>
-__global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
+// RBW: 16-row blocks (R <= 16 * RBW); one workgroup per CU (the stages fill
+// most of the LDS)
+template <int RBW>
+__global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(RowAttnParams p)
 {
     constexpr int RP = 16 * RBW;
-    __shared__ __attribute__((aligned(16))) char lds_v[NW][TT * RB];
-    __shared__ __attribute__((aligned(16))) float lds_o[RP][D];
+    __shared__ __attribute__((aligned(1024))) char lds_stage[NW][NSTG * STG];
+    // the merge area of a segment's end reuses the stages (every load has
+    // landed and every wave is past its reads when it is written); rows are
+    // padded by 16 bytes so that the 16 rows a store instruction touches fall
+    // on different banks
+    constexpr int OS = D + 4;   // floats per merge-area row
+    // one region per wave where they fit (one round of writes), else two
+    // regions that the other two waves add to
+    constexpr int NREG = 4 * RP * OS * 4 <= NW * NSTG * STG ? 4 : 2;
+    static_assert(NREG * RP * OS * 4 <= NW * NSTG * STG, "merge area fits in the stages");
+    float (*lds_o)[RP][OS] = reinterpret_cast<float (*)[RP][OS]>(&lds_stage[0][0]);
+    __shared__ float lds_row[RP][2];   // the merged (max, sum) of each row
     __shared__ float lds_ml[NW][RP][2];
     __shared__ int32_t lds_prefix[kStreamRows + 1];
     __shared__ int32_t lds_nvis[kStreamRows];
     __shared__ int32_t lds_first[kStreamRows];
+    __shared__ int32_t lds_newest[kStreamRows];   // ctx - 1 (the newest position), -1 past the capacity
     __shared__ int lds_waves[NW];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -111,7 +152,7 @@ __global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
     const int R = mq * G;
     const int nr = lane & 15, lg = lane >> 4;   // row within a 16-row block; lane group
 
-    build_tables<NT>(p, TT, lds_prefix, lds_nvis, lds_first, lds_waves);
+    build_tables<NT>(p, TT, lds_prefix, lds_nvis, lds_first, lds_waves, lds_newest);
     if (blockIdx.x == 0 && p.prefix != nullptr)   // the merge kernel reads it from the workspace
         for (int r = tid; r <= p.rows; r += NT) p.prefix[r] = lds_prefix[r];
     const int T = lds_prefix[p.rows];
@@ -119,9 +160,11 @@ __global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
     const int tau0 = (int)slice_start(blockIdx.x, T, W), tau1 = (int)slice_start(blockIdx.x + 1, T, W);
     if (tau0 >= tau1) return;
 
-    char *vw = lds_v[wave];
-    // V loads: lane (row 4 i + lg of the tile, chunk nr); LDS slot nr ^ vsw(row)
-    // transposing reads: lane (group lg, index nr) addresses row 4 lg + nr / 4,
+    char *sw = lds_stage[wave];
+    const uint32_t lds_w = (uint32_t)(uintptr_t)(lds_void_t *)sw;
+    // LDS-direct load i of a tile (i < 4: K, else V) fills rows 4 (i % 4) + lg,
+    // slot nr, with chunk nr ^ swizzle(row) of that row.
+    // Transposing reads: lane (group lg, index nr) addresses V row 4 lg + nr / 4,
     // columns 16 db + 4 (nr % 4) .. +3
     const int tr_row = 4 * lg + (nr >> 2);
 
@@ -134,7 +177,44 @@ __global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
         const int end = min(tau1, c.item0 + c.tiles);
         const int n_seg = end - at;
         const int n_w = n_seg > wave ? (n_seg - wave + NW - 1) / NW : 0;
-        const int ctx_b = p.ctx_lens[b];
+        // the context length from the table (a length past the capacity is clamped to it)
+        const int ctx_b = lds_newest[c.row] >= 0 ? lds_newest[c.row] + 1 : n_vis;
+        // tile k of this wave in the segment: row tile c.jlo + (at - item0) + wave + NW k
+        const int j_first = at - c.item0;
+        auto tile_key0 = [&](int k) { return (c.jlo + j_first + wave + NW * k) * TT; };
+        // the LDS-direct loads of tile k into stage k % NSTG; rows outside
+        // [lo, n_vis), and tiles past the wave's last, read a zero constant
+        auto issue = [&](int k) {
+            const int key0 = tile_key0(k);
+            const int64_t base = k < n_w ? cache_row_wave(cache, b, g, key0) : -1;   // 16 keys: one cache block
+            const uint32_t dst = lds_w + (uint32_t)((k % NSTG) * STG);
+#pragma unroll
+            for (int i = 0; i < DMA_PER_TILE; ++i) {
+                const bool is_v = i >= 4;
+                const int r = 4 * (i % 4) + lg;
+                const int chunk = nr ^ (is_v ? vsw(r) : ksw(r));
+                const char *src = reinterpret_cast<const char *>(&kZero16M);
+                if (base >= 0 && key0 + r < n_vis && key0 + r >= lo)
+                    src = (is_v ? cache.v : cache.k) + (base + r) * RB + chunk * 16;
+                dma16(src, dst + (uint32_t)(i * 1024));
+            }
+        };
+
+        float m_ref[RBW], l_run[RBW];
+        f32x4_t acc[RBW][DB];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) {
+            m_ref[rb] = -INFINITY;
+            l_run[rb] = 0.f;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+
+        // the first tiles start, then the q fragments load behind them; one
+        // full wait then covers both (a wait the compiler inserts itself for
+        // the q loads, unaware of the tile loads, would land inside the loop)
+#pragma unroll
+        for (int k = 0; k < NSTG - 1; ++k) issue(k);
         // this lane's rows: rho = 16 rb + nr -> query position i = rho / G, head j = rho % G
         uint4 qf[RBW][KS];
         int lim[RBW], rlo[RBW];
@@ -152,48 +232,17 @@ __global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
                 qf[rb][ks] = ok ? *reinterpret_cast<const uint4 *>(qrow + ks * 64 + lg * 16) : make_uint4(0, 0, 0, 0);
         }
 
-        // tile k of this wave in the segment: row tile c.jlo + (at - item0) + wave + NW k
-        const int j_first = at - c.item0;
-        auto tile_key0 = [&](int k) { return (c.jlo + j_first + wave + NW * k) * TT; };
-        // K fragments (A operand) and V rows of tile k; keys outside [lo, n_vis) read as zero
-        auto load_tile = [&](int k, uint4 (&kf)[KS], uint4 (&vr)[4]) {
+        wait_vm<0>();
+        auto step = [&](int k) {
             const int key0 = tile_key0(k);
-            const bool live = k < n_w;
-            const int64_t base = live ? cache_row_wave(cache, b, g, key0) : -1;   // 16 keys: one cache block
-            const int kk = key0 + nr;
-            const bool kok = base >= 0 && kk < n_vis && kk >= lo;
+            // tile k + NSTG - 1 goes into the stage read in the previous step
+            issue(k + NSTG - 1);
+            wait_vm<(NSTG - 1) * DMA_PER_TILE>();   // tile k has landed
+            const char *kt = sw + (k % NSTG) * STG, *vt = kt + TT * RB;
+            uint4 kf[KS];
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                kf[ks] = kok ? ld16(cache.k + (base + nr) * RB + ks * 64 + lg * 16) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * i + lg;
-                const bool vok = base >= 0 && key0 + r < n_vis && key0 + r >= lo;
-                vr[i] = vok ? ld16(cache.v + (base + r) * RB + nr * 16) : make_uint4(0, 0, 0, 0);
-            }
-        };
-
-        float m_ref[RBW], l_run[RBW];
-        f32x4_t acc[RBW][DB];
-#pragma unroll
-        for (int rb = 0; rb < RBW; ++rb) {
-            m_ref[rb] = -INFINITY;
-            l_run[rb] = 0.f;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        }
-
-        uint4 kA[KS], vA[4], kB[KS], vB[4];
-        load_tile(0, kA, vA);
-        if constexpr (KD == 2) load_tile(1, kB, vB);
-        auto step = [&](int k, uint4 (&kf)[KS], uint4 (&vr)[4]) {
-            const int key0 = tile_key0(k);
-            // V rows of tile k into the wave's LDS tile
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * i + lg;
-                *reinterpret_cast<uint4 *>(vw + r * RB + ((nr ^ vsw(r)) * 16)) = vr[i];
-            }
+                kf[ks] = *reinterpret_cast<const uint4 *>(kt + nr * RB + (((4 * ks + lg) ^ ksw(nr)) * 16));
             // S^T = K Q^T: lane holds keys key0 + 4 lg + e of row 16 rb + nr
             f32x4_t s[RBW];
 #pragma unroll
@@ -202,8 +251,6 @@ __global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) s[rb] = mfma_s(kf[ks], qf[rb][ks], s[rb]);
             }
-            // tile k + KD starts into the registers just read
-            load_tile(k + KD, kf, vr);
             // mask, tile maximum, lazy rescale
             bool need = false;
             float mt[RBW];
@@ -249,15 +296,13 @@ __global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
             for (int db = 0; db < DB; ++db) {
                 const int col = 16 * db + 4 * (nr & 3);
                 const int chunk = (col >> 3) ^ vsw(tr_row);
-                const uint2 vt = lds_read_tr16(vw + tr_row * RB + chunk * 16 + (col & 7) * 2);
+                const uint2 vf = lds_read_tr16(vt + tr_row * RB + chunk * 16 + (col & 7) * 2);
 #pragma unroll
-                for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = mfma_o(vt, pw[rb], acc[rb][db]);
+                for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = mfma_o(vf, pw[rb], acc[rb][db]);
             }
         };
-        for (int k = 0; k < n_w; ++k) {
-            if (KD == 2 && (k & 1)) step(k, kB, vB);
-            else step(k, kA, vA);
-        }
+        for (int k = 0; k < n_w; ++k) step(k);
+        wait_vm<0>();   // the loads issued past the last tile have landed before the stages are reused
 
         // ---- merge the 4 waves' pieces in LDS, in wave order ------------------
 #pragma unroll
@@ -278,35 +323,51 @@ __global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
             for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_ml[w][row][0]);
             wt[rb] = (n_w > 0 && m_ref[rb] != -INFINITY) ? fast_exp2(m_ref[rb] - M) : 0.f;
         }
-        for (int w = 0; w < NW; ++w) {
-            if (wave == w) {
+        // region wave % NREG: written by the first NREG waves, added to by the rest
+        for (int round = 0; round < NW / NREG; ++round) {
+            if (wave / NREG == round) {
 #pragma unroll
                 for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-                    for (int db = 0; db < DB; ++db)
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float *o = &lds_o[16 * rb + nr][16 * db + 4 * lg + e];
-                            const float x = acc[rb][db][e] * wt[rb];
-                            *o = w == 0 ? x : *o + x;
+                    for (int db = 0; db < DB; ++db) {
+                        float4 *o = reinterpret_cast<float4 *>(&lds_o[wave % NREG][16 * rb + nr][16 * db + 4 * lg]);
+                        float4 x = make_float4(acc[rb][db][0] * wt[rb], acc[rb][db][1] * wt[rb], acc[rb][db][2] * wt[rb],
+                                               acc[rb][db][3] * wt[rb]);
+                        if (round > 0) {
+                            const float4 y = *o;
+                            x.x += y.x; x.y += y.y; x.z += y.z; x.w += y.w;
                         }
+                        *o = x;
+                    }
             }
             __syncthreads();
         }
+        // each row's merged maximum and sum, once
+        if (tid < R) {
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_ml[w][tid][0]);
+            float L = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+                const float mw = lds_ml[w][tid][0];
+                if (mw != -INFINITY) L += lds_ml[w][tid][1] * fast_exp2(mw - M);
+            }
+            lds_row[tid][0] = M;
+            lds_row[tid][1] = L;
+        }
+        __syncthreads();
         const bool whole = at == c.item0 && end == c.item0 + c.tiles;
         const int slot = tau0 < c.item0 ? 1 : 0;
         for (int idx = tid; idx < R * (D / 4); idx += NT) {
             const int rho = idx / (D / 4), col = (idx % (D / 4)) * 4;
-            float M = -INFINITY;
+            const float M = lds_row[rho][0], L = lds_row[rho][1];
+            float4 O = *reinterpret_cast<const float4 *>(&lds_o[0][rho][col]);
 #pragma unroll
-            for (int w = 0; w < NW; ++w) M = fmaxf(M, lds_ml[w][rho][0]);
-            float L = 0.f;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) {
-                const float mw = lds_ml[w][rho][0];
-                if (mw != -INFINITY) L += lds_ml[w][rho][1] * fast_exp2(mw - M);
+            for (int r = 1; r < NREG; ++r) {
+                const float4 y = *reinterpret_cast<const float4 *>(&lds_o[r][rho][col]);
+                O.x += y.x; O.y += y.y; O.z += y.z; O.w += y.w;
             }
-            const float4 O = *reinterpret_cast<const float4 *>(&lds_o[rho][col]);
             if (whole) {
                 const int i = rho / G, j = rho % G;
                 const float inv = L > 0.f ? 1.f / L : 0.f;   // a row with no visible key is zero
@@ -328,8 +389,8 @@ __global__ __launch_bounds__(NT, OCC) void decode_mfma_kernel(RowAttnParams p)
 
 // The pieces of the items cut by slice boundaries: workgroup (g, row, z)
 // merges rows 8 z .. 8 z + 7 of item (sequence row0 + row, group g) with
-// their global max and sum, one float4 of a row per thread; an item with no
-// visible key gets zero rows.
+// their global max and sum (inference-optimisation page §10.2), one float4
+// of a row per thread; an item with no visible key gets zero rows.
 constexpr int kMergeRows = 8;
 __global__ __launch_bounds__(256) void merge_rows_kernel(RowAttnParams p, int W)
 {
@@ -353,46 +414,75 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(RowAttnParams p, int W)
     const int64_t a = p.prefix[row] + (int64_t)g * tiles, e = a + tiles - 1;
     const int64_t wa = slice_owner(a, T, W), wb = slice_owner(e, T, W);
     if (wa == wb) return;
-    if (threadIdx.x == 0) {
-        int n = 0;
-        for (int64_t w = wa; w <= wb; ++w) {
-            const int64_t s0 = slice_start(w, T, W);
-            if (s0 == slice_start(w + 1, T, W)) continue;   // an empty slice holds nothing
-            slots[n++] = (int)(w * 2 + (s0 < a ? 1 : 0));
+    // the workspace slots of the pieces: with at least one tile per slice
+    // (T >= W) the pieces are the slices wa .. wb, the first one in slot 1
+    // when the item starts inside it; otherwise empty slices are skipped
+    const bool dense = T >= W;
+    if (!dense) {
+        if (threadIdx.x == 0) {
+            int n = 0;
+            for (int64_t w = wa; w <= wb; ++w) {
+                const int64_t s0 = slice_start(w, T, W);
+                if (s0 == slice_start(w + 1, T, W)) continue;   // an empty slice holds nothing
+                slots[n++] = (int)(w * 2 + (s0 < a ? 1 : 0));
+            }
+            n_slots = n;
         }
-        n_slots = n;
+        __syncthreads();
     }
-    __syncthreads();
     if (rho >= R) return;
-    const int ns = n_slots;
-    // one pass in slot order: the running maximum rescales what is summed so far
+    const int ns = dense ? (int)(wb - wa + 1) : n_slots;
+    const int slot0 = (int)(wa * 2 + (slice_start(wa, T, W) < a ? 1 : 0));
+    auto slot_of = [&](int k) { return dense ? (k == 0 ? slot0 : (int)(wa + k) * 2) : slots[k]; };
+    // pieces in batches of 8 whose loads are issued together; within a batch
+    // and from batch to batch the running maximum rescales what is summed
+    constexpr int BATCH = 8;
     float M = -INFINITY, L = 0.f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < ns; ++k) {
-        const int64_t sr = (int64_t)slots[k] * R + rho;
-        const float mw = p.ws_ml[sr * 2];
-        if (mw == -INFINITY) continue;
-        const float lw = p.ws_ml[sr * 2 + 1];
-        const float4 os = *reinterpret_cast<const float4 *>(p.ws_o + sr * D + col);
-        const float Mn = fmaxf(M, mw);
-        const float a_old = M == -INFINITY ? 0.f : fast_exp2(M - Mn), a_new = fast_exp2(mw - Mn);
-        L = L * a_old + lw * a_new;
-        O.x = O.x * a_old + os.x * a_new;
-        O.y = O.y * a_old + os.y * a_new;
-        O.z = O.z * a_old + os.z * a_new;
-        O.w = O.w * a_old + os.w * a_new;
+    for (int k0 = 0; k0 < ns; k0 += BATCH) {
+        float mm[BATCH], ll[BATCH];
+        float4 oo[BATCH];
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            mm[j] = -INFINITY;
+            ll[j] = 0.f;
+            oo[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (k0 + j < ns) {
+                const int64_t sr = (int64_t)slot_of(k0 + j) * R + rho;
+                mm[j] = p.ws_ml[sr * 2];
+                ll[j] = p.ws_ml[sr * 2 + 1];
+                oo[j] = *reinterpret_cast<const float4 *>(p.ws_o + sr * D + col);
+            }
+        }
+        float Mn = M;
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) Mn = fmaxf(Mn, mm[j]);
+        if (Mn == -INFINITY) continue;
+        const float a_old = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+        L *= a_old;
+        O.x *= a_old; O.y *= a_old; O.z *= a_old; O.w *= a_old;
+#pragma unroll
+        for (int j = 0; j < BATCH; ++j) {
+            if (mm[j] == -INFINITY) continue;
+            const float wt = fast_exp2(mm[j] - Mn);
+            L += ll[j] * wt;
+            O.x += oo[j].x * wt;
+            O.y += oo[j].y * wt;
+            O.z += oo[j].z * wt;
+            O.w += oo[j].w * wt;
+        }
         M = Mn;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(O.x * inv, O.y * inv), pack_bf16x2(O.z * inv, O.w * inv));
 }
 
-template <int RBW, int KD, int OCC>
+template <int RBW>
 hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
 {
     RowAttnParams p = p0;
-    p.num_wgs = p0.num_wgs * OCC / 2;   // slices resident at once: OCC per CU
-    hipLaunchKernelGGL((decode_mfma_kernel<RBW, KD, OCC>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+    p.num_wgs = p0.num_wgs / 2;   // slices resident at once: one per CU
+    hipLaunchKernelGGL((decode_mfma_kernel<RBW>), dim3(p.num_wgs), dim3(NT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int R = (p.mq > 1 ? p.mq : 1) * p.G;
@@ -415,9 +505,9 @@ hipError_t launch_decode_mfma(const RowAttnParams &p, hipStream_t stream)
 {
     if (!decode_mfma_supported(p)) return hipErrorInvalidValue;
     const int R = (p.mq > 1 ? p.mq : 1) * p.G;
-    if (R <= 16) return launch_m<1, 1, 2>(p, stream);
-    if (R <= 32) return launch_m<2, 1, 1>(p, stream);
-    return launch_m<4, 1, 1>(p, stream);
+    if (R <= 16) return launch_m<1>(p, stream);
+    if (R <= 32) return launch_m<2>(p, stream);
+    return launch_m<4>(p, stream);
 }
 
 }  // namespace gqa
