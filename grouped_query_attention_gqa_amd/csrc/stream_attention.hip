@@ -570,33 +570,65 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(RowAttnParams p, int 
     };
     const int64_t wa = owner(a), wb = owner(e);
     if (wa == wb) return;
-    if (threadIdx.x == 0) {
-        // workgroups whose slice is empty (fewer tiles than workgroups) hold nothing
-        int n = 0;
-        for (int64_t w = wa; w <= wb; ++w) {
-            const int64_t s0 = slice_start(w, T, W);
-            if (s0 == slice_start(w + 1, T, W)) continue;
-            slots[n++] = (int)(w * 2 + (s0 < a ? 1 : 0));
+    // the workspace slots of the pieces: with at least one tile per slice
+    // (T >= W) they are the slices wa .. wb, the first in slot 1 when the
+    // item starts inside it; otherwise empty slices are skipped
+    const bool dense = T >= W;
+    if (!dense) {
+        if (threadIdx.x == 0) {
+            int n = 0;
+            for (int64_t w = wa; w <= wb; ++w) {
+                const int64_t s0 = slice_start(w, T, W);
+                if (s0 == slice_start(w + 1, T, W)) continue;   // an empty slice holds nothing
+                slots[n++] = (int)(w * 2 + (s0 < a ? 1 : 0));
+            }
+            n_slots = n;
         }
-        n_slots = n;
+        __syncthreads();
     }
-    __syncthreads();
-    const int ns = n_slots;
+    const int ns = dense ? (int)(wb - wa + 1) : n_slots;
+    const int slot0 = (int)(wa * 2 + (slice_start(wa, T, W) < a ? 1 : 0));
+    auto slot_of = [&](int k) { return dense ? (k == 0 ? slot0 : (int)(wa + k) * 2) : slots[k]; };
     for (int idx = threadIdx.x; idx < nh * D / 4; idx += 256) {
         const int r = h0 + (4 * idx) / D, col = (4 * idx) % D;
-        float M = -INFINITY;
-        for (int k = 0; k < ns; ++k) M = fmaxf(M, p.ws_ml[((int64_t)slots[k] * G + r) * 2]);
-        float L = 0.f;
+        // pieces in batches whose loads are issued together; the running
+        // maximum rescales what is summed so far (in slot order)
+        constexpr int BATCH = 4;
+        float M = -INFINITY, L = 0.f;
         float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int k = 0; k < ns; ++k) {
-            const int64_t sr = (int64_t)slots[k] * G + r;
-            const float wt = fast_exp2(p.ws_ml[sr * 2] - M);
-            L += p.ws_ml[sr * 2 + 1] * wt;
-            const float4 os = *reinterpret_cast<const float4 *>(p.ws_o + sr * D + col);
-            O.x += os.x * wt;
-            O.y += os.y * wt;
-            O.z += os.z * wt;
-            O.w += os.w * wt;
+        for (int k0 = 0; k0 < ns; k0 += BATCH) {
+            float mm[BATCH], ll[BATCH];
+            float4 oo[BATCH];
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                mm[j] = -INFINITY;
+                ll[j] = 0.f;
+                oo[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (k0 + j < ns) {
+                    const int64_t sr = (int64_t)slot_of(k0 + j) * G + r;
+                    mm[j] = p.ws_ml[sr * 2];
+                    ll[j] = p.ws_ml[sr * 2 + 1];
+                    oo[j] = *reinterpret_cast<const float4 *>(p.ws_o + sr * D + col);
+                }
+            }
+            float Mn = M;
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) Mn = fmaxf(Mn, mm[j]);
+            if (Mn == -INFINITY) continue;
+            const float a_old = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+            L *= a_old;
+            O.x *= a_old; O.y *= a_old; O.z *= a_old; O.w *= a_old;
+#pragma unroll
+            for (int j = 0; j < BATCH; ++j) {
+                if (mm[j] == -INFINITY) continue;
+                const float wt = fast_exp2(mm[j] - Mn);
+                L += ll[j] * wt;
+                O.x += oo[j].x * wt;
+                O.y += oo[j].y * wt;
+                O.z += oo[j].z * wt;
+                O.w += oo[j].w * wt;
+            }
+            M = Mn;
         }
         const float inv = 1.f / L;
         const int64_t o = (head0 - h0 + r) * D + col;
