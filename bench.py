@@ -19,7 +19,8 @@ The same JSON line also carries
     MHA / MQA variants, paged long-context, a Mistral-7B-shaped
     sliding-window decode whose bytes count only the window, and the
     Llama-3-8B decode on an FP8 E4M3 cache with a scale per row, whose bytes
-    are the codes and scales) in GB/s;
+    are the codes and scales, and the same shape with four new positions per
+    sequence decoded at once by gqa_decode_multi) in GB/s;
   * prefill_workloads: a chunked prefill (512 new tokens after a 3584-token
     cached prefix, paged cache) in TFLOP/s;
   * cpu_baseline: the CPU oracle on the host cores, on the same step.
@@ -66,7 +67,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel: decode|step|fp8|prefill|decode70b|paged|mha|mqa|window|chunked|"
+                    help="profile one kernel: decode|step|fp8|multi|prefill|decode70b|paged|mha|mqa|window|chunked|"
                          "copy (a 512 MiB device copy)")
     ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
     return ap.parse_args()
@@ -110,7 +111,7 @@ def causal_flops(wl):
 class DecodeBench:
     """Device-resident copies of one decode workload, rotated per call."""
 
-    def __init__(self, wl, copies=None, fp8=False):
+    def __init__(self, wl, copies=None, fp8=False, mq=1):
         import torch
         from grouped_query_attention_gqa_amd import binding
         from grouped_query_attention_gqa_amd import workloads as W
@@ -120,7 +121,8 @@ class DecodeBench:
         self.inp = inp
         self.ctx = inp.ctx
         self.max_ctx = int(inp.ctx.max())
-        self.alg_bytes = decode_bytes(wl, inp.ctx, fp8)
+        self.alg_bytes = decode_bytes(wl, inp.ctx, fp8) + (mq - 1) * 2 * wl.B * wl.H * wl.d * 2   # q/out of mq rows
+        self.mq = mq
         valid = self.alg_bytes
         n = copies if copies is not None else max(1, min(4, math.ceil(3 * MALL_BYTES / max(valid, 1))))
         self.q = up(inp.q)
@@ -154,6 +156,12 @@ class DecodeBench:
             self.caches.append(binding.KVCache(k, v, bt))
         self.out = torch.empty_like(self.q)
         nbytes = binding.gqa_decode_workspace_bytes(wl.B, wl.H, wl.K, wl.d, self.max_ctx)
+        if mq > 1:
+            # the mq newest positions of every sequence (already in the cache)
+            g = torch.Generator(device="cuda").manual_seed(wl.seed)
+            self.qm = torch.randn((wl.B, mq, wl.H, wl.d), generator=g, device="cuda").to(torch.bfloat16)
+            self.outm = torch.empty_like(self.qm)
+            nbytes = max(nbytes, binding.gqa_decode_multi_workspace_bytes(wl.B, wl.H, wl.K, wl.d, mq, self.max_ctx))
         self.ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda")
         torch.cuda.synchronize()
         log(f"{wl.name}: {n} cache copies, sum ctx {int(inp.ctx.sum())}, "
@@ -168,6 +176,11 @@ class DecodeBench:
         binding.gqa_decode_step(self.q, self.k_new, self.v_new, self.caches[i % len(self.caches)], self.ctx_d,
                                 self.max_ctx, out=self.out, scale=self.wl.scale, workspace=self.ws,
                                 window=self.wl.window)
+
+    def multi(self, i):
+        from grouped_query_attention_gqa_amd import binding
+        binding.gqa_decode_multi(self.qm, self.caches[i % len(self.caches)], self.ctx_d, self.max_ctx, out=self.outm,
+                                 scale=self.wl.scale, workspace=self.ws, window=self.wl.window)
 
     def decode(self, i):
         from grouped_query_attention_gqa_amd import binding
@@ -426,6 +439,17 @@ def main():
             log(f"{name}: {mean_ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
             del d2
             torch.cuda.empty_cache()
+        # ---- four newest positions per sequence at once (speculative verify) -
+        w = W.WORKLOADS["llama3_8b_decode"]
+        d2 = DecodeBench(w, mq=4)
+        mean_ms, med_ms = time_decode_only(d2, max(5, args.steps // 2), 3, d2.multi)
+        gbs = d2.alg_bytes / (mean_ms * 1e-3) / 1e9
+        extra["llama3_8b_decode_4_positions"] = {
+            "us": round(mean_ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": d2.alg_bytes, "call": "gqa_decode_multi, s = 4 causal positions per sequence"}
+        log(f"llama3_8b_decode_4_positions: {mean_ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+        del d2
+        torch.cuda.empty_cache()
         # ---- the Llama-3-8B decode on an FP8 (E4M3, scale per row) cache ----
         w = W.WORKLOADS["llama3_8b_decode"]
         d2 = DecodeBench(w, fp8=True)
@@ -520,9 +544,10 @@ def profile_only(args):
         return
     name = {"decode": "llama3_8b_decode", "step": "llama3_8b_decode", "decode70b": "llama2_70b_decode",
             "paged": "paged_long_decode", "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa",
-            "window": "mistral_7b_window_decode", "fp8": "llama3_8b_decode"}[args.only]
-    db = DecodeBench(W.WORKLOADS[name], fp8=args.only == "fp8")
-    mean_ms, med_ms = time_decode_only(db, args.steps, args.warmup, db.step if args.only == "step" else None)
+            "window": "mistral_7b_window_decode", "fp8": "llama3_8b_decode", "multi": "llama3_8b_decode"}[args.only]
+    db = DecodeBench(W.WORKLOADS[name], fp8=args.only == "fp8", mq=4 if args.only == "multi" else 1)
+    call = {"step": db.step, "multi": getattr(db, "multi", None)}.get(args.only)
+    mean_ms, med_ms = time_decode_only(db, args.steps, args.warmup, call)
     print(json.dumps({"workload": name, "decode_us": round(mean_ms * 1e3, 2),
                       "GB/s": round(db.alg_bytes / (mean_ms * 1e-3) / 1e9, 1), "bytes": db.alg_bytes}), flush=True)
 
