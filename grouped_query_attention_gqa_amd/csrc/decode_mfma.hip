@@ -37,6 +37,10 @@
 //    order (deterministic); a whole item is normalised and stored, a cut item
 //    leaves one partial per workgroup that merge_rows_kernel combines with
 //    their global max and sum (page §10.2).
+//  * A decode step (one position, k_new / v_new given): the newest key and
+//    value of every item are loaded from k_new / v_new instead of the cache,
+//    and the kernel also copies them into the cache (the bytes the append
+//    kernel would write; no launch of this kernel reads those rows).
 #include "common.h"
 #include "kernels.h"
 #include "worklist.h"
@@ -152,7 +156,38 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(RowAttnParams p)
     const int R = mq * G;
     const int nr = lane & 15, lg = lane >> 4;   // row within a 16-row block; lane group
 
+    // decode step: thread (item, K or V, 16-byte piece) loads its piece of a
+    // new row now and stores it into the cache once the tables are built
+    constexpr int IPW = NT / (2 * (RB / 16));   // items per workgroup pass
+    const bool with_new = p.k_new != nullptr;
+    const int64_t cp_items = with_new ? (int64_t)p.rows * cache.K : 0;
+    const int cp_which = (tid / (RB / 16)) & 1, cp_piece = tid % (RB / 16);
+    auto copy_dst = [&](int64_t it, int64_t &src) -> char * {
+        const int b = (int)(p.row0 + it / cache.K), g = (int)(it % cache.K);
+        const int pos = p.ctx_lens[b] - 1;
+        if (pos < 0 || pos >= cache.capacity) return nullptr;
+        const int64_t row = cache_row(cache, b, g, pos);
+        if (row < 0) return nullptr;
+        src = ((int64_t)b * cache.K + g) * RB + cp_piece * 16;
+        return (cp_which ? cache.v : cache.k) + row * RB + cp_piece * 16;
+    };
+    char *cp_to = nullptr;
+    uint4 cp_val = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t it = (int64_t)blockIdx.x * IPW + tid / (2 * (RB / 16)); it < cp_items; it += (int64_t)gridDim.x * IPW) {
+        int64_t src = 0;
+        char *dst = copy_dst(it, src);
+        if (dst == nullptr) continue;
+        const uint4 x = ld16((cp_which ? p.v_new : p.k_new) + src);
+        if (it == (int64_t)blockIdx.x * IPW + tid / (2 * (RB / 16))) {
+            cp_to = dst;   // the first item's store waits until the tables are built
+            cp_val = x;
+        } else {
+            st16(dst, x);
+        }
+    }
+
     build_tables<NT>(p, TT, lds_prefix, lds_nvis, lds_first, lds_waves, lds_newest);
+    if (cp_to != nullptr) st16(cp_to, cp_val);
     if (blockIdx.x == 0 && p.prefix != nullptr)   // the merge kernel reads it from the workspace
         for (int r = tid; r <= p.rows; r += NT) p.prefix[r] = lds_prefix[r];
     const int T = lds_prefix[p.rows];
@@ -174,6 +209,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(RowAttnParams p)
         const int64_t seq = p.row0 + c.row;
         const int b = (int)seq, g = c.g;
         const int n_vis = c.n_vis, lo = c.lo;
+        const int new_key = with_new ? lds_newest[c.row] : -1;   // read from k_new / v_new
         const int end = min(tau1, c.item0 + c.tiles);
         const int n_seg = end - at;
         const int n_w = n_seg > wave ? (n_seg - wave + NW - 1) / NW : 0;
@@ -195,7 +231,8 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(RowAttnParams p)
                 const int chunk = nr ^ (is_v ? vsw(r) : ksw(r));
                 const char *src = reinterpret_cast<const char *>(&kZero16M);
                 if (base >= 0 && key0 + r < n_vis && key0 + r >= lo)
-                    src = (is_v ? cache.v : cache.k) + (base + r) * RB + chunk * 16;
+                    src = key0 + r == new_key ? (is_v ? p.v_new : p.k_new) + ((int64_t)b * cache.K + g) * RB + chunk * 16
+                                              : (is_v ? cache.v : cache.k) + (base + r) * RB + chunk * 16;
                 dma16(src, dst + (uint32_t)(i * 1024));
             }
         };
@@ -497,7 +534,7 @@ bool decode_mfma_supported(const RowAttnParams &p)
 {
     const int mq = p.mq > 1 ? p.mq : 1;
     // paged caches need blocks of at least 16 tokens (a tile stays in one block)
-    return !p.prefill && !p.whole_items && p.cache.elem_bytes == 2 && p.cache.d == D && p.k_new == nullptr &&
+    return !p.prefill && !p.whole_items && p.cache.elem_bytes == 2 && p.cache.d == D && (p.k_new == nullptr || mq == 1) &&
            mq * p.G <= MAX_ROWS && p.num_wgs <= kStreamWGs && (p.cache.block_table == nullptr || p.cache.log2_bs >= 4);
 }
 
