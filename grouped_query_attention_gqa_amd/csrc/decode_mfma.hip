@@ -63,7 +63,10 @@ constexpr int KS = D / 32;         // 32-dimension steps of S^T = K Q^T
 constexpr int DB = D / 16;         // 16-dimension blocks of O^T
 constexpr float TAU = 8.0f;        // lazy-rescale threshold (log2 units)
 constexpr int MAX_ROWS = 64;       // R = mq * G
-constexpr int NSTG = 4;            // LDS stages per wave
+// LDS stages per wave: 2 with two workgroups per CU (up to 16 rows: the
+// registers allow it), 4 with one (more rows)
+__host__ __device__ constexpr int occ_of(int rbw) { return rbw == 1 ? 2 : 1; }
+__host__ __device__ constexpr int nstg_of(int rbw) { return occ_of(rbw) == 2 ? 2 : 4; }
 constexpr int STG = 2 * TT * RB;   // bytes per stage: K rows, then V rows
 constexpr int DMA_PER_TILE = 2 * TT * RB / 1024;   // 1 KB LDS-direct loads per tile (K and V)
 
@@ -124,12 +127,12 @@ __device__ __forceinline__ float row_max(float x)
     return fmaxf(b.x, b.y);
 }
 
-// RBW: 16-row blocks (R <= 16 * RBW); one workgroup per CU (the stages fill
-// most of the LDS)
+// RBW: 16-row blocks (R <= 16 * RBW); occ_of(RBW) workgroups per CU
 template <int RBW>
-__global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(RowAttnParams p)
+__global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnParams p)
 {
     constexpr int RP = 16 * RBW;
+    constexpr int NSTG = nstg_of(RBW);
     __shared__ __attribute__((aligned(1024))) char lds_stage[NW][NSTG * STG];
     // the merge area of a segment's end reuses the stages (every load has
     // landed and every wave is past its reads when it is written); rows are
@@ -138,7 +141,7 @@ __global__ __launch_bounds__(NT, 1) void decode_mfma_kernel(RowAttnParams p)
     constexpr int OS = D + 4;   // floats per merge-area row
     // one region per wave where they fit (one round of writes), else two
     // regions that the other two waves add to
-    constexpr int NREG = 4 * RP * OS * 4 <= NW * NSTG * STG ? 4 : 2;
+    constexpr int NREG = 4 * RP * OS * 4 <= NW * NSTG * STG ? 4 : 2 * RP * OS * 4 <= NW * NSTG * STG ? 2 : 1;
     static_assert(NREG * RP * OS * 4 <= NW * NSTG * STG, "merge area fits in the stages");
     float (*lds_o)[RP][OS] = reinterpret_cast<float (*)[RP][OS]>(&lds_stage[0][0]);
     __shared__ float lds_row[RP][2];   // the merged (max, sum) of each row
@@ -518,7 +521,7 @@ template <int RBW>
 hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
 {
     RowAttnParams p = p0;
-    p.num_wgs = p0.num_wgs / 2;   // slices resident at once: one per CU
+    p.num_wgs = p0.num_wgs * occ_of(RBW) / 2;   // slices resident at once: occ_of(RBW) per CU
     hipLaunchKernelGGL((decode_mfma_kernel<RBW>), dim3(p.num_wgs), dim3(NT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
