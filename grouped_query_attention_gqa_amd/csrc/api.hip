@@ -244,10 +244,8 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
     if (B == 0) return GQA_OK;
     if (!q || !out || !ctx_lens) return fail(GQA_ERR_INVALID_ARG, "NULL q/out/ctx_lens");
     if (step && (!k_new || !v_new)) return fail(GQA_ERR_INVALID_ARG, "NULL k_new or v_new");
-    if (v.elem_bytes == 1) {
-        if (pow2_at_least(num_heads / v.K) > 8) return fail(GQA_ERR_UNSUPPORTED, "FP8 cache with G > 8");
-        if (v.block_table && v.log2_bs < 4) return fail(GQA_ERR_UNSUPPORTED, "FP8 cache with blocks below 16 tokens");
-    }
+    if (v.elem_bytes == 1 && v.block_table && v.log2_bs < 4)
+        return fail(GQA_ERR_UNSUPPORTED, "FP8 cache with blocks below 16 tokens");
     if (max_ctx <= 0) return fail(GQA_ERR_INVALID_ARG, "max_ctx <= 0");
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
     DecodeLayout L;
@@ -335,7 +333,7 @@ gqa_status gqa_decode_multi(const void *q, const gqa_kv_cache *cache, const int3
     if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
     const int32_t G = num_heads / v.K;
     if ((int64_t)s * G > 64) return fail(GQA_ERR_UNSUPPORTED, "s * G above 64");
-    if (v.elem_bytes != 2 || v.d != 128) return fail(GQA_ERR_UNSUPPORTED, "several positions need bf16, d = 128");
+    if (v.elem_bytes == 4 || v.d != 128) return fail(GQA_ERR_UNSUPPORTED, "several positions need bf16 or FP8, d = 128");
     if (v.block_table && v.log2_bs < 4) return fail(GQA_ERR_UNSUPPORTED, "blocks below 16 tokens");
     DecodeLayout L;
     decode_layout(s * G, v.d, &L);

@@ -37,6 +37,12 @@
 //    order (deterministic); a whole item is normalised and stored, a cut item
 //    leaves one partial per workgroup that merge_rows_kernel combines with
 //    their global max and sum (page §10.2).
+//  * FP8 E4M3 cache with a scale per row (inference-optimisation page
+//    §15.5.1): the stages hold the 1-byte rows and the tile's 16 K and 16 V
+//    scales; K fragments become bf16 in registers (every E4M3 value is a bf16
+//    value), the V tile is converted once into a bf16 tile in LDS for the
+//    transposing reads, the K scale multiplies the key's score and the V
+//    scale its probability (so the V product runs on codes).
 //  * A decode step (one position, k_new / v_new given): the newest key and
 //    value of every item are loaded from k_new / v_new instead of the cache,
 //    and the kernel also copies them into the cache (the bytes the append
@@ -66,9 +72,26 @@ constexpr int MAX_ROWS = 64;       // R = mq * G
 // LDS stages per wave: 2 with two workgroups per CU (up to 16 rows: the
 // registers allow it), 4 with one (more rows)
 __host__ __device__ constexpr int occ_of(int rbw) { return rbw == 1 ? 2 : 1; }
-__host__ __device__ constexpr int nstg_of(int rbw) { return occ_of(rbw) == 2 ? 2 : 4; }
-constexpr int STG = 2 * TT * RB;   // bytes per stage: K rows, then V rows
-constexpr int DMA_PER_TILE = 2 * TT * RB / 1024;   // 1 KB LDS-direct loads per tile (K and V)
+__host__ __device__ constexpr int nstg_of(int rbw, bool f8) { return f8 ? (occ_of(rbw) == 2 ? 3 : 6) : (occ_of(rbw) == 2 ? 2 : 4); }
+// FP8: K row r keeps its 16-byte chunk c (of 8) in slot c ^ (r & 7)
+__device__ __forceinline__ constexpr int ksw8(int r) { return r & 7; }
+// two E4M3 codes (bytes 0-1, or 2-3 with HI) -> a bf16 pair, exactly
+template <bool HI>
+__device__ __forceinline__ uint32_t f8x2_bf16x2(uint32_t w)
+{
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+__device__ __forceinline__ uint4 f8x8_bf16x8(uint2 x)
+{
+    return make_uint4(f8x2_bf16x2<false>(x.x), f8x2_bf16x2<true>(x.x), f8x2_bf16x2<false>(x.y), f8x2_bf16x2<true>(x.y));
+}
+// A stage: the tile's K rows, its V rows and (FP8) its 16 K and 16 V scales
+template <bool F8> struct Stage {
+    static constexpr int ROWB = F8 ? D : D * 2;                 // bytes per cached row
+    static constexpr int KV = TT * ROWB;                        // bytes of K (and of V) per tile
+    static constexpr int BYTES = 2 * KV + (F8 ? 2 * TT * 4 : 0);
+    static constexpr int DMA = 2 * KV / 1024 + (F8 ? 1 : 0);   // LDS-direct loads per tile
+};
 
 __device__ const uint4 kZero16M = {0u, 0u, 0u, 0u};
 
@@ -80,6 +103,15 @@ __device__ __forceinline__ void dma16(const void *src, uint32_t lds)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
     asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+// The same with 4 bytes per lane (lane i's bytes land at lds + 4 i).
+__device__ __forceinline__ void dma4(const void *src, uint32_t lds)
+{
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
                  :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds)) : "memory", "m0");
 #pragma clang diagnostic pop
 }
@@ -127,13 +159,16 @@ __device__ __forceinline__ float row_max(float x)
     return fmaxf(b.x, b.y);
 }
 
-// RBW: 16-row blocks (R <= 16 * RBW); occ_of(RBW) workgroups per CU
-template <int RBW>
+// RBW: 16-row blocks (R <= 16 * RBW); occ_of(RBW) workgroups per CU; F8: the
+// cache holds E4M3 codes and a scale per row
+template <int RBW, bool F8>
 __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnParams p)
 {
     constexpr int RP = 16 * RBW;
-    constexpr int NSTG = nstg_of(RBW);
+    constexpr int NSTG = nstg_of(RBW, F8);
+    constexpr int STG = Stage<F8>::BYTES, DMA_PER_TILE = Stage<F8>::DMA, CRB = Stage<F8>::ROWB;
     __shared__ __attribute__((aligned(1024))) char lds_stage[NW][NSTG * STG];
+    __shared__ __attribute__((aligned(16))) char lds_vbf[F8 ? NW : 1][F8 ? TT * RB : 16];   // FP8: the tile's V as bf16
     // the merge area of a segment's end reuses the stages (every load has
     // landed and every wave is past its reads when it is written); rows are
     // padded by 16 bytes so that the 16 rows a store instruction touches fall
@@ -227,16 +262,40 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
             const int key0 = tile_key0(k);
             const int64_t base = k < n_w ? cache_row_wave(cache, b, g, key0) : -1;   // 16 keys: one cache block
             const uint32_t dst = lds_w + (uint32_t)((k % NSTG) * STG);
+            if constexpr (!F8) {
 #pragma unroll
-            for (int i = 0; i < DMA_PER_TILE; ++i) {
-                const bool is_v = i >= 4;
-                const int r = 4 * (i % 4) + lg;
-                const int chunk = nr ^ (is_v ? vsw(r) : ksw(r));
-                const char *src = reinterpret_cast<const char *>(&kZero16M);
-                if (base >= 0 && key0 + r < n_vis && key0 + r >= lo)
-                    src = key0 + r == new_key ? (is_v ? p.v_new : p.k_new) + ((int64_t)b * cache.K + g) * RB + chunk * 16
-                                              : (is_v ? cache.v : cache.k) + (base + r) * RB + chunk * 16;
-                dma16(src, dst + (uint32_t)(i * 1024));
+                for (int i = 0; i < DMA_PER_TILE; ++i) {
+                    const bool is_v = i >= 4;
+                    const int r = 4 * (i % 4) + lg;
+                    const int chunk = nr ^ (is_v ? vsw(r) : ksw(r));
+                    const char *src = reinterpret_cast<const char *>(&kZero16M);
+                    if (base >= 0 && key0 + r < n_vis && key0 + r >= lo)
+                        src = key0 + r == new_key ? (is_v ? p.v_new : p.k_new) + ((int64_t)b * cache.K + g) * RB + chunk * 16
+                                                  : (is_v ? cache.v : cache.k) + (base + r) * RB + chunk * 16;
+                    dma16(src, dst + (uint32_t)(i * 1024));
+                }
+            } else {
+                // K: rows 8 i + lane / 8, slot lane % 8 (chunk slot ^ ksw8(row));
+                // V: the same rows, unswizzled
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool is_v = i >= 2;
+                    const int r = 8 * (i % 2) + lane / 8, slot = lane % 8;
+                    const int chunk = is_v ? slot : slot ^ ksw8(r);
+                    const char *src = reinterpret_cast<const char *>(&kZero16M);
+                    if (base >= 0 && key0 + r < n_vis && key0 + r >= lo)
+                        src = (is_v ? cache.v : cache.k) + (base + r) * CRB + chunk * 16;
+                    dma16(src, dst + (uint32_t)(i * 1024));
+                }
+                // the 16 K scales (lanes 0-15) and the 16 V scales (lanes 16-31),
+                // one per lane; a key outside the visible range reads zero
+                if (lane < 32) {
+                    const int r = lane % 16;
+                    const char *src = reinterpret_cast<const char *>(&kZero16M);
+                    if (base >= 0 && key0 + r < n_vis && key0 + r >= lo)
+                        src = reinterpret_cast<const char *>((lane >= 16 ? cache.v_scale : cache.k_scale) + base + r);
+                    dma4(src, dst + (uint32_t)(2 * Stage<F8>::KV));
+                }
             }
         };
 
@@ -278,11 +337,39 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
             // tile k + NSTG - 1 goes into the stage read in the previous step
             issue(k + NSTG - 1);
             wait_vm<(NSTG - 1) * DMA_PER_TILE>();   // tile k has landed
-            const char *kt = sw + (k % NSTG) * STG, *vt = kt + TT * RB;
+            const char *kt = sw + (k % NSTG) * STG;
+            const char *vt = F8 ? lds_vbf[F8 ? wave : 0] : kt + Stage<F8>::KV;
             uint4 kf[KS];
+            float ksc[4] = {1.f, 1.f, 1.f, 1.f}, vsc[4] = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (!F8) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kf[ks] = *reinterpret_cast<const uint4 *>(kt + nr * RB + (((4 * ks + lg) ^ ksw(nr)) * 16));
+                for (int ks = 0; ks < KS; ++ks)
+                    kf[ks] = *reinterpret_cast<const uint4 *>(kt + nr * RB + (((4 * ks + lg) ^ ksw(nr)) * 16));
+            } else {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int chunk = 2 * ks + (lg >> 1);
+                    kf[ks] = f8x8_bf16x8(*reinterpret_cast<const uint2 *>(kt + nr * CRB + ((chunk ^ ksw8(nr)) * 16) +
+                                                                          (lg & 1) * 8));
+                }
+                // scales of this lane's keys 4 lg .. 4 lg + 3
+                const float4 k4 = *reinterpret_cast<const float4 *>(kt + 2 * Stage<F8>::KV + 16 * lg);
+                const float4 v4 = *reinterpret_cast<const float4 *>(kt + 2 * Stage<F8>::KV + 64 + 16 * lg);
+                ksc[0] = k4.x; ksc[1] = k4.y; ksc[2] = k4.z; ksc[3] = k4.w;
+                vsc[0] = v4.x; vsc[1] = v4.y; vsc[2] = v4.z; vsc[3] = v4.w;
+                // the V tile as bf16 (swizzled as a bf16 tile): lane i converts
+                // the 32 bytes of row i / 4 at columns 32 (i % 4) ..
+                const char *vsrc = kt + Stage<F8>::KV + lane * 32;
+                char *vdst = lds_vbf[F8 ? wave : 0];
+                const int vr = lane >> 2;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint4 x = *reinterpret_cast<const uint4 *>(vsrc + 16 * h);
+                    const int c0 = 4 * (lane & 3) + 2 * h;   // logical bf16 chunk of the first 8 columns
+                    *reinterpret_cast<uint4 *>(vdst + vr * RB + ((c0 ^ vsw(vr)) * 16)) = f8x8_bf16x8(make_uint2(x.x, x.y));
+                    *reinterpret_cast<uint4 *>(vdst + vr * RB + (((c0 + 1) ^ vsw(vr)) * 16)) = f8x8_bf16x8(make_uint2(x.z, x.w));
+                }
+            }
             // S^T = K Q^T: lane holds keys key0 + 4 lg + e of row 16 rb + nr
             f32x4_t s[RBW];
 #pragma unroll
@@ -300,6 +387,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int key = key0 + 4 * lg + e;
+                    if constexpr (F8) s[rb][e] *= ksc[e];   // the key's K scale
                     if (key >= lim[rb] || key < rlo[rb]) s[rb][e] = -INFINITY;
                     m = fmaxf(m, s[rb][e]);
                 }
@@ -330,6 +418,13 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                 pw[rb] = make_uint2(pack_bf16x2(p0, p1), pack_bf16x2(p2, p3));
                 l_run[rb] = dot2_bf16(pw[rb].x, 0x3F803F80u, l_run[rb]);
                 l_run[rb] = dot2_bf16(pw[rb].y, 0x3F803F80u, l_run[rb]);
+                if constexpr (F8) {
+                    // the key's V scale rides on its probability (a masked key's
+                    // probability is 0 and its scale is not looked at)
+                    const float w0 = p0 > 0.f ? p0 * vsc[0] : 0.f, w1 = p1 > 0.f ? p1 * vsc[1] : 0.f;
+                    const float w2 = p2 > 0.f ? p2 * vsc[2] : 0.f, w3 = p3 > 0.f ? p3 * vsc[3] : 0.f;
+                    pw[rb] = make_uint2(pack_bf16x2(w0, w1), pack_bf16x2(w2, w3));
+                }
             }
             // O^T += V^T P^T, one 16-column block of V^T per transposing read
 #pragma unroll
@@ -522,7 +617,8 @@ hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
 {
     RowAttnParams p = p0;
     p.num_wgs = p0.num_wgs * occ_of(RBW) / 2;   // slices resident at once: occ_of(RBW) per CU
-    hipLaunchKernelGGL((decode_mfma_kernel<RBW>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+    if (p.cache.elem_bytes == 1) hipLaunchKernelGGL((decode_mfma_kernel<RBW, true>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+    else hipLaunchKernelGGL((decode_mfma_kernel<RBW, false>), dim3(p.num_wgs), dim3(NT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int R = (p.mq > 1 ? p.mq : 1) * p.G;
@@ -537,7 +633,10 @@ bool decode_mfma_supported(const RowAttnParams &p)
 {
     const int mq = p.mq > 1 ? p.mq : 1;
     // paged caches need blocks of at least 16 tokens (a tile stays in one block)
-    return !p.prefill && !p.whole_items && p.cache.elem_bytes == 2 && p.cache.d == D && (p.k_new == nullptr || mq == 1) &&
+    // bf16, or FP8 E4M3 with row scales (whose new rows the quantising append writes)
+    const bool f8 = p.cache.elem_bytes == 1;
+    return !p.prefill && !p.whole_items && (p.cache.elem_bytes == 2 || f8) && p.cache.d == D &&
+           (p.k_new == nullptr || (mq == 1 && !f8)) &&
            mq * p.G <= MAX_ROWS && p.num_wgs <= kStreamWGs && (p.cache.block_table == nullptr || p.cache.log2_bs >= 4);
 }
 

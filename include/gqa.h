@@ -51,8 +51,8 @@
  *     and gqa_decode_step and read by the decode calls (inference-
  *     optimisation page §15.5-§15.5.1: per-token / per-head scales, FP8
  *     E4M3).  Queries, new K/V rows and outputs are then bf16.  Supported
- *     for head_dim 128 and G <= 8; the prefill calls and larger groups return
- *     GQA_ERR_UNSUPPORTED.
+ *     for head_dim 128 (and paged blocks of at least 16 tokens) by the
+ *     append and decode calls; the prefill calls return GQA_ERR_UNSUPPORTED.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -204,12 +204,12 @@ gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_ne
  * gqa_kv_append(cache, k_new, v_new, start_pos = ctx_lens - 1, B, 1) followed
  * by gqa_decode_window(...) (the concept page, 技术原理: each new token's
  * K/V joins the cache, then its query attends to all cached keys).
- *   k_new, v_new: device [B, 1, K, d] (cache dtype), the token at position
- *                 ctx_lens[b] - 1 of sequence b
+ *   k_new, v_new: device [B, 1, K, d] (the cache dtype; bf16 for an FP8
+ *                 cache), the token at position ctx_lens[b] - 1 of sequence b
  *   window: as for gqa_decode_window (<= 0: no window)
- * For bf16 with G <= 8 one kernel does both: it reads the new token from
- * k_new / v_new and writes it into the cache in the same launch; the other
- * cases launch the append first.  A position at or past the cache capacity,
+ * For a bf16 cache (d = 128, or d = 64 with G <= 8) one kernel does both: it
+ * reads the new token from k_new / v_new and writes it into the cache in the
+ * same launch; the other cases launch the append first.  A position at or past the cache capacity,
  * or whose block id is outside the pool, is not written (as in
  * gqa_kv_append).  All other arguments, layouts, ownership and errors are
  * those of gqa_decode; k_new and v_new must both be given
@@ -232,8 +232,8 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
  * Each (sequence, KV head) item carries s * G query rows, so every K/V row
  * read from memory serves all of them; the products run on the matrix cores
  * (bf16 in, fp32 accumulate), the keys split over the workgroups as in
- * gqa_decode.  s == 1 is gqa_decode_window.  Supported for s > 1: bf16,
- * head_dim 128, s * G <= 64, paged blocks of at least 16 tokens
+ * gqa_decode.  s == 1 is gqa_decode_window.  Supported for s > 1: bf16 or
+ * FP8 cache, head_dim 128, s * G <= 64, paged blocks of at least 16 tokens
  * (GQA_ERR_UNSUPPORTED otherwise).  Other arguments, ownership and errors as
  * for gqa_decode.
  */

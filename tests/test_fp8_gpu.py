@@ -165,7 +165,7 @@ def test_fp8_append_paged_is_bit_exact():
         assert sc_d.cpu().numpy().view(np.uint32).tobytes() == want_s.view(np.uint32).tobytes(), f"{name} scales"
 
 
-@pytest.mark.parametrize("H,K", [(32, 8), (64, 8), (16, 16), (16, 8), (8, 8)])
+@pytest.mark.parametrize("H,K", [(32, 8), (64, 8), (16, 16), (16, 8), (8, 8), (64, 4), (64, 1), (24, 8)])
 def test_fp8_decode_matches_oracle(H, K):
     _decode_case(LLAMA3.replace(B=5, H=H, K=K, ctx=("uniform", 1, 900)), f"H={H} K={K}")
 
@@ -216,3 +216,29 @@ def test_fp8_single_key_returns_the_dequantised_value():
     of the scale-carrying probability and of the output)."""
     wl = LLAMA3.replace(B=2, ctx=("fixed", 1))
     _decode_case(wl, "ctx 1")
+
+
+@pytest.mark.parametrize("s_new,H,K", [(4, 32, 8), (2, 64, 8), (8, 64, 8)])
+def test_fp8_decode_multi_matches_causal_oracle(s_new, H, K):
+    """Several newest positions per sequence on an FP8 cache: row i at
+    ctx - s + i attends causally to the dequantised keys."""
+    wl = LLAMA3.replace(B=4, H=H, K=K, ctx=("uniform", 16, 900))
+    inp = W.make_decode(wl, fill="zero")
+    kc, ks, vc, vs = quantized_inputs(inp)
+    cache = _f8_cache(kc, ks, vc, vs, inp.block_table)
+    rng = np.random.default_rng(wl.seed + 5)
+    q = W.f32_to_bf16_bits(rng.standard_normal((wl.B, s_new, wl.H, wl.d)).astype(np.float32))
+    say("fp8 decode multi", f"s={s_new} H={H} K={K}")
+    out = binding.gqa_decode_multi(to_dev(q), cache, to_dev(inp.ctx), int(inp.ctx.max()), scale=wl.scale)
+    torch.cuda.synchronize()
+    o = from_dev(out)
+    kd = oracle.dequantize_e4m3_rows(kc, ks)
+    vd = oracle.dequantize_e4m3_rows(vc, vs)
+    got, want = [], []
+    for b in range(wl.B):
+        n = int(inp.ctx[b])
+        rows = np.array([[0, i, h] for i in range(s_new) for h in range(wl.H)], dtype=np.int32)
+        want.append(oracle.attention_rows(as_f64(q[b:b + 1], "bf16"), kd[b:b + 1, :, :n], vd[b:b + 1, :, :n],
+                                          [n - s_new], [n], True, wl.scale, rows))
+        got.append(as_f64(o[b][rows[:, 1], rows[:, 2]], "bf16"))
+    check_close(np.concatenate(got), np.concatenate(want), BF16_TOL, f"fp8 decode multi s={s_new}")
