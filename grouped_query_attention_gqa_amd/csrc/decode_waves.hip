@@ -34,8 +34,6 @@
 //    their common maximum (page §10.2); an item that lies wholly in the
 //    segment is normalised and stored, a cut item leaves one partial per
 //    workgroup for the merge kernel.
-#include <type_traits>
-
 #include "common.h"
 #include "kernels.h"
 #include "worklist.h"
@@ -47,21 +45,16 @@ constexpr int NT = 256;            // threads per workgroup; two workgroups per 
 constexpr int NW = NT / kWave;     // waves per workgroup
 constexpr float TAU = 8.0f;        // lazy-rescale threshold (log2 units)
 
-// EB: bytes of a cached element, 2 (bf16) or 1 (FP8 E4M3 with a scale per row)
-template <int D, int GP, int EB>
+template <int D, int GP>
 struct WCfg {
-    static constexpr bool F8 = EB == 1;
-    static constexpr int RB = D * EB;           // bytes per cache row
-    static constexpr int QRB = D * 2;           // bytes per q / out row (bf16)
-    static constexpr int QCPR = QRB / 16;       // 16-byte chunks per q row
-    static constexpr int CPR = RB / 16;         // 16-byte chunks per cache row
+    static constexpr int RB = D * 2;            // bytes per cache row
+    static constexpr int CPR = RB / 16;         // 16-byte chunks per row
     static constexpr int RPL = kWave / CPR;     // rows per 1 KB wave load
     static constexpr int TT = 8192 / RB;        // keys per tile (8 KB of K)
     static constexpr int NL = TT / RPL;         // 16-byte K loads per lane per tile
-    static constexpr int VB = 4 * EB;           // bytes of a V piece: 4 columns
-    static constexpr int VCPR = D / 4;          // V pieces per row
-    static constexpr int VRPL = kWave / VCPR;   // V rows per wave load
-    static constexpr int VNL = TT / VRPL;       // V loads per lane per tile
+    static constexpr int VCPR = RB / 8;         // 8-byte V chunks per row
+    static constexpr int VRPL = kWave / VCPR;   // V rows per 512 B wave load
+    static constexpr int VNL = TT / VRPL;       // 8-byte V loads per lane per tile
     static constexpr int NP = VNL / 2;          // key pairs per lane per tile
     static constexpr int NGR = TT / 16;         // 16-key groups per tile
     static constexpr int KRS = RB + 16;         // LDS row stride of K: 16 lanes reading 16 rows hit distinct banks
@@ -71,20 +64,12 @@ struct WCfg {
     static constexpr int KD = GP >= 8 ? 1 : 2;       // K tiles in flight per wave (register budget)
     static constexpr int K_WAVE = TT * KRS;          // LDS K buffer per wave
     static constexpr int P_WAVE = VRPL * NP * GP;    // P words per wave (bf16 pairs)
-    static constexpr int Q_BYTES = GP * QRB;
+    static constexpr int Q_BYTES = GP * RB;
     static constexpr int CMB = NW * GP * D * 4;      // wave partials, in the K buffers
-    static_assert(NL == 8 && VNL == (F8 ? 32 : 16), "tile shape");
+    static_assert(NL == 8 && VNL == 16 && NP == 8, "tile shape");
     static_assert(GP >= 1 && GP <= 8 && (GP & (GP - 1)) == 0, "heads per group");
     static_assert(CMB <= NW * K_WAVE, "the merge area fits in the K buffers");
 };
-
-// Two FP8 E4M3 codes (bytes 0-1, or 2-3 with HI) -> a bf16 pair, exactly
-// (every E4M3 value is a bf16 value).
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w)
-{
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-}
 
 template <int N>
 __device__ __forceinline__ void read_p(const uint32_t *src, uint32_t (&pp)[N])
@@ -103,10 +88,10 @@ __device__ __forceinline__ void read_p(const uint32_t *src, uint32_t (&pp)[N])
     }
 }
 
-template <int D, int GP, int EB>
+template <int D, int GP>
 __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
 {
-    using C = WCfg<D, GP, EB>;
+    using C = WCfg<D, GP>;
     __shared__ __attribute__((aligned(16))) char lds_k[NW * C::K_WAVE];
     __shared__ __attribute__((aligned(16))) char lds_q[C::Q_BYTES];
     __shared__ __attribute__((aligned(16))) uint32_t lds_p[NW][C::P_WAVE];
@@ -129,9 +114,8 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     // so the copy only has to be done somewhere in it: thread (item, K or V,
     // 16-byte piece) loads its piece now and stores it once the first tiles
     // are on their way; further items, if any, are copied at the end.
-    // (bf16 caches only: an FP8 cache is appended by the quantising kernel)
     constexpr int IPW = NT / (2 * C::CPR);   // items per workgroup pass
-    const int64_t cp_items = !C::F8 && p.k_new != nullptr ? (int64_t)p.rows * cache.K : 0;
+    const int64_t cp_items = p.k_new != nullptr ? (int64_t)p.rows * cache.K : 0;
     const int64_t cp_stride = (int64_t)gridDim.x * IPW;
     const int64_t cp_first = (int64_t)blockIdx.x * IPW + tid / (2 * C::CPR);
     auto copy_dst = [&](int64_t it, int64_t &src) -> char * {
@@ -205,7 +189,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         sg.b = (int)(sg.row_g / p.Sq);
         sg.g = c.g;
         sg.n_vis = c.n_vis;
-        sg.new_key = !C::F8 && p.k_new != nullptr ? lds_newest[c.row] : -1;
+        sg.new_key = p.k_new != nullptr ? lds_newest[c.row] : -1;
         sg.lo = c.lo;
         sg.jlo = c.jlo;
         sg.j_first = c.j;
@@ -245,59 +229,33 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
         return t;
     };
     const uint32_t k_off = (uint32_t)(krow * C::RB + kc * 16);
-    const uint32_t v_off = (uint32_t)(vr * C::RB + vc * C::VB);
+    const uint32_t v_off = (uint32_t)(vr * C::RB + vc * 8);
     auto load_k = [&](const TileRows &t, uint4 (&kr)[C::NL]) {
 #pragma unroll
         for (int i = 0; i < C::NL; ++i) {
             const int r0 = i * C::RPL;                       // first tile row of the load
             const int64_t base = t.base[r0 / 16];
             uint4 x = make_uint4(0u, 0u, 0u, 0u);
-            if (base >= 0 && r0 + krow < t.nvalid) {
-                if constexpr (C::F8) x = ld16(cache.k + (base + r0 % 16) * C::RB + k_off);
-                else x = ld16(r0 + krow == t.new_row ? p.k_new + t.new_off + kc * 16
-                                                     : cache.k + (base + r0 % 16) * C::RB + k_off);
-            }
+            if (base >= 0 && r0 + krow < t.nvalid)
+                x = ld16(r0 + krow == t.new_row ? p.k_new + t.new_off + kc * 16 : cache.k + (base + r0 % 16) * C::RB + k_off);
             kr[i] = x;
         }
     };
-    using VPiece = typename std::conditional<C::F8, uint32_t, uint2>::type;   // 4 columns of a V row
-    auto load_v = [&](const TileRows &t, VPiece (&vv)[C::VNL]) {
+    auto load_v = [&](const TileRows &t, uint2 (&vv)[C::VNL]) {
 #pragma unroll
         for (int i = 0; i < C::VNL; ++i) {
             const int r0 = i * C::VRPL;
             const int64_t base = t.base[r0 / 16];
-            VPiece y{};
-            if (base >= 0 && r0 + vr < t.nvalid) {
-                if constexpr (C::F8) y = *reinterpret_cast<const uint32_t *>(cache.v + (base + r0 % 16) * C::RB + v_off);
-                else y = *reinterpret_cast<const uint2 *>(r0 + vr == t.new_row ? p.v_new + t.new_off + vc * 8
-                                                                               : cache.v + (base + r0 % 16) * C::RB + v_off);
-            }
+            uint2 y = make_uint2(0u, 0u);
+            if (base >= 0 && r0 + vr < t.nvalid)
+                y = *reinterpret_cast<const uint2 *>(r0 + vr == t.new_row ? p.v_new + t.new_off + vc * 8
+                                                                          : cache.v + (base + r0 % 16) * C::RB + v_off);
             vv[i] = y;
         }
     };
-    // FP8: the K and V scales of the score lane's key (lane = key; 0 for a
-    // key that is not visible, so its zero probability stays zero)
-    const int sgi = st / 16;
-    auto load_scales = [&](const TileRows &t, float &sk, float &sv) {
-        sk = 0.f;
-        sv = 0.f;
-        if constexpr (C::F8) {
-            // one load per 16-key group, each with that group's (uniform) row
-            // base: a lane-indexed pick of the base would go through memory
-            const bool vis = st < t.nvalid && st >= t.first;
-#pragma unroll
-            for (int gi = 0; gi < C::NGR; ++gi) {
-                const int64_t base = t.base[gi];
-                if (sgi == gi && base >= 0 && vis) {
-                    sk = cache.k_scale[base + st % 16];
-                    sv = cache.v_scale[base + st % 16];
-                }
-            }
-        }
-    };
     // this thread's 16 bytes of the q rows of a segment's item (padded heads are zero)
-    const bool q_thread = tid < GP * C::QCPR;
-    const int q_r = tid / C::QCPR, q_ch = tid % C::QCPR;
+    const bool q_thread = tid < GP * C::CPR;
+    const int q_r = tid / C::CPR, q_ch = tid % C::CPR;
     auto load_q = [&](const Seg &sg) {
         uint4 x = make_uint4(0u, 0u, 0u, 0u);
         if (q_thread && q_r < G) x = ld16(p.q + ((sg.row_g * H + (int64_t)sg.g * G + q_r) * D) * 2 + q_ch * 16);
@@ -337,8 +295,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     // start V(i) into them; score tile i into P(i).  K has KD steps to
     // arrive, V one, and V needs a single register buffer.
     uint4 kA[C::NL], kB[C::NL];
-    VPiece vbuf[C::VNL];
-    float skA = 0.f, svA = 0.f, skB = 0.f, svB = 0.f;   // FP8: scales of the key tiles in kA / kB
+    uint2 vbuf[C::VNL];
     int gi = 0;
     Seg cur = make_seg(tau0);
     TileRows r1, r2;   // rows of the stream's next tiles (K already started)
@@ -346,12 +303,8 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
     {
         const uint4 x = load_q(cur);
         load_k(r1, kA);
-        load_scales(r1, skA, svA);
-        if constexpr (C::KD == 2) {
-            load_k(r2, kB);
-            load_scales(r2, skB, svB);
-        }
-        if (q_thread) *reinterpret_cast<uint4 *>(lds_q + q_r * C::QRB + q_ch * 16) = x;
+        if constexpr (C::KD == 2) load_k(r2, kB);
+        if (q_thread) *reinterpret_cast<uint4 *>(lds_q + q_r * C::RB + q_ch * 16) = x;
         if (cp_to != nullptr) st16(cp_to, cp_val);
         __syncthreads();
     }
@@ -384,20 +337,10 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             }
 #pragma unroll
             for (int kk = 0; kk < C::NP; ++kk) {
-                // rows 2kk*VRPL + vr and VRPL later; (x, y): columns (4vc, 4vc+1), (4vc+2, 4vc+3)
-                uint32_t ax, ay, bx, by;
-                if constexpr (C::F8) {
-                    ax = fp8x2_to_bf16x2<false>(vbuf[2 * kk]);
-                    ay = fp8x2_to_bf16x2<true>(vbuf[2 * kk]);
-                    bx = fp8x2_to_bf16x2<false>(vbuf[2 * kk + 1]);
-                    by = fp8x2_to_bf16x2<true>(vbuf[2 * kk + 1]);
-                } else {
-                    ax = vbuf[2 * kk].x; ay = vbuf[2 * kk].y;
-                    bx = vbuf[2 * kk + 1].x; by = vbuf[2 * kk + 1].y;
-                }
+                const uint2 a = vbuf[2 * kk], bb = vbuf[2 * kk + 1];   // rows 2kk*VRPL + vr and VRPL later
                 uint32_t vv[4];
-                vv[0] = pair_lo(ax, bx); vv[1] = pair_hi(ax, bx);
-                vv[2] = pair_lo(ay, by); vv[3] = pair_hi(ay, by);
+                vv[0] = pair_lo(a.x, bb.x); vv[1] = pair_hi(a.x, bb.x);
+                vv[2] = pair_lo(a.y, bb.y); vv[3] = pair_hi(a.y, bb.y);
                 uint32_t pp[GP];
                 read_p<GP>(pw + (vr * C::NP + kk) * GP, pp);
 #pragma unroll
@@ -415,18 +358,14 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             const TileRows ra = ia < n_w ? tile_rows(cur.b, cur.g, cur.lo, cur.n_vis, cur.new_key, cur.jlo + cur.j_first + wave + NW * ia)
                                          : (ia == n_w ? after1 : after2);
             // K(i) -> this wave's LDS buffer (padded rows); start K(i + KD) in its place
-            float sk = 0.f, sv = 0.f;   // FP8: the scales of tile i's key on this lane
-            auto k_step = [&](uint4 (&kx)[C::NL], float &skx, float &svx) {
+            auto k_step = [&](uint4 (&kx)[C::NL]) {
 #pragma unroll
                 for (int ii = 0; ii < C::NL; ++ii)
                     *reinterpret_cast<uint4 *>(kw + (ii * C::RPL + krow) * C::KRS + kc * 16) = kx[ii];
                 load_k(ra, kx);
-                sk = skx;
-                sv = svx;
-                load_scales(ra, skx, svx);
             };
-            if (C::KD == 2 && (gi & 1)) k_step(kB, skB, svB);
-            else k_step(kA, skA, svA);
+            if (C::KD == 2 && (gi & 1)) k_step(kB);
+            else k_step(kA);
             if constexpr (C::KD == 2) { r1 = r2; r2 = ra; }
             else r1 = ra;
             // P(i-1) V(i-1), then start V(i)
@@ -442,42 +381,18 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
 #pragma unroll
                 for (int ch = 0; ch < C::CPR; ++ch) {
                     const uint4 kv = *reinterpret_cast<const uint4 *>(kw + st * C::KRS + ch * 16);
-                    if constexpr (C::F8) {
-                        // 16 codes -> 8 bf16 pairs (exact), against 16 q values
-                        uint32_t k2[8];
-                        k2[0] = fp8x2_to_bf16x2<false>(kv.x); k2[1] = fp8x2_to_bf16x2<true>(kv.x);
-                        k2[2] = fp8x2_to_bf16x2<false>(kv.y); k2[3] = fp8x2_to_bf16x2<true>(kv.y);
-                        k2[4] = fp8x2_to_bf16x2<false>(kv.z); k2[5] = fp8x2_to_bf16x2<true>(kv.z);
-                        k2[6] = fp8x2_to_bf16x2<false>(kv.w); k2[7] = fp8x2_to_bf16x2<true>(kv.w);
 #pragma unroll
-                        for (int h = 0; h < C::HPL; ++h) {
-                            const char *qrow = lds_q + (qh * C::HPL + h) * C::QRB + ch * 32;
-                            const uint4 q0 = *reinterpret_cast<const uint4 *>(qrow);
-                            const uint4 q1 = *reinterpret_cast<const uint4 *>(qrow + 16);
-                            a0[h] = dot2_bf16(q0.x, k2[0], a0[h]);
-                            a1[h] = dot2_bf16(q0.y, k2[1], a1[h]);
-                            a0[h] = dot2_bf16(q0.z, k2[2], a0[h]);
-                            a1[h] = dot2_bf16(q0.w, k2[3], a1[h]);
-                            a0[h] = dot2_bf16(q1.x, k2[4], a0[h]);
-                            a1[h] = dot2_bf16(q1.y, k2[5], a1[h]);
-                            a0[h] = dot2_bf16(q1.z, k2[6], a0[h]);
-                            a1[h] = dot2_bf16(q1.w, k2[7], a1[h]);
-                        }
-                    } else {
-#pragma unroll
-                        for (int h = 0; h < C::HPL; ++h) {
-                            const uint4 qv = *reinterpret_cast<const uint4 *>(lds_q + (qh * C::HPL + h) * C::QRB + ch * 16);
-                            a0[h] = dot2_bf16(qv.x, kv.x, a0[h]);
-                            a1[h] = dot2_bf16(qv.y, kv.y, a1[h]);
-                            a0[h] = dot2_bf16(qv.z, kv.z, a0[h]);
-                            a1[h] = dot2_bf16(qv.w, kv.w, a1[h]);
-                        }
+                    for (int h = 0; h < C::HPL; ++h) {
+                        const uint4 qv = *reinterpret_cast<const uint4 *>(lds_q + (qh * C::HPL + h) * C::RB + ch * 16);
+                        a0[h] = dot2_bf16(qv.x, kv.x, a0[h]);
+                        a1[h] = dot2_bf16(qv.y, kv.y, a1[h]);
+                        a0[h] = dot2_bf16(qv.z, kv.z, a0[h]);
+                        a1[h] = dot2_bf16(qv.w, kv.w, a1[h]);
                     }
                 }
                 const bool valid = s_lane && st < rows.nvalid && st >= rows.first;
-                const float sl = C::F8 ? sk * p.scale_log2 : p.scale_log2;   // FP8: the row's K scale
 #pragma unroll
-                for (int h = 0; h < C::HPL; ++h) sc[h] = valid ? (a0[h] + a1[h]) * sl : -INFINITY;
+                for (int h = 0; h < C::HPL; ++h) sc[h] = valid ? (a0[h] + a1[h]) * p.scale_log2 : -INFINITY;
             }
 
             // ---- lazy reference maximum: one vote per tile ---------------------
@@ -503,9 +418,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
                 const float pk = fast_exp2(sc[h] - m_ref[h]);   // 0 for keys past the end
                 const uint32_t pb = f32_to_bf16_rne(pk);
                 l_run[h] += __uint_as_float(pb << 16);
-                // FP8: the row's V scale rides on its probability
-                const uint32_t pvb = C::F8 ? f32_to_bf16_rne(pk * sv) : pb;
-                if (s_lane) pw16[p_slot + 2 * h] = (uint16_t)pvb;
+                if (s_lane) pw16[p_slot + 2 * h] = (uint16_t)pb;
             }
         }
         if (n_w > 0) pv(pend_rescale);   // the last tile's V sum
@@ -576,30 +489,30 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             }
         }
         if (!has_next) break;
-        if (q_thread) *reinterpret_cast<uint4 *>(lds_q + q_r * C::QRB + q_ch * 16) = q_next;
+        if (q_thread) *reinterpret_cast<uint4 *>(lds_q + q_r * C::RB + q_ch * 16) = q_next;
         __syncthreads();   // the merge area is free again and the next q is in place
         cur = nxt;
     }
     copy_rest();
 }
 
-template <int D, int GP, int EB>
+template <int D, int GP>
 hipError_t launch_w(const RowAttnParams &p, hipStream_t s)
 {
-    hipLaunchKernelGGL((decode_waves_kernel<D, GP, EB>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL((decode_waves_kernel<D, GP>), dim3(p.num_wgs), dim3(NT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_merge_pieces(p, WCfg<D, GP, EB>::TT, p.num_wgs, s);
+    return launch_merge_pieces(p, WCfg<D, GP>::TT, p.num_wgs, s);
 }
 
-template <int D, int EB>
+template <int D>
 hipError_t launch_wd(const RowAttnParams &p, int gp, hipStream_t s)
 {
     switch (gp) {
-    case 1: return launch_w<D, 1, EB>(p, s);
-    case 2: return launch_w<D, 2, EB>(p, s);
-    case 4: return launch_w<D, 4, EB>(p, s);
-    case 8: return launch_w<D, 8, EB>(p, s);
+    case 1: return launch_w<D, 1>(p, s);
+    case 2: return launch_w<D, 2>(p, s);
+    case 4: return launch_w<D, 4>(p, s);
+    case 8: return launch_w<D, 8>(p, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -609,9 +522,7 @@ hipError_t launch_wd(const RowAttnParams &p, int gp, hipStream_t s)
 bool decode_waves_supported(const RowAttnParams &p, int gp)
 {
     // paged caches need blocks of at least 16 tokens (a wave load stays in one block)
-    // FP8 (E4M3 with row scales): d = 128 only
-    return !p.prefill && !p.whole_items && (p.cache.elem_bytes == 2 || (p.cache.elem_bytes == 1 && p.cache.d == 128)) &&
-           gp <= 8 &&
+    return !p.prefill && !p.whole_items && p.cache.elem_bytes == 2 && gp <= 8 &&
            (p.cache.d == 64 || p.cache.d == 128) && p.num_wgs <= kStreamWGs &&
            (p.cache.block_table == nullptr || p.cache.log2_bs >= 4);
 }
@@ -619,8 +530,7 @@ bool decode_waves_supported(const RowAttnParams &p, int gp)
 hipError_t launch_decode_waves(const RowAttnParams &p, int gp, hipStream_t stream)
 {
     if (!decode_waves_supported(p, gp)) return hipErrorInvalidValue;
-    if (p.cache.elem_bytes == 1) return launch_wd<128, 1>(p, gp, stream);
-    return p.cache.d == 128 ? launch_wd<128, 2>(p, gp, stream) : launch_wd<64, 2>(p, gp, stream);
+    return p.cache.d == 128 ? launch_wd<128>(p, gp, stream) : launch_wd<64>(p, gp, stream);
 }
 
 }  // namespace gqa
