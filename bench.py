@@ -46,9 +46,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 # gqa_decode is the main kernel plus the small merge of cut items; events time both
-DECODE_KERNELS = ("decode_waves_kernel<128, 4> (with the append of the newest token) + merge_pieces_kernel<128, true> "
+DECODE_KERNELS = ("decode_mfma_kernel<1, false> (with the append of the newest token) + merge_rows_kernel "
                   "(one gqa_decode_step call)")
-DECODE_SOURCES = ("decode_waves.hip", "stream_attention.hip", "worklist.h", "kernels.h", "common.h")
+DECODE_SOURCES = ("decode_mfma.hip", "stream_attention.hip", "worklist.h", "kernels.h", "common.h")
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "GQA decode HBM GB/s (% of peak) + causal prefill TFLOP/s (% MFMA peak), bf16"
 MALL_BYTES = 256 * 2**20
