@@ -145,6 +145,19 @@ class PrefillRun:
             kp, vp = prior
             zero = torch.zeros(wl.B, dtype=torch.int32, device=DEV)
             binding.gqa_kv_append(self.cache, to_dev(kp), to_dev(vp), zero)
+        torch.cuda.synchronize()
+        self.k0, self.v0 = from_dev(self.k).copy(), from_dev(self.v).copy()
+
+    def check_cache(self, what: str):
+        """After run(): the cache bytes are exactly those the oracle's append of the
+        new rows writes into the cache as it was before the call."""
+        for name, before, new, got in (("k", self.k0, self.inp.k_new, self.k), ("v", self.v0, self.inp.v_new, self.v)):
+            want = before.copy()
+            if self.table is None:
+                oracle.kv_append(want, new, self.inp.start_pos)
+            else:
+                oracle.kv_append_paged(want, new, self.inp.start_pos, self.table)
+            assert from_dev(got).tobytes() == want.tobytes(), f"{what}: cache {name} after the prefill"
 
     def run(self, causal=True, window=0) -> torch.Tensor:
         out = binding.gqa_prefill(self.q, self.kn, self.vn, self.cache, self.start, causal=causal,

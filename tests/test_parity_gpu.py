@@ -181,6 +181,7 @@ def _prefill_case(inp, what, rows=None, causal=True, window=0, **kw):
     say("prefill", what, wl.B, wl.s, wl.H, wl.K, wl.d, "causal", causal, "window", window)
     run = PrefillRun(inp, **kw)
     out = from_dev(run.run(causal=causal, window=window))
+    run.check_cache(what)   # the bytes the oracle's append writes
     rows = _all_rows(wl.B, wl.s, wl.H) if rows is None else rows
     want = oracle_prefill_rows(inp, rows, causal=causal, prior=kw.get("prior"), window=window)
     return check_close(gpu_rows(out, rows, wl.dtype), want, _tol(wl.dtype), what), run

@@ -102,6 +102,7 @@ def test_prefill_window_bf16(window, H, K, d):
     say("prefill window", H, K, d, window)
     run = PrefillRun(inp)
     out = from_dev(run.run(window=window))
+    run.check_cache("window prefill")
     rows = np.array([[b, i, h] for b in range(wl.B) for i in range(wl.s) for h in range(wl.H)], np.int32)
     want = oracle_prefill_rows(inp, rows, window=window)
     check_close(gpu_rows(out, rows, "bf16"), want, BF16_TOL, f"bf16 prefill window {window}")
@@ -126,6 +127,7 @@ def test_prefill_window_after_prefix(dtype):
     say("prefill window after a prefix", dtype)
     run = PrefillRun(inp, prior=prior)
     out = from_dev(run.run(window=120))
+    run.check_cache("window prefill after a prefix")
     rows = np.array([[b, i, h] for b in range(wl.B) for i in range(wl.s) for h in range(wl.H)], np.int32)
     want = oracle_prefill_rows(inp, rows, prior=prior, window=120)
     check_close(gpu_rows(out, rows, dtype), want, _tol(dtype), f"{dtype} prefill window after prefix")
@@ -139,6 +141,7 @@ def test_prefill_window_paged():
     say("prefill window paged")
     run = PrefillRun(inp, paged_blocks=(table, n_pool))
     out = from_dev(run.run(window=45))
+    run.check_cache("paged window prefill")
     rows = np.array([[b, i, h] for b in range(wl.B) for i in range(wl.s) for h in range(wl.H)], np.int32)
     want = oracle_prefill_rows(inp, rows, window=45)
     check_close(gpu_rows(out, rows, "bf16"), want, BF16_TOL, "paged prefill window")
