@@ -380,7 +380,8 @@ def main():
         db.step(i)
         ev[i][1].record()
     torch.cuda.synchronize()
-    dec_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ev_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    dec_ms = float(np.mean(ev_ms))
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = step_bytes / (dec_ms * 1e-3) / 1e9
     traffic = committed_traffic("decode/llama3_8b_decode")
@@ -415,7 +416,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": DECODE_KERNELS,
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": step_bytes, "avg_launch_us": round(dec_ms * 1e3, 2)},
+                     "bytes_per_launch": step_bytes, "avg_launch_us": round(dec_ms * 1e3, 2),
+                     "median_launch_us": round(float(np.median(ev_ms)) * 1e3, 2),
+                     "p90_launch_us": round(float(np.percentile(ev_ms, 90)) * 1e3, 2)},
         "two_call_step": {"us": round(two_ms * 1e3, 2), "GB/s": round(step_bytes / (two_ms * 1e-3) / 1e9, 1),
                           "calls": "gqa_kv_append + gqa_decode"},
     }
@@ -512,13 +515,16 @@ def bench_prefill(wl, iters, warmup):
         binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale, window=wl.window)
         b.record()
     torch.cuda.synchronize()
-    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ev_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms = float(np.mean(ev_ms))
     flops = causal_flops(wl)
     tf = flops / (ms * 1e-3) / 1e12
     log(f"prefill {wl.name}: {ms * 1e3:.1f} us (append + attention), {tf:.1f} TFLOP/s "
         f"({100 * tf / BF16_MFMA_PEAK_TFLOPS:.1f}% of bf16 MFMA peak)")
     return {"workload": wl.name, "B": wl.B, "s": wl.s, "start": wl.start, "H": wl.H, "K": wl.K, "d": wl.d,
-            "paged": wl.paged, "us_per_call": round(ms * 1e3, 2), "flops": flops, "TFLOP/s": round(tf, 2),
+            "paged": wl.paged, "us_per_call": round(ms * 1e3, 2),
+            "median_us": round(float(np.median(ev_ms)) * 1e3, 2), "p90_us": round(float(np.percentile(ev_ms, 90)) * 1e3, 2),
+            "flops": flops, "TFLOP/s": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                          "note": "time covers the append and the attention kernel"}}
