@@ -536,6 +536,9 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(RowAttnParams p, int W)
     const int R = mq * G;
     const int rho = blockIdx.z * kMergeRows + (int)threadIdx.x / (D / 4), col = ((int)threadIdx.x % (D / 4)) * 4;
     const int64_t seq = p.row0 + row;
+    // the table entries and the context length are read together (one
+    // memory round trip instead of two)
+    const int64_t T = p.prefix[p.rows], pre = p.prefix[row];
     const int n_vis = row_visible(p, seq);
     const int lo = row_first(p, seq, n_vis);
     uint16_t *dst = reinterpret_cast<uint16_t *>(p.out) +
@@ -544,9 +547,8 @@ __global__ __launch_bounds__(256) void merge_rows_kernel(RowAttnParams p, int W)
         if (rho < R) *reinterpret_cast<uint2 *>(dst) = make_uint2(0u, 0u);
         return;
     }
-    const int64_t T = p.prefix[p.rows];
     const int64_t tiles = item_tiles(lo, n_vis, TT);
-    const int64_t a = p.prefix[row] + (int64_t)g * tiles, e = a + tiles - 1;
+    const int64_t a = pre + (int64_t)g * tiles, e = a + tiles - 1;
     const int64_t wa = slice_owner(a, T, W), wb = slice_owner(e, T, W);
     if (wa == wb) return;
     // the workspace slots of the pieces: with at least one tile per slice
