@@ -245,3 +245,17 @@ def test_full_size_prefill_sampled():
     cache = np.full((wl.B, wl.K, wl.s, wl.d), W.sentinel("bf16", "nan"), dtype=np.uint16)
     oracle.kv_append(cache, inp.k_new, inp.start_pos)
     assert from_dev(run.k).tobytes() == cache.tobytes()
+
+
+def test_full_size_chunked_prefill_sampled():
+    """The chunked paged prefill at the size the bench times: 512 new tokens
+    after a 3584-token prefix already in a shuffled 16-token paged cache."""
+    wl = W.WORKLOADS["chunked_prefill_paged"]
+    inp = W.make_prefill(wl)
+    rng = np.random.default_rng(19)
+    P = wl.start
+    prior = (_random_rows(rng, (wl.B, P, wl.K, wl.d), "bf16"), _random_rows(rng, (wl.B, P, wl.K, wl.d), "bf16"))
+    table, n_pool = W.deal_blocks(rng, np.full(wl.B, P + wl.s, np.int32), wl.block_size)
+    pos = sorted({0, 1, 15, 16, 63, 64, 255, 511} | set(int(x) for x in rng.integers(0, wl.s, 4)))
+    rows = np.array([[b, i, h] for b in range(wl.B) for i in pos for h in (0, 3, 4, 17, 31)], np.int32)
+    _prefill_case(inp, "chunked_prefill_paged (sampled)", rows=rows, paged_blocks=(table, n_pool), prior=prior)

@@ -40,6 +40,19 @@ def test_decode_window_bf16(H, K, window):
     _decode(W.make_decode(wl, ctx_override=CTX), f"bf16 H={H} K={K}", window)
 
 
+def test_full_size_window_decode_sampled():
+    """The Mistral-7B-shaped window decode at the size the bench times
+    (B=32, ctx 16384, window 4096), on sampled sequences and heads."""
+    wl = W.WORKLOADS["mistral_7b_window_decode"]
+    inp = W.make_decode(wl)
+    seqs = [0, 13, wl.B - 1]
+    heads = [0, 3, 4, 17, wl.H - 1]
+    say("decode window full size", wl.B, wl.H, wl.K, wl.d, "window", wl.window)
+    out = from_dev(DecodeRun(inp).run(window=wl.window))
+    rows, want = oracle_decode_rows(inp, seqs=seqs, heads=heads, window=wl.window)
+    check_close(gpu_rows(out, rows, "bf16"), want, BF16_TOL, "mistral_7b_window_decode (sampled)")
+
+
 @pytest.mark.parametrize("window", [1, 33, 600])
 def test_decode_window_f32(window):
     wl = W.WORKLOADS["tiny_decode_f32"].replace(B=4, H=8, K=2, d=64, ctx=("uniform", 1, 1500))
