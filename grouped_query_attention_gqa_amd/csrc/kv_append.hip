@@ -6,27 +6,35 @@
 // page §8.2).  Pure data movement: one thread moves one 16-byte piece, so the
 // copy is bit-exact and both the reads (token-major) and the writes (one
 // contiguous row per KV head) are coalesced.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace gqa {
 
+// WIDE: 64-bit index arithmetic, for launches of 2^31 pieces or more; the
+// usual launch uses 32-bit arithmetic (the divisions are most of the work a
+// thread does besides its one load and store).
+template <bool WIDE>
 __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p)
 {
+    typedef typename std::conditional<WIDE, uint64_t, uint32_t>::type I;
     const CacheView &c = p.cache;
     const int row_bytes = c.d * c.elem_bytes;
-    const int cpr = row_bytes >> 4;                       // 16-byte pieces per row
-    const int64_t per_tensor = (int64_t)p.B * p.s_new * c.K * cpr;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= 2 * per_tensor) return;
-    const int which = idx >= per_tensor;                  // 0: K, 1: V
-    int64_t r = which ? idx - per_tensor : idx;
-    const int piece = (int)(r % cpr);
-    r /= cpr;
-    const int g = (int)(r % c.K);
-    r /= c.K;
-    const int t = (int)(r % p.s_new);
-    const int b = (int)(r / p.s_new);
+    const int lcpr = __builtin_ctz((unsigned)row_bytes >> 4);   // 16-byte pieces per row: a power of two
+    const I rows = (I)p.B * (I)p.s_new * (I)c.K;                 // rows per tensor
+    const I idx = (I)blockIdx.x * (I)blockDim.x + (I)threadIdx.x;
+    if (idx >= (rows << (lcpr + 1))) return;
+    const int piece = (int)(idx & ((1u << lcpr) - 1));
+    I r = idx >> lcpr;
+    const int which = r >= rows;                          // 0: K, 1: V
+    if (which) r -= rows;
+    const I bt = r / (I)c.K;                              // b * s_new + t
+    const int g = (int)(r - bt * (I)c.K);
+    const I b_ = bt / (I)p.s_new;
+    const int t = (int)(bt - b_ * (I)p.s_new);
+    const int b = (int)b_;
 
     const int64_t pos = p.ctx_lens != nullptr ? (int64_t)p.ctx_lens[b] - 1 : (int64_t)p.start_pos[b] + t;
     if (pos < 0 || pos >= c.capacity) return;
@@ -38,18 +46,11 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p)
         if (blk < 0 || blk >= c.num_blocks) return;
         dst_row = (((int64_t)blk * c.K + g) << c.log2_bs) + (pos & ((1 << c.log2_bs) - 1));
     }
-    const char *src = (which ? p.v_new : p.k_new) +
-                      (((int64_t)b * p.s_new + t) * c.K + g) * row_bytes + piece * 16;
+    const char *src = (which ? p.v_new : p.k_new) + ((int64_t)bt * c.K + g) * row_bytes + piece * 16;
     char *dst = (which ? c.v : c.k) + dst_row * row_bytes + piece * 16;
     st16(dst, ld16(src));
 }
 
-// FP8 cache: thread (row, 8-element piece) quantises 8 bf16 values of a new
-// row.  The row's largest magnitude comes from the 16 lanes that hold it
-// (d = 128); scale = amax / 448 and code = E4M3(x / scale) with IEEE fp32
-// divisions and the hardware's round-to-nearest-even conversion, so the
-// codes are those of the format's definition (inference-optimisation page
-// §15.5.1: a scale per token and head, FP8 E4M3).
 constexpr int kF8Lanes = 16;   // lanes per 128-element row
 __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendParams p)
 {
@@ -109,11 +110,15 @@ hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream)
         return hipGetLastError();
     }
     const int cpr = p.cache.d * p.cache.elem_bytes / 16;
+    if (cpr <= 0 || (cpr & (cpr - 1)) != 0) return hipErrorInvalidValue;
     const int64_t total = 2LL * p.B * p.s_new * p.cache.K * cpr;
     if (total == 0) return hipSuccess;
     const int64_t blocks = (total + 255) / 256;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    if (blocks * 256 <= 0x7fffffffLL)
+        hipLaunchKernelGGL(kv_append_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL(kv_append_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
