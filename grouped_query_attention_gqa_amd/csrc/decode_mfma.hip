@@ -523,11 +523,11 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 }
 
 // The pieces of the items cut by slice boundaries: workgroup (g, row, z)
-// merges rows 8 z .. 8 z + 7 of item (sequence row0 + row, group g) with
+// merges rows 4 z .. 4 z + 3 of item (sequence row0 + row, group g) with
 // their global max and sum (inference-optimisation page §10.2), one float4
 // of a row per thread; an item with no visible key gets zero rows.
-constexpr int kMergeRows = 8;
-__global__ __launch_bounds__(256) void merge_rows_kernel(RowAttnParams p, int W)
+constexpr int kMergeRows = 4;   // rows per workgroup (more workgroups for the many-piece items of large groups)
+__global__ __launch_bounds__(kMergeRows * (D / 4)) void merge_rows_kernel(RowAttnParams p, int W)
 {
     __shared__ int slots[kStreamWGs];
     __shared__ int n_slots;
@@ -624,7 +624,7 @@ hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int R = (p.mq > 1 ? p.mq : 1) * p.G;
-    hipLaunchKernelGGL(merge_rows_kernel, dim3(p.cache.K, p.rows, (R + kMergeRows - 1) / kMergeRows), dim3(256), 0, s,
+    hipLaunchKernelGGL(merge_rows_kernel, dim3(p.cache.K, p.rows, (R + kMergeRows - 1) / kMergeRows), dim3(kMergeRows * (D / 4)), 0, s,
                        p, p.num_wgs);
     return hipGetLastError();
 }
