@@ -127,6 +127,16 @@ __device__ __forceinline__ uint2 gld8(gmem_t *p)
 {
     return __builtin_bit_cast(uint2, *(const __attribute__((address_space(1))) u32x2_t *)p);
 }
+// Non-temporal (streaming) loads, for cache rows a call reads once: their
+// lines are the first the caches give up.
+__device__ __forceinline__ uint4 ld16_nt(const void *p)
+{
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p)));
+}
+__device__ __forceinline__ uint2 ld8_nt(const void *p)
+{
+    return __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p)));
+}
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
 }  // namespace gqa

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             const int64_t base = t.base[r0 / 16];
             uint4 x = make_uint4(0u, 0u, 0u, 0u);
             if (base >= 0 && r0 + krow < t.nvalid)
-                x = ld16(r0 + krow == t.new_row ? p.k_new + t.new_off + kc * 16 : cache.k + (base + r0 % 16) * C::RB + k_off);
+                x = ld16_nt(r0 + krow == t.new_row ? p.k_new + t.new_off + kc * 16 : cache.k + (base + r0 % 16) * C::RB + k_off);
             kr[i] = x;
         }
     };
@@ -248,8 +248,8 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
             const int64_t base = t.base[r0 / 16];
             uint2 y = make_uint2(0u, 0u);
             if (base >= 0 && r0 + vr < t.nvalid)
-                y = *reinterpret_cast<const uint2 *>(r0 + vr == t.new_row ? p.v_new + t.new_off + vc * 8
-                                                                          : cache.v + (base + r0 % 16) * C::RB + v_off);
+                y = ld8_nt(r0 + vr == t.new_row ? p.v_new + t.new_off + vc * 8
+                                                : cache.v + (base + r0 % 16) * C::RB + v_off);
             vv[i] = y;
         }
     };
