@@ -340,7 +340,7 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus above 1 is not supported",
                           "n_gpus": args.gpus}))
-        sys.stderr.write("bench.py: only --gpus 1 is supported (single-GPU build)\n")
+        sys.stderr.write("bench.py: only --gpus 1 is supported: the library runs on one GPU\n")
         sys.exit(2)
     import torch
     from grouped_query_attention_gqa_amd import binding
