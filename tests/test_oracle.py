@@ -411,6 +411,195 @@ def test_paged_attention_equals_contiguous(oracle_lib):
 
 
 # ---------------------------------------------------------------------------
+# paged cache: the oracle's append and gathers against plain NumPy indexing
+# (inference-optimisation page §8.2: token t of a sequence lives in physical
+# block table[b, t // bs], slot t % bs; the pool is [blocks, K, bs, d])
+# ---------------------------------------------------------------------------
+
+def _coded_pool(N, K, bs, d, dtype):
+    """A pool whose every element names its (block, head, slot, column): any
+    wrong block, head, slot or stride shows as a different value."""
+    n, g, s, c = np.meshgrid(np.arange(N), np.arange(K), np.arange(bs), np.arange(d), indexing="ij")
+    code = ((n * K + g) * bs + s) * d + c
+    if dtype == np.uint16:               # bf16 bit patterns, stored as raw 16-bit words
+        return (code % 65000 + 1).astype(np.uint16)
+    return (code + 1).astype(dtype)
+
+
+def _paged_case(rng, bs, K=3, d=5):
+    ctx = np.array([1, bs, 3 * bs + 1, 2 * bs - 1], np.int32)
+    need = (ctx + bs - 1) // bs
+    n_pool = int(need.sum()) + 3                   # three blocks no sequence owns
+    perm = rng.permutation(n_pool).astype(np.int32)
+    table = np.full((len(ctx), int(need.max()) + 1), -1, np.int32)   # one spare column
+    off = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[off:off + nb]
+        off += int(nb)
+    return ctx, table, n_pool, K, d
+
+
+def _numpy_gather(pool, table, ctx, S_out, fill):
+    """out[b, g, t] = pool[table[b, t // bs], g, t % bs] for t < ctx[b], written
+    independently of the oracle with fancy indexing."""
+    N, K, bs, d = pool.shape
+    out = np.full((len(ctx), K, S_out, d), fill, dtype=pool.dtype)
+    for b in range(len(ctx)):
+        t = np.arange(min(int(ctx[b]), S_out))
+        blk = table[b, t // bs]
+        out[b, :, t] = pool[blk, :, t % bs]       # advanced indices first: [t, K, d]
+    return out
+
+
+def _gather_raw_pin_holds(gather):
+    """True when `gather(pool, table, ctx, S_out, fill)` equals the NumPy
+    indexing on every block size, element type and sequence."""
+    rng = np.random.default_rng(31)
+    for bs in (1, 4, 16):
+        for dtype in (np.uint16, np.float32, np.float64):
+            ctx, table, N, K, d = _paged_case(rng, bs)
+            pool = _coded_pool(N, K, bs, d, dtype)
+            S_out = int(ctx.max()) + 2
+            fill = dtype(0) if dtype == np.uint16 else dtype(-1)
+            got = gather(pool, table, ctx, S_out, fill)
+            if got.shape != (len(ctx), K, S_out, d) or not np.array_equal(got, _numpy_gather(pool, table, ctx, S_out,
+                                                                                               fill)):
+                return False
+    return True
+
+
+def test_gather_paged_raw_matches_numpy_indexing(oracle_lib):
+    assert _gather_raw_pin_holds(oracle.gather_paged_raw)
+
+
+def test_gather_paged_f64_matches_numpy_indexing(oracle_lib):
+    rng = np.random.default_rng(32)
+    for bs in (1, 4, 16):
+        ctx, table, N, K, d = _paged_case(rng, bs)
+        pool = _coded_pool(N, K, bs, d, np.float64)
+        S_out = int(ctx.max()) + 2
+        got = oracle.gather_paged(pool, table, ctx, S_out)
+        want = _numpy_gather(pool, table, ctx, S_out, np.nan)
+        assert np.array_equal(got, want, equal_nan=True)
+
+
+def test_gather_paged_raw_leaves_fill_for_invalid_blocks(oracle_lib):
+    """Visible positions whose block id is outside the pool are counted and keep the fill."""
+    rng = np.random.default_rng(33)
+    ctx, table, N, K, d = _paged_case(rng, 4)
+    pool = _coded_pool(N, K, 4, d, np.float32)
+    table = table.copy()
+    table[2, 1] = N            # one past the pool
+    table[3, 0] = -5
+    S_out = int(ctx.max())
+    out = np.full((len(ctx), K, S_out, d), -1.0, np.float32)
+    lib = oracle._load()
+    cl = np.ascontiguousarray(ctx, np.int32)
+    bad = lib.oracle_gather_paged_raw(pool.ctypes.data, 4, table.ctypes.data, table.shape[1], N, 4,
+                                      cl.ctypes.data, len(ctx), K, d, S_out, out.ctypes.data)
+    assert bad == 2 * 4 * K    # two 4-token blocks of K heads each
+    want = _numpy_gather(pool, np.where((table >= 0) & (table < N), table, 0), ctx, S_out, -1.0)
+    want[2, :, 4:8] = -1.0
+    want[3, :, 0:4] = -1.0
+    assert np.array_equal(out, want)
+    with pytest.raises(ValueError):
+        oracle.gather_paged_raw(pool, table, ctx, S_out, np.float32(-1))
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+@pytest.mark.parametrize("dtype", [np.uint16, np.float32])
+def test_append_paged_matches_numpy_indexing(oracle_lib, bs, dtype):
+    """pool[table[b, p // bs], g, p % bs] = new[b, t, g] with p = start[b] + t; every
+    other slot keeps its value, and positions past the table are dropped."""
+    rng = np.random.default_rng(34 + bs)
+    ctx, table, N, K, d = _paged_case(rng, bs)
+    B, s_new = len(ctx), 3
+    start = np.array([0, bs - 1, 3 * bs - 1, 2 * bs - 3], np.int32)
+    pool = _coded_pool(N, K, bs, d, dtype)
+    new = (np.arange(B * s_new * K * d).reshape(B, s_new, K, d) % 50000 + 60000).astype(dtype)
+    want = pool.copy()
+    dropped_want = 0
+    for b in range(B):
+        for t in range(s_new):
+            p = int(start[b]) + t
+            blk = table[b, p // bs] if p // bs < table.shape[1] else -1
+            if not 0 <= blk < N:
+                dropped_want += K
+                continue
+            want[blk, :, p % bs] = new[b, t]
+    got = pool.copy()
+    dropped = oracle.kv_append_paged(got, new, start, table)
+    assert dropped == dropped_want
+    assert np.array_equal(got, want)
+
+
+# planted mistakes in the paged indexing: each must fail the pins above,
+# while an append/gather round trip with the same mistake on both sides
+# would still pass
+
+def _mutant_gather(kind):
+    def gather(pool, table, ctx, S_out, fill):
+        N, K, bs, d = pool.shape
+        flat = pool.reshape(-1)
+        out = np.full((len(ctx), K, S_out, d), fill, dtype=pool.dtype)
+        for b in range(len(ctx)):
+            for g in range(K):
+                for t in range(min(int(ctx[b]), S_out)):
+                    col = t // bs + (1 if kind == "block_column_off_by_one" else 0)
+                    blk = int(table[b, col])
+                    if not 0 <= blk < N:
+                        continue
+                    if kind == "head_slot_swapped":          # reads the pool as [N, bs, K, d]
+                        row = (blk * bs + t % bs) * K + g
+                    else:
+                        row = (blk * K + g) * bs + t % bs
+                    out[b, g, t] = flat[row * d:(row + 1) * d]
+        return out
+    return gather
+
+
+def _byte_stride_gather(pool, table, ctx, S_out, fill):
+    """The oracle's raw gather called with a 1-byte element size."""
+    pool = np.ascontiguousarray(pool)
+    N, K, bs, d = pool.shape
+    out = np.full((len(ctx), K, S_out, d), fill, dtype=pool.dtype)
+    cl = np.ascontiguousarray(ctx, np.int32)
+    bt = np.ascontiguousarray(table, np.int32)
+    oracle._load().oracle_gather_paged_raw(pool.ctypes.data, 1, bt.ctypes.data, bt.shape[1], N, bs, cl.ctypes.data,
+                                           len(ctx), K, d, S_out, out.ctypes.data)
+    return out
+
+
+def _roundtrip_passes(kind):
+    """Append coded rows with the mutant's layout, gather them back with it."""
+    rng = np.random.default_rng(35)
+    ctx, table, N, K, d = _paged_case(rng, 4)
+    pool = np.zeros((N, K, 4, d), np.float32)
+    flat = pool.reshape(-1)
+    s = int(ctx.max())
+    new = (np.arange(len(ctx) * s * K * d).reshape(len(ctx), s, K, d) + 1).astype(np.float32)
+    for b in range(len(ctx)):
+        for t in range(int(ctx[b])):
+            blk = int(table[b, t // 4])
+            for g in range(K):
+                row = (blk * 4 + t % 4) * K + g if kind == "head_slot_swapped" else (blk * K + g) * 4 + t % 4
+                flat[row * d:(row + 1) * d] = new[b, t, g]
+    got = _mutant_gather(kind)(pool, table, ctx, s, np.float32(0))
+    return all(np.array_equal(got[b, g, :ctx[b]], new[b, :ctx[b], g]) for b in range(len(ctx)) for g in range(K))
+
+
+@pytest.mark.parametrize("kind", ["head_slot_swapped", "block_column_off_by_one", "byte_stride"])
+def test_planted_paged_mistakes_are_caught(oracle_lib, kind):
+    assert _gather_raw_pin_holds(_mutant_gather("none"))
+    broken = _byte_stride_gather if kind == "byte_stride" else _mutant_gather(kind)
+    assert not _gather_raw_pin_holds(broken)
+    if kind == "head_slot_swapped":
+        # the swap made consistently on both sides survives a round trip: only
+        # the independent indexing above catches it
+        assert _roundtrip_passes(kind)
+
+
+# ---------------------------------------------------------------------------
 # planted mistakes: a broken copy of the reference must fail some pin
 # ---------------------------------------------------------------------------
 
