@@ -205,8 +205,10 @@ def gqa_decode_workspace_bytes(B: int, num_heads: int, num_kv_heads: int, head_d
     return int(load_library().gqa_decode_workspace_bytes(B, num_heads, num_kv_heads, head_dim, max_ctx))
 
 
-# Default decode workspaces, one per (device, stream), zero-filled once; the
-# library leaves them zeroed after every completed call.
+# Default decode workspaces, one per (device, stream), allocated on first use
+# and grown when a call needs more.  The library needs no initialisation of
+# the workspace (every slot it reads was written by the same call), so calls
+# on one stream can share it; calls that may overlap need their own.
 _workspaces: dict = {}
 
 

@@ -36,6 +36,23 @@ gqa_status fail(gqa_status s, const char *what)
     return s;
 }
 
+// The softmax scale must be positive and finite: the kernels take each
+// tile's maximum of the raw dot products and scale it afterwards, which
+// commutes with the maximum only for a positive scale.
+bool scale_ok(float scale) { return std::isfinite(scale) && scale > 0.f; }
+
+// GQA_DECODE_WGS=n (1 .. kStreamWGs): the number of workgroups a decode
+// launch splits its keys over, instead of the default for the kernel that
+// runs.  The result is the same for every n up to the rounding of the
+// merge; 0 (unset) is the default.
+int32_t decode_wgs_override()
+{
+    const char *e = std::getenv("GQA_DECODE_WGS");
+    if (!e) return 0;
+    const int n = std::atoi(e);
+    return n >= 1 && n <= kStreamWGs ? n : 0;
+}
+
 bool is_pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 int ilog2(int32_t x)
@@ -247,7 +264,7 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
     if (v.elem_bytes == 1 && v.block_table && v.log2_bs < 4)
         return fail(GQA_ERR_UNSUPPORTED, "FP8 cache with blocks below 16 tokens");
     if (max_ctx <= 0) return fail(GQA_ERR_INVALID_ARG, "max_ctx <= 0");
-    if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
+    if (!scale_ok(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not a positive finite number");
     DecodeLayout L;
     decode_layout(num_heads / v.K, v.d, &L);
     if (!workspace || workspace_bytes < L.total)
@@ -255,9 +272,12 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
     if (check_mode()) {
         std::vector<int32_t> cl;
         if (!fetch_i32(ctx_lens, B, cl)) return fail(GQA_ERR_LAUNCH, "ctx_lens copy failed");
-        for (int b = 0; b < B; ++b)
-            if (cl[b] < 1 || cl[b] > max_ctx) return fail(GQA_ERR_DEVICE_ARG, "ctx_lens outside [1, max_ctx]");
         std::vector<int32_t> lo(B, 0);
+        for (int b = 0; b < B; ++b) {
+            if (cl[b] < 1 || cl[b] > max_ctx) return fail(GQA_ERR_DEVICE_ARG, "ctx_lens outside [1, max_ctx]");
+            // keys below the window are never read: their blocks may be stale
+            if (window > 0) lo[b] = std::max(0, cl[b] - window);
+        }
         if ((st = check_positions(v, lo, cl)) != GQA_OK) return st;
     }
     RowAttnParams p{};
@@ -279,6 +299,7 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
     p.whole_items = 0;
     p.window = window > 0 ? window : 0;
     p.num_wgs = kStreamWGs;
+    p.wgs_override = decode_wgs_override();
     p.scale_log2 = scale * 1.4426950408889634f;
     const hipStream_t hs = static_cast<hipStream_t>(stream);
     if (step) {
@@ -330,7 +351,7 @@ gqa_status gqa_decode_multi(const void *q, const gqa_kv_cache *cache, const int3
     if (B == 0 || s == 0) return GQA_OK;
     if (!q || !out || !ctx_lens) return fail(GQA_ERR_INVALID_ARG, "NULL q/out/ctx_lens");
     if (max_ctx <= 0) return fail(GQA_ERR_INVALID_ARG, "max_ctx <= 0");
-    if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
+    if (!scale_ok(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not a positive finite number");
     const int32_t G = num_heads / v.K;
     if ((int64_t)s * G > 64) return fail(GQA_ERR_UNSUPPORTED, "s * G above 64");
     if (v.elem_bytes == 4 || v.d != 128) return fail(GQA_ERR_UNSUPPORTED, "several positions need bf16 or FP8, d = 128");
@@ -342,9 +363,12 @@ gqa_status gqa_decode_multi(const void *q, const gqa_kv_cache *cache, const int3
     if (check_mode()) {
         std::vector<int32_t> cl;
         if (!fetch_i32(ctx_lens, B, cl)) return fail(GQA_ERR_LAUNCH, "ctx_lens copy failed");
-        for (int b = 0; b < B; ++b)
-            if (cl[b] < s || cl[b] > max_ctx) return fail(GQA_ERR_DEVICE_ARG, "ctx_lens outside [s, max_ctx]");
         std::vector<int32_t> lo(B, 0);
+        for (int b = 0; b < B; ++b) {
+            if (cl[b] < s || cl[b] > max_ctx) return fail(GQA_ERR_DEVICE_ARG, "ctx_lens outside [s, max_ctx]");
+            // the oldest row sits at ctx - s; keys below its window are never read
+            if (window > 0) lo[b] = (int32_t)std::max<int64_t>(0, (int64_t)cl[b] - s + 1 - window);
+        }
         if ((st = check_positions(v, lo, cl)) != GQA_OK) return st;
     }
     RowAttnParams p{};
@@ -364,6 +388,7 @@ gqa_status gqa_decode_multi(const void *q, const gqa_kv_cache *cache, const int3
     p.G = G;
     p.window = window > 0 ? window : 0;
     p.num_wgs = kStreamWGs;
+    p.wgs_override = decode_wgs_override();
     p.scale_log2 = scale * 1.4426950408889634f;
     return launch_status(launch_row_attention(p, pow2_at_least(p.G), static_cast<hipStream_t>(stream)),
                          "decode (several positions)");
@@ -388,7 +413,7 @@ gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_ne
     if (B < 0 || s < 0) return fail(GQA_ERR_INVALID_ARG, "B or s negative");
     if (B == 0 || s == 0) return GQA_OK;
     if (!q || !k_new || !v_new || !start_pos || !out) return fail(GQA_ERR_INVALID_ARG, "NULL pointer");
-    if (!std::isfinite(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not finite");
+    if (!scale_ok(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not a positive finite number");
     if (v.elem_bytes == 1) return fail(GQA_ERR_UNSUPPORTED, "prefill on an FP8 cache");
     const bool bf16 = v.elem_bytes == 2;
     if (check_mode()) {
@@ -398,6 +423,8 @@ gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_ne
         for (int b = 0; b < B; ++b) {
             if (sp[b] < 0) return fail(GQA_ERR_DEVICE_ARG, "start_pos negative");
             hi[b] = (int32_t)std::min<int64_t>((int64_t)sp[b] + s, 0x7fffffff);
+            // row 0 (position start_pos) is the oldest; keys below its window are never read
+            if (window > 0) lo[b] = (int32_t)std::max<int64_t>(0, (int64_t)sp[b] + 1 - window);
         }
         if ((st = check_positions(v, lo, hi)) != GQA_OK) return st;
     }

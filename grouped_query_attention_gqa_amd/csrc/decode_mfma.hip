@@ -621,7 +621,8 @@ template <int RBW>
 hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
 {
     RowAttnParams p = p0;
-    p.num_wgs = p0.num_wgs * occ_of(RBW) / 2;   // slices resident at once: occ_of(RBW) per CU
+    // slices resident at once: occ_of(RBW) per CU, unless the caller fixed the count
+    p.num_wgs = p0.wgs_override > 0 ? p0.wgs_override : p0.num_wgs * occ_of(RBW) / 2;
     if (p.cache.elem_bytes == 1) hipLaunchKernelGGL((decode_mfma_kernel<RBW, true>), dim3(p.num_wgs), dim3(NT), 0, s, p);
     else hipLaunchKernelGGL((decode_mfma_kernel<RBW, false>), dim3(p.num_wgs), dim3(NT), 0, s, p);
     hipError_t e = hipGetLastError();

@@ -497,8 +497,10 @@ __global__ __launch_bounds__(NT, 2) void decode_waves_kernel(RowAttnParams p)
 }
 
 template <int D, int GP>
-hipError_t launch_w(const RowAttnParams &p, hipStream_t s)
+hipError_t launch_w(const RowAttnParams &p0, hipStream_t s)
 {
+    RowAttnParams p = p0;
+    if (p.wgs_override > 0) p.num_wgs = p.wgs_override;
     hipLaunchKernelGGL((decode_waves_kernel<D, GP>), dim3(p.num_wgs), dim3(NT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -64,6 +64,7 @@ struct RowAttnParams {
     int32_t window;             // > 0: a row sees only its `window` most recent positions
     int32_t mq;                 // decode: query positions per sequence, the newest mq (0 or 1: one)
     int32_t num_wgs;            // W
+    int32_t wgs_override;       // decode: > 0 fixes the workgroups of the launch (else the kernel's default)
     float scale_log2;           // softmax scale * log2(e)
 };
 

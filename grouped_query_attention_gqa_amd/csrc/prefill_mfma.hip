@@ -197,6 +197,7 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
         voff[k] = (uint32_t)(r * C::RB + (slot ^ C::vsw(r)) * 16);
     }
     const bool contiguous = cache.block_table == nullptr;
+    const bool small_blocks = !contiguous && cache.log2_bs < 4;
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;   // LDS address of the stages
     const char *kseq = cache.k + ((int64_t)b * cache.K + g) * cache.S_max * C::RB;
     const char *vseq = cache.v + ((int64_t)b * cache.K + g) * cache.S_max * C::RB;
@@ -222,10 +223,17 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
             const char *srck = reinterpret_cast<const char *>(&kZero16P), *srcv = srck;
             // rows below kv_begin are outside every row's window: not read
             if (t < ntiles && j0 + blk * C::RPK < kv_len && j0 + blk * C::RPK + C::RPK > kv_begin) {
-                // the block's rows lie in one 16-row group, hence in one cache block
-                const int64_t row0 = cache_row_wave(cache, b, g, j0 + blk * C::RPK);
-                if (row0 >= 0 && j0 + r < kv_len && j0 + r >= kv_begin) {
-                    const int64_t row = row0 + (r - blk * C::RPK);
+                int64_t row = -1;
+                if (small_blocks) {
+                    // blocks of fewer than 16 tokens: the load's RPK rows may
+                    // span several cache blocks, so each lane looks up its own
+                    if (j0 + r < kv_len && j0 + r >= kv_begin) row = cache_row(cache, b, g, j0 + r);
+                } else {
+                    // the load's rows lie in one 16-row group, hence in one cache block
+                    const int64_t row0 = cache_row_wave(cache, b, g, j0 + blk * C::RPK);
+                    if (row0 >= 0 && j0 + r < kv_len && j0 + r >= kv_begin) row = row0 + (r - blk * C::RPK);
+                }
+                if (row >= 0) {
                     srck = cache.k + row * C::RB + (slot ^ C::ksw(r)) * 16;
                     srcv = cache.v + row * C::RB + (slot ^ C::vsw(r)) * 16;
                 }

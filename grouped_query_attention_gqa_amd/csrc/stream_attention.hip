@@ -650,7 +650,8 @@ hipError_t launch_g(const RowAttnParams &p0, hipStream_t s)
 {
     using C = Cfg<D, GP, BF16>;
     RowAttnParams p = p0;
-    if (C::LIMIT > LDS_LIMIT && p.num_wgs > 1) p.num_wgs /= 2;
+    if (p.wgs_override > 0) p.num_wgs = p.wgs_override;
+    else if (C::LIMIT > LDS_LIMIT && p.num_wgs > 1) p.num_wgs /= 2;
     hipLaunchKernelGGL((stream_attention_kernel<D, GP, BF16>), dim3(p.num_wgs), dim3(NT), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.whole_items) return e;

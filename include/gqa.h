@@ -46,6 +46,14 @@
  *   - Supported: dtype GQA_BF16 or GQA_F32, head_dim 64 or 128,
  *     1 <= K <= H, H % K == 0, G = H / K <= 64, block_size a power of two in
  *     [1, 1024].
+ *   - The softmax scale must be a positive finite number (normally
+ *     1 / sqrt(d), the concept page's 1/sqrt(d_k)); any other value returns
+ *     GQA_ERR_INVALID_ARG.
+ *   - Environment knobs, read at every call: GQA_CHECK=1 (above);
+ *     GQA_DECODE_WGS=n with 1 <= n <= 512 fixes the number of workgroups a
+ *     decode launch splits the keys over (flash-decoding's split count,
+ *     inference-optimisation page §10.2; the result is the same for every n
+ *     up to the rounding of the merge); unset, each kernel picks its own.
  *   - Quantised cache (GQA_FP8_E4M3): K/V rows stored as FP8 E4M3 with one
  *     fp32 scale per cached row (token x KV head), written by gqa_kv_append
  *     and gqa_decode_step and read by the decode calls (inference-
@@ -132,6 +140,9 @@ gqa_status gqa_kv_append(const gqa_kv_cache *cache, const void *k_new, const voi
  * Workspace bytes gqa_decode needs for these sizes (a few MB at most; the
  * amount depends on G = H / K and d only, the other sizes are checked).
  * Host-only; no GPU needed.  Returns 0 on invalid sizes.
+ * num_kv_heads is an argument beside num_heads because the partial results
+ * are kept per KV group (G = H / K rows of d values per split): sized from H
+ * alone, the workspace would have to assume the multi-query end (G = H).
  */
 size_t gqa_decode_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t max_ctx);

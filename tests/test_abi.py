@@ -161,3 +161,24 @@ def test_fp8_cache_argument_rules(lib):
     pf = lib.gqa_prefill(FAKE, FAKE, FAKE, ctypes.byref(_cache(**f8, **sc)), FAKE, 1, 4, 32, ctypes.c_float(0.1), 1,
                          FAKE, None)
     assert pf == binding.GQA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, -0.0, float("-inf")])
+def test_every_call_rejects_a_scale_that_is_not_positive(lib, scale):
+    """The kernels take each tile's maximum of the raw dot products before
+    scaling it, which is the scaled maximum only for a positive scale; zero
+    and negative scales are refused before anything is launched."""
+    c = _cache()
+    sc = ctypes.c_float(scale)
+    assert _decode(lib, c, scale=scale) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_decode_window(FAKE, ctypes.byref(c), FAKE, 128, 1, 8, sc, 16, FAKE, FAKE, 1 << 30,
+                                 None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_decode_step(FAKE, FAKE, FAKE, ctypes.byref(c), FAKE, 128, 1, 8, sc, 0, FAKE, FAKE, 1 << 30,
+                               None) == binding.GQA_ERR_INVALID_ARG
+    c128 = _cache(head_dim=128, dtype=binding.GQA_BF16)
+    assert lib.gqa_decode_multi(FAKE, ctypes.byref(c128), FAKE, 128, 1, 2, 8, sc, 0, FAKE, FAKE, 1 << 30,
+                                None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_prefill(FAKE, FAKE, FAKE, ctypes.byref(c), FAKE, 1, 4, 8, sc, 1, FAKE,
+                           None) == binding.GQA_ERR_INVALID_ARG
+    assert lib.gqa_prefill_window(FAKE, FAKE, FAKE, ctypes.byref(c), FAKE, 1, 4, 8, sc, 1, 8, FAKE,
+                                  None) == binding.GQA_ERR_INVALID_ARG

@@ -20,6 +20,8 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+
 from grouped_query_attention_gqa_amd import binding
 from grouped_query_attention_gqa_amd import workloads as W
 from gpu_common import DecodeRun, PrefillRun, as_f64, from_dev, requires_gpu, say, to_dev
@@ -168,3 +170,138 @@ def test_zero_context_gives_zero_rows():
     out = from_dev(run.run())
     assert (out[0] == 0).all()
     assert np.isfinite(as_f64(out[1], "bf16")).all()
+
+
+# ---------------------------------------------------------------------------
+# paged prefill over a cached prefix (chunked prefill, inference-optimisation
+# page §11.7, through the block table of §8.2): the same window and spike
+# inputs, placed in the prefix that earlier calls cached.  Every new query row
+# sees the whole prefix, so every output of every row is exact.
+# ---------------------------------------------------------------------------
+
+def _prefix_case(starts_pos, window_starts, width, *, spike=False, seed=0, bs=16, H=32, K=8, d=128, s=512):
+    """Inputs of a paged prefill of s new tokens after starts_pos[b] cached ones.
+
+    Cached key t of group g of sequence b is 2.5 u (u = the group's query row)
+    for t in [window_starts[b][g], + width), zero elsewhere; cached value t is
+    the one-hot e_(t mod d) (or, with spike, a distinct row).  New keys are zero
+    and new values random, so all weight sits on the window."""
+    B = len(starts_pos)
+    G = H // K
+    rng = np.random.default_rng(seed)
+    start = np.asarray(starts_pos, np.int32)
+    table, n_pool = W.deal_blocks(rng, start + s, bs)
+    nan = W.BF16_QNAN
+    pk = np.full((n_pool, K, bs, d), nan, np.uint16)
+    pv = np.full((n_pool, K, bs, d), nan, np.uint16)
+    u = rng.choice([-1.0, 1.0], size=(B, K, d)).astype(np.float32)
+    q = np.empty((B, s, H, d), np.uint16)
+    for b in range(B):
+        n = int(start[b])
+        t = np.arange(n)
+        blk, slot = table[b, t // bs].astype(np.int64), t % bs
+        for g in range(K):
+            q[b, :, g * G:(g + 1) * G] = BF16(u[b, g])
+            lo = int(window_starts[b][g])
+            inside = (t >= lo) & (t < lo + width)
+            pk[blk, g, slot] = BF16(np.where(inside[:, None], 2.5 * u[b, g][None, :], 0.0))
+            if spike:
+                sign = rng.choice([-1.0, 1.0], size=(n, d))
+                pv[blk, g, slot] = BF16(sign * (1.0 + ((t + g) % 7) / 8.0)[:, None])
+            else:
+                rows = np.zeros((n, d), np.float32)
+                rows[t, t % d] = 1.0
+                pv[blk, g, slot] = BF16(rows)
+    kn = np.zeros((B, s, K, d), np.uint16)
+    vn = W.f32_to_bf16_bits(rng.standard_normal((B, s, K, d)).astype(np.float32))
+    return start, table, pk, pv, q, kn, vn
+
+
+def _run_prefix_case(case, what):
+    start, table, pk, pv, q, kn, vn = case
+    cache = binding.KVCache(to_dev(pk), to_dev(pv), to_dev(table))
+    say("paged prefill", what, f"block_size={pk.shape[2]} d={pk.shape[3]} starts={list(start)}")
+    out = binding.gqa_prefill(to_dev(q), to_dev(kn), to_dev(vn), cache, to_dev(start), causal=True,
+                              scale=1.0 / np.sqrt(pk.shape[3]))
+    torch.cuda.synchronize()
+    # the new rows were appended bit for bit, nothing else in the pool changed
+    for name, pool, new, dev in (("k", pk, kn, cache.k), ("v", pv, vn, cache.v)):
+        want = pool.copy()
+        oracle.kv_append_paged(want, new, start, table)
+        assert from_dev(dev).tobytes() == want.tobytes(), f"{what}: pool {name} after the prefill"
+    return from_dev(out)
+
+
+def _window_starts(rng, n, K, width, bs):
+    """Window starts over a prefix of n tokens: block-aligned, unaligned, the
+    first window, and the window that ends on the prefix's last slot."""
+    top = n - width
+    cands = [0, top, bs * (top // (2 * bs)), max(0, top - 7), int(rng.integers(0, top + 1)),
+             bs * int(rng.integers(0, top // bs + 1)), int(rng.integers(0, top + 1)) | 1, min(top, bs - 1)]
+    return [cands[(g + int(rng.integers(0, len(cands)))) % len(cands)] for g in range(K)]
+
+
+@pytest.mark.parametrize("launch", range(3))
+def test_chunked_paged_prefill_window_coverage_exact(launch):
+    """The bench's chunked prefill shape: 512 new tokens after a 3584-token
+    prefix in shuffled 16-token blocks; a 128-token window per (sequence,
+    group) in the prefix; every output is exactly 1/128."""
+    rng = np.random.default_rng(100 + launch)
+    starts = [3584] * 4
+    ws = [_window_starts(rng, n, 8, 128, 16) for n in starts]
+    out = _run_prefix_case(_prefix_case(starts, ws, 128, seed=launch), f"window coverage {launch}")
+    got = as_f64(out, "bf16")
+    assert np.array_equal(got, np.full(got.shape, 1.0 / 128.0)), ws
+
+
+def test_chunked_paged_prefill_window_ragged_prefix_exact():
+    """Prefixes that end inside a block: the window ends on the last cached
+    slot of a partly filled block, and the new rows continue that block."""
+    starts = [3579, 3001, 130, 2049]
+    ws = [[n - 128] * 4 + [max(0, n - 135), 0, (n - 128) // 2, n - 129] for n in starts]
+    out = _run_prefix_case(_prefix_case(starts, ws, 128, seed=7), "window ragged prefix")
+    got = as_f64(out, "bf16")
+    assert np.array_equal(got, np.full(got.shape, 1.0 / 128.0)), ws
+
+
+@pytest.mark.parametrize("launch", range(2))
+def test_chunked_paged_prefill_spikes_exact(launch):
+    """One cached token per (sequence, group) carries all the weight: the first
+    or last slot of a block, or the prefix's last slot; every row of the group
+    returns that token's V row bit for bit."""
+    starts = [3584, 3584, 3577, 1000] if launch else [3584] * 4
+    ws = []
+    for b, n in enumerate(starts):
+        cand = [0, 15, 16, 31, n - 1, n - 16, 16 * (n // 32) - 1, 16 * (n // 48)]
+        ws.append([min(n - 1, cand[(g + launch) % len(cand)]) for g in range(8)])
+    start, table, pk, pv, q, kn, vn = case = _prefix_case(starts, ws, 1, spike=True, seed=11 + launch)
+    out = _run_prefix_case(case, f"spikes {launch}")
+    for b in range(4):
+        for g in range(8):
+            t = ws[b][g]
+            want = pv[int(table[b, t // 16]), g, t % 16]
+            for r in range(4):
+                assert np.array_equal(out[b, :, g * 4 + r], np.broadcast_to(want, out[b, :, g * 4 + r].shape)), (b, g, t)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("bs", [1, 2, 4, 8, 32])
+def test_paged_prefill_small_blocks_exact(bs, d):
+    """Blocks smaller than one 16-row load of the prefill's tile: each row is
+    looked up through the table on its own.  Window and spike inputs, exact."""
+    rng = np.random.default_rng(bs * 1000 + d)
+    starts = [300, 157]
+    ws = [_window_starts(rng, n, 2, d, bs) for n in starts]
+    out = _run_prefix_case(_prefix_case(starts, ws, d, seed=bs, bs=bs, H=8, K=2, d=d, s=100),
+                           f"small blocks window bs={bs}")
+    got = as_f64(out, "bf16")
+    assert np.array_equal(got, np.full(got.shape, 1.0 / d)), ws
+    sp = [[5, 299], [156, bs]]
+    start, table, pk, pv, q, kn, vn = case = _prefix_case(starts, sp, 1, spike=True, seed=bs + 1, bs=bs, H=8, K=2,
+                                                          d=d, s=100)
+    out = _run_prefix_case(case, f"small blocks spikes bs={bs}")
+    for b in range(2):
+        for g in range(2):
+            t = sp[b][g]
+            want = pv[int(table[b, t // bs]), g, t % bs]
+            assert np.array_equal(out[b, :, g * 4:(g + 1) * 4], np.broadcast_to(want, (100, 4, d))), (b, g, t)

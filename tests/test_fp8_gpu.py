@@ -242,3 +242,91 @@ def test_fp8_decode_multi_matches_causal_oracle(s_new, H, K):
                                           [n - s_new], [n], True, wl.scale, rows))
         got.append(as_f64(o[b][rows[:, 1], rows[:, 2]], "bf16"))
     check_close(np.concatenate(got), np.concatenate(want), BF16_TOL, f"fp8 decode multi s={s_new}")
+
+
+# ---------------------------------------------------------------------------
+# exact coverage of the paged FP8 decode: the block table walk and the scales
+# it loads beside the codes (a wrong block, slot or scale changes an output
+# bit).  The values are chosen so that the FP8 round trip is exact: every V
+# row's scale is a power of two (amax = 1.75 * 2^e, so scale = 2^(e-8)) and
+# its values have at most three mantissa bits.
+# ---------------------------------------------------------------------------
+
+BF16 = lambda x: W.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def _paged_f8_structured(ctx, starts, width, spike, seed, H=64, K=8):
+    """Paged FP8 inputs whose group g of sequence b puts all its weight on the
+    cached keys [starts[b][g], + width): K rows there are 2.5 u (u the group's
+    query row), zero elsewhere."""
+    wl = W.WORKLOADS["paged_long_decode"].replace(B=len(ctx), H=H, K=K)
+    rng = np.random.default_rng(seed)
+    inp = W.make_decode(wl, fill="zero", ctx_override=ctx)
+    bs, d = wl.block_size, wl.d
+    u = rng.choice([-1.0, 1.0], size=(wl.B, wl.K, d)).astype(np.float32)
+    for b in range(wl.B):
+        n = int(ctx[b])
+        t = np.arange(n)
+        blk, slot = inp.block_table[b, t // bs].astype(np.int64), t % bs
+        for g in range(wl.K):
+            inp.q[b, 0, g * wl.G:(g + 1) * wl.G] = BF16(u[b, g])
+            lo = int(starts[b][g])
+            inside = (t >= lo) & (t < lo + width)
+            inp.k[blk, g, slot] = BF16(np.where(inside[:, None], 2.5 * u[b, g][None, :], 0.0))
+            if spike:
+                sign = rng.choice([-1.0, 1.0], size=(n, d))
+                mant = 1.0 + ((t[:, None] + np.arange(d)[None, :]) % 7) / 8.0     # 1 .. 1.75: amax 1.75
+                inp.v[blk, g, slot] = BF16(sign * mant * np.exp2((t % 5) - 2.0)[:, None])
+            else:
+                rows = np.zeros((n, d), np.float32)
+                rows[t, t % d] = 1.75
+                inp.v[blk, g, slot] = BF16(rows)
+    kc, ks, vc, vs = quantized_inputs(inp)
+    return wl, inp, kc, ks, vc, vs
+
+
+def _run_f8(wl, inp, kc, ks, vc, vs, what, window=0):
+    cache = _f8_cache(kc, ks, vc, vs, inp.block_table)
+    say("fp8 paged exact", what)
+    out = binding.gqa_decode(to_dev(inp.q), cache, to_dev(inp.ctx), int(inp.ctx.max()), scale=wl.scale,
+                             window=window)
+    torch.cuda.synchronize()
+    return from_dev(out)
+
+
+def test_fp8_paged_window_coverage_exact():
+    ctx = np.array([128, 1000, 3001, 4096], np.int32)
+    starts = []
+    for n in ctx:
+        n = int(n)
+        cand = [0, n - 128, 16 * ((n - 128) // 32), max(0, n - 135), (n - 128) // 3, 1 % max(1, n - 127), 17, 31]
+        starts.append([max(0, min(n - 128, c)) for c in cand])
+    wl, inp, kc, ks, vc, vs = _paged_f8_structured(ctx, starts, 128, False, 41)
+    # one-hot rows of 1.75: scale 2^-8, code 448, value 1.75 exactly
+    assert (vs[inp.block_table[0, 0], 0, :1] == np.float32(2.0 ** -8)).all()
+    out = as_f64(_run_f8(wl, inp, kc, ks, vc, vs, "window"), "bf16")
+    assert np.array_equal(out, np.full(out.shape, 1.75 / 128.0)), starts
+
+
+def test_fp8_paged_spikes_exact():
+    """One cached key per (sequence, group): the first or last slot of a block or
+    the last valid slot.  Every head of the group returns the oracle's
+    dequantised V row of that key bit for bit."""
+    ctx = np.array([520, 1601, 33, 4000], np.int32)
+    starts = []
+    for n in ctx:
+        n = int(n)
+        cand = [0, 15, 16, 31, 32, n - 1, n - 16, (n // 2) // 16 * 16 - 1]
+        starts.append([max(0, min(n - 1, c)) for c in cand])
+    wl, inp, kc, ks, vc, vs = _paged_f8_structured(ctx, starts, 1, True, 42)
+    vd = oracle.dequantize_e4m3_rows(vc, vs)
+    out = as_f64(_run_f8(wl, inp, kc, ks, vc, vs, "spikes"), "bf16")
+    for b in range(wl.B):
+        for g in range(wl.K):
+            t = starts[b][g]
+            blk, slot = int(inp.block_table[b, t // 16]), t % 16
+            want = vd[blk, g, slot]
+            # the round trip through E4M3 is exact for these rows
+            assert np.array_equal(want, as_f64(inp.v[blk, g, slot], "bf16"))
+            for r in range(wl.G):
+                assert np.array_equal(out[b, 0, g * wl.G + r], want), (b, g, t)
