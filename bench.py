@@ -23,7 +23,14 @@ The same JSON line also carries
     sequence decoded at once by gqa_decode_multi) in GB/s;
   * prefill_workloads: a chunked prefill (512 new tokens after a 3584-token
     cached prefix, paged cache) in TFLOP/s;
-  * cpu_baseline: the CPU oracle on the host cores, on the same step.
+  * tiny_workloads: the two tiny fp32 workloads (causal prefill of 128
+    tokens, decode over 128 cached tokens) in microseconds per call;
+  * cpu_baseline: the CPU oracle on the host cores, on the same step, with
+    the host's CPU model; its `workloads` entry times the oracle on bounded
+    samples of the other workloads (decode GB/s, prefill GFLOP/s, tiny-call
+    microseconds);
+  * pages_context: the pages' own figures with the hardware they were
+    measured on (context only, not targets).
 
 The K/V caches are rotated over several copies so that the ~256 MB
 Infinity Cache cannot serve them between steps; inputs are resident in HBM
@@ -53,6 +60,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "GQA decode HBM GB/s (% of peak) + causal prefill TFLOP/s (% MFMA peak), bf16"
 MALL_BYTES = 256 * 2**20
 COPY_BYTES = 512 * 2**20   # calibration copy for the HBM byte counters
+LEG_CALLS = 50             # timed calls of every leg beside the headline, whatever --steps is
 
 
 def log(*a):
@@ -295,7 +303,25 @@ def summarize_traffic(fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_
 # CPU baseline: the oracle on the host cores
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(db: DecodeBench, budget_s: float = 12.0):
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _oracle_threads() -> int:
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+def cpu_baseline(db: DecodeBench, budget_s: float = 8.0):
+    """The oracle (fp64, untuned) over whole decode steps of the headline workload."""
     import oracle
     wl, inp = db.wl, db.inp
     oracle._load()
@@ -319,15 +345,159 @@ def cpu_baseline(db: DecodeBench, budget_s: float = 12.0):
         t_total += time.perf_counter() - t0
         done_bytes += db.alg_bytes + append_bytes(wl, 1)
         passes += 1
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = _oracle_threads()
     return {
         "value": round(done_bytes / t_total / 1e9, 3),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"the whole {wl.name} decode step (all {wl.B} sequences x {wl.H} heads, append + "
                   f"attention, fp64), {passes} pass(es) in {t_total:.1f} s on {threads} threads",
     }
+
+
+def _time_oracle(fn, budget_s: float, max_passes: int = 1000):
+    """Passes of fn() until budget_s of work (at least one); returns (passes, seconds)."""
+    t_total, passes = 0.0, 0
+    while passes < max_passes and (passes == 0 or t_total < budget_s):
+        t0 = time.perf_counter()
+        fn()
+        t_total += time.perf_counter() - t0
+        passes += 1
+    return passes, t_total
+
+
+def cpu_baseline_workloads(budget_s: float = 3.0):
+    """The oracle on the other workloads, each on a bounded sample of the same
+    shapes and value distributions, scaled to the metric's unit: decode in GB/s
+    of algorithmic bytes, prefill in GFLOP/s of causal work, the tiny fp32
+    workloads in microseconds per whole call."""
+    import oracle
+    from grouped_query_attention_gqa_amd import workloads as W
+    oracle._load()
+    res = {}
+    # tiny fp32 prefill and decode: the whole call
+    wl = W.WORKLOADS["tiny_prefill_f32"]
+    inp = W.make_prefill(wl)
+    q = oracle.to_f64(inp.q, "f32")
+    k64 = oracle.to_f64(np.ascontiguousarray(inp.k_new.transpose(0, 2, 1, 3)), "f32")
+    v64 = oracle.to_f64(np.ascontiguousarray(inp.v_new.transpose(0, 2, 1, 3)), "f32")
+    n, t = _time_oracle(lambda: oracle.attention(q, k64, v64, inp.start_pos, inp.start_pos + wl.s, True, wl.scale),
+                        0.5)
+    res[wl.name] = {"us_per_call": round(t / n * 1e6, 1), "sample": f"the whole call, {n} passes"}
+    wl = W.WORKLOADS["tiny_decode_f32"]
+    inp = W.make_decode(wl)
+    n0 = int(inp.ctx[0])
+    q, k64, v64 = (oracle.to_f64(x, "f32") for x in (inp.q, inp.k[:, :, :n0], inp.v[:, :, :n0]))
+    n, t = _time_oracle(lambda: oracle.attention(q, k64, v64, inp.ctx - 1, inp.ctx, False, wl.scale), 0.5)
+    res[wl.name] = {"us_per_call": round(t / n * 1e6, 1), "sample": f"the whole call, {n} passes"}
+    # decode shapes: a few whole sequences (every head) of the same shape
+    for name, b_sample in (("llama2_70b_decode", 2), ("paged_long_decode", 6)):
+        wl = W.WORKLOADS[name].replace(B=b_sample)
+        inp = W.make_decode(wl, fill="zero")
+        q64 = oracle.to_f64(inp.q, wl.dtype)
+        rows = np.array([[0, 0, h] for h in range(wl.H)], np.int32)
+        # as in the headline leg, the rows are decoded to fp64 (and paged
+        # sequences gathered through their table) before the timed passes
+        prepared = []
+        for b in range(wl.B):
+            n_b = int(inp.ctx[b])
+            if inp.block_table is None:
+                kb, vb = inp.k[b:b + 1, :, :n_b], inp.v[b:b + 1, :, :n_b]
+            else:
+                kb = oracle.gather_paged_raw(inp.k, inp.block_table[b:b + 1], inp.ctx[b:b + 1], n_b, 0)
+                vb = oracle.gather_paged_raw(inp.v, inp.block_table[b:b + 1], inp.ctx[b:b + 1], n_b, 0)
+            prepared.append((b, n_b, oracle.to_f64(kb, wl.dtype), oracle.to_f64(vb, wl.dtype)))
+
+        def one_pass():
+            for b, n_b, kb, vb in prepared:
+                oracle.attention_rows(q64[b:b + 1], kb, vb, [n_b - 1], [n_b], False, wl.scale, rows)
+        n, t = _time_oracle(one_pass, budget_s)
+        nbytes = decode_bytes(wl, inp.ctx)
+        res[name] = {"GB/s": round(nbytes * n / t / 1e9, 3),
+                     "sample": f"{b_sample} whole sequences of the {name} shape (ctx {[int(c) for c in inp.ctx]}, "
+                               f"every head, fp64), {n} pass(es) in "
+                               f"{t:.1f} s"}
+    # causal prefill: randomly chosen (sequence, position, head) rows of the
+    # full workload, each against its whole causal key range
+    wl = W.WORKLOADS["causal_prefill_4k"]
+    inp = W.make_prefill(wl)
+    rng = np.random.default_rng(7)
+    n_rows = 512
+    rows = np.stack([rng.integers(0, wl.B, n_rows), rng.integers(0, wl.s, n_rows), rng.integers(0, wl.H, n_rows)],
+                    axis=1).astype(np.int32)
+    q64 = oracle.to_f64(inp.q, wl.dtype)
+    k64 = oracle.to_f64(np.ascontiguousarray(inp.k_new.transpose(0, 2, 1, 3)), wl.dtype)
+    v64 = oracle.to_f64(np.ascontiguousarray(inp.v_new.transpose(0, 2, 1, 3)), wl.dtype)
+    flops = 4 * wl.d * int(np.sum(rows[:, 1].astype(np.int64) + 1))
+    n, t = _time_oracle(lambda: oracle.attention_rows(q64, k64, v64, inp.start_pos, inp.start_pos + wl.s, True,
+                                                      wl.scale, rows), budget_s)
+    gfs = flops * n / t / 1e9
+    res[wl.name] = {"GFLOP/s": round(gfs, 3),
+                    "full_call_s_estimate": round(causal_flops(wl) / (gfs * 1e9), 1),
+                    "sample": f"{n_rows} random (sequence, position, head) rows of the full workload, each over its "
+                              f"whole causal key range ({flops / 1e9:.2f} GFLOP), {n} pass(es) in {t:.1f} s"}
+    return res
+
+
+def pages_context():
+    """The pages' own figures, with their hardware: context for the numbers
+    above, not targets.  The first one is recomputed with the library's
+    cache-size call."""
+    from grouped_query_attention_gqa_amd import binding
+    layers, tokens = 80, 2048
+    mha = binding.gqa_cache_elems_per_token(64, 128) * tokens * layers
+    gqa = binding.gqa_cache_elems_per_token(8, 128) * tokens * layers
+    return [
+        {"figure": f"Llama-2-70B KV cache for 2048 tokens over 80 layers: {mha:,} elements with 64 KV heads (MHA) "
+                   f"against {gqa:,} with 8 (GQA), which the page writes as about 2.68 and 0.33 'GB'",
+         "source": "concept page (compassingai.com), 关键参数 #2", "hardware": "none (arithmetic)",
+         "recomputed": {"mha_elements": mha, "gqa_elements": gqa, "ratio": mha / gqa}},
+        {"figure": "GQA instead of MHA raises serving throughput by about 30-50% (a 70B model, 8k context, large "
+                   "batches), a figure the page credits to an NVIDIA blog",
+         "source": "concept page (compassingai.com), 关键参数 #4", "hardware": "NVIDIA H100"},
+        {"figure": "a 7B model (Qwen2-7B with Int4 weights and an fp16 KV cache) served on a single 40 GB A100",
+         "source": "blog post (discosf.com), §1", "hardware": "NVIDIA A100 40G"},
+    ]
+
+
+def bench_tiny(iters: int, warmup: int):
+    """The tiny fp32 workloads (causal prefill s = 128; decode over 128 cached
+    tokens): launch-bound, reported in microseconds per call (HIP events)."""
+    import torch
+    from grouped_query_attention_gqa_amd import binding
+    from grouped_query_attention_gqa_amd import workloads as W
+    out = {}
+    wl = W.WORKLOADS["tiny_prefill_f32"]
+    inp = W.make_prefill(wl)
+    q, kn, vn, start = up(inp.q), up(inp.k_new), up(inp.v_new), up(inp.start_pos)
+    kc = torch.zeros(wl.B, wl.K, wl.s, wl.d, dtype=torch.float32, device="cuda")
+    cache = binding.KVCache(kc, torch.zeros_like(kc))
+    o = torch.empty_like(q)
+    call = lambda: binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=o, scale=wl.scale)
+    out[wl.name] = _event_time(call, iters, warmup)
+    wl = W.WORKLOADS["tiny_decode_f32"]
+    db = DecodeBench(wl, copies=1)
+    mean_ms, med_ms = time_decode_only(db, iters, warmup)
+    out[wl.name] = {"us": round(mean_ms * 1e3, 2), "median_us": round(med_ms * 1e3, 2), "calls": iters}
+    return out
+
+
+def _event_time(call, iters, warmup):
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in evs:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ts = np.array([a.elapsed_time(b) for a, b in evs])
+    return {"us": round(float(np.mean(ts)) * 1e3, 2), "median_us": round(float(np.median(ts)) * 1e3, 2),
+            "calls": iters}
 
 
 # ---------------------------------------------------------------------------
@@ -427,7 +597,7 @@ def main():
 
     if not args.no_extra:
         # ---- causal prefill ------------------------------------------------
-        result["prefill"] = bench_prefill(W.WORKLOADS["causal_prefill_4k"], max(10, args.steps // 2), 5)
+        result["prefill"] = bench_prefill(W.WORKLOADS["causal_prefill_4k"], max(LEG_CALLS, args.steps), 5)
         torch.cuda.empty_cache()
         # ---- the other decode shapes --------------------------------------
         extra = {}
@@ -435,7 +605,7 @@ def main():
                      "mistral_7b_window_decode"):
             w = W.WORKLOADS[name]
             d2 = DecodeBench(w)
-            mean_ms, med_ms = time_decode_only(d2, max(5, args.steps // 2), 3)
+            mean_ms, med_ms = time_decode_only(d2, max(LEG_CALLS, args.steps), 3)
             gbs = d2.alg_bytes / (mean_ms * 1e-3) / 1e9
             extra[name] = {"us": round(mean_ms * 1e3, 2), "GB/s": round(gbs, 1),
                            "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": d2.alg_bytes}
@@ -445,7 +615,7 @@ def main():
         # ---- four newest positions per sequence at once (speculative verify) -
         w = W.WORKLOADS["llama3_8b_decode"]
         d2 = DecodeBench(w, mq=4)
-        mean_ms, med_ms = time_decode_only(d2, max(5, args.steps // 2), 3, d2.multi)
+        mean_ms, med_ms = time_decode_only(d2, max(LEG_CALLS, args.steps), 3, d2.multi)
         gbs = d2.alg_bytes / (mean_ms * 1e-3) / 1e9
         extra["llama3_8b_decode_4_positions"] = {
             "us": round(mean_ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -456,7 +626,7 @@ def main():
         # ---- the Llama-3-8B decode on an FP8 (E4M3, scale per row) cache ----
         w = W.WORKLOADS["llama3_8b_decode"]
         d2 = DecodeBench(w, fp8=True)
-        mean_ms, med_ms = time_decode_only(d2, max(5, args.steps // 2), 3)
+        mean_ms, med_ms = time_decode_only(d2, max(LEG_CALLS, args.steps), 3)
         gbs = d2.alg_bytes / (mean_ms * 1e-3) / 1e9
         extra["llama3_8b_decode_fp8_cache"] = {
             "us": round(mean_ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
@@ -467,14 +637,23 @@ def main():
         result["decode_workloads"] = extra
         # ---- chunked prefill: new tokens after a cached prefix, paged ----
         result["prefill_workloads"] = {
-            "chunked_prefill_paged": bench_prefill(W.WORKLOADS["chunked_prefill_paged"], max(10, args.steps // 2), 5)}
+            "chunked_prefill_paged": bench_prefill(W.WORKLOADS["chunked_prefill_paged"], max(LEG_CALLS, args.steps), 5)}
         torch.cuda.empty_cache()
+
+        # ---- the tiny fp32 workloads: launch-bound, in microseconds --------
+        result["tiny_workloads"] = bench_tiny(max(LEG_CALLS, args.steps), 10)
+        log(f"tiny workloads: {result['tiny_workloads']}")
 
     if not args.no_cpu_baseline:
         wl = W.WORKLOADS["llama3_8b_decode"]
         db = DecodeBench(wl, copies=1)
         result["cpu_baseline"] = cpu_baseline(db)
+        del db
+        torch.cuda.empty_cache()
+        if not args.no_extra:
+            result["cpu_baseline"]["workloads"] = cpu_baseline_workloads()
         log(f"cpu baseline: {result['cpu_baseline']}")
+    result["pages_context"] = pages_context()
 
     print(json.dumps(result), flush=True)
 
