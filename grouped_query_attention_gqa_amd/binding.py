@@ -27,7 +27,7 @@ EXPORTED_SYMBOLS = (
     "gqa_abi_version", "gqa_status_string", "gqa_cache_elems_per_token",
     "gqa_kv_append", "gqa_decode_workspace_bytes", "gqa_decode", "gqa_prefill",
     "gqa_decode_window", "gqa_prefill_window", "gqa_decode_step",
-    "gqa_decode_multi_workspace_bytes", "gqa_decode_multi",
+    "gqa_decode_multi_workspace_bytes", "gqa_decode_multi", "gqa_decode_step_noalloc",
 )
 
 
@@ -93,6 +93,8 @@ def load_library():
         lib.gqa_decode_multi.argtypes = [vp, cp, vp, i32, i32, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
         lib.gqa_decode_step.restype = i32
         lib.gqa_decode_step.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp, sz, vp]
+        lib.gqa_decode_step_noalloc.restype = i32
+        lib.gqa_decode_step_noalloc.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp]
         lib.gqa_prefill_window.restype = i32
         lib.gqa_prefill_window.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
         if lib.gqa_abi_version() != 2:
@@ -301,6 +303,36 @@ def gqa_decode_step(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, c
     st = lib.gqa_decode_step(_ptr(q), _ptr(k_new), _ptr(v_new), cache.struct, _ptr(ctx_lens), int(max_ctx), B, H,
                              ctypes.c_float(scale), int(window), _ptr(out), _ptr(workspace), ws_bytes, hs)
     _check(st, "gqa_decode_step")
+    return out
+
+
+def gqa_decode_step_noalloc(q: torch.Tensor, k_new: Optional[torch.Tensor], v_new: Optional[torch.Tensor],
+                            cache: KVCache, ctx_lens: torch.Tensor, max_ctx: int, out: Optional[torch.Tensor] = None,
+                            scale: Optional[float] = None, stream=None, window: int = 0) -> torch.Tensor:
+    """gqa_decode_step with the library's static workspace (no workspace argument;
+    the library allocates nothing).  k_new/v_new may both be None: a plain decode."""
+    _need(q, "q", dtype=cache.act_dtype, dim=4)
+    _need(ctx_lens, "ctx_lens", dtype=torch.int32, dim=1)
+    B, one, H, d = q.shape
+    if one != 1 or d != cache.head_dim or ctx_lens.shape[0] != B:
+        raise ValueError("decode shapes disagree with the cache")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        _need(k_new, "k_new", dtype=cache.act_dtype, dim=4)
+        _need(v_new, "v_new", dtype=cache.act_dtype, dim=4)
+        if k_new.shape != (B, 1, cache.num_kv_heads, d) or v_new.shape != k_new.shape:
+            raise ValueError("k_new / v_new must be [B, 1, K, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", dtype=q.dtype, dim=4)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = load_library().gqa_decode_step_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), cache.struct, _ptr(ctx_lens),
+                                                int(max_ctx), B, H, ctypes.c_float(scale), int(window), _ptr(out),
+                                                _stream(stream))
+    _check(st, "gqa_decode_step_noalloc")
     return out
 
 

@@ -251,6 +251,20 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
                            const int32_t *ctx_lens, int32_t max_ctx, int32_t B, int32_t num_heads, float scale,
                            int32_t window, void *out, void *workspace, size_t workspace_bytes, void *stream)
 {
+    return gqa::decode_step(q, k_new, v_new, cache, ctx_lens, max_ctx, B, num_heads, scale, window, out, workspace,
+                            workspace_bytes, nullptr, stream);
+}
+
+}  // extern "C"
+
+// The decode step behind gqa_decode_step and gqa_decode_step_noalloc: with
+// `scratch` given, the workspace is the one it returns for the bytes this
+// call needs (asked for only once every host-side check has passed).
+gqa_status gqa::decode_step(const void *q, const void *k_new, const void *v_new, const gqa_kv_cache *cache,
+                            const int32_t *ctx_lens, int32_t max_ctx, int32_t B, int32_t num_heads, float scale,
+                            int32_t window, void *out, void *workspace, size_t workspace_bytes,
+                            gqa_status (*scratch)(size_t need, void **ws, size_t *ws_bytes), void *stream)
+{
     // k_new == v_new == nullptr: the plain decode (gqa_decode_window)
     const bool step = k_new != nullptr || v_new != nullptr;
     CacheView v;
@@ -267,6 +281,8 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
     if (!scale_ok(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not a positive finite number");
     DecodeLayout L;
     decode_layout(num_heads / v.K, v.d, &L);
+    if (scratch != nullptr && (st = scratch(L.total, &workspace, &workspace_bytes)) != GQA_OK)
+        return fail(st, "the library's static workspace is too small for this call, or unavailable");
     if (!workspace || workspace_bytes < L.total)
         return fail(GQA_ERR_WORKSPACE, "workspace smaller than gqa_decode_workspace_bytes()");
     if (check_mode()) {
@@ -323,6 +339,8 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
     }
     return launch_status(launch_row_attention(p, pow2_at_least(p.G), hs), "decode");
 }
+
+extern "C" {
 
 size_t gqa_decode_multi_workspace_bytes(int32_t B, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                         int32_t s, int32_t max_ctx)

@@ -6,6 +6,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/gqa.h"
+
 namespace gqa {
 
 // Where the cache rows of one layer live.
@@ -143,6 +145,14 @@ hipError_t launch_merge_pieces(const RowAttnParams &p, int tt, int W, hipStream_
 hipError_t launch_prefill_mfma(const PrefillParams &p, hipStream_t stream);
 
 constexpr int kKeyTile = 64;   // prefill key tile
+
+// gqa_decode_step's body.  scratch == nullptr: the caller's workspace;
+// otherwise scratch(need, &ws, &bytes) supplies it once the host-side checks
+// have passed (the static buffer of gqa_decode_step_noalloc).
+gqa_status decode_step(const void *q, const void *k_new, const void *v_new, const gqa_kv_cache *cache,
+                       const int32_t *ctx_lens, int32_t max_ctx, int32_t B, int32_t num_heads, float scale,
+                       int32_t window, void *out, void *workspace, size_t workspace_bytes,
+                       gqa_status (*scratch)(size_t need, void **ws, size_t *ws_bytes), void *stream);
 int32_t pow2_at_least(int32_t g);
 
 }  // namespace gqa

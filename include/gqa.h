@@ -231,6 +231,29 @@ gqa_status gqa_decode_step(const void *q, const void *k_new, const void *v_new, 
                            int32_t window, void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * gqa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  This call allocates nothing.
+ * The decode's split partials go to a static buffer inside the library,
+ * 12 MiB per GPU, held from the first use on that GPU until the process
+ * ends.  The buffer is the current device's, so `stream` must belong to the
+ * current device.
+ *   - A call whose gqa_decode_workspace_bytes(B, H, K, d, max_ctx) exceeds
+ *     12 MiB (G * d above 2048, e.g. G = 32 at d = 128) returns
+ *     GQA_ERR_WORKSPACE and launches nothing.
+ *   - Every call on one GPU shares that GPU's buffer.  Calls on one stream
+ *     run in order and are safe.  Calls that may overlap on one GPU (several
+ *     streams, or host threads with their own streams) race on it.
+ *   - k_new and v_new are both given (the step) or both NULL (a plain
+ *     decode, the newest token already appended).
+ * Results, cache bytes, arguments and errors are otherwise exactly those of
+ * gqa_decode_step.
+ */
+gqa_status gqa_decode_step_noalloc(const void *q, const void *k_new, const void *v_new, const gqa_kv_cache *cache,
+                                   const int32_t *ctx_lens, int32_t max_ctx, int32_t B, int32_t num_heads,
+                                   float scale, int32_t window, void *out, void *stream);
+
+/*
  * Decode of several new positions per sequence at once (a block of s
  * speculative tokens verified in one step, inference-optimisation page §14.2;
  * the concept page's rows are [B, s, H, d] for any s): row i of sequence b is
