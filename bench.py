@@ -22,7 +22,8 @@ The same JSON line also carries
     are the codes and scales, and the same shape with four new positions per
     sequence decoded at once by gqa_decode_multi) in GB/s;
   * prefill_workloads: a chunked prefill (512 new tokens after a 3584-token
-    cached prefix, paged cache) in TFLOP/s;
+    cached prefix, paged cache) in TFLOP/s, on a bf16 cache and on an FP8
+    E4M3 cache with a scale per row;
   * tiny_workloads: the two tiny fp32 workloads (causal prefill of 128
     tokens, decode over 128 cached tokens) in microseconds per call;
   * cpu_baseline: the CPU oracle on the host cores, on the same step, with
@@ -75,7 +76,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel: decode|step|fp8|multi|prefill|decode70b|paged|mha|mqa|window|chunked|"
+                    help="profile one kernel: decode|step|fp8|multi|prefill|decode70b|paged|mha|mqa|window|chunked|chunked_fp8|"
                          "copy (a 512 MiB device copy)")
     ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
     return ap.parse_args()
@@ -637,7 +638,9 @@ def main():
         result["decode_workloads"] = extra
         # ---- chunked prefill: new tokens after a cached prefix, paged ----
         result["prefill_workloads"] = {
-            "chunked_prefill_paged": bench_prefill(W.WORKLOADS["chunked_prefill_paged"], max(LEG_CALLS, args.steps), 5)}
+            "chunked_prefill_paged": bench_prefill(W.WORKLOADS["chunked_prefill_paged"], max(LEG_CALLS, args.steps), 5),
+            "chunked_prefill_paged_fp8_cache": bench_prefill(W.WORKLOADS["chunked_prefill_paged"],
+                                                             max(LEG_CALLS, args.steps), 5, fp8=True)}
         torch.cuda.empty_cache()
 
         # ---- the tiny fp32 workloads: launch-bound, in microseconds --------
@@ -658,7 +661,10 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def bench_prefill(wl, iters, warmup):
+def bench_prefill(wl, iters, warmup, fp8=False):
+    """Append + attention of the prefill workload, HIP events per call.  fp8:
+    the cache holds E4M3 codes and a scale per row (the new rows are quantised
+    by the call)."""
     import torch
     from grouped_query_attention_gqa_amd import binding
     from grouped_query_attention_gqa_amd import workloads as W
@@ -670,13 +676,17 @@ def bench_prefill(wl, iters, warmup):
         # prefix holds zeros (its values do not change the work)
         rng = np.random.default_rng(wl.seed)
         table, n_pool = W.deal_blocks(rng, np.full(wl.B, S, np.int32), wl.block_size)
-        kc = torch.zeros(n_pool, wl.K, wl.block_size, wl.d, dtype=torch.bfloat16, device="cuda")
-        vc = torch.zeros_like(kc)
-        cache = binding.KVCache(kc, vc, up(table))
+        shape = (n_pool, wl.K, wl.block_size, wl.d)
     else:
-        kc = torch.zeros(wl.B, wl.K, S, wl.d, dtype=torch.bfloat16, device="cuda")
+        table, shape = None, (wl.B, wl.K, S, wl.d)
+    if fp8:
+        kc = torch.zeros(shape, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
         vc = torch.zeros_like(kc)
-        cache = binding.KVCache(kc, vc)
+        ks = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
+        cache = binding.KVCache(kc, vc, None if table is None else up(table), k_scale=ks, v_scale=torch.zeros_like(ks))
+    else:
+        kc = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+        cache = binding.KVCache(kc, torch.zeros_like(kc), None if table is None else up(table))
     out = torch.empty_like(q)
     # warm-up: at least `warmup` calls and ~0.3 s of work, so that the
     # clocks have left the idle state the host-side input generation leaves
@@ -701,7 +711,8 @@ def bench_prefill(wl, iters, warmup):
     log(f"prefill {wl.name}: {ms * 1e3:.1f} us (append + attention), {tf:.1f} TFLOP/s "
         f"({100 * tf / BF16_MFMA_PEAK_TFLOPS:.1f}% of bf16 MFMA peak)")
     return {"workload": wl.name, "B": wl.B, "s": wl.s, "start": wl.start, "H": wl.H, "K": wl.K, "d": wl.d,
-            "paged": wl.paged, "us_per_call": round(ms * 1e3, 2),
+            "paged": wl.paged, "cache": "FP8 E4M3 codes + one fp32 scale per row" if fp8 else "bf16",
+            "us_per_call": round(ms * 1e3, 2),
             "median_us": round(float(np.median(ev_ms)) * 1e3, 2), "p90_us": round(float(np.percentile(ev_ms, 90)) * 1e3, 2),
             "flops": flops, "TFLOP/s": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
@@ -713,9 +724,9 @@ def profile_only(args):
     """A short run of one kernel, for rocprofv3 (no JSON contract)."""
     import torch
     from grouped_query_attention_gqa_amd import workloads as W
-    if args.only in ("prefill", "chunked"):
+    if args.only in ("prefill", "chunked", "chunked_fp8"):
         name = "causal_prefill_4k" if args.only == "prefill" else "chunked_prefill_paged"
-        r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup)
+        r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup, fp8=args.only == "chunked_fp8")
         print(json.dumps(r), flush=True)
         return
     if args.only == "copy":

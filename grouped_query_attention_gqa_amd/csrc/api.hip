@@ -432,8 +432,7 @@ gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_ne
     if (B == 0 || s == 0) return GQA_OK;
     if (!q || !k_new || !v_new || !start_pos || !out) return fail(GQA_ERR_INVALID_ARG, "NULL pointer");
     if (!scale_ok(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not a positive finite number");
-    if (v.elem_bytes == 1) return fail(GQA_ERR_UNSUPPORTED, "prefill on an FP8 cache");
-    const bool bf16 = v.elem_bytes == 2;
+    const bool bf16 = v.elem_bytes == 2, fp8 = v.elem_bytes == 1;
     if (check_mode()) {
         std::vector<int32_t> sp;
         if (!fetch_i32(start_pos, B, sp)) return fail(GQA_ERR_LAUNCH, "start_pos copy failed");
@@ -457,7 +456,7 @@ gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_ne
     if ((st = launch_status(launch_kv_append(ap, hs), "prefill append")) != GQA_OK) return st;
 
     const float scale_log2 = scale * 1.4426950408889634f;
-    if (bf16) {
+    if (bf16 || fp8) {
         PrefillParams pp{};
         pp.cache = v;
         pp.q = static_cast<const char *>(q);
@@ -470,7 +469,7 @@ gqa_status gqa_prefill_window(const void *q, const void *k_new, const void *v_ne
         pp.causal = causal != 0;
         pp.window = window > 0 ? window : 0;
         pp.scale_log2 = scale_log2;
-        return launch_status(launch_prefill_mfma(pp, hs), "prefill");
+        return launch_status(fp8 ? launch_prefill_fp8(pp, hs) : launch_prefill_mfma(pp, hs), "prefill");
     }
     RowAttnParams p{};
     p.cache = v;

@@ -143,6 +143,8 @@ hipError_t launch_decode_mfma(const RowAttnParams &p, hipStream_t stream);
 // merge of the partial pieces that W workgroup slices of tt-key tiles left in the workspace
 hipError_t launch_merge_pieces(const RowAttnParams &p, int tt, int W, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillParams &p, hipStream_t stream);
+// the same over an FP8 E4M3 cache with row scales (d = 128)
+hipError_t launch_prefill_fp8(const PrefillParams &p, hipStream_t stream);
 
 constexpr int kKeyTile = 64;   // prefill key tile
 

@@ -55,12 +55,12 @@
  *     inference-optimisation page §10.2; the result is the same for every n
  *     up to the rounding of the merge); unset, each kernel picks its own.
  *   - Quantised cache (GQA_FP8_E4M3): K/V rows stored as FP8 E4M3 with one
- *     fp32 scale per cached row (token x KV head), written by gqa_kv_append
- *     and gqa_decode_step and read by the decode calls (inference-
- *     optimisation page §15.5-§15.5.1: per-token / per-head scales, FP8
- *     E4M3).  Queries, new K/V rows and outputs are then bf16.  Supported
- *     for head_dim 128 (and paged blocks of at least 16 tokens) by the
- *     append and decode calls; the prefill calls return GQA_ERR_UNSUPPORTED.
+ *     fp32 scale per cached row (token x KV head), written by gqa_kv_append,
+ *     gqa_decode_step and the prefill calls and read by the decode and
+ *     prefill calls (inference-optimisation page §15.5-§15.5.1: per-token /
+ *     per-head scales, FP8 E4M3).  Queries, new K/V rows and outputs are then
+ *     bf16.  Supported for head_dim 128; the decode calls need paged blocks
+ *     of at least 16 tokens.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -181,6 +181,10 @@ gqa_status gqa_decode(const void *q, const gqa_kv_cache *cache, const int32_t *c
  *   causal == 0: every row sees keys 0 .. start_pos[b] + s - 1
  * bf16 runs on the matrix cores (bf16 products, fp32 accumulation and
  * softmax statistics); fp32 runs on the vector ALUs in fp32 throughout.
+ * An FP8 cache (chunked prefill over a quantised prefix, inference-
+ * optimisation page §11.7 with §15.5.1): the new rows are quantised into the
+ * cache as gqa_kv_append does it, and every row, old and new, is read as its
+ * scale times its E4M3 value; queries and outputs are bf16.
  */
 gqa_status gqa_prefill(const void *q, const void *k_new, const void *v_new,
                        const gqa_kv_cache *cache, const int32_t *start_pos, int32_t B, int32_t s,

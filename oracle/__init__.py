@@ -302,3 +302,46 @@ def dequantize_e4m3_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     out = np.empty(codes.shape, dtype=np.float64)
     _load().oracle_dequantize_e4m3_rows(_ptr(codes), _ptr(scales), codes.size // d if d else 0, d, _ptr(out))
     return out
+
+
+# ---------------------------------------------------------------------------
+# prefill over an FP8 cache (inference-optimisation page §11.7, a chunk of new
+# tokens after a cached prefix, with §15.5.1's quantised K/V): the new rows are
+# quantised into the cache exactly as the append quantises them, and every
+# cached row, old or new, stands for scale * E4M3(code).  Attention is then
+# the plain definition over those values.  Composed only of the functions
+# above (quantiser, indexed copies, decoder, attention).
+# ---------------------------------------------------------------------------
+
+def fp8_cache_after_append(codes: np.ndarray, scales: np.ndarray, new_rows: np.ndarray, start_pos,
+                           block_table=None):
+    """(codes, scales) of an FP8 cache after the quantising append of new_rows
+    [B, s, K, d] (bf16 bits or fp32) at start_pos: codes [B,K,S,d] / [N,K,bs,d]
+    uint8, scales [B,K,S] / [N,K,bs] float32."""
+    qc, qs = quantize_e4m3_rows(new_rows)
+    codes = np.ascontiguousarray(codes).copy()
+    scales = np.ascontiguousarray(scales, dtype=np.float32).copy()
+    sc4, qs4 = scales[..., None], np.ascontiguousarray(qs[..., None])
+    if block_table is None:
+        kv_append(codes, qc, start_pos)
+        kv_append(sc4, qs4, start_pos)
+    else:
+        kv_append_paged(codes, qc, start_pos, block_table)
+        kv_append_paged(sc4, qs4, start_pos, block_table)
+    return codes, sc4[..., 0]
+
+
+def prefill_fp8_rows(q, k_codes, k_scales, v_codes, v_scales, start_pos, s: int, causal: bool, scale: float, rows,
+                     window: int = 0, block_table=None) -> np.ndarray:
+    """Attention rows (b, i, h) of a prefill of s new tokens over an FP8 cache
+    that already holds them (fp8_cache_after_append): keys 0 .. start+s-1 of
+    sequence b, each scale * E4M3(code).  q is [B, s, H, d] fp64."""
+    kd = dequantize_e4m3_rows(k_codes, k_scales)
+    vd = dequantize_e4m3_rows(v_codes, v_scales)
+    start = np.asarray(start_pos, dtype=np.int32)
+    kv_len = start + s
+    if block_table is not None:
+        S = int(kv_len.max())
+        kd = gather_paged(kd, block_table, kv_len, S)
+        vd = gather_paged(vd, block_table, kv_len, S)
+    return attention_rows(q, kd, vd, start, kv_len, causal, scale, rows, window)

@@ -146,7 +146,7 @@ def test_decode_step_rejects_bad_args(lib):
 
 def test_fp8_cache_argument_rules(lib):
     """An FP8 cache needs both scale arrays and head_dim 128; decode takes blocks
-    of at least 16 tokens; prefill is not offered on it."""
+    of at least 16 tokens."""
     f8 = dict(dtype=binding.GQA_FP8_E4M3, head_dim=128, S_max=4096, num_kv_heads=8)
     sc = dict(k_scale=0x50000, v_scale=0x60000)
     ws = lib.gqa_decode_workspace_bytes(1, 32, 8, 128, 4096)
@@ -158,9 +158,11 @@ def test_fp8_cache_argument_rules(lib):
     assert dec(_cache(**{**f8, "head_dim": 64}, **sc)) == binding.GQA_ERR_UNSUPPORTED
     paged = dict(block_table=0x40000, block_size=8, max_blocks_per_seq=4, num_blocks=4)
     assert dec(_cache(**f8, **sc, **paged)) == binding.GQA_ERR_UNSUPPORTED      # 8-token blocks
-    pf = lib.gqa_prefill(FAKE, FAKE, FAKE, ctypes.byref(_cache(**f8, **sc)), FAKE, 1, 4, 32, ctypes.c_float(0.1), 1,
-                         FAKE, None)
-    assert pf == binding.GQA_ERR_UNSUPPORTED
+    # prefill over an FP8 cache: head_dim 128 only, both scale arrays
+    pf = lambda cache: lib.gqa_prefill(FAKE, FAKE, FAKE, ctypes.byref(cache), FAKE, 1, 4, 32, ctypes.c_float(0.1), 1,
+                                       FAKE, None)
+    assert pf(_cache(**{**f8, "head_dim": 64}, **sc)) == binding.GQA_ERR_UNSUPPORTED
+    assert pf(_cache(**f8, v_scale=0x60000)) == binding.GQA_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, -0.0, float("-inf")])

@@ -330,3 +330,137 @@ def test_fp8_paged_spikes_exact():
             assert np.array_equal(want, as_f64(inp.v[blk, g, slot], "bf16"))
             for r in range(wl.G):
                 assert np.array_equal(out[b, 0, g * wl.G + r], want), (b, g, t)
+
+
+# ---------------------------------------------------------------------------
+# prefill over an FP8 cache (inference-optimisation page §11.7 with §15.5.1):
+# the new rows are quantised into the cache by the call, and every row, old
+# and new, is read as scale * E4M3(code); the oracle is the plain attention
+# over those values (oracle.prefill_fp8_rows).
+# ---------------------------------------------------------------------------
+
+def _fp8_prefill_run(B, H, K, s, start, *, paged=False, bs=16, causal=True, window=0, seed=0, rows=None,
+                     inputs=None):
+    """Runs gqa_prefill on an FP8 cache holding start[b] quantised prefix tokens
+    of sequence b; returns (out [B,s,H,d] bf16 bits, expected rows, rows).
+    inputs = (q, k_new, v_new, k_prefix, v_prefix) as bf16 bits, else random.
+    Unused cache slots hold the NaN code and NaN scales; the cache after the
+    call must be the oracle's quantising append of the new rows, bit for bit."""
+    d = 128
+    rng = np.random.default_rng(seed)
+    starts = np.full(B, start, np.int32) if np.isscalar(start) else np.asarray(start, np.int32)
+    S = int(starts.max()) + s
+    if inputs is None:
+        bits = lambda *shape, f=1.0: W.f32_to_bf16_bits((rng.standard_normal(shape) * 0.5 * f).astype(np.float32))
+        q, kn, vn = bits(B, s, H, d), bits(B, s, K, d), bits(B, s, K, d)
+        kp = bits(B, S, K, d, f=rng.lognormal(0, 1, (B, S, K, 1)))
+        vp = bits(B, S, K, d)
+    else:
+        q, kn, vn, kp, vp = inputs
+    table = None
+    if paged:
+        table, n_pool = W.deal_blocks(rng, starts + s, bs, slack_blocks=2)
+        shape = (n_pool, K, bs, d)
+    else:
+        shape = (B, K, S, d)
+    codes = {n: np.full(shape, NAN_CODE, np.uint8) for n in "kv"}
+    scales = {n: np.full(shape[:-1], np.nan, np.float32) for n in "kv"}
+    # the prefix: positions t < starts[b] of sequence b, quantised by the oracle
+    for n, pre in (("k", kp), ("v", vp)):
+        for b in range(B):
+            if starts[b] == 0:
+                continue
+            rows_b = np.ascontiguousarray(pre[b:b + 1, :starts[b]])
+            if table is None:
+                c, sc = oracle.fp8_cache_after_append(codes[n][b:b + 1], scales[n][b:b + 1], rows_b, [0])
+                codes[n][b], scales[n][b] = c[0], sc[0]
+            else:
+                codes[n], scales[n] = oracle.fp8_cache_after_append(codes[n], scales[n], rows_b, [0], table[b:b + 1])
+    cache = _f8_cache(codes["k"], scales["k"], codes["v"], scales["v"], table)
+    say("fp8 prefill", f"B={B} H={H} K={K} s={s} start={list(starts)} paged={paged} bs={bs} window={window}")
+    out = binding.gqa_prefill(to_dev(q), to_dev(kn), to_dev(vn), cache, to_dev(starts), causal=causal,
+                              scale=1.0 / np.sqrt(d), window=window)
+    torch.cuda.synchronize()
+    after = {}
+    for n, new in (("k", kn), ("v", vn)):
+        want_c, want_s = oracle.fp8_cache_after_append(codes[n], scales[n], new, starts, table)
+        got_c = f8_host(getattr(cache, n))
+        got_s = getattr(cache, n + "_scale").cpu().numpy()
+        assert np.array_equal(got_c, want_c), f"{n} codes after the prefill"
+        assert got_s.view(np.uint32).tobytes() == want_s.view(np.uint32).tobytes(), f"{n} scales after the prefill"
+        after[n] = (want_c, want_s)
+    if rows is None:
+        rows = np.array([[b, i, h] for b in range(B) for i in range(s) for h in range(H)], np.int32)
+    want = oracle.prefill_fp8_rows(as_f64(q, "bf16"), after["k"][0], after["k"][1], after["v"][0], after["v"][1],
+                                   starts, s, causal, 1.0 / np.sqrt(d), rows, window, table)
+    return from_dev(out), want, rows, after, table
+
+
+def _check_fp8_prefill(what, **kw):
+    out, want, rows, _, _ = _fp8_prefill_run(**kw)
+    got = as_f64(out[rows[:, 0], rows[:, 1], rows[:, 2]], "bf16")
+    check_close(got, want, BF16_TOL, what)
+
+
+@pytest.mark.parametrize("H,K", [(32, 8), (64, 8), (8, 8), (64, 1), (24, 8)])
+def test_fp8_prefill_matches_oracle(H, K):
+    _check_fp8_prefill(f"fp8 prefill H={H} K={K}", B=2, H=H, K=K, s=150, start=0, seed=H + K)
+
+
+@pytest.mark.parametrize("paged,bs", [(False, 16), (True, 16), (True, 4), (True, 64)])
+def test_fp8_prefill_after_a_quantised_prefix(paged, bs):
+    _check_fp8_prefill(f"fp8 chunked prefill paged={paged} bs={bs}", B=3, H=32, K=8, s=70, start=[200, 63, 1],
+                       paged=paged, bs=bs, seed=bs)
+
+
+@pytest.mark.parametrize("window,causal", [(40, True), (1, True), (0, False)])
+def test_fp8_prefill_window_and_full(window, causal):
+    _check_fp8_prefill(f"fp8 prefill window={window} causal={causal}", B=2, H=32, K=8, s=100, start=[90, 17],
+                       window=window, causal=causal, seed=7)
+
+
+def test_fp8_chunked_prefill_full_size_sampled():
+    """The bench's chunked shape on an FP8 cache: 512 new tokens after a
+    3584-token quantised prefix in shuffled 16-token blocks; 300 sampled rows."""
+    rng = np.random.default_rng(9)
+    B, H, s = 4, 32, 512
+    rows = np.stack([rng.integers(0, B, 300), rng.integers(0, s, 300), rng.integers(0, H, 300)], axis=1).astype(np.int32)
+    rows[:4] = [[0, 0, 0], [3, s - 1, H - 1], [1, 255, 17], [2, 511, 3]]
+    _check_fp8_prefill("fp8 chunked prefill, full size", B=B, H=H, K=8, s=s, start=3584, paged=True, rows=rows,
+                       seed=3)
+
+
+def test_fp8_prefill_spikes_over_the_prefix_exact():
+    """All weight on one cached key per (sequence, group), the first or last slot
+    of a block or the prefix's last slot, whose V row has a power-of-two scale:
+    every new row of the group returns that dequantised row bit for bit."""
+    B, H, K, d, s, start = 2, 32, 8, 128, 64, 1000
+    G = H // K
+    rng = np.random.default_rng(61)
+    u = rng.choice([-1.0, 1.0], size=(B, K, d)).astype(np.float32)
+    kp = np.zeros((B, start, K, d), np.float32)
+    t = np.arange(start)
+    mant = 1.0 + ((t[:, None] + np.arange(d)[None, :]) % 7) / 8.0          # 1 .. 1.75: amax 1.75
+    vp = (rng.choice([-1.0, 1.0], size=(B, start, K, d)) * mant[None, :, None, :] *
+          np.exp2((t % 5) - 2.0)[None, :, None, None]).astype(np.float32)
+    spikes = [[0, 15, 16, 999, 511, 512, 31, 640], [1, 14, 999, 998, 32, 47, 48, 100]]
+    for b in range(B):
+        for g in range(K):
+            kp[b, spikes[b][g], g] = 2.5 * u[b, g]
+    q = np.zeros((B, s, H, d), np.float32)
+    for g in range(K):
+        q[:, :, g * G:(g + 1) * G] = u[:, g][:, None, None, :]
+    kn = np.zeros((B, s, K, d), np.float32)
+    vn = rng.standard_normal((B, s, K, d)).astype(np.float32)
+    bits = W.f32_to_bf16_bits
+    out, want, rows, after, table = _fp8_prefill_run(B=B, H=H, K=K, s=s, start=start, paged=True, seed=62,
+                                                     inputs=(bits(q), bits(kn), bits(vn), bits(kp), bits(vp)))
+    vd = oracle.dequantize_e4m3_rows(*after["v"])
+    got = as_f64(out, "bf16")
+    for b in range(B):
+        for g in range(K):
+            tt = spikes[b][g]
+            want_row = vd[int(table[b, tt // 16]), g, tt % 16]
+            assert np.array_equal(want_row, vp[b, tt, g].astype(np.float64))   # the round trip is exact here
+            assert np.array_equal(got[b, :, g * G:(g + 1) * G], np.broadcast_to(want_row, (s, G, d))), (b, g, tt)
+    check_close(got[rows[:, 0], rows[:, 1], rows[:, 2]], want, BF16_TOL, "fp8 spikes against the oracle")

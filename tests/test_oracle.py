@@ -750,3 +750,73 @@ def test_bf16_bits_input_is_the_same_as_fp32_values(oracle_lib):
     a = oracle.quantize_e4m3_rows(x)
     b = oracle.quantize_e4m3_rows(bits)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# prefill over an FP8 cache: the reading (the new rows quantised as the append
+# quantises them, every cached row read as scale * E4M3(code)) pinned to the
+# bf16 attention where quantisation is exact, and to per-row scaling
+# ---------------------------------------------------------------------------
+
+def _e4m3_exact_rows(rng, shape, scale_exp):
+    """Rows whose values are E4M3 values times a power-of-two row scale, each
+    row reaching 448 * scale: quantisation returns them unchanged."""
+    grid = np.array([oracle.e4m3_value(c) for c in range(0x7F)])       # 0 .. 448, non-negative codes
+    grid = grid[np.isfinite(grid)]
+    x = rng.choice(grid, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+    x[..., 0] = 448.0 * rng.choice([-1.0, 1.0], size=shape[:-1])
+    return (x * np.exp2(scale_exp)[..., None]).astype(np.float32)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_fp8_prefill_equals_attention_when_quantisation_is_exact(oracle_lib, paged):
+    rng = np.random.default_rng(51)
+    B, H, K, d, start, s = 2, 4, 2, 8, 5, 6
+    S = start + s
+    kp = _e4m3_exact_rows(rng, (B, start, K, d), rng.integers(-9, -3, (B, start, K)))
+    vp = _e4m3_exact_rows(rng, (B, start, K, d), rng.integers(-9, -3, (B, start, K)))
+    kn = _e4m3_exact_rows(rng, (B, s, K, d), rng.integers(-9, -3, (B, s, K)))
+    vn = _e4m3_exact_rows(rng, (B, s, K, d), rng.integers(-9, -3, (B, s, K)))
+    q = rand(rng, B, s, H, d)
+    table = None
+    if paged:
+        table, n_pool = np.array([[2, 0, 5], [1, 4, 3]], np.int32), 6
+        shape = (n_pool, K, 4, d)
+    else:
+        shape = (B, K, S, d)
+    codes = {n: np.full(shape, 0x7F, np.uint8) for n in "kv"}
+    scales = {n: np.full(shape[:-1], np.nan, np.float32) for n in "kv"}
+    zero = np.zeros(B, np.int32)
+    for n, pre in (("k", kp), ("v", vp)):
+        codes[n], scales[n] = oracle.fp8_cache_after_append(codes[n], scales[n], pre, zero, table)
+    start_pos = np.full(B, start, np.int32)
+    for n, new in (("k", kn), ("v", vn)):
+        codes[n], scales[n] = oracle.fp8_cache_after_append(codes[n], scales[n], new, start_pos, table)
+    rows = np.array([[b, i, h] for b in range(B) for i in range(s) for h in range(H)], np.int32)
+    got = oracle.prefill_fp8_rows(q, codes["k"], scales["k"], codes["v"], scales["v"], start_pos, s, True, 0.3, rows,
+                                  block_table=table)
+    k_all = np.concatenate([kp, kn], axis=1).transpose(0, 2, 1, 3).astype(np.float64)
+    v_all = np.concatenate([vp, vn], axis=1).transpose(0, 2, 1, 3).astype(np.float64)
+    want = sdpa_ref(q, k_all, v_all, start_pos, start_pos + s, True, 0.3)
+    np.testing.assert_allclose(got, want[rows[:, 0], rows[:, 1], rows[:, 2]], rtol=0, atol=1e-12)
+
+
+def test_fp8_prefill_scales_with_the_value_rows(oracle_lib):
+    """Multiplying every V row by 2^k multiplies the FP8 prefill by 2^k exactly
+    (the codes stay, the per-row scales double), while the bf16 rounding of the
+    rows before quantisation is exact for powers of two."""
+    rng = np.random.default_rng(52)
+    B, H, K, d, s = 1, 2, 1, 16, 7
+    kn = rng.standard_normal((B, s, K, d)).astype(np.float32)
+    vn = rng.standard_normal((B, s, K, d)).astype(np.float32)
+    q = rand(rng, B, s, H, d)
+    rows = np.array([[0, i, h] for i in range(s) for h in range(H)], np.int32)
+    zero = np.zeros(B, np.int32)
+
+    def run(v):
+        c = {n: np.zeros((B, K, s, d), np.uint8) for n in "kv"}
+        sc = {n: np.zeros((B, K, s), np.float32) for n in "kv"}
+        c["k"], sc["k"] = oracle.fp8_cache_after_append(c["k"], sc["k"], kn, zero)
+        c["v"], sc["v"] = oracle.fp8_cache_after_append(c["v"], sc["v"], v, zero)
+        return oracle.prefill_fp8_rows(q, c["k"], sc["k"], c["v"], sc["v"], zero, s, True, 0.25, rows)
+    np.testing.assert_array_equal(run(vn * np.float32(8.0)), 8.0 * run(vn))
