@@ -57,6 +57,18 @@ HBM_PEAK_GBS = 8000.0
 DECODE_KERNELS = ("decode_mfma_kernel<1, false> (with the append of the newest token) + merge_rows_kernel "
                   "(one gqa_decode_step call)")
 DECODE_SOURCES = ("decode_mfma.hip", "stream_attention.hip", "worklist.h", "kernels.h", "common.h")
+PREFILL_SOURCES = ("prefill_mfma.hip", "kv_append.hip", "kernels.h", "common.h")
+PREFILL_FP8_SOURCES = ("prefill_fp8.hip", "kv_append.hip", "kernels.h", "common.h")
+# the kernel sources each committed byte-counter figure was taken on
+TRAFFIC_SOURCES = {
+    "decode/llama3_8b_decode": DECODE_SOURCES,
+    "decode/llama2_70b_decode": DECODE_SOURCES,
+    "decode/paged_long_decode": DECODE_SOURCES,
+    "decode/llama2_70b_decode_mqa": DECODE_SOURCES,
+    "decode/llama3_8b_decode_fp8_cache": DECODE_SOURCES + ("kv_append.hip",),
+    "prefill/causal_prefill_4k": PREFILL_SOURCES,
+    "prefill/chunked_prefill_paged_fp8_cache": PREFILL_FP8_SOURCES,
+}
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "GQA decode HBM GB/s (% of peak) + causal prefill TFLOP/s (% MFMA peak), bf16"
 MALL_BYTES = 256 * 2**20
@@ -79,6 +91,9 @@ def parse():
                     help="profile one kernel: decode|step|fp8|multi|prefill|decode70b|paged|mha|mqa|window|chunked|chunked_fp8|"
                          "copy (a 512 MiB device copy)")
     ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
+    ap.add_argument("--traffic", nargs=6, default=None,
+                    metavar=("KEY", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "ALG_BYTES"),
+                    help="record one leg's byte counters (rocprofv3 --pmc runs) in profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -235,7 +250,8 @@ def kernel_source_hash(names=DECODE_SOURCES) -> str:
 
 
 def committed_traffic(key: str):
-    """HBM bytes per launch from profiles/traffic.json, if taken on the current kernel sources."""
+    """HBM bytes per call from profiles/traffic.json, if they were taken on the
+    current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -243,9 +259,37 @@ def committed_traffic(key: str):
     except (OSError, ValueError):
         return None
     ent = table.get(key)
-    if not ent or ent.get("source_sha") != kernel_source_hash():
+    if not ent or ent.get("source_sha") != kernel_source_hash(tuple(ent.get("sources", ()))):
         return None
     return ent.get("bytes_per_launch")
+
+
+def record_traffic(key: str, fetch_dir: str, write_dir: str, copy_fetch_dir: str, copy_write_dir: str,
+                   algorithmic: int):
+    """Writes the byte counters of one leg (FETCH_SIZE and WRITE_SIZE runs, each
+    scaled by a device copy's reading) into profiles/traffic.json, tagged with
+    the hash of the kernel sources, and prints the summary lines."""
+    summ = summarize_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, COPY_BYTES)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    sources = TRAFFIC_SOURCES[key]
+    total = sum(k["hbm_bytes"] for k in summ["kernels"].values())
+    table[key] = {"source_sha": kernel_source_hash(sources), "sources": list(sources), "bytes_per_launch": total,
+                  "algorithmic_bytes": algorithmic, "kernels": summ["kernels"],
+                  "calibration": {k: summ[k] for k in ("copy_bytes", "copy_FETCH_SIZE_KiB", "copy_WRITE_SIZE_KiB",
+                                                       "fetch_scale", "write_scale")}}
+    with open(path, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    print(key)
+    for name, k in summ["kernels"].items():
+        print(f"  {name[:60]:60s} FETCH {k['FETCH_SIZE_KiB']:12.1f} KiB  WRITE {k['WRITE_SIZE_KiB']:10.1f} KiB  -> "
+              f"{k['hbm_bytes']:12d} B")
+    if algorithmic:
+        print(f"  one call: {total} B measured vs {algorithmic} B algorithmic (ratio {total / algorithmic:.3f})")
 
 
 def _csv_rows(path):
@@ -464,8 +508,11 @@ def pages_context():
 
 
 def bench_tiny(iters: int, warmup: int):
-    """The tiny fp32 workloads (causal prefill s = 128; decode over 128 cached
-    tokens): launch-bound, reported in microseconds per call (HIP events)."""
+    """The tiny fp32 workloads (causal prefill of s = 128; decode over 128
+    cached tokens): launch-bound, reported in microseconds per call.  `us` is
+    the device time per call, from a HIP graph of 20 calls replayed back to
+    back (no host work between the calls); `eager_us` brackets single eager
+    calls with HIP events, so it also holds the host's launch path."""
     import torch
     from grouped_query_attention_gqa_amd import binding
     from grouped_query_attention_gqa_amd import workloads as W
@@ -476,16 +523,15 @@ def bench_tiny(iters: int, warmup: int):
     kc = torch.zeros(wl.B, wl.K, wl.s, wl.d, dtype=torch.float32, device="cuda")
     cache = binding.KVCache(kc, torch.zeros_like(kc))
     o = torch.empty_like(q)
-    call = lambda: binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=o, scale=wl.scale)
-    out[wl.name] = _event_time(call, iters, warmup)
+    out[wl.name] = _tiny_times(lambda: binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=o,
+                                                           scale=wl.scale), iters, warmup)
     wl = W.WORKLOADS["tiny_decode_f32"]
     db = DecodeBench(wl, copies=1)
-    mean_ms, med_ms = time_decode_only(db, iters, warmup)
-    out[wl.name] = {"us": round(mean_ms * 1e3, 2), "median_us": round(med_ms * 1e3, 2), "calls": iters}
+    out[wl.name] = _tiny_times(lambda: db.decode(0), iters, warmup)
     return out
 
 
-def _event_time(call, iters, warmup):
+def _tiny_times(call, iters, warmup, per_graph=20):
     import torch
     for _ in range(warmup):
         call()
@@ -496,9 +542,25 @@ def _event_time(call, iters, warmup):
         call()
         b.record()
     torch.cuda.synchronize()
-    ts = np.array([a.elapsed_time(b) for a, b in evs])
-    return {"us": round(float(np.mean(ts)) * 1e3, 2), "median_us": round(float(np.median(ts)) * 1e3, 2),
-            "calls": iters}
+    eager = np.array([a.elapsed_time(b) for a, b in evs])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(per_graph):
+            call()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(3, iters // per_graph)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    dev_us = a.elapsed_time(b) * 1e3 / (reps * per_graph)
+    del g
+    return {"us": round(dev_us, 2), "eager_us": round(float(np.mean(eager)) * 1e3, 2),
+            "eager_median_us": round(float(np.median(eager)) * 1e3, 2), "calls": reps * per_graph}
 
 
 # ---------------------------------------------------------------------------
@@ -507,6 +569,10 @@ def main():
     args = parse()
     if args.summarize:
         print(summarize_trace(args.summarize))
+        return
+    if args.traffic:
+        key, fd, wd, cfd, cwd, alg = args.traffic
+        record_traffic(key, fd, wd, cfd, cwd, int(alg))
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this library runs on one GPU; --gpus above 1 is not supported",
@@ -609,7 +675,9 @@ def main():
             mean_ms, med_ms = time_decode_only(d2, max(LEG_CALLS, args.steps), 3)
             gbs = d2.alg_bytes / (mean_ms * 1e-3) / 1e9
             extra[name] = {"us": round(mean_ms * 1e3, 2), "GB/s": round(gbs, 1),
-                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": d2.alg_bytes}
+                           "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": d2.alg_bytes,
+                           "median_us": round(med_ms * 1e3, 2), "calls": max(LEG_CALLS, args.steps),
+                           "traffic": committed_traffic("decode/" + name)}
             log(f"{name}: {mean_ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
             del d2
             torch.cuda.empty_cache()
@@ -631,7 +699,9 @@ def main():
         gbs = d2.alg_bytes / (mean_ms * 1e-3) / 1e9
         extra["llama3_8b_decode_fp8_cache"] = {
             "us": round(mean_ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "bytes": d2.alg_bytes, "cache": "FP8 E4M3 codes + one fp32 scale per row; q/out bf16"}
+            "bytes": d2.alg_bytes, "cache": "FP8 E4M3 codes + one fp32 scale per row; q/out bf16",
+            "median_us": round(med_ms * 1e3, 2), "calls": max(LEG_CALLS, args.steps),
+            "traffic": committed_traffic("decode/llama3_8b_decode_fp8_cache")}
         log(f"llama3_8b_decode_fp8_cache: {mean_ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
         del d2
         torch.cuda.empty_cache()
@@ -714,7 +784,8 @@ def bench_prefill(wl, iters, warmup, fp8=False):
             "paged": wl.paged, "cache": "FP8 E4M3 codes + one fp32 scale per row" if fp8 else "bf16",
             "us_per_call": round(ms * 1e3, 2),
             "median_us": round(float(np.median(ev_ms)) * 1e3, 2), "p90_us": round(float(np.percentile(ev_ms, 90)) * 1e3, 2),
-            "flops": flops, "TFLOP/s": round(tf, 2),
+            "flops": flops, "TFLOP/s": round(tf, 2), "calls": iters,
+            "traffic": committed_traffic(("prefill/" + wl.name) + ("_fp8_cache" if fp8 else "")),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                          "note": "time covers the append and the attention kernel"}}
