@@ -89,7 +89,7 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
     ap.add_argument("--only", default=None,
                     help="profile one kernel: decode|step|fp8|multi|prefill|decode70b|paged|mha|mqa|window|chunked|chunked_fp8|"
-                         "copy (a 512 MiB device copy)")
+                         "tiny_prefill|tiny_decode (both tiny fp32 workloads)|copy (a 512 MiB device copy)")
     ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
     ap.add_argument("--traffic", nargs=6, default=None,
                     metavar=("KEY", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR", "ALG_BYTES"),
@@ -801,6 +801,10 @@ def profile_only(args):
     if args.only in ("prefill", "chunked", "chunked_fp8"):
         name = "causal_prefill_4k" if args.only == "prefill" else "chunked_prefill_paged"
         r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup, fp8=args.only == "chunked_fp8")
+        print(json.dumps(r), flush=True)
+        return
+    if args.only in ("tiny_prefill", "tiny_decode"):
+        r = bench_tiny(args.steps, args.warmup)
         print(json.dumps(r), flush=True)
         return
     if args.only == "copy":

@@ -532,8 +532,6 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 constexpr int kMergeRows = 4;   // rows per workgroup (more workgroups for the many-piece items of large groups)
 __global__ __launch_bounds__(kMergeRows * (D / 4)) void merge_rows_kernel(RowAttnParams p, int W)
 {
-    __shared__ int slots[kStreamWGs];
-    __shared__ int n_slots;
     const int g = blockIdx.x, row = blockIdx.y;
     const int G = p.G, H = p.H, mq = p.mq > 1 ? p.mq : 1;
     const int R = mq * G;
@@ -556,24 +554,15 @@ __global__ __launch_bounds__(kMergeRows * (D / 4)) void merge_rows_kernel(RowAtt
     if (wa == wb) return;
     // the workspace slots of the pieces: with at least one tile per slice
     // (T >= W) the pieces are the slices wa .. wb, the first one in slot 1
-    // when the item starts inside it; otherwise empty slices are skipped
+    // when the item starts inside it; otherwise every tile of the item is a
+    // piece of its own, in slot 0 of its slice
     const bool dense = T >= W;
-    if (!dense) {
-        if (threadIdx.x == 0) {
-            int n = 0;
-            for (int64_t w = wa; w <= wb; ++w) {
-                const int64_t s0 = slice_start(w, T, W);
-                if (s0 == slice_start(w + 1, T, W)) continue;   // an empty slice holds nothing
-                slots[n++] = (int)(w * 2 + (s0 < a ? 1 : 0));
-            }
-            n_slots = n;
-        }
-        __syncthreads();
-    }
     if (rho >= R) return;
-    const int ns = dense ? (int)(wb - wa + 1) : n_slots;
+    const int ns = dense ? (int)(wb - wa + 1) : (int)(e - a + 1);
     const int slot0 = (int)(wa * 2 + (slice_start(wa, T, W) < a ? 1 : 0));
-    auto slot_of = [&](int k) { return dense ? (k == 0 ? slot0 : (int)(wa + k) * 2) : slots[k]; };
+    auto slot_of = [&](int k) {
+        return dense ? (k == 0 ? slot0 : (int)(wa + k) * 2) : (int)sparse_slot(a + k, T, W);
+    };
     // pieces in batches of 8 whose loads are issued together; within a batch
     // and from batch to batch the running maximum rescales what is summed
     constexpr int BATCH = 8;

@@ -534,15 +534,13 @@ __global__ __launch_bounds__(NT, (Cfg<D, GP, BF16>::LIMIT > LDS_LIMIT ? 1 : 2)) 
 // sum: M = max_s m_s, L = sum_s l_s 2^(m_s - M), out = sum_s o_s 2^(m_s - M) / L
 // (m in log2 units).  Items held by one workgroup were stored by it; rows
 // without a visible key get zeros.  Block (g, row, z) handles heads
-// z*kMergeHeads .. of the item; the workspace slots of its pieces are listed
-// once in LDS.
+// z*kMergeHeads .. of the item; the workspace slots of its pieces follow
+// from the tile table.
 constexpr int kMergeHeads = 8;
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void merge_pieces_kernel(RowAttnParams p, int tt, int W)
 {
-    __shared__ int slots[kStreamWGs];
-    __shared__ int n_slots;
     const int g = blockIdx.x;
     const int row = blockIdx.y;                       // local row of this launch
     const int G = p.G;
@@ -562,33 +560,18 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(RowAttnParams p, int 
     const int64_t T = p.prefix[p.rows];
     const int64_t tiles = item_tiles(row_first(p, (int64_t)p.row0 + row, n_vis), n_vis, tt);
     const int64_t a = p.prefix[row] + (int64_t)g * tiles, e = a + tiles - 1;
-    auto owner = [&](int64_t x) {
-        int64_t w = x * W / T;
-        while (w + 1 < W && slice_start(w + 1, T, W) <= x) ++w;
-        while (w > 0 && slice_start(w, T, W) > x) --w;
-        return w;
-    };
-    const int64_t wa = owner(a), wb = owner(e);
+    const int64_t wa = slice_owner(a, T, W), wb = slice_owner(e, T, W);
     if (wa == wb) return;
     // the workspace slots of the pieces: with at least one tile per slice
     // (T >= W) they are the slices wa .. wb, the first in slot 1 when the
-    // item starts inside it; otherwise empty slices are skipped
+    // item starts inside it; otherwise every tile of the item is a piece of
+    // its own, in slot 0 of its slice
     const bool dense = T >= W;
-    if (!dense) {
-        if (threadIdx.x == 0) {
-            int n = 0;
-            for (int64_t w = wa; w <= wb; ++w) {
-                const int64_t s0 = slice_start(w, T, W);
-                if (s0 == slice_start(w + 1, T, W)) continue;   // an empty slice holds nothing
-                slots[n++] = (int)(w * 2 + (s0 < a ? 1 : 0));
-            }
-            n_slots = n;
-        }
-        __syncthreads();
-    }
-    const int ns = dense ? (int)(wb - wa + 1) : n_slots;
+    const int ns = dense ? (int)(wb - wa + 1) : (int)(e - a + 1);
     const int slot0 = (int)(wa * 2 + (slice_start(wa, T, W) < a ? 1 : 0));
-    auto slot_of = [&](int k) { return dense ? (k == 0 ? slot0 : (int)(wa + k) * 2) : slots[k]; };
+    auto slot_of = [&](int k) {
+        return dense ? (k == 0 ? slot0 : (int)(wa + k) * 2) : (int)sparse_slot(a + k, T, W);
+    };
     for (int idx = threadIdx.x; idx < nh * D / 4; idx += 256) {
         const int r = h0 + (4 * idx) / D, col = (4 * idx) % D;
         // pieces in batches whose loads are issued together; the running

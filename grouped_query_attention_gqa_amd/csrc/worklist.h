@@ -159,14 +159,13 @@ __device__ __forceinline__ void cursor_next(const int32_t *nvis, const int32_t *
 
 __device__ __forceinline__ int64_t slice_start(int64_t w, int64_t T, int64_t W) { return w * T / W; }
 
-// The workgroup whose slice holds flat tile x (slices may be empty when there
-// are fewer tiles than workgroups; the one returned is never empty).
-__device__ __forceinline__ int64_t slice_owner(int64_t x, int64_t T, int64_t W)
-{
-    int64_t w = x * W / T;
-    while (w + 1 < W && slice_start(w + 1, T, W) <= x) ++w;
-    while (w > 0 && slice_start(w, T, W) > x) --w;
-    return w;
-}
+// The workgroup whose slice holds flat tile x: the last w whose slice starts
+// at or before x, i.e. the largest w with w T < (x + 1) W.  Its slice is never
+// empty (it runs to the next start, which lies past x).
+__device__ __forceinline__ int64_t slice_owner(int64_t x, int64_t T, int64_t W) { return ((x + 1) * W - 1) / T; }
+
+// With no more tiles than workgroups (T <= W) a slice holds at most one tile,
+// so the partial of tile x is its slice's first segment, in workspace slot 0.
+__device__ __forceinline__ int64_t sparse_slot(int64_t x, int64_t T, int64_t W) { return 2 * slice_owner(x, T, W); }
 
 }  // namespace gqa

@@ -184,3 +184,18 @@ def test_every_call_rejects_a_scale_that_is_not_positive(lib, scale):
                            None) == binding.GQA_ERR_INVALID_ARG
     assert lib.gqa_prefill_window(FAKE, FAKE, FAKE, ctypes.byref(c), FAKE, 1, 4, 8, sc, 1, 8, FAKE,
                                   None) == binding.GQA_ERR_INVALID_ARG
+
+
+def test_noalloc_step_checks_arguments_before_touching_the_device(lib):
+    """gqa_decode_step_noalloc validates like gqa_decode_step, and refuses a call
+    whose workspace exceeds its static buffer, before any HIP call."""
+    c = _cache()
+    step = lambda kn, vn, B=1, H=8, cache=c, scale=0.125: lib.gqa_decode_step_noalloc(
+        FAKE, kn, vn, ctypes.byref(cache), FAKE, 128, B, H, ctypes.c_float(scale), 0, FAKE, None)
+    assert step(FAKE, None) == binding.GQA_ERR_INVALID_ARG
+    assert step(FAKE, FAKE, H=7) == binding.GQA_ERR_INVALID_ARG
+    assert step(FAKE, FAKE, scale=-1.0) == binding.GQA_ERR_INVALID_ARG
+    assert step(FAKE, FAKE, B=0) == binding.GQA_OK
+    # G = 64 at d = 128: ~33 MiB of partials, beyond the 12 MiB static buffer
+    big = _cache(num_kv_heads=1, head_dim=128, dtype=binding.GQA_BF16, S_max=4096)
+    assert step(FAKE, FAKE, H=64, cache=big) == binding.GQA_ERR_WORKSPACE

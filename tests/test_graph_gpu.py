@@ -77,3 +77,28 @@ def test_prefill_in_a_graph():
     out = torch.empty_like(q)
     _replays_match(lambda: binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale),
                    out, "chunked paged prefill")
+
+
+def test_fp8_prefill_and_noalloc_step_in_a_graph():
+    """The FP8-cache prefill (append + prefill kernels) and the decode step with
+    the library's static workspace, captured and replayed."""
+    wl = W.WORKLOADS["chunked_prefill_paged"].replace(B=2, s=130, start=200)
+    inp = W.make_prefill(wl)
+    q, kn, vn, start = to_dev(inp.q), to_dev(inp.k_new), to_dev(inp.v_new), to_dev(inp.start_pos)
+    S = wl.start + wl.s
+    k = torch.zeros((wl.B, wl.K, S, wl.d), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    v = torch.zeros_like(k)
+    ks = torch.zeros((wl.B, wl.K, S), dtype=torch.float32, device="cuda")
+    cache = binding.KVCache(k, v, None, k_scale=ks, v_scale=torch.zeros_like(ks))
+    out = torch.empty_like(q)
+    _replays_match(lambda: binding.gqa_prefill(q, kn, vn, cache, start, causal=True, out=out, scale=wl.scale),
+                   out, "fp8 prefill")
+    dw = W.WORKLOADS["llama3_8b_decode"].replace(B=5, ctx=("uniform", 40, 2000))
+    dinp = W.make_decode(dw)
+    dkn, dvn = dinp.new_token_rows()
+    dq, dctx, dkn, dvn = to_dev(dinp.q), to_dev(dinp.ctx), to_dev(dkn), to_dev(dvn)
+    dcache = binding.KVCache(to_dev(dinp.k), to_dev(dinp.v))
+    dout = torch.empty_like(dq)
+    m = int(dinp.ctx.max())
+    _replays_match(lambda: binding.gqa_decode_step_noalloc(dq, dkn, dvn, dcache, dctx, m, out=dout, scale=dw.scale),
+                   dout, "decode step, static workspace")
