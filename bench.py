@@ -667,7 +667,7 @@ def main():
 
     if not args.no_extra:
         # ---- causal prefill ------------------------------------------------
-        result["prefill"] = bench_prefill(W.WORKLOADS["causal_prefill_4k"], max(LEG_CALLS, args.steps), 5)
+        result["prefill"] = bench_prefill(W.WORKLOADS["causal_prefill_4k"], max(LEG_CALLS, args.steps), 5, probe=True)
         torch.cuda.empty_cache()
         # ---- the other decode shapes --------------------------------------
         extra = {}
@@ -734,7 +734,56 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def bench_prefill(wl, iters, warmup, fp8=False):
+def sustained_mfma(operands):
+    """The rate (TFLOP/s) at which the device sustains v_mfma_f32_32x32x16_bf16
+    with nothing else running, from the probe library beside libgqa.so: with
+    `operands` (a device tensor whose bytes are read as bf16 values; the
+    prefill leg passes its own q), and with all-zero operands.  One wave per
+    SIMD, each with four independent accumulators; HIP events on the current
+    stream."""
+    import ctypes
+    import torch
+    from grouped_query_attention_gqa_amd import build as gbuild
+    if not os.path.exists(gbuild.PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(gbuild.PROBE_LIB)
+    lib.gqa_probe_mfma_rate.restype = ctypes.c_int
+    lib.gqa_probe_mfma_rate.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.gqa_probe_mfma_count.restype = ctypes.c_int64
+    lib.gqa_probe_mfma_count.argtypes = [ctypes.c_int, ctypes.c_int]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 512, dtype=torch.float32, device="cuda")
+    zeros = torch.zeros(1 << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    iters, reps = 2000, 20
+    out = {}
+    for label, buf in (("workload_operands", operands), ("zero_operands", zeros)):
+        for w in (1,):
+            def call():
+                rc = lib.gqa_probe_mfma_rate(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                             sink.numel(), w, iters, stream)
+                if rc != 0:
+                    raise RuntimeError(f"gqa_probe_mfma_rate failed ({rc})")
+            # ~0.3 s of the same work first, as for the timed legs: the clock
+            # under matrix load settles over milliseconds
+            t_end = time.perf_counter() + 0.3
+            while time.perf_counter() < t_end:
+                for _ in range(8):
+                    call()
+                torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            flop = 32768.0 * lib.gqa_probe_mfma_count(w, iters) * reps
+            out[f"{label}_{w}_wave_per_simd"] = round(flop / (a.elapsed_time(b) * 1e-3) / 1e12, 1)
+    return out
+
+
+def bench_prefill(wl, iters, warmup, fp8=False, probe=False):
     """Append + attention of the prefill workload, HIP events per call.  fp8:
     the cache holds E4M3 codes and a scale per row (the new rows are quantised
     by the call)."""
@@ -783,15 +832,25 @@ def bench_prefill(wl, iters, warmup, fp8=False):
     tf = flops / (ms * 1e-3) / 1e12
     log(f"prefill {wl.name}: {ms * 1e3:.1f} us (append + attention), {tf:.1f} TFLOP/s "
         f"({100 * tf / BF16_MFMA_PEAK_TFLOPS:.1f}% of bf16 MFMA peak)")
+    roof = {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+            "note": "time covers the append and the attention kernel"}
+    if probe:
+        # context: what the matrix cores sustain on these operands with no
+        # softmax, LDS or memory work (their clock under load depends on the data)
+        sus = sustained_mfma(q)
+        if sus:
+            best = sus["workload_operands_1_wave_per_simd"]
+            roof["sustained_mfma_tflops"] = sus
+            roof["frac_of_sustained"] = round(tf / best, 4)
+            log(f"sustained matrix rate on the leg's q values: {best:.0f} TFLOP/s; the call reaches {100 * tf / best:.1f}%")
     return {"workload": wl.name, "B": wl.B, "s": wl.s, "start": wl.start, "H": wl.H, "K": wl.K, "d": wl.d,
             "paged": wl.paged, "cache": "FP8 E4M3 codes + one fp32 scale per row" if fp8 else "bf16",
             "us_per_call": round(ms * 1e3, 2),
             "median_us": round(float(np.median(ev_ms)) * 1e3, 2), "p90_us": round(float(np.percentile(ev_ms, 90)) * 1e3, 2),
             "flops": flops, "TFLOP/s": round(tf, 2), "calls": iters,
             "traffic": committed_traffic(("prefill/" + wl.name) + ("_fp8_cache" if fp8 else "")),
-            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
-                         "note": "time covers the append and the attention kernel"}}
+            "roofline": roof}
 
 
 def profile_only(args):
@@ -800,7 +859,8 @@ def profile_only(args):
     from grouped_query_attention_gqa_amd import workloads as W
     if args.only in ("prefill", "chunked", "chunked_fp8"):
         name = "causal_prefill_4k" if args.only == "prefill" else "chunked_prefill_paged"
-        r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup, fp8=args.only == "chunked_fp8")
+        r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup, fp8=args.only == "chunked_fp8",
+                          probe=args.only == "prefill")
         print(json.dumps(r), flush=True)
         return
     if args.only in ("tiny_prefill", "tiny_decode"):

@@ -67,5 +67,27 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE_DIR = os.path.join(HERE, "probe")
+PROBE_LIB = os.path.join(HERE, "libgqa_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """libgqa_probe.so: measurement aids the bench uses beside the library
+    (the sustained matrix-core rate); never linked into libgqa.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(PROBE_DIR, "*.hip")))
+    objs = [_compile(s) for s in srcs]
+    tmp = PROBE_LIB + ".tmp"
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs,
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
+
+
 if __name__ == "__main__":
     build(verbose=True)
+    build_probe(verbose=True)

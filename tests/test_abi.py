@@ -199,3 +199,14 @@ def test_noalloc_step_checks_arguments_before_touching_the_device(lib):
     # G = 64 at d = 128: ~33 MiB of partials, beyond the 12 MiB static buffer
     big = _cache(num_kv_heads=1, head_dim=128, dtype=binding.GQA_BF16, S_max=4096)
     assert step(FAKE, FAKE, H=64, cache=big) == binding.GQA_ERR_WORKSPACE
+
+
+def test_probe_library_stays_outside_the_attention_library(lib):
+    # the bench's matrix-rate probe lives in libgqa_probe.so; libgqa.so does not carry it
+    from grouped_query_attention_gqa_amd import build as gbuild
+    assert not hasattr(lib, "gqa_probe_mfma_rate")
+    if not os.path.exists(gbuild.PROBE_LIB):
+        pytest.skip("libgqa_probe.so not built")
+    probe = ctypes.CDLL(gbuild.PROBE_LIB)
+    for name in ("gqa_probe_mfma_rate", "gqa_probe_mfma_count"):
+        assert hasattr(probe, name), name
