@@ -243,6 +243,21 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
     // Transposing reads: lane (group lg, index nr) addresses V row 4 lg + nr / 4,
     // columns 16 db + 4 (nr % 4) .. +3
     const int tr_row = 4 * lg + (nr >> 2);
+    // Byte offsets of this lane's piece in the loads of a tile whose rows are
+    // all visible (the common case): load i fills tile row 4 (i % 4) + lg
+    // (bf16) or 8 (i % 2) + lane / 8 (FP8), K first, then V; the tile's first
+    // cache row is added as a wave-uniform base.
+    uint32_t lane_off[F8 ? 4 : DMA_PER_TILE];
+#pragma unroll
+    for (int i = 0; i < (F8 ? 4 : DMA_PER_TILE); ++i) {
+        if constexpr (!F8) {
+            const int r = 4 * (i % 4) + lg;
+            lane_off[i] = (uint32_t)(r * RB + (nr ^ (i >= 4 ? vsw(r) : ksw(r))) * 16);
+        } else {
+            const int r = 8 * (i % 2) + lane / 8, slot = lane % 8;
+            lane_off[i] = (uint32_t)(r * CRB + (i >= 2 ? slot : slot ^ ksw8(r)) * 16);
+        }
+    }
 
     int at = tau0;
     while (at < tau1) {
@@ -265,6 +280,23 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
             const int key0 = tile_key0(k);
             const int64_t base = k < n_w ? cache_row_wave(cache, b, g, key0) : -1;   // 16 keys: one cache block
             const uint32_t dst = lds_w + (uint32_t)((k % NSTG) * STG);
+            // every row of the tile visible and none of them the newest token:
+            // a uniform base plus the lane offsets, no per-lane tests
+            const int full = __builtin_amdgcn_readfirstlane(
+                (int)(base >= 0 && key0 >= lo && key0 + TT <= n_vis && (unsigned)(new_key - key0) >= (unsigned)TT));
+            if (full) {
+                const char *kb = cache.k + base * CRB, *vb = cache.v + base * CRB;
+#pragma unroll
+                for (int i = 0; i < (F8 ? 4 : DMA_PER_TILE); ++i)
+                    dma16((i >= (F8 ? 2 : 4) ? vb : kb) + lane_off[i], dst + (uint32_t)(i * 1024));
+                if constexpr (F8) {
+                    // the 16 K scales (lanes 0-15) and the 16 V scales (lanes 16-31)
+                    if (lane < 32)
+                        dma4(reinterpret_cast<const char *>((lane >= 16 ? cache.v_scale : cache.k_scale) + base + lane % 16),
+                             dst + (uint32_t)(2 * Stage<F8>::KV));
+                }
+                return;
+            }
             if constexpr (!F8) {
 #pragma unroll
                 for (int i = 0; i < DMA_PER_TILE; ++i) {
@@ -334,6 +366,11 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                 qf[rb][ks] = ok ? *reinterpret_cast<const uint4 *>(qrow + ks * 64 + lg * 16) : make_uint4(0, 0, 0, 0);
         }
 
+        // keys [rlo_max, lim_min) are visible to every row of the item: the
+        // oldest position's limit and the newest position's window start
+        const int lim_min = (int)min(max((int64_t)ctx_b - mq + 1, (int64_t)0), (int64_t)n_vis);
+        const int rlo_max = p.window > 0 ? (int)max((int64_t)0, (int64_t)ctx_b - p.window) : 0;
+
         wait_vm<0>();
         auto step = [&](int k) {
             const int key0 = tile_key0(k);
@@ -381,19 +418,30 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) s[rb] = mfma_s(kf[ks], qf[rb][ks], s[rb]);
             }
-            // mask, tile maximum, lazy rescale
+            // mask (only where the tile reaches past some row's visible keys),
+            // tile maximum, lazy rescale
+            if constexpr (F8) {
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[rb][e] *= ksc[e];   // the key's K scale
+            }
+            if (key0 < rlo_max || key0 + TT > lim_min) {
+#pragma unroll
+                for (int rb = 0; rb < RBW; ++rb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int key = key0 + 4 * lg + e;
+                        if (key >= lim[rb] || key < rlo[rb]) s[rb][e] = -INFINITY;
+                    }
+            }
             bool need = false;
             float mt[RBW];
 #pragma unroll
             for (int rb = 0; rb < RBW; ++rb) {
                 float m = -INFINITY;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int key = key0 + 4 * lg + e;
-                    if constexpr (F8) s[rb][e] *= ksc[e];   // the key's K scale
-                    if (key >= lim[rb] || key < rlo[rb]) s[rb][e] = -INFINITY;
-                    m = fmaxf(m, s[rb][e]);
-                }
+                for (int e = 0; e < 4; ++e) m = fmaxf(m, s[rb][e]);
                 mt[rb] = row_max(m) * p.scale_log2;   // scale > 0: the max commutes with it
                 need |= mt[rb] > m_ref[rb] + TAU;
             }
