@@ -28,6 +28,8 @@
 //    V product runs on the codes (the decode kernel's rule).
 //  * Online softmax in exp2 units with the lazy maximum (threshold 2^8), the
 //    causal / window mask on the tiles that need it.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -226,20 +228,30 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillParams p)
     };
     // Conversion of tile t's codes (stage t % NS) into converted tile t & 1:
     // thread i converts the 16 codes of chunk i % 8 of row i / 8, for K and V;
-    // threads 0-63 copy a K scale, 64-127 a V scale.
-    auto convert = [&](int t) __attribute__((always_inline)) {
-        const char *st = smem + (t % NS) * STAGE;
-        char *ct = smem + NS * STAGE + (t & 1) * CTILE;
-        const int r = tid / 8, c = tid % 8;
-        const uint4 xk = *reinterpret_cast<const uint4 *>(st + r * CB + c * 16);
-        const uint4 xv = *reinterpret_cast<const uint4 *>(st + ST_CODES + r * CB + c * 16);
+    // threads 0-63 copy a K scale, 64-127 a V scale.  Split into the reads and
+    // the conversion with its stores, K and V apart, so that both can sit
+    // beside matrix work.
+    const int cv_r = tid / 8, cv_c = tid % 8;
+    auto conv_read = [&](int t, bool v) __attribute__((always_inline)) {
+        return *reinterpret_cast<const uint4 *>(smem + (t % NS) * STAGE + (v ? ST_CODES : 0) + cv_r * CB + cv_c * 16);
+    };
+    auto scale_read = [&](int t) __attribute__((always_inline)) {
+        return tid < 2 * BN ? *reinterpret_cast<const float *>(smem + (t % NS) * STAGE + ST_KSC + tid * 4) : 0.f;
+    };
+    auto conv_write = [&](int t, bool v, uint4 x) __attribute__((always_inline)) {
         // 16 codes = bf16 chunks 2c and 2c + 1 of the row
-        *reinterpret_cast<uint4 *>(ct + r * RB + (((2 * c) ^ ksw(r)) * 16)) = f8x8_bf16x8(xk.x, xk.y);
-        *reinterpret_cast<uint4 *>(ct + r * RB + (((2 * c + 1) ^ ksw(r)) * 16)) = f8x8_bf16x8(xk.z, xk.w);
-        *reinterpret_cast<uint4 *>(ct + CT_V + r * RB + (((2 * c) ^ vsw(r)) * 16)) = f8x8_bf16x8(xv.x, xv.y);
-        *reinterpret_cast<uint4 *>(ct + CT_V + r * RB + (((2 * c + 1) ^ vsw(r)) * 16)) = f8x8_bf16x8(xv.z, xv.w);
-        if (tid < 2 * BN)
-            *reinterpret_cast<float *>(ct + CT_KSC + tid * 4) = *reinterpret_cast<const float *>(st + ST_KSC + tid * 4);
+        char *ct = smem + NS * STAGE + (t & 1) * CTILE + (v ? CT_V : 0) + cv_r * RB;
+        const int sw = v ? vsw(cv_r) : ksw(cv_r);
+        *reinterpret_cast<uint4 *>(ct + (((2 * cv_c) ^ sw) * 16)) = f8x8_bf16x8(x.x, x.y);
+        *reinterpret_cast<uint4 *>(ct + (((2 * cv_c + 1) ^ sw) * 16)) = f8x8_bf16x8(x.z, x.w);
+    };
+    auto scale_write = [&](int t, float x) __attribute__((always_inline)) {
+        if (tid < 2 * BN) *reinterpret_cast<float *>(smem + NS * STAGE + (t & 1) * CTILE + CT_KSC + tid * 4) = x;
+    };
+    auto convert = [&](int t) __attribute__((always_inline)) {
+        conv_write(t, false, conv_read(t, false));
+        conv_write(t, true, conv_read(t, true));
+        scale_write(t, scale_read(t));
     };
 
     // ---- softmax state and accumulators ------------------------------------------
@@ -251,49 +263,49 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillParams p)
         for (int i = 0; i < 16; ++i) acc[db][i] = 0.f;
 
     const int tr_g = lane >> 4, tr_j = lane & 15;
-    // tile t, from converted tile t & 1: scores, K scales, mask, softmax, the V product
-    auto math = [&](int t) __attribute__((always_inline)) {
-        const char *ct = smem + NS * STAGE + (t & 1) * CTILE;
-        f32x16_t s[2];
+    // fragments from converted tile ct: K (key block kb, k-step ks) and V^T
+    // (key block kb, 16-key step half, 32-column block db)
+    auto k_frag = [&](const char *ct, int kb, int ks) __attribute__((always_inline)) {
+        const int key = kb * 32 + nq;
+        return *reinterpret_cast<const uint4 *>(ct + key * RB + (((2 * ks + hh) ^ ksw(key)) * 16));
+    };
+    auto v_frag = [&](const char *ct, int kb, int half, int db) __attribute__((always_inline)) {
+        uint2 part[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) s[kb][i] = 0.f;
-#pragma unroll
-        for (int st = 0; st < 2 * KS; ++st) {
-            const int ks = st / 2, kb = st % 2;
-            const int key = kb * 32 + nq;
-            const uint4 kf = *reinterpret_cast<const uint4 *>(ct + key * RB + (((2 * ks + hh) ^ ksw(key)) * 16));
-            s[kb] = mfma32(kf, qf[ks], s[kb]);
+        for (int rd = 0; rd < 2; ++rd) {
+            const int row = kb * 32 + half * 16 + 4 * (tr_g >> 1) + 8 * rd + (tr_j >> 2);
+            const int col = db * 32 + 16 * (tr_g & 1) + 4 * (tr_j & 3);
+            const int chunk = (col >> 3) ^ vsw(row);
+            part[rd] = lds_read_tr16(ct + CT_V + row * RB + chunk * 16 + (col & 7) * 2);
         }
-        // element i of s[kb] holds key kb * 32 + (i / 4) * 8 + 4 hh + i % 4 of
-        // this lane's row: four consecutive keys per group of four elements
-        auto scales4 = [&](int off, int kb, int gq) __attribute__((always_inline)) {
-            return *reinterpret_cast<const float4 *>(ct + off + (kb * 32 + gq * 8 + 4 * hh) * 4);
-        };
-        const bool masked = t >= t_mask || t < t_lo_end;
-        const int lim = p.causal ? min(qpos + 1, kv_len) : kv_len;
-        float m = -INFINITY;
+        return make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
+    };
+    // element i of a score block holds key kb * 32 + (i / 4) * 8 + 4 hh + i % 4
+    // of this lane's row: four consecutive keys per group of four elements
+    auto scales4 = [&](const char *ct, int off, int kb, int gq) __attribute__((always_inline)) {
+        return *reinterpret_cast<const float4 *>(ct + off + (kb * 32 + gq * 8 + 4 * hh) * 4);
+    };
+    // K scale, mask and running maximum of elements 4 gq .. 4 gq + 3 of s
+    auto scale_max4 = [&](const char *ct, int t, int kb, int gq, f32x16_t &s, auto masked, int lim, float &m)
+        __attribute__((always_inline)) {
+        const float4 k4 = scales4(ct, CT_KSC, kb, gq);
+        const float kq[4] = {k4.x, k4.y, k4.z, k4.w};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const float4 k4 = scales4(CT_KSC, kb, gq);
-                const float kq[4] = {k4.x, k4.y, k4.z, k4.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int i = 4 * gq + e;
-                    s[kb][i] *= kq[e];   // the key's K scale
-                    if (masked) {
-                        const int key = t * BN + kb * 32 + gq * 8 + hh * 4 + e;
-                        if (key >= lim || key < row_lo) s[kb][i] = -INFINITY;
-                    }
-                    m = fmaxf(m, s[kb][i]);
-                }
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * gq + e;
+            s[i] *= kq[e];   // the key's K scale
+            if constexpr (decltype(masked)::value) {
+                const int key = t * BN + kb * 32 + gq * 8 + hh * 4 + e;
+                if (key >= lim || key < row_lo) s[i] = -INFINITY;
             }
+            m = fmaxf(m, s[i]);
+        }
+    };
+    auto vote = [&](float m) __attribute__((always_inline)) {
         // (the maximum is of the K-scaled scores; scale > 0 commutes with it)
         const float mt = max_xor32(m) * p.scale_log2;
-        if (__ballot(mt > m_ref + TAU) != 0) {
+        if (__builtin_expect(__ballot(mt > m_ref + TAU) != 0, 0)) {
+            asm volatile("" ::: "memory");   // keep the rare rescale a branch
             if (mt > m_ref + TAU) {
                 const float alpha = fast_exp2(m_ref - mt);   // 0 on the first tile
                 m_ref = mt;
@@ -304,54 +316,118 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillParams p)
                     for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
             }
         }
+    };
+    // probabilities of pair j of k-step half (keys 8 half + 2 j, +1 of the
+    // block's elements): the bf16 values into the row sum, and times the keys'
+    // V scales as the V product's operand.  Every key of a loaded tile is
+    // either a cached row visible to the workgroup's first row (whose scale
+    // the cache's contract makes finite) or a row loaded as zeros, so a
+    // masked key's 0 probability times its scale stays 0.
+    auto prob_pair = [&](const char *ct, int kb, const f32x16_t &s, int half, int j, float mu, uint32_t (&w)[2][4],
+                         float &ps) __attribute__((always_inline)) {
+        const int e0 = half * 8 + 2 * j;
+        const float4 v4 = scales4(ct, CT_VSC, kb, e0 / 4);
+        const float vq0 = (e0 & 2) ? v4.z : v4.x, vq1 = (e0 & 2) ? v4.w : v4.y;
+        const float p0 = fast_exp2(fmaf(s[e0], p.scale_log2, -mu));
+        const float p1 = fast_exp2(fmaf(s[e0 + 1], p.scale_log2, -mu));
+        ps = dot2_bf16(pack_bf16x2(p0, p1), 0x3F803F80u, ps);   // + both rounded probabilities
+        w[half][j] = pack_bf16x2(p0 * vq0, p1 * vq1);
+    };
+    // V product of key block kb with the probabilities of its scores s,
+    // formed one k-step ahead; `side(st)` runs beside matrix step st
+    auto pv_block = [&](const char *ct, int kb, const f32x16_t &s, auto &&side) __attribute__((always_inline)) {
         const float mu = m_ref == -INFINITY ? 0.f : m_ref;
-        uint4 pb[2][2];
-        float ps = 0.f;
+        uint32_t w[2][4];
+        float ps0 = 0.f, ps1 = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int j = 0; j < 4; ++j) prob_pair(ct, kb, s, 0, j, mu, w, (j & 1) ? ps1 : ps0);
+        uint4 vf = v_frag(ct, kb, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                uint32_t w[4];
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const float4 v4 = scales4(CT_VSC, kb, 2 * half + jj);   // keys of elements 8 half + 4 jj ..
-                    const float vq[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-                    for (int j2 = 0; j2 < 2; ++j2) {
-                        const int j = 2 * jj + j2, e0 = half * 8 + 2 * j, e1 = e0 + 1;
-                        const float p0 = fast_exp2(fmaf(s[kb][e0], p.scale_log2, -mu));
-                        const float p1 = fast_exp2(fmaf(s[kb][e1], p.scale_log2, -mu));
-                        ps = dot2_bf16(pack_bf16x2(p0, p1), 0x3F803F80u, ps);   // + both rounded probabilities
-                        // the key's V scale rides on its probability (a masked key's
-                        // probability is 0 and its scale is not looked at)
-                        w[j] = pack_bf16x2(p0 > 0.f ? p0 * vq[2 * j2] : 0.f, p1 > 0.f ? p1 * vq[2 * j2 + 1] : 0.f);
-                    }
-                }
-                pb[kb][half] = make_uint4(w[0], w[1], w[2], w[3]);
-            }
-        l_run += ps;
-        // O^T += V^T P^T
-#pragma unroll
-        for (int st = 0; st < DB * 4; ++st) {
-            const int db = st % DB, kb = st / DB / 2, half = (st / DB) % 2;
-            uint2 part[2];
-#pragma unroll
-            for (int rd = 0; rd < 2; ++rd) {
-                const int row = kb * 32 + half * 16 + 4 * (tr_g >> 1) + 8 * rd + (tr_j >> 2);
-                const int col = db * 32 + 16 * (tr_g & 1) + 4 * (tr_j & 3);
-                const int chunk = (col >> 3) ^ vsw(row);
-                part[rd] = lds_read_tr16(ct + CT_V + row * RB + chunk * 16 + (col & 7) * 2);
-            }
-            acc[db] = mfma32(make_uint4(part[0].x, part[0].y, part[1].x, part[1].y), pb[kb][half], acc[db]);
+        for (int st = 0; st < 2 * DB; ++st) {
+            const int db = st % DB, half = st / DB;
+            const uint4 a = vf;
+            if (st + 1 < 2 * DB) vf = v_frag(ct, kb, (st + 1) / DB, (st + 1) % DB);
+            acc[db] = mfma32(a, make_uint4(w[half][0], w[half][1], w[half][2], w[half][3]), acc[db]);
+            if (half == 0) prob_pair(ct, kb, s, 1, db, mu, w, (db & 1) ? ps1 : ps0);
+            side(st);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        l_run += ps0 + ps1;
+    };
+    // Tile t from converted tile t & 1, in two 32-key halves so that one
+    // half's softmax runs beside the other's matrix work:
+    //   S0 = K0 Q^T (beside: the reads of tile t + 1's K codes, then their
+    //   conversion); S1 = K1 Q^T (beside: scale, mask and maximum of S0); the
+    //   V product of half 0 (beside: its probabilities, and scale, mask and
+    //   maximum of S1); the V product of half 1 (beside: its probabilities,
+    //   and tile t + 1's V codes and scales).  With `conv`, tile t + 1 is
+    //   converted into the other converted tile.  `masked` (the tile needs
+    //   the causal or window mask) is a compile-time flag, and so is `conv` on
+    //   the steady tiles, which run without branches.
+    auto math = [&](int t, auto masked, auto conv_c) __attribute__((always_inline)) {
+        const bool conv = conv_c;   // a constant where conv_c is std::true_type
+        const char *ct = smem + NS * STAGE + (t & 1) * CTILE;
+        const int lim = p.causal ? min(qpos + 1, kv_len) : kv_len;
+        f32x16_t s0, s1;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { s0[i] = 0.f; s1[i] = 0.f; }
+        uint4 ck = make_uint4(0u, 0u, 0u, 0u);
+        {
+            uint4 kf = k_frag(ct, 0, 0);
+            if (conv) ck = conv_read(t + 1, false);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint4 a = kf;
+                if (ks + 1 < KS) kf = k_frag(ct, 0, ks + 1);
+                s0 = mfma32(a, qf[ks], s0);
+                if (conv && ks == 2) conv_write(t + 1, false, ck);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        float m0 = -INFINITY;
+        {
+            uint4 kf = k_frag(ct, 1, 0);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const uint4 a = kf;
+                if (ks + 1 < KS) kf = k_frag(ct, 1, ks + 1);
+                s1 = mfma32(a, qf[ks], s1);
+                if (ks % 2 == 1) scale_max4(ct, t, 0, ks / 2, s0, masked, lim, m0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        vote(m0);
+        float m1 = -INFINITY;
+        pv_block(ct, 0, s0, [&](int st) __attribute__((always_inline)) {
+            if (st % 2 == 1) scale_max4(ct, t, 1, st / 2, s1, masked, lim, m1);
+        });
+        vote(m1);
+        uint4 cv = make_uint4(0u, 0u, 0u, 0u);
+        float sc = 0.f;
+        pv_block(ct, 1, s1, [&](int st) __attribute__((always_inline)) {
+            if (conv) {
+                if (st == 0) {
+                    cv = conv_read(t + 1, true);
+                    sc = scale_read(t + 1);
+                }
+                if (st == 3) {
+                    conv_write(t + 1, true, cv);
+                    scale_write(t + 1, sc);
+                }
+            }
+        });
     };
 
     // ---- the pipeline ---------------------------------------------------------------
     // Iteration t: tile t + 1's codes have landed (waited for), barrier (every
     // wave is past the math of tile t - 1, so converted tile (t + 1) & 1 is
     // free, and past the conversion of tile t, so stage t % NS is free), tile
-    // t + NS starts into stage t % NS, tile t + 1 is converted, tile t's math
-    // runs.  Every wave issues LOADS loads per tile (zeros past the last).
+    // t + NS starts into stage t % NS, tile t's math runs with the conversion
+    // of tile t + 1 beside it.  Every wave issues LOADS loads per tile (zeros
+    // past the last).
     if (ntiles > t_first) {
 #pragma unroll
         for (int k = 0; k < NS; ++k) issue(t_first + k);
@@ -361,13 +437,20 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillParams p)
         wait_vm<0>();
         barrier();
         convert(t_first);
-        for (int t = t_first; t < ntiles; ++t) {
+        auto step = [&](int t, auto masked, auto conv) __attribute__((always_inline)) {
             wait_vm<(NS - 2) * LOADS>();   // tile t + 1 has landed
             barrier();
             issue(t + NS);
-            if (t + 1 < ntiles) convert(t + 1);
-            math(t);
-        }
+            math(t, masked, conv);
+        };
+        // tiles below the window's lower edge, then the steady tiles (no mask,
+        // a next tile to convert), then the tiles at the causal diagonal or
+        // the end of the keys and the last tile
+        const int t_steady = min(t_mask, ntiles - 1);
+        int t = t_first;
+        for (; t < ntiles && t < t_lo_end; ++t) step(t, std::true_type{}, t + 1 < ntiles);
+        for (; t < t_steady; ++t) step(t, std::false_type{}, std::true_type{});
+        for (; t < ntiles; ++t) step(t, std::true_type{}, t + 1 < ntiles);
         wait_vm<0>();   // the loads past the last tile have landed before the LDS is released
     }
 
