@@ -859,8 +859,7 @@ def profile_only(args):
     from grouped_query_attention_gqa_amd import workloads as W
     if args.only in ("prefill", "chunked", "chunked_fp8"):
         name = "causal_prefill_4k" if args.only == "prefill" else "chunked_prefill_paged"
-        r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup, fp8=args.only == "chunked_fp8",
-                          probe=args.only == "prefill")
+        r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup, fp8=args.only == "chunked_fp8")
         print(json.dumps(r), flush=True)
         return
     if args.only in ("tiny_prefill", "tiny_decode"):
