@@ -123,3 +123,65 @@ def test_fp8_prefill_sweep(case):
     _check_fp8_prefill(f"fp8 prefill sweep {case}", B=case["B"], H=case["H"], K=case["K"], s=case["s"],
                        start=case["start"], paged=case["paged"], bs=case["bs"], causal=case["causal"],
                        window=case["window"], seed=case["seed"])
+
+
+# ---------------------------------------------------------------------------
+# the other kernels: bf16 at d = 64 (the vector decode kernels, the d = 64
+# matrix-core prefill) and fp32 at d = 64 and 128 (the row-streaming kernel)
+# ---------------------------------------------------------------------------
+
+def _other_cases(n, seed, kind):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        H, K = HEADS[rng.integers(0, len(HEADS))]
+        dtype, d = [("bf16", 64), ("f32", 64), ("f32", 128)][rng.integers(0, 3)]
+        paged = dtype == "bf16" and bool(rng.integers(0, 2))
+        c = dict(i=i, H=H, K=K, dtype=dtype, d=d, paged=paged, bs=int(rng.choice([16, 32, 64])),
+                 seed=int(rng.integers(1 << 30)))
+        if kind == "decode":
+            c.update(B=int(rng.integers(1, 5)), window=0 if rng.integers(0, 2) == 0 else int(rng.integers(1, 300)))
+            c["ctx"] = _draw_ctx(rng, c["B"], 600)
+        else:
+            c.update(B=int(rng.integers(1, 3)), s=int(rng.choice([1, 33, 64, int(rng.integers(2, 100))])),
+                     causal=bool(rng.integers(0, 4) != 0))
+            c["window"] = 0 if (not c["causal"] or rng.integers(0, 2) == 0) else int(rng.integers(1, 200))
+        cases.append(c)
+    return cases
+
+
+def _tol(dtype):
+    from gpu_common import F32_TOL
+    return BF16_TOL if dtype == "bf16" else F32_TOL
+
+
+@pytest.mark.parametrize("case", _other_cases(12, 99, "decode"),
+                         ids=lambda c: f"decode_{c['dtype']}_d{c['d']}_{c['i']}")
+def test_other_decode_sweep(case):
+    base = W.WORKLOADS["llama3_8b_decode"] if case["dtype"] == "bf16" else W.WORKLOADS["tiny_decode_f32"]
+    wl = base.replace(B=case["B"], H=case["H"], K=case["K"], d=case["d"], seed=case["seed"],
+                      ctx=("uniform", 1, 600), paged=case["paged"], block_size=case["bs"])
+    inp = W.make_decode(wl, ctx_override=case["ctx"])
+    what = f"decode sweep {case}"
+    say(what)
+    out = from_dev(DecodeRun(inp).run(window=case["window"]))
+    rows, want = oracle_decode_rows(inp, window=case["window"])
+    check_close(gpu_rows(out, rows, case["dtype"]), want, _tol(case["dtype"]), what)
+
+
+@pytest.mark.parametrize("case", _other_cases(10, 1234, "prefill"), ids=lambda c: f"prefill_{c['dtype']}_d{c['d']}_{c['i']}")
+def test_other_prefill_sweep(case):
+    base = W.WORKLOADS["causal_prefill_4k"] if case["dtype"] == "bf16" else W.WORKLOADS["tiny_prefill_f32"]
+    wl = base.replace(B=case["B"], s=case["s"], H=case["H"], K=case["K"], d=case["d"], seed=case["seed"],
+                      block_size=case["bs"])
+    inp = W.make_prefill(wl)
+    rng = np.random.default_rng(case["seed"])
+    paged_blocks = W.deal_blocks(rng, inp.start_pos + wl.s, wl.block_size, slack_blocks=2) if case["paged"] else None
+    what = f"prefill sweep {case}"
+    say(what)
+    run = PrefillRun(inp, paged_blocks=paged_blocks)
+    out = from_dev(run.run(causal=case["causal"], window=case["window"]))
+    run.check_cache(what)
+    rows = np.array([[b, i, h] for b in range(wl.B) for i in range(wl.s) for h in range(wl.H)], np.int32)
+    want = oracle_prefill_rows(inp, rows, causal=case["causal"], window=case["window"])
+    check_close(gpu_rows(out, rows, case["dtype"]), want, _tol(case["dtype"]), what)
