@@ -37,9 +37,19 @@ COMMON_FLAGS = [
 ]
 
 
+# Per-file additions.  decode_mfma.hip: its 32- and 64-row kernels run one
+# wave per SIMD, where the compiler would otherwise put the matrix
+# accumulators in AGPRs and copy all of them into VGPRs on every tile (176
+# v_accvgpr moves per 16-key tile at 64 rows); the VGPR form keeps them where
+# the softmax and the final merge use them.
+FILE_FLAGS = {
+    "decode_mfma.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON_FLAGS + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON_FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
