@@ -241,11 +241,14 @@ def time_decode_only(db: DecodeBench, iters: int, warmup: int, call=None):
 # ---------------------------------------------------------------------------
 
 def kernel_source_hash(names=DECODE_SOURCES) -> str:
-    """Hash of the kernel sources the traffic counters were taken on."""
+    """Hash of the kernel sources the traffic counters were taken on, and of
+    the compiler flags they are built with."""
+    from grouped_query_attention_gqa_amd import build as gbuild
     h = hashlib.sha256()
     for name in names:
         with open(os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc", name), "rb") as f:
             h.update(f.read())
+        h.update(" ".join(gbuild.COMMON_FLAGS + gbuild.FILE_FLAGS.get(name, [])).encode())
     return h.hexdigest()[:16]
 
 

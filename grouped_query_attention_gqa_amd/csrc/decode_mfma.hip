@@ -576,14 +576,25 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 // The pieces of the items cut by slice boundaries: workgroup (g, row, z)
 // merges rows 4 z .. 4 z + 3 of item (sequence row0 + row, group g) with
 // their global max and sum (inference-optimisation page §10.2), one float4
-// of a row per thread; an item with no visible key gets zero rows.
+// of a row per thread; an item with no visible key gets zero rows.  With
+// PG > 1 the pieces are dealt to PG thread groups (piece k to group k % PG),
+// so that an item cut into many pieces loads them all in one memory round
+// trip; the groups' partial results are then combined in group order.
 constexpr int kMergeRows = 4;   // rows per workgroup (more workgroups for the many-piece items of large groups)
-__global__ __launch_bounds__(kMergeRows * (D / 4)) void merge_rows_kernel(RowAttnParams p, int W)
+template <int PG>
+__global__ __launch_bounds__(PG * kMergeRows * (D / 4)) void merge_rows_kernel(RowAttnParams p, int W)
 {
+    constexpr int TPG = kMergeRows * (D / 4);   // threads per piece group
+    __shared__ float4 lds_o[PG > 1 ? PG : 1][TPG];
+    __shared__ float2 lds_ml[PG > 1 ? PG : 1][TPG];
     const int g = blockIdx.x, row = blockIdx.y;
     const int G = p.G, H = p.H, mq = p.mq > 1 ? p.mq : 1;
     const int R = mq * G;
-    const int rho = blockIdx.z * kMergeRows + (int)threadIdx.x / (D / 4), col = ((int)threadIdx.x % (D / 4)) * 4;
+    // the piece group is uniform over a wave (TPG is two waves), so the slot
+    // arithmetic below stays scalar
+    const int pg = PG > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x / TPG) : 0;
+    const int t = (int)threadIdx.x % TPG;
+    const int rho = blockIdx.z * kMergeRows + t / (D / 4), col = (t % (D / 4)) * 4;
     const int64_t seq = p.row0 + row;
     // the table entries and the context length are read together (one
     // memory round trip instead of two)
@@ -593,30 +604,34 @@ __global__ __launch_bounds__(kMergeRows * (D / 4)) void merge_rows_kernel(RowAtt
     uint16_t *dst = reinterpret_cast<uint16_t *>(p.out) +
                     ((seq * mq + rho / G) * H + (int64_t)g * G + rho % G) * D + col;
     if (n_vis <= lo) {
-        if (rho < R) *reinterpret_cast<uint2 *>(dst) = make_uint2(0u, 0u);
+        if (rho < R && pg == 0) *reinterpret_cast<uint2 *>(dst) = make_uint2(0u, 0u);
         return;
     }
     const int64_t tiles = item_tiles(lo, n_vis, TT);
     const int64_t a = pre + (int64_t)g * tiles, e = a + tiles - 1;
     const int64_t wa = slice_owner(a, T, W), wb = slice_owner(e, T, W);
-    if (wa == wb) return;
+    if (wa == wb) return;   // one piece: the main kernel stored the rows
     // the workspace slots of the pieces: with at least one tile per slice
     // (T >= W) the pieces are the slices wa .. wb, the first one in slot 1
     // when the item starts inside it; otherwise every tile of the item is a
     // piece of its own, in slot 0 of its slice
     const bool dense = T >= W;
-    if (rho >= R) return;
+    if constexpr (PG == 1) {
+        if (rho >= R) return;
+    }
+    const bool live = PG == 1 || rho < R;   // with PG > 1 every thread reaches the barrier below
     const int ns = dense ? (int)(wb - wa + 1) : (int)(e - a + 1);
     const int slot0 = (int)(wa * 2 + (slice_start(wa, T, W) < a ? 1 : 0));
     auto slot_of = [&](int k) {
         return dense ? (k == 0 ? slot0 : (int)(wa + k) * 2) : (int)sparse_slot(a + k, T, W);
     };
-    // pieces in batches of 8 whose loads are issued together; within a batch
-    // and from batch to batch the running maximum rescales what is summed
+    // this group's pieces pg, pg + PG, ... in batches of 8 whose loads are
+    // issued together; within a batch and from batch to batch the running
+    // maximum rescales what is summed
     constexpr int BATCH = 8;
     float M = -INFINITY, L = 0.f;
     float4 O = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k0 = 0; k0 < ns; k0 += BATCH) {
+    for (int k0 = pg; k0 < ns; k0 += BATCH * PG) {
         float mm[BATCH], ll[BATCH];
         float4 oo[BATCH];
 #pragma unroll
@@ -624,8 +639,9 @@ __global__ __launch_bounds__(kMergeRows * (D / 4)) void merge_rows_kernel(RowAtt
             mm[j] = -INFINITY;
             ll[j] = 0.f;
             oo[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (k0 + j < ns) {
-                const int64_t sr = (int64_t)slot_of(k0 + j) * R + rho;
+            const int k = k0 + j * PG;
+            if (live && k < ns) {
+                const int64_t sr = (int64_t)slot_of(k) * R + rho;
                 mm[j] = p.ws_ml[sr * 2];
                 ll[j] = p.ws_ml[sr * 2 + 1];
                 oo[j] = *reinterpret_cast<const float4 *>(p.ws_o + sr * D + col);
@@ -650,6 +666,32 @@ __global__ __launch_bounds__(kMergeRows * (D / 4)) void merge_rows_kernel(RowAtt
         }
         M = Mn;
     }
+    if constexpr (PG > 1) {
+        // the groups' (max, sum, row) combined by group 0, in group order
+        lds_o[pg][t] = O;
+        lds_ml[pg][t] = make_float2(M, L);
+        __syncthreads();
+        if (pg != 0) return;
+        float Mx = M;
+#pragma unroll
+        for (int q = 1; q < PG; ++q) Mx = fmaxf(Mx, lds_ml[q][t].x);
+        float Ls = 0.f;
+        float4 Os = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (Mx != -INFINITY) {
+#pragma unroll
+            for (int q = 0; q < PG; ++q) {
+                const float2 ml = lds_ml[q][t];
+                if (ml.x == -INFINITY) continue;
+                const float wt = fast_exp2(ml.x - Mx);
+                const float4 o = lds_o[q][t];
+                Ls += ml.y * wt;
+                Os.x += o.x * wt; Os.y += o.y * wt; Os.z += o.z * wt; Os.w += o.w * wt;
+            }
+        }
+        L = Ls;
+        O = Os;
+    }
+    if (!live) return;
     const float inv = L > 0.f ? 1.f / L : 0.f;
     *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(O.x * inv, O.y * inv), pack_bf16x2(O.z * inv, O.w * inv));
 }
@@ -665,8 +707,11 @@ hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int R = (p.mq > 1 ? p.mq : 1) * p.G;
-    hipLaunchKernelGGL(merge_rows_kernel, dim3(p.cache.K, p.rows, (R + kMergeRows - 1) / kMergeRows), dim3(kMergeRows * (D / 4)), 0, s,
-                       p, p.num_wgs);
+    const dim3 mgrid(p.cache.K, p.rows, (R + kMergeRows - 1) / kMergeRows);
+    // items of 32 rows or more (large groups: few, long items) are cut into
+    // many pieces; their merge loads the pieces in four groups at once
+    if (R >= 32) hipLaunchKernelGGL(merge_rows_kernel<4>, mgrid, dim3(4 * kMergeRows * (D / 4)), 0, s, p, p.num_wgs);
+    else hipLaunchKernelGGL(merge_rows_kernel<1>, mgrid, dim3(kMergeRows * (D / 4)), 0, s, p, p.num_wgs);
     return hipGetLastError();
 }
 
