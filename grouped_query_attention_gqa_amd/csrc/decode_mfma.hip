@@ -173,15 +173,15 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
     __shared__ __attribute__((aligned(1024))) char lds_stage[NW][NSTG * STG];
     __shared__ __attribute__((aligned(16))) char lds_vbf[F8 ? NW : 1][F8 ? TT * RB : 16];   // FP8: the tile's V as bf16
     // the merge area of a segment's end reuses the stages (every load has
-    // landed and every wave is past its reads when it is written); rows are
-    // padded by 16 bytes so that the 16 rows a store instruction touches fall
-    // on different banks
-    constexpr int OS = D + 4;   // floats per merge-area row
+    // landed and every wave is past its reads when it is written); row r keeps
+    // its 16-byte chunk c in slot c ^ (r & 15), so that the 16 rows a store
+    // instruction touches fall on different banks without padding
+    constexpr int C4 = D / 4;   // 16-byte chunks per merge-area row
     // one region per wave where they fit (one round of writes), else two
     // regions that the other two waves add to
-    constexpr int NREG = 4 * RP * OS * 4 <= NW * NSTG * STG ? 4 : 2 * RP * OS * 4 <= NW * NSTG * STG ? 2 : 1;
-    static_assert(NREG * RP * OS * 4 <= NW * NSTG * STG, "merge area fits in the stages");
-    float (*lds_o)[RP][OS] = reinterpret_cast<float (*)[RP][OS]>(&lds_stage[0][0]);
+    constexpr int NREG = 4 * RP * D * 4 <= NW * NSTG * STG ? 4 : 2 * RP * D * 4 <= NW * NSTG * STG ? 2 : 1;
+    static_assert(NREG * RP * D * 4 <= NW * NSTG * STG, "merge area fits in the stages");
+    float4 (*lds_o)[RP][C4] = reinterpret_cast<float4 (*)[RP][C4]>(&lds_stage[0][0]);
     __shared__ float lds_row[RP][2];   // the merged (max, sum) of each row
     __shared__ float lds_ml[NW][RP][2];
     __shared__ int32_t lds_prefix[kStreamRows + 1];
@@ -516,7 +516,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                 for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
                     for (int db = 0; db < DB; ++db) {
-                        float4 *o = reinterpret_cast<float4 *>(&lds_o[wave % NREG][16 * rb + nr][16 * db + 4 * lg]);
+                        float4 *o = &lds_o[wave % NREG][16 * rb + nr][(4 * db + lg) ^ nr];
                         float4 x = make_float4(acc[rb][db][0] * wt[rb], acc[rb][db][1] * wt[rb], acc[rb][db][2] * wt[rb],
                                                acc[rb][db][3] * wt[rb]);
                         if (round > 0) {
@@ -548,10 +548,11 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
         for (int idx = tid; idx < R * (D / 4); idx += NT) {
             const int rho = idx / (D / 4), col = (idx % (D / 4)) * 4;
             const float M = lds_row[rho][0], L = lds_row[rho][1];
-            float4 O = *reinterpret_cast<const float4 *>(&lds_o[0][rho][col]);
+            const int c4 = (col >> 2) ^ (rho & 15);
+            float4 O = lds_o[0][rho][c4];
 #pragma unroll
             for (int r = 1; r < NREG; ++r) {
-                const float4 y = *reinterpret_cast<const float4 *>(&lds_o[r][rho][col]);
+                const float4 y = lds_o[r][rho][c4];
                 O.x += y.x; O.y += y.y; O.z += y.z; O.w += y.w;
             }
             if (whole) {
