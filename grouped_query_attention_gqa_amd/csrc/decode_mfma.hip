@@ -33,6 +33,12 @@
 //  * Online softmax per row in exp2 units (inference-optimisation page
 //    §9.2.1) with a lazy maximum that moves only by >= 2^8; the 4 lanes of a
 //    row combine through permlane swaps.
+//  * More than 32 rows per KV head (large groups, the multi-query end): the
+//    G heads form two items of G / 2 heads over the same K/V head, each
+//    streamed by the 32-row kernel.  Each tile is read twice, the second time
+//    mostly from the caches; with half the rows per wave the per-item costs
+//    (query fragments, the merge of the waves, the store) halve and each
+//    wave streams twice as many tiles.
 //  * At the end of a segment the 4 waves' (m, l, O) are merged in LDS in wave
 //    order (deterministic); a whole item is normalised and stored, a cut item
 //    leaves one partial per workgroup that merge_rows_kernel combines with
@@ -196,6 +202,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
     const int G = p.G, H = p.H, mq = p.mq > 1 ? p.mq : 1;
     const int R = mq * G;
     const int nr = lane & 15, lg = lane >> 4;   // row within a 16-row block; lane group
+    const int ls = p.kv_split > 1 ? __builtin_ctz((unsigned)p.kv_split) : 0;   // items per KV head: 2^ls
 
     // decode step: thread (item, K or V, 16-byte piece) loads its piece of a
     // new row now and stores it into the cache once the tables are built
@@ -264,6 +271,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
         const Cursor c = cursor_at(lds_prefix, lds_nvis, lds_first, p.rows, at, TT);
         const int64_t seq = p.row0 + c.row;
         const int b = (int)seq, g = c.g;
+        const int gc = g >> ls;   // the item's KV head
         const int n_vis = c.n_vis, lo = c.lo;
         const int new_key = with_new ? lds_newest[c.row] : -1;   // read from k_new / v_new
         const int end = min(tau1, c.item0 + c.tiles);
@@ -278,7 +286,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
         // [lo, n_vis), and tiles past the wave's last, read a zero constant
         auto issue = [&](int k) {
             const int key0 = tile_key0(k);
-            const int64_t base = k < n_w ? cache_row_wave(cache, b, g, key0) : -1;   // 16 keys: one cache block
+            const int64_t base = k < n_w ? cache_row_wave(cache, b, gc, key0) : -1;   // 16 keys: one cache block
             const uint32_t dst = lds_w + (uint32_t)((k % NSTG) * STG);
             // every row of the tile visible and none of them the newest token:
             // a uniform base plus the lane offsets, no per-lane tests
@@ -305,7 +313,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                     const int chunk = nr ^ (is_v ? vsw(r) : ksw(r));
                     const char *src = reinterpret_cast<const char *>(&kZero16M);
                     if (base >= 0 && key0 + r < n_vis && key0 + r >= lo)
-                        src = key0 + r == new_key ? (is_v ? p.v_new : p.k_new) + ((int64_t)b * cache.K + g) * RB + chunk * 16
+                        src = key0 + r == new_key ? (is_v ? p.v_new : p.k_new) + ((int64_t)b * cache.K + gc) * RB + chunk * 16
                                                   : (is_v ? cache.v : cache.k) + (base + r) * RB + chunk * 16;
                     dma16(src, dst + (uint32_t)(i * 1024));
                 }
@@ -708,7 +716,7 @@ hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int R = (p.mq > 1 ? p.mq : 1) * p.G;
-    const dim3 mgrid(p.cache.K, p.rows, (R + kMergeRows - 1) / kMergeRows);
+    const dim3 mgrid(p.cache.K * (p.kv_split > 1 ? p.kv_split : 1), p.rows, (R + kMergeRows - 1) / kMergeRows);
     // items of 32 rows or more (large groups: few, long items) are cut into
     // many pieces; their merge loads the pieces in four groups at once
     if (R >= 32) hipLaunchKernelGGL(merge_rows_kernel<4>, mgrid, dim3(4 * kMergeRows * (D / 4)), 0, s, p, p.num_wgs);
@@ -735,6 +743,16 @@ hipError_t launch_decode_mfma(const RowAttnParams &p, hipStream_t stream)
     const int R = (p.mq > 1 ? p.mq : 1) * p.G;
     if (R <= 16) return launch_m<1>(p, stream);
     if (R <= 32) return launch_m<2>(p, stream);
+    if (p.G % 2 == 0) {
+        // more than 32 rows per KV head (the multi-query end): two items of
+        // G / 2 heads each read the head's K/V (the second read mostly from
+        // the caches) in the 32-row kernel; measured faster than one 64-row
+        // item (and than four 16-row items, or two at two workgroups per CU)
+        RowAttnParams q = p;
+        q.kv_split = 2;
+        q.G = p.G / 2;
+        return launch_m<2>(q, stream);
+    }
     return launch_m<4>(p, stream);
 }
 

@@ -67,6 +67,7 @@ struct RowAttnParams {
     int32_t mq;                 // decode: query positions per sequence, the newest mq (0 or 1: one)
     int32_t num_wgs;            // W
     int32_t wgs_override;       // decode: > 0 fixes the workgroups of the launch (else the kernel's default)
+    int32_t kv_split;           // decode: each KV head's G heads form kv_split items of G / kv_split heads (0, 1: one item)
     float scale_log2;           // softmax scale * log2(e)
 };
 

@@ -69,6 +69,7 @@ __device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, in
     const int rows = p.rows;
     const int per = (rows + NT - 1) / NT;
     const int r0 = tid * per;
+    const int items = p.cache.K * (p.kv_split > 1 ? p.kv_split : 1);   // items per row
     int local = 0;
     for (int k = 0; k < per; ++k) {
         const int r = r0 + k;
@@ -98,11 +99,11 @@ __device__ void build_tables(const RowAttnParams &p, int tt, int32_t *prefix, in
     for (int k = 0; k < per; ++k) {
         const int r = r0 + k;
         if (r < rows) {
-            prefix[r] = run * p.cache.K;
+            prefix[r] = run * items;
             run += item_tiles(first[r], nvis[r], tt);
         }
     }
-    if (tid == NT - 1) prefix[rows] = (before + x) * p.cache.K;
+    if (tid == NT - 1) prefix[rows] = (before + x) * items;
     __syncthreads();
 }
 
