@@ -21,7 +21,8 @@ pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(),
 LLAMA70 = W.WORKLOADS["llama2_70b_decode"]
 
 
-@pytest.mark.parametrize("H,K", [(64, 4), (64, 2), (64, 1), (48, 3), (32, 1)])
+# G = 64 and 40 run as two items of G / 2 heads, G = 33 on the 64-row kernel
+@pytest.mark.parametrize("H,K", [(64, 4), (64, 2), (64, 1), (48, 3), (32, 1), (33, 1), (40, 1)])
 def test_large_group_decode(H, K):
     wl = LLAMA70.replace(B=5, H=H, K=K, ctx=("uniform", 1, 1500))
     inp = W.make_decode(wl)
@@ -50,13 +51,16 @@ def test_large_group_decode_paged():
     check_close(gpu_rows(out, rows, "bf16"), want, BF16_TOL, "paged G=64")
 
 
-def test_large_group_id_is_exact():
-    """V of KV head g is the constant g: every head h of group h // G returns g exactly."""
-    wl = LLAMA70.replace(B=3, H=64, K=4, ctx=("uniform", 20, 900))
+@pytest.mark.parametrize("H,K", [(64, 4), (64, 2), (64, 1), (66, 2)])
+def test_large_group_id_is_exact(H, K):
+    """V of KV head g is the constant g: every head h of group h // G returns g
+    exactly (G = 64 and 32 and 33: split into two items, the 32-row and the
+    64-row kernel)."""
+    wl = LLAMA70.replace(B=3, H=H, K=K, ctx=("uniform", 20, 900))
     inp = W.make_decode(wl)
     for g in range(wl.K):
         inp.v[:, g] = W.f32_to_bf16_bits(np.float32([g]))[0]
-    say("mfma decode group id")
+    say("mfma decode group id", f"H={H} K={K}")
     out = as_f64(from_dev(DecodeRun(inp).run()), "bf16")
     G = wl.H // wl.K
     for h in range(wl.H):
@@ -93,7 +97,7 @@ LLAMA3 = W.WORKLOADS["llama3_8b_decode"]
 
 
 @pytest.mark.parametrize("s,H,K", [(2, 32, 8), (4, 32, 8), (8, 32, 8), (8, 64, 8), (4, 64, 4), (3, 24, 8),
-                                   (2, 8, 8), (16, 32, 8)])
+                                   (2, 8, 8), (16, 32, 8), (16, 24, 8), (5, 40, 4)])
 def test_decode_multi_matches_causal_oracle(s, H, K):
     wl = LLAMA3.replace(B=5, H=H, K=K, ctx=("uniform", 16, 1200))
     _multi_case(wl, s, f"H={H} K={K}")
