@@ -30,11 +30,16 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p)
     I r = idx >> lcpr;
     const int which = r >= rows;                          // 0: K, 1: V
     if (which) r -= rows;
-    const I bt = r / (I)c.K;                              // b * s_new + t
-    const int g = (int)(r - bt * (I)c.K);
-    const I b_ = bt / (I)p.s_new;
-    const int t = (int)(bt - b_ * (I)p.s_new);
+    // rows in (sequence, KV head, position) order: the 64 lanes of a wave
+    // write 4 consecutive positions of one head (1 KB of the cache) and read
+    // them from 4 rows of k_new / v_new (measured 24.5 -> 23.3 us on a
+    // 4 x 4096-token prefill against (sequence, position, head) order)
+    const I bg = r / (I)p.s_new;                          // b * K + g
+    const int t = (int)(r - bg * (I)p.s_new);
+    const I b_ = bg / (I)c.K;
+    const int g = (int)(bg - b_ * (I)c.K);
     const int b = (int)b_;
+    const I bt = (I)b * (I)p.s_new + (I)t;                // b * s_new + t
 
     const int64_t pos = p.ctx_lens != nullptr ? (int64_t)p.ctx_lens[b] - 1 : (int64_t)p.start_pos[b] + t;
     if (pos < 0 || pos >= c.capacity) return;
