@@ -76,7 +76,9 @@ def _step_case(wl: W.Workload, what: str, window: int = 0, seqs=None):
 LLAMA3 = W.WORKLOADS["llama3_8b_decode"]
 
 
-@pytest.mark.parametrize("H,K", [(32, 8), (64, 8), (16, 16), (16, 8), (64, 64)])
+# G = 4, 8, 1, 2; G = 32 (the 32-row kernel), 64 (two items of 32 heads) and
+# 33 (the 64-row kernel)
+@pytest.mark.parametrize("H,K", [(32, 8), (64, 8), (16, 16), (16, 8), (64, 64), (32, 1), (64, 1), (66, 2)])
 def test_step_matches_append_then_decode_bf16(H, K):
     wl = LLAMA3.replace(B=6, H=H, K=K, ctx=("uniform", 1, 700))
     _step_case(wl, f"bf16 H={H} K={K}")
@@ -115,6 +117,11 @@ def test_step_with_window(window):
 def test_step_paged(block_size):
     wl = W.WORKLOADS["paged_long_decode"].replace(B=5, ctx=("loguniform", 20, 3000), block_size=block_size)
     _step_case(wl, f"paged bs={block_size}", seqs=[0, 2, 4])
+
+
+def test_step_paged_large_group():
+    wl = W.WORKLOADS["paged_long_decode"].replace(B=4, H=64, K=1, ctx=("loguniform", 20, 3000), block_size=16)
+    _step_case(wl, "paged G=64", seqs=[0, 1, 3])
 
 
 def test_step_fp32_appends_first():
