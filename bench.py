@@ -667,6 +667,13 @@ def main():
     }
     del db
     torch.cuda.empty_cache()
+    # context: what the device streams from HBM with nothing else running
+    sus = sustained_hbm_read()
+    if sus:
+        best = max(sus.values())
+        result["roofline"]["sustained_hbm_read_gbs"] = sus
+        result["roofline"]["frac_of_sustained"] = round(achieved / best, 4)
+        log(f"sustained HBM read: {best:.0f} GB/s; the step's kernels reach {100 * achieved / best:.1f}%")
 
     if not args.no_extra:
         # ---- causal prefill ------------------------------------------------
@@ -735,6 +742,53 @@ def main():
     result["pages_context"] = pages_context()
 
     print(json.dumps(result), flush=True)
+
+
+def sustained_hbm_read():
+    """The rate (GB/s) at which the device streams a 1 GiB buffer (four times
+    the Infinity Cache) into its compute units with nothing else running, from
+    the probe library beside libgqa.so: 16-byte loads, eight in flight per
+    thread, plain and non-temporal, with four and eight workgroups of 256
+    threads per CU; HIP events on the current stream.  Returns the rates by
+    configuration, or None when the probe library is missing."""
+    import ctypes
+    import torch
+    from grouped_query_attention_gqa_amd import build as gbuild
+    if not os.path.exists(gbuild.PROBE_LIB):
+        return None
+    lib = ctypes.CDLL(gbuild.PROBE_LIB)
+    lib.gqa_probe_stream_read.restype = ctypes.c_int
+    lib.gqa_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(cus * 8 * 256, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    reps, out = 20, {}
+    for nt in (0, 1):
+        for per_cu in (4, 8):
+            wgs = cus * per_cu
+            def call():
+                rc = lib.gqa_probe_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), sink.numel(), wgs, nt, stream)
+                if rc != 0:
+                    raise RuntimeError(f"gqa_probe_stream_read failed ({rc})")
+            t_end = time.perf_counter() + 0.2
+            while time.perf_counter() < t_end:
+                for _ in range(8):
+                    call()
+                torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                call()
+            b.record()
+            torch.cuda.synchronize()
+            label = ("nontemporal" if nt else "plain") + f"_{per_cu}_wg_per_cu"
+            out[label] = round(nbytes * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def sustained_mfma(operands):
