@@ -88,7 +88,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel: decode|step|fp8|multi|prefill|decode70b|paged|mha|mqa|window|chunked|chunked_fp8|"
+                    help="profile one kernel: decode|step|fp8|multi|prefill|decode70b|paged|mha|mqa|window|d64|chunked|chunked_fp8|"
                          "tiny_prefill|tiny_decode (both tiny fp32 workloads)|copy (a 512 MiB device copy)")
     ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
     ap.add_argument("--traffic", nargs=6, default=None,
@@ -682,7 +682,7 @@ def main():
         # ---- the other decode shapes --------------------------------------
         extra = {}
         for name in ("llama2_70b_decode", "paged_long_decode", "llama2_70b_decode_mha", "llama2_70b_decode_mqa",
-                     "mistral_7b_window_decode"):
+                     "mistral_7b_window_decode", "d64_decode"):
             w = W.WORKLOADS[name]
             d2 = DecodeBench(w)
             mean_ms, med_ms = time_decode_only(d2, max(LEG_CALLS, args.steps), 3)
@@ -934,7 +934,8 @@ def profile_only(args):
         return
     name = {"decode": "llama3_8b_decode", "step": "llama3_8b_decode", "decode70b": "llama2_70b_decode",
             "paged": "paged_long_decode", "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa",
-            "window": "mistral_7b_window_decode", "fp8": "llama3_8b_decode", "multi": "llama3_8b_decode"}[args.only]
+            "window": "mistral_7b_window_decode", "fp8": "llama3_8b_decode", "multi": "llama3_8b_decode",
+            "d64": "d64_decode"}[args.only]
     db = DecodeBench(W.WORKLOADS[name], fp8=args.only == "fp8", mq=4 if args.only == "multi" else 1)
     call = {"step": db.step, "multi": getattr(db, "multi", None)}.get(args.only)
     mean_ms, med_ms = time_decode_only(db, args.steps, args.warmup, call)

@@ -1,6 +1,7 @@
-// decode_mfma.hip -- bf16 decode on the matrix cores for many query rows per
-// KV head: large groups (up to G = 64, the multi-query end) and a block of
-// several newest query positions per sequence (speculative-verify shaped).
+// decode_mfma.hip -- decode on the matrix cores for bf16 caches at head size
+// 128 and 64 and FP8 caches at 128: every group size up to G = 64 (the
+// multi-query end) and a block of several newest query positions per
+// sequence (speculative-verify shaped).
 //
 // What it computes ("Grouped-Query Attention" concept page, 技术原理 steps
 // 2-4): for sequence b and KV group g, the R = mq * G rows -- query position i
@@ -68,17 +69,27 @@ typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int NT = 256;            // threads per workgroup; two workgroups per CU
 constexpr int NW = NT / kWave;     // waves
-constexpr int D = 128;             // head dim
-constexpr int RB = D * 2;          // bytes per K/V row
 constexpr int TT = 16;             // keys per tile
-constexpr int KS = D / 32;         // 32-dimension steps of S^T = K Q^T
-constexpr int DB = D / 16;         // 16-dimension blocks of O^T
 constexpr float TAU = 8.0f;        // lazy-rescale threshold (log2 units)
 constexpr int MAX_ROWS = 64;       // R = mq * G
-// LDS stages per wave: 2 with two workgroups per CU (up to 16 rows: the
-// registers allow it), 4 with one (more rows)
+// Head dimensions: 128 (bf16 and FP8 caches) and 64 (bf16).  A bf16 row of D
+// values is CPR 16-byte chunks, and one 1 KB LDS-direct load fills RPL rows.
+template <int D> struct Dim {
+    static constexpr int RB = D * 2;          // bytes per bf16 K/V row
+    static constexpr int KS = D / 32;         // 32-dimension steps of S^T = K Q^T
+    static constexpr int DB = D / 16;         // 16-dimension blocks of O^T
+    static constexpr int CPR = RB / 16;       // 16-byte chunks per row
+    static constexpr int RPL = 64 / CPR;      // rows per 1 KB load
+    static constexpr int LPT = TT / RPL;      // 1 KB loads per tile, for K and again for V
+};
+// LDS stages per wave: with two workgroups per CU (up to 16 rows: the
+// registers allow it) 2 at d = 128 and 4 at d = 64 (half the bytes per
+// stage); with one (more rows) twice that
 __host__ __device__ constexpr int occ_of(int rbw) { return rbw == 1 ? 2 : 1; }
-__host__ __device__ constexpr int nstg_of(int rbw, bool f8) { return f8 ? (occ_of(rbw) == 2 ? 3 : 6) : (occ_of(rbw) == 2 ? 2 : 4); }
+__host__ __device__ constexpr int nstg_of(int rbw, bool f8, int d)
+{
+    return f8 ? (occ_of(rbw) == 2 ? 3 : 6) : (occ_of(rbw) == 2 ? 2 : 4) * (d == 64 ? 2 : 1);
+}
 // FP8: K row r keeps its 16-byte chunk c (of 8) in slot c ^ (r & 7)
 __device__ __forceinline__ constexpr int ksw8(int r) { return r & 7; }
 // two E4M3 codes (bytes 0-1, or 2-3 with HI) -> a bf16 pair, exactly
@@ -92,7 +103,7 @@ __device__ __forceinline__ uint4 f8x8_bf16x8(uint2 x)
     return make_uint4(f8x2_bf16x2<false>(x.x), f8x2_bf16x2<true>(x.x), f8x2_bf16x2<false>(x.y), f8x2_bf16x2<true>(x.y));
 }
 // A stage: the tile's K rows, its V rows and (FP8) its 16 K and 16 V scales
-template <bool F8> struct Stage {
+template <bool F8, int D> struct Stage {
     static constexpr int ROWB = F8 ? D : D * 2;                 // bytes per cached row
     static constexpr int KV = TT * ROWB;                        // bytes of K (and of V) per tile
     static constexpr int BYTES = 2 * KV + (F8 ? 2 * TT * 4 : 0);
@@ -130,9 +141,12 @@ __device__ __forceinline__ void wait_vm()
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
-// K row r keeps its 16-byte chunk c in slot c ^ (r & 15): the 16 lanes of an
-// A-operand read (16 keys, one chunk) then hit 16 different slots
-__device__ __forceinline__ constexpr int ksw(int r) { return r & 15; }
+// K row r keeps its 16-byte chunk c in slot c ^ ksw(r): the 16 lanes of an
+// A-operand read (16 keys, one chunk) then fall on 16 different bank groups
+// (at d = 64 two rows share the 64 banks, so consecutive row pairs take
+// consecutive slots)
+template <int D>
+__device__ __forceinline__ constexpr int ksw(int r) { return Dim<D>::CPR >= 16 ? (r & 15) : ((r >> 1) & (Dim<D>::CPR - 1)); }
 
 __device__ __forceinline__ f32x4_t mfma_s(uint4 a, uint4 b, f32x4_t c)
 {
@@ -146,7 +160,8 @@ __device__ __forceinline__ f32x4_t mfma_o(uint2 a, uint2 b, f32x4_t c)
 }
 // V row r keeps its 16-byte chunk c in slot c ^ vsw(r): the transposing reads
 // (16 lanes, 4 rows x 4 pieces of 4 columns) then spread over the banks
-__device__ __forceinline__ constexpr int vsw(int r) { return 4 * (r & 3); }
+template <int D>
+__device__ __forceinline__ constexpr int vsw(int r) { return Dim<D>::CPR >= 16 ? 4 * (r & 3) : 2 * (r & 3); }
 __device__ __forceinline__ uint2 lds_read_tr16(const char *p)
 {
     const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t *)(lds_void_t *)p);
@@ -169,13 +184,16 @@ __device__ __forceinline__ float row_max(float x)
 }
 
 // RBW: 16-row blocks (R <= 16 * RBW); occ_of(RBW) workgroups per CU; F8: the
-// cache holds E4M3 codes and a scale per row
-template <int RBW, bool F8>
+// cache holds E4M3 codes and a scale per row (d = 128); D: the head dimension
+template <int RBW, bool F8, int D>
 __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnParams p)
 {
+    static_assert(!F8 || D == 128, "FP8 caches at d = 128");
+    constexpr int RB = Dim<D>::RB, KS = Dim<D>::KS, DB = Dim<D>::DB;
+    constexpr int CPR = Dim<D>::CPR, RPL = Dim<D>::RPL, LPT = Dim<D>::LPT;
     constexpr int RP = 16 * RBW;
-    constexpr int NSTG = nstg_of(RBW, F8);
-    constexpr int STG = Stage<F8>::BYTES, DMA_PER_TILE = Stage<F8>::DMA, CRB = Stage<F8>::ROWB;
+    constexpr int NSTG = nstg_of(RBW, F8, D);
+    constexpr int STG = Stage<F8, D>::BYTES, DMA_PER_TILE = Stage<F8, D>::DMA, CRB = Stage<F8, D>::ROWB;
     __shared__ __attribute__((aligned(1024))) char lds_stage[NW][NSTG * STG];
     __shared__ __attribute__((aligned(16))) char lds_vbf[F8 ? NW : 1][F8 ? TT * RB : 16];   // FP8: the tile's V as bf16
     // the merge area of a segment's end reuses the stages (every load has
@@ -258,8 +276,8 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 #pragma unroll
     for (int i = 0; i < (F8 ? 4 : DMA_PER_TILE); ++i) {
         if constexpr (!F8) {
-            const int r = 4 * (i % 4) + lg;
-            lane_off[i] = (uint32_t)(r * RB + (nr ^ (i >= 4 ? vsw(r) : ksw(r))) * 16);
+            const int r = RPL * (i % LPT) + lane / CPR, slot = lane % CPR;
+            lane_off[i] = (uint32_t)(r * RB + (slot ^ (i >= LPT ? vsw<D>(r) : ksw<D>(r))) * 16);
         } else {
             const int r = 8 * (i % 2) + lane / 8, slot = lane % 8;
             lane_off[i] = (uint32_t)(r * CRB + (i >= 2 ? slot : slot ^ ksw8(r)) * 16);
@@ -296,21 +314,21 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                 const char *kb = cache.k + base * CRB, *vb = cache.v + base * CRB;
 #pragma unroll
                 for (int i = 0; i < (F8 ? 4 : DMA_PER_TILE); ++i)
-                    dma16((i >= (F8 ? 2 : 4) ? vb : kb) + lane_off[i], dst + (uint32_t)(i * 1024));
+                    dma16((i >= (F8 ? 2 : LPT) ? vb : kb) + lane_off[i], dst + (uint32_t)(i * 1024));
                 if constexpr (F8) {
                     // the 16 K scales (lanes 0-15) and the 16 V scales (lanes 16-31)
                     if (lane < 32)
                         dma4(reinterpret_cast<const char *>((lane >= 16 ? cache.v_scale : cache.k_scale) + base + lane % 16),
-                             dst + (uint32_t)(2 * Stage<F8>::KV));
+                             dst + (uint32_t)(2 * Stage<F8, D>::KV));
                 }
                 return;
             }
             if constexpr (!F8) {
 #pragma unroll
                 for (int i = 0; i < DMA_PER_TILE; ++i) {
-                    const bool is_v = i >= 4;
-                    const int r = 4 * (i % 4) + lg;
-                    const int chunk = nr ^ (is_v ? vsw(r) : ksw(r));
+                    const bool is_v = i >= LPT;
+                    const int r = RPL * (i % LPT) + lane / CPR;
+                    const int chunk = (lane % CPR) ^ (is_v ? vsw<D>(r) : ksw<D>(r));
                     const char *src = reinterpret_cast<const char *>(&kZero16M);
                     if (base >= 0 && key0 + r < n_vis && key0 + r >= lo)
                         src = key0 + r == new_key ? (is_v ? p.v_new : p.k_new) + ((int64_t)b * cache.K + gc) * RB + chunk * 16
@@ -337,7 +355,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                     const char *src = reinterpret_cast<const char *>(&kZero16M);
                     if (base >= 0 && key0 + r < n_vis && key0 + r >= lo)
                         src = reinterpret_cast<const char *>((lane >= 16 ? cache.v_scale : cache.k_scale) + base + r);
-                    dma4(src, dst + (uint32_t)(2 * Stage<F8>::KV));
+                    dma4(src, dst + (uint32_t)(2 * Stage<F8, D>::KV));
                 }
             }
         };
@@ -386,13 +404,13 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
             issue(k + NSTG - 1);
             wait_vm<(NSTG - 1) * DMA_PER_TILE>();   // tile k has landed
             const char *kt = sw + (k % NSTG) * STG;
-            const char *vt = F8 ? lds_vbf[F8 ? wave : 0] : kt + Stage<F8>::KV;
+            const char *vt = F8 ? lds_vbf[F8 ? wave : 0] : kt + Stage<F8, D>::KV;
             uint4 kf[KS];
             float ksc[4] = {1.f, 1.f, 1.f, 1.f}, vsc[4] = {1.f, 1.f, 1.f, 1.f};
             if constexpr (!F8) {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    kf[ks] = *reinterpret_cast<const uint4 *>(kt + nr * RB + (((4 * ks + lg) ^ ksw(nr)) * 16));
+                    kf[ks] = *reinterpret_cast<const uint4 *>(kt + nr * RB + (((4 * ks + lg) ^ ksw<D>(nr)) * 16));
             } else {
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
@@ -401,21 +419,21 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                                                                           (lg & 1) * 8));
                 }
                 // scales of this lane's keys 4 lg .. 4 lg + 3
-                const float4 k4 = *reinterpret_cast<const float4 *>(kt + 2 * Stage<F8>::KV + 16 * lg);
-                const float4 v4 = *reinterpret_cast<const float4 *>(kt + 2 * Stage<F8>::KV + 64 + 16 * lg);
+                const float4 k4 = *reinterpret_cast<const float4 *>(kt + 2 * Stage<F8, D>::KV + 16 * lg);
+                const float4 v4 = *reinterpret_cast<const float4 *>(kt + 2 * Stage<F8, D>::KV + 64 + 16 * lg);
                 ksc[0] = k4.x; ksc[1] = k4.y; ksc[2] = k4.z; ksc[3] = k4.w;
                 vsc[0] = v4.x; vsc[1] = v4.y; vsc[2] = v4.z; vsc[3] = v4.w;
                 // the V tile as bf16 (swizzled as a bf16 tile): lane i converts
                 // the 32 bytes of row i / 4 at columns 32 (i % 4) ..
-                const char *vsrc = kt + Stage<F8>::KV + lane * 32;
+                const char *vsrc = kt + Stage<F8, D>::KV + lane * 32;
                 char *vdst = lds_vbf[F8 ? wave : 0];
                 const int vr = lane >> 2;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const uint4 x = *reinterpret_cast<const uint4 *>(vsrc + 16 * h);
                     const int c0 = 4 * (lane & 3) + 2 * h;   // logical bf16 chunk of the first 8 columns
-                    *reinterpret_cast<uint4 *>(vdst + vr * RB + ((c0 ^ vsw(vr)) * 16)) = f8x8_bf16x8(make_uint2(x.x, x.y));
-                    *reinterpret_cast<uint4 *>(vdst + vr * RB + (((c0 + 1) ^ vsw(vr)) * 16)) = f8x8_bf16x8(make_uint2(x.z, x.w));
+                    *reinterpret_cast<uint4 *>(vdst + vr * RB + ((c0 ^ vsw<D>(vr)) * 16)) = f8x8_bf16x8(make_uint2(x.x, x.y));
+                    *reinterpret_cast<uint4 *>(vdst + vr * RB + (((c0 + 1) ^ vsw<D>(vr)) * 16)) = f8x8_bf16x8(make_uint2(x.z, x.w));
                 }
             }
             // S^T = K Q^T: lane holds keys key0 + 4 lg + e of row 16 rb + nr
@@ -489,7 +507,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 const int col = 16 * db + 4 * (nr & 3);
-                const int chunk = (col >> 3) ^ vsw(tr_row);
+                const int chunk = (col >> 3) ^ vsw<D>(tr_row);
                 const uint2 vf = lds_read_tr16(vt + tr_row * RB + chunk * 16 + (col & 7) * 2);
 #pragma unroll
                 for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = mfma_o(vf, pw[rb], acc[rb][db]);
@@ -590,7 +608,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 // so that an item cut into many pieces loads them all in one memory round
 // trip; the groups' partial results are then combined in group order.
 constexpr int kMergeRows = 4;   // rows per workgroup (more workgroups for the many-piece items of large groups)
-template <int PG>
+template <int PG, int D>
 __global__ __launch_bounds__(PG * kMergeRows * (D / 4)) void merge_rows_kernel(RowAttnParams p, int W)
 {
     constexpr int TPG = kMergeRows * (D / 4);   // threads per piece group
@@ -705,22 +723,26 @@ __global__ __launch_bounds__(PG * kMergeRows * (D / 4)) void merge_rows_kernel(R
     *reinterpret_cast<uint2 *>(dst) = make_uint2(pack_bf16x2(O.x * inv, O.y * inv), pack_bf16x2(O.z * inv, O.w * inv));
 }
 
-template <int RBW>
+template <int RBW, int D>
 hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
 {
     RowAttnParams p = p0;
     // slices resident at once: occ_of(RBW) per CU, unless the caller fixed the count
     p.num_wgs = p0.wgs_override > 0 ? p0.wgs_override : p0.num_wgs * occ_of(RBW) / 2;
-    if (p.cache.elem_bytes == 1) hipLaunchKernelGGL((decode_mfma_kernel<RBW, true>), dim3(p.num_wgs), dim3(NT), 0, s, p);
-    else hipLaunchKernelGGL((decode_mfma_kernel<RBW, false>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+    if (p.cache.elem_bytes == 1) {
+        if constexpr (D == 128) hipLaunchKernelGGL((decode_mfma_kernel<RBW, true, D>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+        else return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((decode_mfma_kernel<RBW, false, D>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int R = (p.mq > 1 ? p.mq : 1) * p.G;
     const dim3 mgrid(p.cache.K * (p.kv_split > 1 ? p.kv_split : 1), p.rows, (R + kMergeRows - 1) / kMergeRows);
     // items of 32 rows or more (large groups: few, long items) are cut into
     // many pieces; their merge loads the pieces in four groups at once
-    if (R >= 32) hipLaunchKernelGGL(merge_rows_kernel<4>, mgrid, dim3(4 * kMergeRows * (D / 4)), 0, s, p, p.num_wgs);
-    else hipLaunchKernelGGL(merge_rows_kernel<1>, mgrid, dim3(kMergeRows * (D / 4)), 0, s, p, p.num_wgs);
+    if (R >= 32) hipLaunchKernelGGL((merge_rows_kernel<4, D>), mgrid, dim3(4 * kMergeRows * (D / 4)), 0, s, p, p.num_wgs);
+    else hipLaunchKernelGGL((merge_rows_kernel<1, D>), mgrid, dim3(kMergeRows * (D / 4)), 0, s, p, p.num_wgs);
     return hipGetLastError();
 }
 
@@ -730,19 +752,23 @@ bool decode_mfma_supported(const RowAttnParams &p)
 {
     const int mq = p.mq > 1 ? p.mq : 1;
     // paged caches need blocks of at least 16 tokens (a tile stays in one block)
-    // bf16, or FP8 E4M3 with row scales (whose new rows the quantising append writes)
+    // bf16 at d = 128 or 64, or FP8 E4M3 with row scales at d = 128 (whose new
+    // rows the quantising append writes)
     const bool f8 = p.cache.elem_bytes == 1;
-    return !p.prefill && !p.whole_items && (p.cache.elem_bytes == 2 || f8) && p.cache.d == D &&
+    return !p.prefill && !p.whole_items && (p.cache.elem_bytes == 2 || f8) &&
+           (p.cache.d == 128 || (p.cache.d == 64 && !f8)) &&
            (p.k_new == nullptr || (mq == 1 && !f8)) &&
            mq * p.G <= MAX_ROWS && p.num_wgs <= kStreamWGs && (p.cache.block_table == nullptr || p.cache.log2_bs >= 4);
 }
 
-hipError_t launch_decode_mfma(const RowAttnParams &p, hipStream_t stream)
+namespace {
+
+template <int D>
+hipError_t launch_decode_mfma_d(const RowAttnParams &p, hipStream_t stream)
 {
-    if (!decode_mfma_supported(p)) return hipErrorInvalidValue;
     const int R = (p.mq > 1 ? p.mq : 1) * p.G;
-    if (R <= 16) return launch_m<1>(p, stream);
-    if (R <= 32) return launch_m<2>(p, stream);
+    if (R <= 16) return launch_m<1, D>(p, stream);
+    if (R <= 32) return launch_m<2, D>(p, stream);
     if (p.G % 2 == 0) {
         // more than 32 rows per KV head (the multi-query end): two items of
         // G / 2 heads each read the head's K/V (the second read mostly from
@@ -751,9 +777,17 @@ hipError_t launch_decode_mfma(const RowAttnParams &p, hipStream_t stream)
         RowAttnParams q = p;
         q.kv_split = 2;
         q.G = p.G / 2;
-        return launch_m<2>(q, stream);
+        return launch_m<2, D>(q, stream);
     }
-    return launch_m<4>(p, stream);
+    return launch_m<4, D>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const RowAttnParams &p, hipStream_t stream)
+{
+    if (!decode_mfma_supported(p)) return hipErrorInvalidValue;
+    return p.cache.d == 64 ? launch_decode_mfma_d<64>(p, stream) : launch_decode_mfma_d<128>(p, stream);
 }
 
 }  // namespace gqa

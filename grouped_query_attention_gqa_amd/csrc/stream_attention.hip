@@ -686,9 +686,9 @@ hipError_t launch_row_attention(const RowAttnParams &p0, int gp, hipStream_t str
         p.row0 = r0;
         p.rows = (int32_t)(p0.total_rows - r0 < kStreamRows ? p0.total_rows - r0 : kStreamRows);
         hipError_t e = hipErrorInvalidValue;
-        // bf16 at d = 128: the matrix-core kernel, whatever the group size (it
-        // keeps more bytes in flight than the vector kernel); FP8 caches and
-        // d = 64: the vector kernels
+        // bf16 at d = 128 and 64 and FP8 at d = 128: the matrix-core kernel,
+        // whatever the group size; the rest (fp32, bf16 paged in blocks under
+        // 16 tokens, more than 64 rows per KV head): this file's kernel
         if (decode_mfma_supported(p)) e = launch_decode_mfma(p, stream);
         else if (p.mq > 1) return hipErrorInvalidValue;   // several positions: the matrix-core kernel only
         else if (decode_waves_supported(p, gp)) e = launch_decode_waves(p, gp, stream);

@@ -115,6 +115,12 @@ WORKLOADS = {
         ctx=("fixed", 16384), window=4096,
         description="Mistral-7B-shaped sliding-window decode, bf16, B=32 H=32 K=8 d=128, ctx = 16384, "
                     "window 4096"),
+    # the d = 64 head size (the vector-ALU decode kernel): the Llama-3-8B
+    # decode's batch and head counts with half the head dimension
+    "d64_decode": Workload(
+        "d64_decode", "decode", "bf16", B=32, H=32, K=8, d=64, seed=1008,
+        ctx=("uniform", 1024, 4096),
+        description="decode at head size 64, bf16, B=32 H=32 K=8 d=64, ctx ~ U[1024,4096]"),
     "chunked_prefill_paged": Workload(
         "chunked_prefill_paged", "prefill", "bf16", B=4, H=32, K=8, d=128, seed=1007, s=512, start=3584,
         value_scale=0.5, paged=True,
