@@ -323,9 +323,10 @@ gqa_status gqa::decode_step(const void *q, const void *k_new, const void *v_new,
         // k_new / v_new; every other path appends first
         p.k_new = static_cast<const char *>(k_new);
         p.v_new = static_cast<const char *>(v_new);
-        // the bf16 decode kernels write the new rows themselves; an FP8 cache
-        // is written by the quantising append kernel, and so are the rest
-        if (v.elem_bytes != 2 || !(decode_mfma_supported(p) || decode_waves_supported(p, pow2_at_least(p.G)))) {
+        // the matrix-core decode writes the new bf16 rows itself; an FP8
+        // cache is written by the quantising append kernel, and so are the
+        // rest
+        if (v.elem_bytes != 2 || !decode_mfma_supported(p)) {
             AppendParams ap{};
             ap.cache = v;
             ap.k_new = p.k_new;

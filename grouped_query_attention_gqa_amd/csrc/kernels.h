@@ -135,10 +135,8 @@ __device__ __forceinline__ int64_t cache_row_wave(const CacheView &c, int b, int
 
 hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream);
 hipError_t launch_row_attention(const RowAttnParams &p, int gp, hipStream_t stream);
-// bf16 decode for padded group sizes gp <= 8 (one launch of at most kStreamRows rows)
-bool decode_waves_supported(const RowAttnParams &p, int gp);
-hipError_t launch_decode_waves(const RowAttnParams &p, int gp, hipStream_t stream);
-// bf16 decode on the matrix cores: mq query positions x G heads per (sequence, KV head), up to 64 rows
+// decode on the matrix cores (bf16 at d = 128 and 64, FP8 at d = 128): mq query
+// positions x G heads per (sequence, KV head), up to 64 rows
 bool decode_mfma_supported(const RowAttnParams &p);
 hipError_t launch_decode_mfma(const RowAttnParams &p, hipStream_t stream);
 // merge of the partial pieces that W workgroup slices of tt-key tiles left in the workspace

@@ -691,7 +691,6 @@ hipError_t launch_row_attention(const RowAttnParams &p0, int gp, hipStream_t str
         // 16 tokens, more than 64 rows per KV head): this file's kernel
         if (decode_mfma_supported(p)) e = launch_decode_mfma(p, stream);
         else if (p.mq > 1) return hipErrorInvalidValue;   // several positions: the matrix-core kernel only
-        else if (decode_waves_supported(p, gp)) e = launch_decode_waves(p, gp, stream);
         else if (p.cache.elem_bytes == 1) return hipErrorInvalidValue;   // FP8: the decode kernel only
         else if (p.cache.d == 128) e = bf16 ? launch_d<128, true>(p, gp, stream) : launch_d<128, false>(p, gp, stream);
         else if (p.cache.d == 64) e = bf16 ? launch_d<64, true>(p, gp, stream) : launch_d<64, false>(p, gp, stream);

@@ -157,9 +157,12 @@ SPLIT_CASES = {
     "mfma_g64_paged": (W.WORKLOADS["paged_long_decode"].replace(B=3, H=64, K=1, ctx=("loguniform", 30, 4000)),
                        BF16_TOL),
     "mfma_g32": (W.WORKLOADS["llama3_8b_decode"].replace(B=3, H=64, K=2, ctx=("uniform", 1, 2000)), BF16_TOL),
-    "waves_d64": (W.WORKLOADS["llama3_8b_decode"].replace(B=4, d=64, ctx=("uniform", 1, 2000)), BF16_TOL),
-    "stream_d64_g16": (W.WORKLOADS["llama3_8b_decode"].replace(B=3, d=64, H=32, K=2, ctx=("uniform", 1, 1500)),
-                       BF16_TOL),
+    "mfma_d64": (W.WORKLOADS["llama3_8b_decode"].replace(B=4, d=64, ctx=("uniform", 1, 2000)), BF16_TOL),
+    "mfma_d64_g16": (W.WORKLOADS["llama3_8b_decode"].replace(B=3, d=64, H=32, K=2, ctx=("uniform", 1, 1500)),
+                     BF16_TOL),
+    # blocks of 4 tokens: the stream kernel's bf16 path
+    "stream_bf16_blocks4": (W.WORKLOADS["paged_long_decode"].replace(B=3, H=32, K=8, ctx=("loguniform", 30, 1500),
+                                                                     block_size=4), BF16_TOL),
     "stream_f32": (W.WORKLOADS["tiny_decode_f32"].replace(B=3, ctx=("uniform", 1, 700)), F32_TOL),
 }
 
