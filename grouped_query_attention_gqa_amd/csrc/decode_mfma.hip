@@ -82,11 +82,14 @@ template <int D> struct Dim {
     static constexpr int RPL = 64 / CPR;      // rows per 1 KB load
     static constexpr int LPT = TT / RPL;      // 1 KB loads per tile, for K and again for V
 };
-// LDS stages per wave: 2 with two workgroups per CU (up to 16 rows: the
-// registers allow it), 4 with one (more rows); at d = 64 too (4 stages there
-// measured 38.1 us against 37.1 us with 2 on the d = 64 leg)
+// Workgroups per CU: two up to 16 rows (the registers allow it), one above.
+// LDS stages per wave: two in every case.  More stages measured slower: 4
+// against 2 at one workgroup per CU (MQA 27.9 against 26.9 us), 3 against 2
+// for FP8 (43.9 against 42.0 us), 6 against 2 for FP8 at one workgroup per CU
+// (an FP8 MQA decode, 34.2 against 30.6 us), 4 against 2 at d = 64 (38.1
+// against 37.1 us).
+constexpr int NSTG = 2;
 __host__ __device__ constexpr int occ_of(int rbw) { return rbw == 1 ? 2 : 1; }
-__host__ __device__ constexpr int nstg_of(int rbw, bool f8) { return f8 ? (occ_of(rbw) == 2 ? 3 : 6) : (occ_of(rbw) == 2 ? 2 : 4); }
 // FP8: K row r keeps its 16-byte chunk c (of 8) in slot c ^ (r & 7)
 __device__ __forceinline__ constexpr int ksw8(int r) { return r & 7; }
 // two E4M3 codes (bytes 0-1, or 2-3 with HI) -> a bf16 pair, exactly
@@ -189,7 +192,6 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
     constexpr int RB = Dim<D>::RB, KS = Dim<D>::KS, DB = Dim<D>::DB;
     constexpr int CPR = Dim<D>::CPR, RPL = Dim<D>::RPL, LPT = Dim<D>::LPT;
     constexpr int RP = 16 * RBW;
-    constexpr int NSTG = nstg_of(RBW, F8);
     constexpr int STG = Stage<F8, D>::BYTES, DMA_PER_TILE = Stage<F8, D>::DMA, CRB = Stage<F8, D>::ROWB;
     __shared__ __attribute__((aligned(1024))) char lds_stage[NW][NSTG * STG];
     __shared__ __attribute__((aligned(16))) char lds_vbf[F8 ? NW : 1][F8 ? TT * RB : 16];   // FP8: the tile's V as bf16
