@@ -116,6 +116,41 @@ __device__ __forceinline__ int32_t scalar_load_i32(const int32_t *p)
     return v;
 }
 
+// Four consecutive wave-uniform 32-bit values through the scalar data cache
+// (s_load_dwordx4), one wait for all four.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t scalar_load_i32x4(const int32_t *p)
+{
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+    const uint64_t ua = ((uint64_t)hi << 32) | (uint64_t)lo;
+    i32x4_t v;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_load_dwordx4 %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ua) : "memory");
+#pragma clang diagnostic pop
+    return v;
+}
+
+// The blocks of the four 16-key groups of a 64-key tile (keys j0, j0 + 16,
+// j0 + 32 and j0 + 48, j0 a multiple of 64) of sequence b, with blocks of at
+// least 16 tokens: one scalar load of the table entries from column
+// j0 / block_size on.  Returns false (and sets nothing) when those four
+// entries would pass the end of the sequence's table row.
+__device__ __forceinline__ bool tile_block_ids(const CacheView &c, int b, int j0, int (&id)[4])
+{
+    const int col = __builtin_amdgcn_readfirstlane(j0) >> c.log2_bs;
+    if (col < 0 || col + 4 > c.max_blocks) return false;
+    const i32x4_t v = scalar_load_i32x4(c.block_table + (int64_t)b * c.max_blocks + col);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int e = ((j0 + 16 * q) >> c.log2_bs) - col;   // 0 .. 3
+        id[q] = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    }
+    return true;
+}
+
 // The same lookup for loads where all active lanes of a wave ask for
 // positions inside one 16-aligned group of 16 tokens.  With blocks of 16 or
 // more tokens that group lies in one block, so one wave-uniform scalar

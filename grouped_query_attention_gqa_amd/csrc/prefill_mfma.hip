@@ -36,6 +36,11 @@
 //    scores tile t while the other finishes tile t-1), so one wave's softmax
 //    overlaps the other's matrix work; the K and V^T fragments are read from
 //    LDS a few matrix instructions ahead of their use.
+//  * Paged caches (a block table, blocks of 16 or more tokens): a 64-key tile
+//    spans at most four blocks, whose ids come from one scalar load of four
+//    table entries per tile; each 1 KB load's rows lie in one of them, so its
+//    lanes take a wave-uniform base plus the same offsets as a contiguous
+//    tile.  A separate instantiation, so the contiguous kernel is unchanged.
 //  * Persistent workgroups, one per CU: the query blocks are taken heaviest
 //    first (largest causal key range) in rounds of one block per workgroup,
 //    the order reversed every other round so that each workgroup's blocks
@@ -131,7 +136,10 @@ struct PCfg {
     static_assert(NS * STAGE <= 160 * 1024, "LDS");
 };
 
-template <int D, int GP, int NT_>
+// PAGED: the cache goes through a block table (blocks of any size); else it
+// is contiguous.  Two instantiations, so that the contiguous kernel carries
+// none of the paged path's registers.
+template <int D, int GP, int NT_, bool PAGED>
 __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
 {
     using C = PCfg<D, GP, NT_>;
@@ -207,7 +215,7 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
             koff[k] = (uint32_t)(r * C::RB + (slot ^ C::ksw(r)) * 16);
             voff[k] = (uint32_t)(r * C::RB + (slot ^ C::vsw(r)) * 16);
         }
-        const bool contiguous = cache.block_table == nullptr;
+        const bool contiguous = !PAGED && cache.block_table == nullptr;
         const bool small_blocks = !contiguous && cache.log2_bs < 4;
         const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void_t *)smem;   // LDS address of the stages
         const char *kseq = cache.k + ((int64_t)b * cache.K + g) * cache.S_max * C::RB;
@@ -225,6 +233,34 @@ __global__ __launch_bounds__(NT_) void prefill_mfma_kernel(PrefillParams p)
                     src[2 * k + 1] = vseq + (int64_t)j0 * C::RB + voff[k];
                 }
                 return;
+            }
+            if constexpr (PAGED) {
+                // paged, blocks of 16 or more, every row of the tile visible: each
+                // load's rows lie in one 16-key group, whose block comes from one
+                // table read per tile; uniform bases and the same lane offsets
+                int id[4];
+                if (t < ntiles && !small_blocks && j0 >= kv_begin && j0 + BN <= kv_len &&
+                    tile_block_ids(cache, b, j0, id)) {
+                    bool ok = true;
+                    int64_t row[C::LPW];
+    #pragma unroll
+                    for (int k = 0; k < C::LPW; ++k) {
+                        const int r0 = (wave + NW * k) * C::RPK;   // the load's first tile row
+                        const int blk_id = id[r0 / 16];
+                        ok = ok && blk_id >= 0 && blk_id < cache.num_blocks;
+                        row[k] = (((int64_t)blk_id * cache.K + g) << cache.log2_bs) +
+                                 ((j0 + r0) & ((1 << cache.log2_bs) - 1));
+                    }
+                    if (ok) {
+    #pragma unroll
+                        for (int k = 0; k < C::LPW; ++k) {
+                            const uint32_t rel = (uint32_t)((wave + NW * k) * C::RPK * C::RB);
+                            src[2 * k] = cache.k + row[k] * C::RB + (koff[k] - rel);
+                            src[2 * k + 1] = cache.v + row[k] * C::RB + (voff[k] - rel);
+                        }
+                        return;
+                    }
+                }
             }
     #pragma unroll
             for (int k = 0; k < C::LPW; ++k) {
@@ -613,6 +649,16 @@ int compute_units()
     return cached[dev];
 }
 
+template <int D, int GP, int NT_>
+hipError_t launch_gp(const PrefillParams &p, dim3 grid, hipStream_t s)
+{
+    if (p.cache.block_table != nullptr)
+        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, NT_, true>), grid, dim3(NT_), 0, s, p);
+    else
+        hipLaunchKernelGGL((prefill_mfma_kernel<D, GP, NT_, false>), grid, dim3(NT_), 0, s, p);
+    return hipGetLastError();
+}
+
 template <int D, int NT_>
 hipError_t launch_d(const PrefillParams &p, int gp, hipStream_t s)
 {
@@ -622,16 +668,15 @@ hipError_t launch_d(const PrefillParams &p, int gp, hipStream_t s)
     // one persistent workgroup per compute unit (one fits, by its LDS)
     const dim3 grid((unsigned)std::min<int64_t>(nqb * p.cache.K * p.B, compute_units()));
     switch (gp) {
-    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<D, 1, NT_>), grid, dim3(NT_), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<D, 2, NT_>), grid, dim3(NT_), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<D, 4, NT_>), grid, dim3(NT_), 0, s, p); break;
-    case 8: hipLaunchKernelGGL((prefill_mfma_kernel<D, 8, NT_>), grid, dim3(NT_), 0, s, p); break;
-    case 16: hipLaunchKernelGGL((prefill_mfma_kernel<D, 16, NT_>), grid, dim3(NT_), 0, s, p); break;
-    case 32: hipLaunchKernelGGL((prefill_mfma_kernel<D, 32, NT_>), grid, dim3(NT_), 0, s, p); break;
-    case 64: hipLaunchKernelGGL((prefill_mfma_kernel<D, 64, NT_>), grid, dim3(NT_), 0, s, p); break;
+    case 1: return launch_gp<D, 1, NT_>(p, grid, s);
+    case 2: return launch_gp<D, 2, NT_>(p, grid, s);
+    case 4: return launch_gp<D, 4, NT_>(p, grid, s);
+    case 8: return launch_gp<D, 8, NT_>(p, grid, s);
+    case 16: return launch_gp<D, 16, NT_>(p, grid, s);
+    case 32: return launch_gp<D, 32, NT_>(p, grid, s);
+    case 64: return launch_gp<D, 64, NT_>(p, grid, s);
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 constexpr int kPrefillThreads = 512;   // workgroup shape of the prefill kernel
