@@ -137,10 +137,11 @@ def test_decode_more_rows_than_one_launch():
 
 def test_decode_workspace_reused_across_layouts():
     """One workspace serves calls whose split layouts overlap each other's bytes."""
-    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
     a = W.make_decode(W.WORKLOADS["llama2_70b_decode"].replace(B=2, ctx=("fixed", 3000)))
     b = W.make_decode(W.WORKLOADS["llama3_8b_decode"].replace(B=8, ctx=("uniform", 300, 1300)))
     c = W.make_decode(W.WORKLOADS["llama2_70b_decode_mqa"].replace(B=3, ctx=("uniform", 900, 5000)))
+    need = max(binding.gqa_decode_workspace_bytes(i.wl.B, i.wl.H, i.wl.K, i.wl.d, int(i.ctx.max())) for i in (a, b, c))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for inp, what in ((a, "A"), (b, "B"), (c, "C"), (a, "A again"), (b, "B again")):
         say("workspace reuse", what)
         out = from_dev(DecodeRun(inp).run(workspace=ws))
