@@ -84,6 +84,10 @@ def _load():
         lib.oracle_quantize_e4m3_rows.argtypes = [vp, i64, i32, vp, vp]
         lib.oracle_dequantize_e4m3_rows.restype = None
         lib.oracle_dequantize_e4m3_rows.argtypes = [vp, vp, i64, i32, vp]
+        lib.oracle_quantize_i8_rows.restype = None
+        lib.oracle_quantize_i8_rows.argtypes = [vp, i64, i32, vp, vp]
+        lib.oracle_dequantize_i8_rows.restype = None
+        lib.oracle_dequantize_i8_rows.argtypes = [vp, vp, i64, i32, vp]
         _lib = lib
         return lib
 
@@ -304,6 +308,34 @@ def dequantize_e4m3_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return out
 
 
+def quantize_i8_rows(x: np.ndarray):
+    """Rows x[..., d] (fp32 values; bf16 bits may be given as uint16) -> (codes
+    int8 [..., d], scales float32 [...]): scale = amax / 127 and codes the
+    nearest integers to x * (1 / scale), ties to even, decided in fp32."""
+    if x.dtype == np.uint16:
+        x = (x.astype(np.uint32) << 16).view(np.float32)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    rows = x.size // d if d else 0
+    codes = np.empty(x.shape, dtype=np.int8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    _load().oracle_quantize_i8_rows(_ptr(x), rows, d, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequantize_i8_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """scale[r] * codes[r, i] in fp64 (exact)."""
+    codes = np.ascontiguousarray(codes, dtype=np.int8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    d = codes.shape[-1]
+    out = np.empty(codes.shape, dtype=np.float64)
+    _load().oracle_dequantize_i8_rows(_ptr(codes), _ptr(scales), codes.size // d if d else 0, d, _ptr(out))
+    return out
+
+
+_CODECS = {"fp8": (quantize_e4m3_rows, dequantize_e4m3_rows), "int8": (quantize_i8_rows, dequantize_i8_rows)}
+
+
 # ---------------------------------------------------------------------------
 # prefill over an FP8 cache (inference-optimisation page §11.7, a chunk of new
 # tokens after a cached prefix, with §15.5.1's quantised K/V): the new rows are
@@ -314,11 +346,12 @@ def dequantize_e4m3_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def fp8_cache_after_append(codes: np.ndarray, scales: np.ndarray, new_rows: np.ndarray, start_pos,
-                           block_table=None):
-    """(codes, scales) of an FP8 cache after the quantising append of new_rows
-    [B, s, K, d] (bf16 bits or fp32) at start_pos: codes [B,K,S,d] / [N,K,bs,d]
-    uint8, scales [B,K,S] / [N,K,bs] float32."""
-    qc, qs = quantize_e4m3_rows(new_rows)
+                           block_table=None, codec: str = "fp8"):
+    """(codes, scales) of an FP8 (or, with codec="int8", INT8) cache after the
+    quantising append of new_rows [B, s, K, d] (bf16 bits or fp32) at
+    start_pos: codes [B,K,S,d] / [N,K,bs,d] uint8 (int8), scales [B,K,S] /
+    [N,K,bs] float32."""
+    qc, qs = _CODECS[codec][0](new_rows)
     codes = np.ascontiguousarray(codes).copy()
     scales = np.ascontiguousarray(scales, dtype=np.float32).copy()
     sc4, qs4 = scales[..., None], np.ascontiguousarray(qs[..., None])
@@ -332,12 +365,13 @@ def fp8_cache_after_append(codes: np.ndarray, scales: np.ndarray, new_rows: np.n
 
 
 def prefill_fp8_rows(q, k_codes, k_scales, v_codes, v_scales, start_pos, s: int, causal: bool, scale: float, rows,
-                     window: int = 0, block_table=None) -> np.ndarray:
-    """Attention rows (b, i, h) of a prefill of s new tokens over an FP8 cache
-    that already holds them (fp8_cache_after_append): keys 0 .. start+s-1 of
-    sequence b, each scale * E4M3(code).  q is [B, s, H, d] fp64."""
-    kd = dequantize_e4m3_rows(k_codes, k_scales)
-    vd = dequantize_e4m3_rows(v_codes, v_scales)
+                     window: int = 0, block_table=None, codec: str = "fp8") -> np.ndarray:
+    """Attention rows (b, i, h) of a prefill of s new tokens over an FP8 (or
+    INT8) cache that already holds them (fp8_cache_after_append): keys 0 ..
+    start+s-1 of sequence b, each scale * E4M3(code) (scale * code).  q is
+    [B, s, H, d] fp64."""
+    kd = _CODECS[codec][1](k_codes, k_scales)
+    vd = _CODECS[codec][1](v_codes, v_scales)
     start = np.asarray(start_pos, dtype=np.int32)
     kv_len = start + s
     if block_table is not None:

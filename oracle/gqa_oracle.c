@@ -415,3 +415,49 @@ void oracle_dequantize_e4m3_rows(const uint8_t *codes, const float *scales, int6
         for (int i = 0; i < d; ++i)
             out[r * d + i] = (double)scales[r] * oracle_e4m3_value(codes[r * d + i]);
 }
+
+/* ---------------------------------------------------------------------- */
+/* INT8 KV cache with one scale per cached row                            */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * The inference-optimisation page, §15.5-§15.5.1, names INT8 beside FP8 for
+ * K/V quantisation, with a scale per token or per head, and gives no formula.
+ * Reading: symmetric INT8 with one fp32 scale per cached row (one token of
+ * one KV head), scale = amax / 127, and every element stored as the integer
+ * nearest to x * (1 / scale) (ties to even), |code| <= 127.  The reciprocal
+ * and the product are IEEE fp32 operations, as in PyTorch's per-channel
+ * qint8 quantiser, and the device takes the same decisions in the same
+ * precision, so codes and scales compare bit for bit.  A row that is all zero
+ * has scale 0 and all-zero codes.  The value a code stands for is
+ * scale * code.
+ */
+void oracle_quantize_i8_rows(const float *x, int64_t rows, int d, int8_t *codes, float *scales)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = x + r * d;
+        float amax = 0.0f;
+        for (int i = 0; i < d; ++i) {
+            const float a = fabsf(xr[i]);
+            if (a > amax) amax = a;
+        }
+        const float scale = amax / 127.0f;
+        scales[r] = scale;
+        const float inv = amax > 0.0f ? 1.0f / scale : 0.0f;
+        for (int i = 0; i < d; ++i) {
+            const float q = xr[i] * inv;          /* fp32 product */
+            float n = rintf(q);                   /* nearest, ties to even (default mode) */
+            if (n > 127.0f) n = 127.0f;
+            if (n < -127.0f) n = -127.0f;
+            codes[r * d + i] = (int8_t)n;
+        }
+    }
+}
+
+/* The values a quantised row stands for: scale[r] * codes[r, i], exact in fp64. */
+void oracle_dequantize_i8_rows(const int8_t *codes, const float *scales, int64_t rows, int d, double *out)
+{
+    for (int64_t r = 0; r < rows; ++r)
+        for (int i = 0; i < d; ++i)
+            out[r * d + i] = (double)scales[r] * (double)codes[r * d + i];
+}

@@ -820,3 +820,150 @@ def test_fp8_prefill_scales_with_the_value_rows(oracle_lib):
         c["v"], sc["v"] = oracle.fp8_cache_after_append(c["v"], sc["v"], v, zero)
         return oracle.prefill_fp8_rows(q, c["k"], sc["k"], c["v"], sc["v"], zero, s, True, 0.25, rows)
     np.testing.assert_array_equal(run(vn * np.float32(8.0)), 8.0 * run(vn))
+
+
+# ---------------------------------------------------------------------------
+# INT8 KV cache: one fp32 scale per cached row (inference-optimisation page
+# §15.5.1 names INT8 beside FP8).  Reading: symmetric, scale = amax / 127,
+# code = nearest integer to x * (1 / scale), ties to even, in fp32: the codes
+# PyTorch's per-channel qint8 quantiser gives for the same scales.
+# ---------------------------------------------------------------------------
+
+def _torch_qint8_codes(x: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """torch.quantize_per_channel along rows with zero points 0 (a library
+    routine, independent of the oracle's C code)."""
+    x2 = torch.from_numpy(np.ascontiguousarray(x, np.float32).reshape(-1, x.shape[-1]))
+    s = torch.from_numpy(np.ascontiguousarray(scales, np.float32).reshape(-1).astype(np.float64))
+    q = torch.quantize_per_channel(x2, s, torch.zeros(s.numel(), dtype=torch.int64), 0, torch.qint8)
+    return q.int_repr().numpy().reshape(x.shape)
+
+
+def _int8_tie_rows(rng, n, d):
+    """Rows of (integer + 1/2) multiples of a power-of-two step, one element at
+    127 steps: every element but the largest is an exact tie."""
+    k = rng.integers(-126, 126, size=(n, d)).astype(np.float32) + np.float32(0.5)
+    step = np.exp2(rng.integers(-10, 4, size=(n, 1))).astype(np.float32)
+    x = (k * step).astype(np.float32)
+    x[:, 0] = np.float32(127) * step[:, 0] * rng.choice([-1, 1], size=n).astype(np.float32)
+    return x
+
+
+def test_int8_codes_match_torch_per_channel_quantiser(oracle_lib):
+    """Random rows over many magnitudes and rows of exact ties: the oracle's
+    codes are the ones torch.quantize_per_channel (qint8, zero point 0) gives
+    for the same per-row scales."""
+    rng = np.random.default_rng(61)
+    x = _bf16_rows(rng, (3000, 128), 1.0) * rng.lognormal(0, 3, (3000, 1)).astype(np.float32)
+    codes, scales = oracle.quantize_i8_rows(x)
+    assert codes.dtype == np.int8 and scales.dtype == np.float32
+    assert np.array_equal(codes, _torch_qint8_codes(x, scales))
+    t = _int8_tie_rows(rng, 2000, 64)
+    tc, ts = oracle.quantize_i8_rows(t)
+    assert np.array_equal(tc, _torch_qint8_codes(t, ts))
+    # the ties really are ties, resolved to the even neighbour
+    assert np.all(np.abs(tc[:, 1:]) % 2 == 0)
+
+
+def test_int8_row_max_maps_to_127_and_error_is_bounded(oracle_lib):
+    """Per row: the largest magnitude becomes +-127, scale * 127 is the row's
+    largest magnitude to fp32 rounding, and every element comes back within
+    half a step (scale / 2) of its value."""
+    rng = np.random.default_rng(62)
+    x = _bf16_rows(rng, (400, 128), 1.0) * rng.lognormal(0, 2, (400, 1)).astype(np.float32)
+    codes, scales = oracle.quantize_i8_rows(x)
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    arg = np.abs(x).argmax(axis=1)
+    assert np.all(np.abs(codes[np.arange(400), arg].astype(np.int32)) == 127)
+    assert np.all(np.abs(codes.astype(np.int32)) <= 127)
+    assert np.all(np.abs(scales.astype(np.float64) * 127 - amax) <= amax * 2.0 ** -23)
+    err = np.abs(oracle.dequantize_i8_rows(codes, scales) - x.astype(np.float64))
+    assert np.all(err <= scales[:, None].astype(np.float64) * (0.5 + 2.0 ** -16))
+
+
+def test_int8_quantization_is_per_row(oracle_lib):
+    """Scaling one row by a power of two scales only that row's scale and keeps
+    every code; an all-zero row has scale 0 and zero codes."""
+    rng = np.random.default_rng(63)
+    x = _bf16_rows(rng, (6, 64))
+    x[4] = 0.0
+    c0, s0 = oracle.quantize_i8_rows(x)
+    y = x.copy()
+    y[2] *= np.float32(2.0 ** -7)
+    c1, s1 = oracle.quantize_i8_rows(y)
+    assert np.array_equal(c0, c1)
+    assert s1[2] == s0[2] * 2.0 ** -7
+    assert np.array_equal(np.delete(s1, 2), np.delete(s0, 2))
+    assert s0[4] == 0 and not c0[4].any()
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)   # bf16 bits in, the same rows
+    cb, sb = oracle.quantize_i8_rows(bits)
+    assert np.array_equal(cb, c0) and np.array_equal(sb, s0)
+
+
+def _i8_exact_rows(rng, shape, scale_exp):
+    """Rows of integers in [-127, 127] times a power-of-two row scale, each row
+    reaching 127 * scale: quantisation returns them unchanged."""
+    x = rng.integers(-127, 128, size=shape).astype(np.float64)
+    x[..., 0] = 127.0 * rng.choice([-1.0, 1.0], size=shape[:-1])
+    return (x * np.exp2(scale_exp)[..., None]).astype(np.float32)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_int8_prefill_equals_attention_when_quantisation_is_exact(oracle_lib, paged):
+    rng = np.random.default_rng(64)
+    B, H, K, d, start, s = 2, 4, 2, 8, 5, 6
+    S = start + s
+    kp = _i8_exact_rows(rng, (B, start, K, d), rng.integers(-12, -6, (B, start, K)))
+    vp = _i8_exact_rows(rng, (B, start, K, d), rng.integers(-12, -6, (B, start, K)))
+    kn = _i8_exact_rows(rng, (B, s, K, d), rng.integers(-12, -6, (B, s, K)))
+    vn = _i8_exact_rows(rng, (B, s, K, d), rng.integers(-12, -6, (B, s, K)))
+    q = rand(rng, B, s, H, d)
+    table = None
+    if paged:
+        table, n_pool = np.array([[2, 0, 5], [1, 4, 3]], np.int32), 6
+        shape = (n_pool, K, 4, d)
+    else:
+        shape = (B, K, S, d)
+    codes = {n: np.full(shape, 0x7F, np.int8) for n in "kv"}
+    scales = {n: np.full(shape[:-1], np.nan, np.float32) for n in "kv"}
+    zero = np.zeros(B, np.int32)
+    for n, pre in (("k", kp), ("v", vp)):
+        codes[n], scales[n] = oracle.fp8_cache_after_append(codes[n], scales[n], pre, zero, table, codec="int8")
+    start_pos = np.full(B, start, np.int32)
+    for n, new in (("k", kn), ("v", vn)):
+        codes[n], scales[n] = oracle.fp8_cache_after_append(codes[n], scales[n], new, start_pos, table, codec="int8")
+    assert codes["k"].dtype == np.int8
+    rows = np.array([[b, i, h] for b in range(B) for i in range(s) for h in range(H)], np.int32)
+    got = oracle.prefill_fp8_rows(q, codes["k"], scales["k"], codes["v"], scales["v"], start_pos, s, True, 0.3, rows,
+                                  block_table=table, codec="int8")
+    k_all = np.concatenate([kp, kn], axis=1).transpose(0, 2, 1, 3).astype(np.float64)
+    v_all = np.concatenate([vp, vn], axis=1).transpose(0, 2, 1, 3).astype(np.float64)
+    want = sdpa_ref(q, k_all, v_all, start_pos, start_pos + s, True, 0.3)
+    np.testing.assert_allclose(got, want[rows[:, 0], rows[:, 1], rows[:, 2]], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("kind", ["truncate", "scale_128", "divide_by_reciprocal_of_128", "round_half_away"])
+def test_planted_int8_mistakes_are_caught(oracle_lib, kind):
+    """A plausible wrong INT8 quantiser, written out on the CPU, fails the
+    torch pin above on the same rows."""
+    rng = np.random.default_rng(65)
+    x = np.concatenate([_bf16_rows(rng, (500, 64)) * rng.lognormal(0, 2, (500, 1)).astype(np.float32),
+                        _int8_tie_rows(rng, 500, 64)])
+    amax = np.abs(x).max(axis=1).astype(np.float32)
+    if kind == "scale_128":
+        scale = (amax / np.float32(128)).astype(np.float32)
+    else:
+        scale = (amax / np.float32(127)).astype(np.float32)
+    inv = (np.float32(1) / scale).astype(np.float32)
+    qf = (x * inv[:, None]).astype(np.float32)
+    if kind == "truncate":
+        codes = np.trunc(qf)
+    elif kind == "round_half_away":
+        codes = np.sign(qf) * np.floor(np.abs(qf) + np.float32(0.5))
+    elif kind == "divide_by_reciprocal_of_128":
+        codes = np.rint((x * (np.float32(1) / (amax / np.float32(128)))[:, None]).astype(np.float32))
+    else:
+        codes = np.rint(qf)
+    codes = np.clip(codes, -127, 127).astype(np.int8)
+    ok_scale = (amax / np.float32(127)).astype(np.float32)
+    caught = not np.array_equal(codes, _torch_qint8_codes(x, ok_scale)) or not np.array_equal(scale, ok_scale)
+    assert caught, kind
