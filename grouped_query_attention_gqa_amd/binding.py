@@ -21,7 +21,7 @@ _lib = None
 _lock = threading.Lock()
 
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_LAUNCH, GQA_ERR_DEVICE_ARG = range(6)
-GQA_F32, GQA_BF16, GQA_FP8_E4M3 = 0, 1, 2
+GQA_F32, GQA_BF16, GQA_FP8_E4M3, GQA_INT8 = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
     "gqa_abi_version", "gqa_status_string", "gqa_cache_elems_per_token",
@@ -97,7 +97,7 @@ def load_library():
         lib.gqa_decode_step_noalloc.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, vp, vp]
         lib.gqa_prefill_window.restype = i32
         lib.gqa_prefill_window.argtypes = [vp, vp, vp, cp, vp, i32, i32, i32, ctypes.c_float, i32, i32, vp, vp]
-        if lib.gqa_abi_version() != 2:
+        if lib.gqa_abi_version() != 3:
             raise RuntimeError("libgqa.so ABI version mismatch")
         _lib = lib
         return lib
@@ -122,6 +122,8 @@ def _dtype_code(t: torch.dtype) -> int:
         return GQA_F32
     if t == torch.float8_e4m3fn:
         return GQA_FP8_E4M3
+    if t == torch.int8:
+        return GQA_INT8
     raise TypeError(f"unsupported dtype {t}")
 
 
@@ -151,9 +153,9 @@ def _need(t: torch.Tensor, name: str, dtype=None, dim=None):
 class KVCache:
     """One layer's cache: contiguous [B,K,S_max,d] or paged [N,K,bs,d] + block table.
 
-    An FP8 cache (k, v of torch.float8_e4m3fn) also takes k_scale / v_scale:
-    float32 [B,K,S_max] or [N,K,bs], one scale per cached row; its queries,
-    new rows and outputs are bf16."""
+    A quantised cache (k, v of torch.float8_e4m3fn for FP8 E4M3, or torch.int8
+    for INT8) also takes k_scale / v_scale: float32 [B,K,S_max] or [N,K,bs],
+    one scale per cached row; its queries, new rows and outputs are bf16."""
 
     def __init__(self, k: torch.Tensor, v: torch.Tensor, block_table: Optional[torch.Tensor] = None,
                  k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None):
@@ -164,14 +166,15 @@ class KVCache:
         self.k, self.v, self.block_table = k, v, block_table
         self.k_scale, self.v_scale = k_scale, v_scale
         self.dtype = k.dtype
-        self.act_dtype = torch.bfloat16 if k.dtype == torch.float8_e4m3fn else k.dtype
+        quant = k.dtype in (torch.float8_e4m3fn, torch.int8)
+        self.act_dtype = torch.bfloat16 if quant else k.dtype
         self.num_kv_heads = int(k.shape[1])
         self.head_dim = int(k.shape[3])
         self.paged = block_table is not None
         s = _CacheStruct()
         s.k, s.v = k.data_ptr(), v.data_ptr()
         s.num_kv_heads, s.head_dim, s.dtype = self.num_kv_heads, self.head_dim, _dtype_code(k.dtype)
-        if k.dtype == torch.float8_e4m3fn:
+        if quant:
             for name, sc in (("k_scale", k_scale), ("v_scale", v_scale)):
                 _need(sc, name, dtype=torch.float32, dim=3)
                 if tuple(sc.shape) != tuple(k.shape[:3]):

@@ -70,11 +70,12 @@ gqa_status make_view(const gqa_kv_cache *c, CacheView *out)
     if (c->num_kv_heads <= 0) return fail(GQA_ERR_INVALID_ARG, "num_kv_heads <= 0");
     if (c->head_dim <= 0) return fail(GQA_ERR_INVALID_ARG, "head_dim <= 0");
     if (c->head_dim != 64 && c->head_dim != 128) return fail(GQA_ERR_UNSUPPORTED, "head_dim not 64 or 128");
-    if (c->dtype != GQA_F32 && c->dtype != GQA_BF16 && c->dtype != GQA_FP8_E4M3)
+    if (c->dtype != GQA_F32 && c->dtype != GQA_BF16 && c->dtype != GQA_FP8_E4M3 && c->dtype != GQA_INT8)
         return fail(GQA_ERR_UNSUPPORTED, "unknown dtype");
-    if (c->dtype == GQA_FP8_E4M3) {
-        if (!c->k_scale || !c->v_scale) return fail(GQA_ERR_INVALID_ARG, "FP8 cache without scales");
-        if (c->head_dim != 128) return fail(GQA_ERR_UNSUPPORTED, "FP8 cache needs head_dim 128");
+    const bool quant = c->dtype == GQA_FP8_E4M3 || c->dtype == GQA_INT8;
+    if (quant) {
+        if (!c->k_scale || !c->v_scale) return fail(GQA_ERR_INVALID_ARG, "quantised cache without scales");
+        if (c->head_dim != 128) return fail(GQA_ERR_UNSUPPORTED, "quantised cache needs head_dim 128");
     }
     CacheView v{};
     v.k = static_cast<char *>(c->k);
@@ -82,9 +83,10 @@ gqa_status make_view(const gqa_kv_cache *c, CacheView *out)
     v.block_table = c->block_table;
     v.K = c->num_kv_heads;
     v.d = c->head_dim;
-    v.elem_bytes = c->dtype == GQA_FP8_E4M3 ? 1 : c->dtype == GQA_BF16 ? 2 : 4;
-    v.k_scale = c->dtype == GQA_FP8_E4M3 ? c->k_scale : nullptr;
-    v.v_scale = c->dtype == GQA_FP8_E4M3 ? c->v_scale : nullptr;
+    v.elem_bytes = quant ? 1 : c->dtype == GQA_BF16 ? 2 : 4;
+    v.int8 = c->dtype == GQA_INT8 ? 1 : 0;
+    v.k_scale = quant ? c->k_scale : nullptr;
+    v.v_scale = quant ? c->v_scale : nullptr;
     if (c->block_table == nullptr) {
         if (c->S_max <= 0) return fail(GQA_ERR_INVALID_ARG, "S_max <= 0");
         v.S_max = c->S_max;
@@ -276,7 +278,7 @@ gqa_status gqa::decode_step(const void *q, const void *k_new, const void *v_new,
     if (!q || !out || !ctx_lens) return fail(GQA_ERR_INVALID_ARG, "NULL q/out/ctx_lens");
     if (step && (!k_new || !v_new)) return fail(GQA_ERR_INVALID_ARG, "NULL k_new or v_new");
     if (v.elem_bytes == 1 && v.block_table && v.log2_bs < 4)
-        return fail(GQA_ERR_UNSUPPORTED, "FP8 cache with blocks below 16 tokens");
+        return fail(GQA_ERR_UNSUPPORTED, "quantised cache with blocks below 16 tokens");
     if (max_ctx <= 0) return fail(GQA_ERR_INVALID_ARG, "max_ctx <= 0");
     if (!scale_ok(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not a positive finite number");
     DecodeLayout L;

@@ -33,6 +33,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v_t));
 }
 
+// Four INT8 codes (code i in byte i of w) -> four bf16 values, two per word,
+// exactly: a code of magnitude <= 127 has at most 7 significant bits, so
+// its fp32 value's upper half is its bf16 value.
+__device__ __forceinline__ uint2 i8x4_bf16x4(uint32_t w)
+{
+    const uint32_t u = w ^ 0x80808080u;   // code + 128 in each byte, in [1, 255]
+    const float f0 = (float)(u & 0xFFu) - 128.f, f1 = (float)((u >> 8) & 0xFFu) - 128.f;
+    const float f2 = (float)((u >> 16) & 0xFFu) - 128.f, f3 = (float)(u >> 24) - 128.f;
+    return make_uint2(__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u),
+                      __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u));
+}
+
 // Two bf16 products summed into an fp32 accumulator (v_dot2_f32_bf16).
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c)

@@ -98,8 +98,15 @@ __device__ __forceinline__ uint32_t f8x2_bf16x2(uint32_t w)
 {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
-__device__ __forceinline__ uint4 f8x8_bf16x8(uint2 x)
+// eight 1-byte codes -> eight bf16 values, exactly: E4M3 codes, or INT8
+// codes with I8
+template <bool I8>
+__device__ __forceinline__ uint4 c8x8_bf16x8(uint2 x)
 {
+    if constexpr (I8) {
+        const uint2 a = i8x4_bf16x4(x.x), b = i8x4_bf16x4(x.y);
+        return make_uint4(a.x, a.y, b.x, b.y);
+    }
     return make_uint4(f8x2_bf16x2<false>(x.x), f8x2_bf16x2<true>(x.x), f8x2_bf16x2<false>(x.y), f8x2_bf16x2<true>(x.y));
 }
 // A stage: the tile's K rows, its V rows and (FP8) its 16 K and 16 V scales
@@ -185,7 +192,7 @@ __device__ __forceinline__ float row_max(float x)
 
 // RBW: 16-row blocks (R <= 16 * RBW); occ_of(RBW) workgroups per CU; F8: the
 // cache holds E4M3 codes and a scale per row (d = 128); D: the head dimension
-template <int RBW, bool F8, int D>
+template <int RBW, bool F8, int D, bool I8 = false>
 __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnParams p)
 {
     static_assert(!F8 || D == 128, "FP8 caches at d = 128");
@@ -414,7 +421,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const int chunk = 2 * ks + (lg >> 1);
-                    kf[ks] = f8x8_bf16x8(*reinterpret_cast<const uint2 *>(kt + nr * CRB + ((chunk ^ ksw8(nr)) * 16) +
+                    kf[ks] = c8x8_bf16x8<I8>(*reinterpret_cast<const uint2 *>(kt + nr * CRB + ((chunk ^ ksw8(nr)) * 16) +
                                                                           (lg & 1) * 8));
                 }
                 // scales of this lane's keys 4 lg .. 4 lg + 3
@@ -431,8 +438,8 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                 for (int h = 0; h < 2; ++h) {
                     const uint4 x = *reinterpret_cast<const uint4 *>(vsrc + 16 * h);
                     const int c0 = 4 * (lane & 3) + 2 * h;   // logical bf16 chunk of the first 8 columns
-                    *reinterpret_cast<uint4 *>(vdst + vr * RB + ((c0 ^ vsw<D>(vr)) * 16)) = f8x8_bf16x8(make_uint2(x.x, x.y));
-                    *reinterpret_cast<uint4 *>(vdst + vr * RB + (((c0 + 1) ^ vsw<D>(vr)) * 16)) = f8x8_bf16x8(make_uint2(x.z, x.w));
+                    *reinterpret_cast<uint4 *>(vdst + vr * RB + ((c0 ^ vsw<D>(vr)) * 16)) = c8x8_bf16x8<I8>(make_uint2(x.x, x.y));
+                    *reinterpret_cast<uint4 *>(vdst + vr * RB + (((c0 + 1) ^ vsw<D>(vr)) * 16)) = c8x8_bf16x8<I8>(make_uint2(x.z, x.w));
                 }
             }
             // S^T = K Q^T: lane holds keys key0 + 4 lg + e of row 16 rb + nr
@@ -729,7 +736,10 @@ hipError_t launch_m(const RowAttnParams &p0, hipStream_t s)
     // slices resident at once: occ_of(RBW) per CU, unless the caller fixed the count
     p.num_wgs = p0.wgs_override > 0 ? p0.wgs_override : p0.num_wgs * occ_of(RBW) / 2;
     if (p.cache.elem_bytes == 1) {
-        if constexpr (D == 128) hipLaunchKernelGGL((decode_mfma_kernel<RBW, true, D>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+        if constexpr (D == 128) {
+            if (p.cache.int8) hipLaunchKernelGGL((decode_mfma_kernel<RBW, true, D, true>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+            else hipLaunchKernelGGL((decode_mfma_kernel<RBW, true, D, false>), dim3(p.num_wgs), dim3(NT), 0, s, p);
+        }
         else return hipErrorInvalidValue;
     } else {
         hipLaunchKernelGGL((decode_mfma_kernel<RBW, false, D>), dim3(p.num_wgs), dim3(NT), 0, s, p);

@@ -21,9 +21,10 @@ struct CacheView {
     int32_t S_max;              // contiguous capacity per sequence
     int32_t K;                  // KV heads
     int32_t d;                  // head dim
-    int32_t elem_bytes;         // bytes of a stored element: 1 (FP8 E4M3), 2 (bf16) or 4 (fp32)
+    int32_t elem_bytes;         // bytes of a stored element: 1 (FP8 E4M3 or INT8), 2 (bf16) or 4 (fp32)
+    int32_t int8;               // 1: the 1-byte codes are INT8 (else E4M3)
     int32_t capacity;           // tokens a sequence can hold
-    float *k_scale;             // FP8 only: one scale per cached row, indexed like the rows
+    float *k_scale;             // FP8 / INT8 only: one scale per cached row, indexed like the rows
     float *v_scale;
 };
 

@@ -56,7 +56,13 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p)
     st16(dst, ld16(src));
 }
 
+// The quantising append of a 1-byte cache with one fp32 scale per row
+// (inference-optimisation page §15.5.1): 16 lanes per 128-element row reduce
+// its largest magnitude, then each lane stores its 8 codes.  I8: INT8 codes,
+// scale = amax / 127 and code = nearest-even of x * (1 / scale); else E4M3,
+// scale = amax / 448 and code = E4M3(x / scale).
 constexpr int kF8Lanes = 16;   // lanes per 128-element row
+template <bool I8>
 __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendParams p)
 {
     const CacheView &c = p.cache;
@@ -91,9 +97,21 @@ __global__ __launch_bounds__(256) void kv_append_fp8_kernel(AppendParams p)
     if (pos < 0 || pos >= c.capacity) return;
     const int64_t dst_row = cache_row(c, b, g, (int)pos);
     if (dst_row < 0) return;
-    const float scale = amax / 448.0f;
+    const float scale = amax / (I8 ? 127.0f : 448.0f);
     uint32_t lo = 0, hi = 0;
-    if (amax > 0.f) {
+    if (I8) {
+        if (amax > 0.f) {
+            const float inv = 1.0f / scale;
+            uint32_t b[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float n = fminf(fmaxf(__builtin_rintf(f[i] * inv), -127.f), 127.f);
+                b[i] = (uint32_t)(int)n & 0xFFu;
+            }
+            lo = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+            hi = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+        }
+    } else if (amax > 0.f) {
         lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[0] / scale, f[1] / scale, 0, false);
         lo = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[2] / scale, f[3] / scale, (int)lo, true);
         hi = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(f[4] / scale, f[5] / scale, 0, false);
@@ -111,7 +129,10 @@ hipError_t launch_kv_append(const AppendParams &p, hipStream_t stream)
         if (total == 0) return hipSuccess;
         const int64_t blocks = (total + 255) / 256;
         if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-        hipLaunchKernelGGL(kv_append_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+        if (p.cache.int8)
+            hipLaunchKernelGGL(kv_append_fp8_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+        else
+            hipLaunchKernelGGL(kv_append_fp8_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
         return hipGetLastError();
     }
     const int cpr = p.cache.d * p.cache.elem_bytes / 16;

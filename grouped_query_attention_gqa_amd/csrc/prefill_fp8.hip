@@ -1,11 +1,13 @@
 // prefill_fp8.hip -- causal (or full) grouped-query attention of a block of
-// new query tokens over an FP8 E4M3 KV cache with one fp32 scale per cached
-// row, on the CDNA4 matrix cores (bf16 products, fp32 accumulation).
+// new query tokens over an FP8 E4M3 (or INT8) KV cache with one fp32 scale
+// per cached row, on the CDNA4 matrix cores (bf16 products, fp32
+// accumulation).
 //
 // What it computes ("Grouped-Query Attention" concept page, 技术原理 steps 2-4,
 // over the quantised cache of the inference-optimisation page §15.5.1):
 // out[b,i,h] = softmax(q[b,i,h] K_g^T * scale) V_g, g = h / G, where cached
-// row j of K (and V) stands for k_scale[j] * E4M3(code_j).  The new tokens
+// row j of K (and V) stands for k_scale[j] * E4M3(code_j) (k_scale[j] * code_j
+// for INT8).  The new tokens
 // were quantised into the cache by the append kernel first, so the prefix and
 // the new rows are read the same way; the visible keys are those of the bf16
 // prefill (causal from start_pos, optional sliding window).
@@ -17,7 +19,8 @@
 //    LDS-direct loads, NS stages deep (16.5 KB per stage, half the bytes of a
 //    bf16 stage).
 //  * Once a tile's codes have landed, the workgroup converts them into a bf16
-//    tile (every E4M3 value is a bf16 value, so the conversion is exact),
+//    tile (every E4M3 value and every integer of magnitude <= 127 is a bf16
+//    value, so the conversion is exact),
 //    laid out and swizzled as the bf16 prefill's stages, together with a copy
 //    of the scales.  Two such tiles alternate: tile t + 1 is converted while
 //    the matrix cores work on tile t, with one barrier per tile.
@@ -123,12 +126,19 @@ __device__ __forceinline__ uint32_t f8x2_bf16x2(uint32_t w)
 {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
-__device__ __forceinline__ uint4 f8x8_bf16x8(uint32_t lo, uint32_t hi)
+// eight 1-byte codes -> eight bf16 values, exactly: E4M3 codes, or INT8
+// codes with I8
+template <bool I8>
+__device__ __forceinline__ uint4 c8x8_bf16x8(uint32_t lo, uint32_t hi)
 {
+    if constexpr (I8) {
+        const uint2 a = i8x4_bf16x4(lo), b = i8x4_bf16x4(hi);
+        return make_uint4(a.x, a.y, b.x, b.y);
+    }
     return make_uint4(f8x2_bf16x2<false>(lo), f8x2_bf16x2<true>(lo), f8x2_bf16x2<false>(hi), f8x2_bf16x2<true>(hi));
 }
 
-template <int GP>
+template <int GP, bool I8>
 __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillParams p)
 {
     constexpr int RPW = ROWS / NW;        // 32 rows per wave
@@ -242,8 +252,8 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillParams p)
         // 16 codes = bf16 chunks 2c and 2c + 1 of the row
         char *ct = smem + NS * STAGE + (t & 1) * CTILE + (v ? CT_V : 0) + cv_r * RB;
         const int sw = v ? vsw(cv_r) : ksw(cv_r);
-        *reinterpret_cast<uint4 *>(ct + (((2 * cv_c) ^ sw) * 16)) = f8x8_bf16x8(x.x, x.y);
-        *reinterpret_cast<uint4 *>(ct + (((2 * cv_c + 1) ^ sw) * 16)) = f8x8_bf16x8(x.z, x.w);
+        *reinterpret_cast<uint4 *>(ct + (((2 * cv_c) ^ sw) * 16)) = c8x8_bf16x8<I8>(x.x, x.y);
+        *reinterpret_cast<uint4 *>(ct + (((2 * cv_c + 1) ^ sw) * 16)) = c8x8_bf16x8<I8>(x.z, x.w);
     };
     auto scale_write = [&](int t, float x) __attribute__((always_inline)) {
         if (tid < 2 * BN) *reinterpret_cast<float *>(smem + NS * STAGE + (t & 1) * CTILE + CT_KSC + tid * 4) = x;
@@ -470,6 +480,22 @@ __global__ __launch_bounds__(NT) void prefill_fp8_kernel(PrefillParams p)
         }
 }
 
+template <bool I8>
+hipError_t launch_gp(const PrefillParams &p, int gp, dim3 grid, hipStream_t s)
+{
+    switch (gp) {
+    case 1: hipLaunchKernelGGL((prefill_fp8_kernel<1, I8>), grid, dim3(NT), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((prefill_fp8_kernel<2, I8>), grid, dim3(NT), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((prefill_fp8_kernel<4, I8>), grid, dim3(NT), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((prefill_fp8_kernel<8, I8>), grid, dim3(NT), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((prefill_fp8_kernel<16, I8>), grid, dim3(NT), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((prefill_fp8_kernel<32, I8>), grid, dim3(NT), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((prefill_fp8_kernel<64, I8>), grid, dim3(NT), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_prefill_fp8(const PrefillParams &p, hipStream_t s)
@@ -479,17 +505,7 @@ hipError_t launch_prefill_fp8(const PrefillParams &p, hipStream_t s)
     const int64_t nqb = (p.s + ROWS / gp - 1) / (ROWS / gp);
     if (nqb * p.cache.K * p.B > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(nqb * p.cache.K * p.B));
-    switch (gp) {
-    case 1: hipLaunchKernelGGL(prefill_fp8_kernel<1>, grid, dim3(NT), 0, s, p); break;
-    case 2: hipLaunchKernelGGL(prefill_fp8_kernel<2>, grid, dim3(NT), 0, s, p); break;
-    case 4: hipLaunchKernelGGL(prefill_fp8_kernel<4>, grid, dim3(NT), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(prefill_fp8_kernel<8>, grid, dim3(NT), 0, s, p); break;
-    case 16: hipLaunchKernelGGL(prefill_fp8_kernel<16>, grid, dim3(NT), 0, s, p); break;
-    case 32: hipLaunchKernelGGL(prefill_fp8_kernel<32>, grid, dim3(NT), 0, s, p); break;
-    case 64: hipLaunchKernelGGL(prefill_fp8_kernel<64>, grid, dim3(NT), 0, s, p); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return p.cache.int8 ? launch_gp<true>(p, gp, grid, s) : launch_gp<false>(p, gp, grid, s);
 }
 
 }  // namespace gqa

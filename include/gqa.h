@@ -54,13 +54,14 @@
  *     decode launch splits the keys over (flash-decoding's split count,
  *     inference-optimisation page §10.2; the result is the same for every n
  *     up to the rounding of the merge); unset, each kernel picks its own.
- *   - Quantised cache (GQA_FP8_E4M3): K/V rows stored as FP8 E4M3 with one
- *     fp32 scale per cached row (token x KV head), written by gqa_kv_append,
- *     gqa_decode_step and the prefill calls and read by the decode and
- *     prefill calls (inference-optimisation page §15.5-§15.5.1: per-token /
- *     per-head scales, FP8 E4M3).  Queries, new K/V rows and outputs are then
- *     bf16.  Supported for head_dim 128; the decode calls need paged blocks
- *     of at least 16 tokens.
+ *   - Quantised cache (GQA_FP8_E4M3 or GQA_INT8): K/V rows stored as FP8
+ *     E4M3 or INT8 codes with one fp32 scale per cached row (token x KV
+ *     head), written by gqa_kv_append, gqa_decode_step and the prefill calls
+ *     and read by the decode and prefill calls (inference-optimisation page
+ *     §15.5-§15.5.1: per-token / per-head scales, FP8 E4M3 or INT8).
+ *     Queries, new K/V rows and outputs are then bf16.  Supported for
+ *     head_dim 128; the decode calls need paged blocks of at least 16
+ *     tokens.
  */
 #ifndef GQA_H
 #define GQA_H
@@ -72,7 +73,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 2
+#define GQA_ABI_VERSION 3
 
 typedef enum {
     GQA_OK = 0,
@@ -86,8 +87,10 @@ typedef enum {
 typedef enum {
     GQA_F32 = 0,               /* IEEE binary32 */
     GQA_BF16 = 1,              /* bfloat16 (upper half of a binary32), stored as 16-bit words */
-    GQA_FP8_E4M3 = 2           /* cache only: OCP FP8 E4M3 codes (bias 7, largest finite 448, no
+    GQA_FP8_E4M3 = 2,          /* cache only: OCP FP8 E4M3 codes (bias 7, largest finite 448, no
                                 * infinities) with one fp32 scale per row: value = scale * E4M3(code) */
+    GQA_INT8 = 3               /* cache only: signed 8-bit codes in [-127, 127] with one fp32 scale
+                                * per row: value = scale * code */
 } gqa_dtype;
 
 /* One layer's KV cache for K KV heads of width head_dim. */
@@ -102,7 +105,7 @@ typedef struct {
     int32_t num_kv_heads;         /* K */
     int32_t head_dim;             /* d */
     int32_t dtype;                /* gqa_dtype */
-    float *k_scale;               /* GQA_FP8_E4M3 only (else ignored): one scale per cached row,
+    float *k_scale;               /* GQA_FP8_E4M3 and GQA_INT8 only (else ignored): one scale per cached row,
                                      contiguous [B, K, S_max], paged [num_blocks, K, block_size] */
     float *v_scale;               /* the same for V */
 } gqa_kv_cache;
@@ -124,6 +127,9 @@ int32_t gqa_cache_elems_per_token(int32_t num_kv_heads, int32_t head_dim);
  * FP8 cache: a row x of d bf16 values is stored as scale = amax(|x|) / 448
  * and codes E4M3(x_i / scale), nearest value with ties to the even code,
  * both divisions in IEEE fp32; an all-zero row has scale 0 and zero codes.
+ * INT8 cache: scale = amax(|x|) / 127 and codes the integers nearest to
+ * x_i * (1 / scale), ties to even, the reciprocal and the product in IEEE
+ * fp32 (|code| <= 127); an all-zero row has scale 0 and zero codes.
  *
  * Append s_new tokens to every sequence of the cache:
  *     pos = start_pos[b] + t,  cache row (b, g, pos) <- new row (b, t, g)

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.gqa_abi_version() == 2
+    assert lib.gqa_abi_version() == 3
     assert lib.gqa_status_string(0) == b"ok"
     assert b"workspace" in lib.gqa_status_string(3)
 
@@ -144,10 +144,12 @@ def test_decode_step_rejects_bad_args(lib):
     assert step(FAKE, FAKE, B=0) == binding.GQA_OK
 
 
-def test_fp8_cache_argument_rules(lib):
-    """An FP8 cache needs both scale arrays and head_dim 128; decode takes blocks
-    of at least 16 tokens."""
-    f8 = dict(dtype=binding.GQA_FP8_E4M3, head_dim=128, S_max=4096, num_kv_heads=8)
+@pytest.mark.parametrize("qdtype", ["fp8", "int8"])
+def test_fp8_cache_argument_rules(lib, qdtype):
+    """A quantised cache (FP8 E4M3 or INT8) needs both scale arrays and
+    head_dim 128; decode takes blocks of at least 16 tokens."""
+    f8 = dict(dtype=binding.GQA_FP8_E4M3 if qdtype == "fp8" else binding.GQA_INT8, head_dim=128, S_max=4096,
+              num_kv_heads=8)
     sc = dict(k_scale=0x50000, v_scale=0x60000)
     ws = lib.gqa_decode_workspace_bytes(1, 32, 8, 128, 4096)
     dec = lambda cache, H=32: lib.gqa_decode(FAKE, ctypes.byref(cache), FAKE, 4096, 1, H, ctypes.c_float(0.088),
@@ -163,6 +165,10 @@ def test_fp8_cache_argument_rules(lib):
                                        FAKE, None)
     assert pf(_cache(**{**f8, "head_dim": 64}, **sc)) == binding.GQA_ERR_UNSUPPORTED
     assert pf(_cache(**f8, v_scale=0x60000)) == binding.GQA_ERR_INVALID_ARG
+
+
+def test_unknown_dtype_is_refused(lib):
+    assert _decode(lib, _cache(dtype=4)) == binding.GQA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.125, -0.0, float("-inf")])

@@ -19,13 +19,22 @@ from gpu_common import BF16_TOL, as_f64, check_close, from_dev, say, to_dev
 pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 NAN_CODE = 0x7F
+# The helpers below take codec="fp8" (E4M3) or "int8" (tests/test_int8_gpu.py):
+# the quantiser and decoder of the oracle, the torch dtype of the codes and
+# the code that fills unused slots (the E4M3 NaN code; -128, a code the INT8
+# quantiser never writes).
+QUANT = {"fp8": (oracle.quantize_e4m3_rows, oracle.dequantize_e4m3_rows, torch.float8_e4m3fn, NAN_CODE),
+         "int8": (oracle.quantize_i8_rows, oracle.dequantize_i8_rows, torch.int8, 0x80)}
 
 
-def f8_dev(codes: np.ndarray) -> torch.Tensor:
-    return torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).to("cuda").view(torch.float8_e4m3fn)
+def f8_dev(codes: np.ndarray, codec: str = "fp8") -> torch.Tensor:
+    """Codes (uint8 bytes or int8) on the device, as the codec's torch dtype."""
+    raw = np.ascontiguousarray(codes).view(np.uint8)
+    return torch.from_numpy(raw).to("cuda").view(QUANT[codec][2])
 
 
 def f8_host(t: torch.Tensor) -> np.ndarray:
+    """The code bytes of a device tensor (uint8)."""
     return t.detach().view(torch.uint8).cpu().numpy()
 
 
@@ -45,23 +54,30 @@ def _used_slots(inp: W.DecodeInputs) -> np.ndarray:
     return used
 
 
-def quantized_inputs(inp: W.DecodeInputs):
-    """The oracle's codes and scales of the (zero-filled) bf16 cache, with every
-    unused slot set to the NaN code and a NaN scale."""
-    kc, ks = oracle.quantize_e4m3_rows(inp.k)
-    vc, vs = oracle.quantize_e4m3_rows(inp.v)
+def quantized_inputs(inp: W.DecodeInputs, codec: str = "fp8"):
+    """The oracle's codes (as uint8 bytes) and scales of the (zero-filled) bf16
+    cache, with every unused slot set to the fill code and a NaN scale."""
+    quant = QUANT[codec][0]
+    kc, ks = quant(inp.k)
+    vc, vs = quant(inp.v)
+    kc, vc = kc.view(np.uint8), vc.view(np.uint8)
     used = _used_slots(inp)
     for c, s in ((kc, ks), (vc, vs)):
-        c[~used] = NAN_CODE
+        c[~used] = QUANT[codec][3]
         s[~used] = np.nan
     return kc, ks, vc, vs
 
 
-def oracle_rows_f8(inp, kc, ks, vc, vs, seqs, window=0):
+def dequant(codes, scales, codec: str = "fp8"):
+    """The oracle's values of code bytes and scales."""
+    return QUANT[codec][1](codes.view(np.int8) if codec == "int8" else codes, scales)
+
+
+def oracle_rows_f8(inp, kc, ks, vc, vs, seqs, window=0, codec: str = "fp8"):
     """fp64 oracle attention over the dequantised cache for the listed sequences."""
     wl = inp.wl
-    kd = oracle.dequantize_e4m3_rows(kc, ks)
-    vd = oracle.dequantize_e4m3_rows(vc, vs)
+    kd = dequant(kc, ks, codec)
+    vd = dequant(vc, vs, codec)
     rows_all, outs = [], []
     for b in seqs:
         n = int(inp.ctx[b])
@@ -81,24 +97,24 @@ def oracle_rows_f8(inp, kc, ks, vc, vs, seqs, window=0):
     return np.concatenate(rows_all), np.concatenate(outs)
 
 
-def _f8_cache(kc, ks, vc, vs, table):
-    return binding.KVCache(f8_dev(kc), f8_dev(vc), None if table is None else to_dev(table),
+def _f8_cache(kc, ks, vc, vs, table, codec: str = "fp8"):
+    return binding.KVCache(f8_dev(kc, codec), f8_dev(vc, codec), None if table is None else to_dev(table),
                            k_scale=to_dev(ks), v_scale=to_dev(vs))
 
 
-def _decode_case(wl, what, window=0, seqs=None):
+def _decode_case(wl, what, window=0, seqs=None, codec: str = "fp8"):
     inp = W.make_decode(wl, fill="zero")
-    kc, ks, vc, vs = quantized_inputs(inp)
-    cache = _f8_cache(kc, ks, vc, vs, inp.block_table)
+    kc, ks, vc, vs = quantized_inputs(inp, codec)
+    cache = _f8_cache(kc, ks, vc, vs, inp.block_table, codec)
     seqs = list(range(wl.B)) if seqs is None else seqs
-    say("fp8 decode", what, f"window={window}")
+    say(f"{codec} decode", what, f"window={window}")
     out = binding.gqa_decode(to_dev(inp.q), cache, to_dev(inp.ctx), int(inp.ctx.max()), scale=wl.scale,
                              window=window)
     torch.cuda.synchronize()
     o = from_dev(out)
-    rows, want = oracle_rows_f8(inp, kc, ks, vc, vs, seqs, window)
+    rows, want = oracle_rows_f8(inp, kc, ks, vc, vs, seqs, window, codec)
     got = as_f64(o[rows[:, 0], rows[:, 1], rows[:, 2]], "bf16")
-    check_close(got, want, BF16_TOL, f"fp8 decode {what}")
+    check_close(got, want, BF16_TOL, f"{codec} decode {what}")
 
 
 LLAMA3 = W.WORKLOADS["llama3_8b_decode"]
@@ -340,7 +356,7 @@ def test_fp8_paged_spikes_exact():
 # ---------------------------------------------------------------------------
 
 def _fp8_prefill_run(B, H, K, s, start, *, paged=False, bs=16, causal=True, window=0, seed=0, rows=None,
-                     inputs=None):
+                     inputs=None, codec="fp8"):
     """Runs gqa_prefill on an FP8 cache holding start[b] quantised prefix tokens
     of sequence b; returns (out [B,s,H,d] bf16 bits, expected rows, rows).
     inputs = (q, k_new, v_new, k_prefix, v_prefix) as bf16 bits, else random.
@@ -363,7 +379,8 @@ def _fp8_prefill_run(B, H, K, s, start, *, paged=False, bs=16, causal=True, wind
         shape = (n_pool, K, bs, d)
     else:
         shape = (B, K, S, d)
-    codes = {n: np.full(shape, NAN_CODE, np.uint8) for n in "kv"}
+    cdt = np.int8 if codec == "int8" else np.uint8
+    codes = {n: np.full(shape, QUANT[codec][3], np.uint8).view(cdt) for n in "kv"}
     scales = {n: np.full(shape[:-1], np.nan, np.float32) for n in "kv"}
     # the prefix: positions t < starts[b] of sequence b, quantised by the oracle
     for n, pre in (("k", kp), ("v", vp)):
@@ -372,19 +389,21 @@ def _fp8_prefill_run(B, H, K, s, start, *, paged=False, bs=16, causal=True, wind
                 continue
             rows_b = np.ascontiguousarray(pre[b:b + 1, :starts[b]])
             if table is None:
-                c, sc = oracle.fp8_cache_after_append(codes[n][b:b + 1], scales[n][b:b + 1], rows_b, [0])
+                c, sc = oracle.fp8_cache_after_append(codes[n][b:b + 1], scales[n][b:b + 1], rows_b, [0],
+                                                      codec=codec)
                 codes[n][b], scales[n][b] = c[0], sc[0]
             else:
-                codes[n], scales[n] = oracle.fp8_cache_after_append(codes[n], scales[n], rows_b, [0], table[b:b + 1])
-    cache = _f8_cache(codes["k"], scales["k"], codes["v"], scales["v"], table)
-    say("fp8 prefill", f"B={B} H={H} K={K} s={s} start={list(starts)} paged={paged} bs={bs} window={window}")
+                codes[n], scales[n] = oracle.fp8_cache_after_append(codes[n], scales[n], rows_b, [0], table[b:b + 1],
+                                                                    codec=codec)
+    cache = _f8_cache(codes["k"], scales["k"], codes["v"], scales["v"], table, codec)
+    say(f"{codec} prefill", f"B={B} H={H} K={K} s={s} start={list(starts)} paged={paged} bs={bs} window={window}")
     out = binding.gqa_prefill(to_dev(q), to_dev(kn), to_dev(vn), cache, to_dev(starts), causal=causal,
                               scale=1.0 / np.sqrt(d), window=window)
     torch.cuda.synchronize()
     after = {}
     for n, new in (("k", kn), ("v", vn)):
-        want_c, want_s = oracle.fp8_cache_after_append(codes[n], scales[n], new, starts, table)
-        got_c = f8_host(getattr(cache, n))
+        want_c, want_s = oracle.fp8_cache_after_append(codes[n], scales[n], new, starts, table, codec=codec)
+        got_c = f8_host(getattr(cache, n)).view(cdt)
         got_s = getattr(cache, n + "_scale").cpu().numpy()
         assert np.array_equal(got_c, want_c), f"{n} codes after the prefill"
         assert got_s.view(np.uint32).tobytes() == want_s.view(np.uint32).tobytes(), f"{n} scales after the prefill"
@@ -392,7 +411,7 @@ def _fp8_prefill_run(B, H, K, s, start, *, paged=False, bs=16, causal=True, wind
     if rows is None:
         rows = np.array([[b, i, h] for b in range(B) for i in range(s) for h in range(H)], np.int32)
     want = oracle.prefill_fp8_rows(as_f64(q, "bf16"), after["k"][0], after["k"][1], after["v"][0], after["v"][1],
-                                   starts, s, causal, 1.0 / np.sqrt(d), rows, window, table)
+                                   starts, s, causal, 1.0 / np.sqrt(d), rows, window, table, codec=codec)
     return from_dev(out), want, rows, after, table
 
 
