@@ -66,8 +66,10 @@ TRAFFIC_SOURCES = {
     "decode/paged_long_decode": DECODE_SOURCES,
     "decode/llama2_70b_decode_mqa": DECODE_SOURCES,
     "decode/llama3_8b_decode_fp8_cache": DECODE_SOURCES + ("kv_append.hip",),
+    "decode/llama3_8b_decode_int8_cache": DECODE_SOURCES + ("kv_append.hip",),
     "prefill/causal_prefill_4k": PREFILL_SOURCES,
     "prefill/chunked_prefill_paged_fp8_cache": PREFILL_FP8_SOURCES,
+    "prefill/chunked_prefill_paged_int8_cache": PREFILL_FP8_SOURCES,
 }
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "GQA decode HBM GB/s (% of peak) + causal prefill TFLOP/s (% MFMA peak), bf16"
@@ -88,7 +90,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="only the headline decode step")
     ap.add_argument("--only", default=None,
-                    help="profile one kernel: decode|step|fp8|multi|prefill|decode70b|paged|mha|mqa|window|d64|chunked|chunked_fp8|"
+                    help="profile one kernel: decode|step|fp8|int8|multi|prefill|decode70b|paged|mha|mqa|window|d64|chunked|"
+                         "chunked_fp8|chunked_int8|"
                          "tiny_prefill|tiny_decode (both tiny fp32 workloads)|copy (a 512 MiB device copy)")
     ap.add_argument("--summarize", default=None, help="print the per-kernel summary of a rocprofv3 trace directory")
     ap.add_argument("--traffic", nargs=6, default=None,
@@ -112,7 +115,8 @@ def up(x: np.ndarray):
 def decode_bytes(wl, ctx, fp8=False):
     """Algorithmic bytes of one decode: each visible K and V row once (with a
     sliding window only the window's rows), Q read, O written.  An FP8 cache
-    row is d one-byte codes plus its 4-byte scale; Q and O stay bf16."""
+    row (or INT8) is d one-byte codes plus its 4-byte scale; Q and O stay
+    bf16."""
     es = 2 if wl.dtype == "bf16" else 4
     rows = np.minimum(ctx, wl.window) if wl.window > 0 else ctx
     row_bytes = wl.d + 4 if fp8 else wl.d * es
@@ -135,11 +139,12 @@ def causal_flops(wl):
 class DecodeBench:
     """Device-resident copies of one decode workload, rotated per call."""
 
-    def __init__(self, wl, copies=None, fp8=False, mq=1):
+    def __init__(self, wl, copies=None, fp8=False, mq=1, int8=False):
         import torch
         from grouped_query_attention_gqa_amd import binding
         from grouped_query_attention_gqa_amd import workloads as W
         self.wl = wl
+        fp8 = fp8 or int8   # a 1-byte cache: the same bytes, INT8 codes with int8
         t0 = time.time()
         inp = W.make_decode(wl, fill="zero")
         self.inp = inp
@@ -158,15 +163,16 @@ class DecodeBench:
         k0, v0 = up(inp.k), up(inp.v)
         bt = None if inp.block_table is None else up(inp.block_table)
         if fp8:
-            # the FP8 cache is filled by the library's quantising append of
-            # every cached position (contiguous caches)
-            assert bt is None, "the FP8 bench leg uses a contiguous cache"
+            # the FP8 (INT8) cache is filled by the library's quantising append
+            # of every cached position (contiguous caches)
+            assert bt is None, "the quantised-cache bench legs use a contiguous cache"
             B, K, S, d = k0.shape
             kt, vt = k0.permute(0, 2, 1, 3).contiguous(), v0.permute(0, 2, 1, 3).contiguous()
             zero = torch.zeros(B, dtype=torch.int32, device="cuda")
             del k0, v0
             for i in range(n):
-                kq = torch.empty((B, K, S, d), dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+                kq = torch.empty((B, K, S, d), dtype=torch.uint8, device="cuda").view(
+                    torch.int8 if int8 else torch.float8_e4m3fn)
                 vq = torch.empty_like(kq)
                 ks = torch.empty((B, K, S), dtype=torch.float32, device="cuda")
                 vs = torch.empty_like(ks)
@@ -718,12 +724,26 @@ def main():
         log(f"llama3_8b_decode_fp8_cache: {mean_ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
         del d2
         torch.cuda.empty_cache()
+        # ---- the same on an INT8 (scale per row) cache ----------------------
+        d2 = DecodeBench(w, int8=True)
+        mean_ms, med_ms = time_decode_only(d2, max(LEG_CALLS, args.steps), 3)
+        gbs = d2.alg_bytes / (mean_ms * 1e-3) / 1e9
+        extra["llama3_8b_decode_int8_cache"] = {
+            "us": round(mean_ms * 1e3, 2), "GB/s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "bytes": d2.alg_bytes, "cache": "INT8 codes + one fp32 scale per row; q/out bf16",
+            "median_us": round(med_ms * 1e3, 2), "calls": max(LEG_CALLS, args.steps),
+            "traffic": committed_traffic("decode/llama3_8b_decode_int8_cache")}
+        log(f"llama3_8b_decode_int8_cache: {mean_ms * 1e3:.1f} us, {gbs:.0f} GB/s ({100 * gbs / HBM_PEAK_GBS:.1f}%)")
+        del d2
+        torch.cuda.empty_cache()
         result["decode_workloads"] = extra
         # ---- chunked prefill: new tokens after a cached prefix, paged ----
         result["prefill_workloads"] = {
             "chunked_prefill_paged": bench_prefill(W.WORKLOADS["chunked_prefill_paged"], max(LEG_CALLS, args.steps), 5),
             "chunked_prefill_paged_fp8_cache": bench_prefill(W.WORKLOADS["chunked_prefill_paged"],
-                                                             max(LEG_CALLS, args.steps), 5, fp8=True)}
+                                                             max(LEG_CALLS, args.steps), 5, fp8=True),
+            "chunked_prefill_paged_int8_cache": bench_prefill(W.WORKLOADS["chunked_prefill_paged"],
+                                                              max(LEG_CALLS, args.steps), 5, int8=True)}
         torch.cuda.empty_cache()
 
         # ---- the tiny fp32 workloads: launch-bound, in microseconds --------
@@ -840,7 +860,7 @@ def sustained_mfma(operands):
     return out
 
 
-def bench_prefill(wl, iters, warmup, fp8=False, probe=False):
+def bench_prefill(wl, iters, warmup, fp8=False, probe=False, int8=False):
     """Append + attention of the prefill workload, HIP events per call.  fp8:
     the cache holds E4M3 codes and a scale per row (the new rows are quantised
     by the call)."""
@@ -858,8 +878,9 @@ def bench_prefill(wl, iters, warmup, fp8=False, probe=False):
         shape = (n_pool, wl.K, wl.block_size, wl.d)
     else:
         table, shape = None, (wl.B, wl.K, S, wl.d)
-    if fp8:
-        kc = torch.zeros(shape, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    quant = "int8" if int8 else "fp8" if fp8 else None
+    if quant:
+        kc = torch.zeros(shape, dtype=torch.uint8, device="cuda").view(torch.int8 if int8 else torch.float8_e4m3fn)
         vc = torch.zeros_like(kc)
         ks = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
         cache = binding.KVCache(kc, vc, None if table is None else up(table), k_scale=ks, v_scale=torch.zeros_like(ks))
@@ -902,11 +923,13 @@ def bench_prefill(wl, iters, warmup, fp8=False, probe=False):
             roof["frac_of_sustained"] = round(tf / best, 4)
             log(f"sustained matrix rate on the leg's q values: {best:.0f} TFLOP/s; the call reaches {100 * tf / best:.1f}%")
     return {"workload": wl.name, "B": wl.B, "s": wl.s, "start": wl.start, "H": wl.H, "K": wl.K, "d": wl.d,
-            "paged": wl.paged, "cache": "FP8 E4M3 codes + one fp32 scale per row" if fp8 else "bf16",
+            "paged": wl.paged,
+            "cache": {"fp8": "FP8 E4M3 codes + one fp32 scale per row", "int8": "INT8 codes + one fp32 scale per row",
+                      None: "bf16"}[quant],
             "us_per_call": round(ms * 1e3, 2),
             "median_us": round(float(np.median(ev_ms)) * 1e3, 2), "p90_us": round(float(np.percentile(ev_ms, 90)) * 1e3, 2),
             "flops": flops, "TFLOP/s": round(tf, 2), "calls": iters,
-            "traffic": committed_traffic(("prefill/" + wl.name) + ("_fp8_cache" if fp8 else "")),
+            "traffic": committed_traffic(("prefill/" + wl.name) + (f"_{quant}_cache" if quant else "")),
             "roofline": roof}
 
 
@@ -914,9 +937,10 @@ def profile_only(args):
     """A short run of one kernel, for rocprofv3 (no JSON contract)."""
     import torch
     from grouped_query_attention_gqa_amd import workloads as W
-    if args.only in ("prefill", "chunked", "chunked_fp8"):
+    if args.only in ("prefill", "chunked", "chunked_fp8", "chunked_int8"):
         name = "causal_prefill_4k" if args.only == "prefill" else "chunked_prefill_paged"
-        r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup, fp8=args.only == "chunked_fp8")
+        r = bench_prefill(W.WORKLOADS[name], args.steps, args.warmup, fp8=args.only == "chunked_fp8",
+                          int8=args.only == "chunked_int8")
         print(json.dumps(r), flush=True)
         return
     if args.only in ("tiny_prefill", "tiny_decode"):
@@ -934,9 +958,11 @@ def profile_only(args):
         return
     name = {"decode": "llama3_8b_decode", "step": "llama3_8b_decode", "decode70b": "llama2_70b_decode",
             "paged": "paged_long_decode", "mha": "llama2_70b_decode_mha", "mqa": "llama2_70b_decode_mqa",
-            "window": "mistral_7b_window_decode", "fp8": "llama3_8b_decode", "multi": "llama3_8b_decode",
+            "window": "mistral_7b_window_decode", "fp8": "llama3_8b_decode", "int8": "llama3_8b_decode",
+            "multi": "llama3_8b_decode",
             "d64": "d64_decode"}[args.only]
-    db = DecodeBench(W.WORKLOADS[name], fp8=args.only == "fp8", mq=4 if args.only == "multi" else 1)
+    db = DecodeBench(W.WORKLOADS[name], fp8=args.only == "fp8", mq=4 if args.only == "multi" else 1,
+                     int8=args.only == "int8")
     call = {"step": db.step, "multi": getattr(db, "multi", None)}.get(args.only)
     mean_ms, med_ms = time_decode_only(db, args.steps, args.warmup, call)
     print(json.dumps({"workload": name, "decode_us": round(mean_ms * 1e3, 2),
