@@ -98,13 +98,25 @@ __device__ __forceinline__ uint32_t f8x2_bf16x2(uint32_t w)
 {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
-// eight 1-byte codes -> eight bf16 values, exactly: E4M3 codes, or INT8
-// codes with I8
+// four INT8 codes c (byte i of w) -> the bf16 values of c + 128, exactly
+// (integers 1 .. 255 have at most 8 significant bits): one byte-to-float
+// conversion per code and a byte permute per pair
+__device__ __forceinline__ uint2 i8x4_biased_bf16x4(uint32_t w)
+{
+    const uint32_t u = w ^ 0x80808080u;
+    const float f0 = (float)(u & 0xFFu), f1 = (float)((u >> 8) & 0xFFu);
+    const float f2 = (float)((u >> 16) & 0xFFu), f3 = (float)(u >> 24);
+    return make_uint2(__builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u),
+                      __builtin_amdgcn_perm(__float_as_uint(f3), __float_as_uint(f2), 0x07060302u));
+}
+// eight 1-byte codes -> eight bf16 values, exactly: E4M3 codes, or with I8
+// INT8 codes biased by +128 (the kernel takes the bias back out of the
+// scores and the weighted sum, see the decode kernel)
 template <bool I8>
 __device__ __forceinline__ uint4 c8x8_bf16x8(uint2 x)
 {
     if constexpr (I8) {
-        const uint2 a = i8x4_bf16x4(x.x), b = i8x4_bf16x4(x.y);
+        const uint2 a = i8x4_biased_bf16x4(x.x), b = i8x4_biased_bf16x4(x.y);
         return make_uint4(a.x, a.y, b.x, b.y);
     }
     return make_uint4(f8x2_bf16x2<false>(x.x), f8x2_bf16x2<true>(x.x), f8x2_bf16x2<false>(x.y), f8x2_bf16x2<true>(x.y));
@@ -367,11 +379,15 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
         };
 
         float m_ref[RBW], l_run[RBW];
+        // INT8: the sum of the V product's operands (the bf16 weights), for
+        // the +128 bias of the converted V codes
+        float w_run[RBW];
         f32x4_t acc[RBW][DB];
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
             m_ref[rb] = -INFINITY;
             l_run[rb] = 0.f;
+            w_run[rb] = 0.f;
 #pragma unroll
             for (int db = 0; db < DB; ++db) acc[rb][db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
@@ -403,7 +419,28 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
         const int lim_min = (int)min(max((int64_t)ctx_b - mq + 1, (int64_t)0), (int64_t)n_vis);
         const int rlo_max = p.window > 0 ? (int)max((int64_t)0, (int64_t)ctx_b - p.window) : 0;
 
+        // INT8: 128 times the sum of each row's query values, the bias the
+        // +128-biased K codes add to every score of the row (exact for the
+        // integer-valued rows of the exact tests; otherwise the fp32
+        // cancellation error is ~2^-24 of 128 sum |q| per score)
+        float qbias[RBW];
+#pragma unroll
+        for (int rb = 0; rb < RBW; ++rb) qbias[rb] = 0.f;
         wait_vm<0>();
+        if constexpr (I8) {
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                float qs = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    qs = dot2_bf16(qf[rb][ks].x, 0x3F803F80u, qs);
+                    qs = dot2_bf16(qf[rb][ks].y, 0x3F803F80u, qs);
+                    qs = dot2_bf16(qf[rb][ks].z, 0x3F803F80u, qs);
+                    qs = dot2_bf16(qf[rb][ks].w, 0x3F803F80u, qs);
+                }
+                qbias[rb] = 128.f * row_sum(qs);
+            }
+        }
         auto step = [&](int k) {
             const int key0 = tile_key0(k);
             // tile k + NSTG - 1 goes into the stage read in the previous step
@@ -456,7 +493,10 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
 #pragma unroll
                 for (int rb = 0; rb < RBW; ++rb)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) s[rb][e] *= ksc[e];   // the key's K scale
+                    for (int e = 0; e < 4; ++e) {
+                        if constexpr (I8) s[rb][e] -= qbias[rb];   // the +128 bias of the K codes
+                        s[rb][e] *= ksc[e];                        // the key's K scale
+                    }
             }
             if (key0 < rlo_max || key0 + TT > lim_min) {
 #pragma unroll
@@ -484,6 +524,7 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                         const float al = fast_exp2(m_ref[rb] - mt[rb]);   // 0 on the first tile
                         m_ref[rb] = mt[rb];
                         l_run[rb] *= al;
+                        if constexpr (I8) w_run[rb] *= al;
 #pragma unroll
                         for (int db = 0; db < DB; ++db) acc[rb][db] *= al;
                     }
@@ -507,6 +548,10 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                     const float w0 = p0 > 0.f ? p0 * vsc[0] : 0.f, w1 = p1 > 0.f ? p1 * vsc[1] : 0.f;
                     const float w2 = p2 > 0.f ? p2 * vsc[2] : 0.f, w3 = p3 > 0.f ? p3 * vsc[3] : 0.f;
                     pw[rb] = make_uint2(pack_bf16x2(w0, w1), pack_bf16x2(w2, w3));
+                    if constexpr (I8) {
+                        w_run[rb] = dot2_bf16(pw[rb].x, 0x3F803F80u, w_run[rb]);
+                        w_run[rb] = dot2_bf16(pw[rb].y, 0x3F803F80u, w_run[rb]);
+                    }
                 }
             }
             // O^T += V^T P^T, one 16-column block of V^T per transposing read
@@ -523,6 +568,15 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
         wait_vm<0>();   // the loads issued past the last tile have landed before the stages are reused
 
         // ---- merge the 4 waves' pieces in LDS, in wave order ------------------
+        if constexpr (I8) {
+            // take the +128 bias of the V codes out: sum w (c + 128) - 128 sum w
+#pragma unroll
+            for (int rb = 0; rb < RBW; ++rb) {
+                const float wb = 128.f * row_sum(w_run[rb]);
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[rb][db] -= wb;
+            }
+        }
 #pragma unroll
         for (int rb = 0; rb < RBW; ++rb) {
             l_run[rb] = row_sum(l_run[rb]);
