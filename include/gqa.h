@@ -129,7 +129,8 @@ int32_t gqa_cache_elems_per_token(int32_t num_kv_heads, int32_t head_dim);
  * both divisions in IEEE fp32; an all-zero row has scale 0 and zero codes.
  * INT8 cache: scale = amax(|x|) / 127 and codes the integers nearest to
  * x_i * (1 / scale), ties to even, the reciprocal and the product in IEEE
- * fp32 (|code| <= 127); an all-zero row has scale 0 and zero codes.
+ * fp32 (|code| <= 127); an all-zero row has scale 0 and zero codes.  Rows
+ * are expected to hold finite values (a NaN element is stored as -127).
  *
  * Append s_new tokens to every sequence of the cache:
  *     pos = start_pos[b] + t,  cache row (b, g, pos) <- new row (b, t, g)

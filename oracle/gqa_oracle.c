@@ -448,7 +448,7 @@ void oracle_quantize_i8_rows(const float *x, int64_t rows, int d, int8_t *codes,
             const float q = xr[i] * inv;          /* fp32 product */
             float n = rintf(q);                   /* nearest, ties to even (default mode) */
             if (n > 127.0f) n = 127.0f;
-            if (n < -127.0f) n = -127.0f;
+            if (!(n >= -127.0f)) n = -127.0f;     /* below, or NaN (a non-finite row): no cast of NaN */
             codes[r * d + i] = (int8_t)n;
         }
     }
