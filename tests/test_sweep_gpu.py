@@ -7,7 +7,7 @@ cached prefix, the chunk length and causal or full attention.  The case list
 is fixed by its seed; every output row is compared (bf16 tolerance 2e-2),
 and the bf16 prefill's cache bytes must equal the oracle's append.  The
 sweep reaches the decode kernel's uniform fast paths (whole visible tiles,
-tiles inside every row's window) and their edges, and the FP8 prefill's
+tiles inside every row's window) and their edges, and the FP8 (and INT8) prefill's
 steady and masked tile code."""
 import numpy as np
 import pytest
@@ -123,6 +123,22 @@ def test_fp8_prefill_sweep(case):
     _check_fp8_prefill(f"fp8 prefill sweep {case}", B=case["B"], H=case["H"], K=case["K"], s=case["s"],
                        start=case["start"], paged=case["paged"], bs=case["bs"], causal=case["causal"],
                        window=case["window"], seed=case["seed"])
+
+
+@pytest.mark.parametrize("case", _decode_cases(8, 8888), ids=lambda c: f"int8decode{c['i']}")
+def test_int8_decode_sweep(case):
+    from test_fp8_gpu import _decode_case as q_decode_case
+    wl = W.WORKLOADS["llama3_8b_decode"].replace(B=case["B"], H=case["H"], K=case["K"], seed=case["seed"],
+                                                ctx=("uniform", 1, 900), paged=case["paged"], block_size=case["bs"])
+    q_decode_case(wl, f"sweep {case}", window=case["window"], codec="int8")
+
+
+@pytest.mark.parametrize("case", _prefill_cases(8, 5353), ids=lambda c: f"int8prefill{c['i']}")
+def test_int8_prefill_sweep(case):
+    from test_fp8_gpu import _check_fp8_prefill
+    _check_fp8_prefill(f"int8 prefill sweep {case}", B=case["B"], H=case["H"], K=case["K"], s=case["s"],
+                       start=case["start"], paged=case["paged"], bs=case["bs"], causal=case["causal"],
+                       window=case["window"], seed=case["seed"], codec="int8")
 
 
 # ---------------------------------------------------------------------------
