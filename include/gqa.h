@@ -43,7 +43,8 @@
  *     context length below 1 yields an all-zero output row.  With GQA_CHECK=1
  *     the host copies them back, validates them and returns
  *     GQA_ERR_DEVICE_ARG before launching if one is out of range.
- *   - Supported: dtype GQA_BF16 or GQA_F32, head_dim 64 or 128,
+ *   - Supported: dtype GQA_BF16 or GQA_F32 (and the quantised caches
+ *     below), head_dim 64 or 128,
  *     1 <= K <= H, H % K == 0, G = H / K <= 64, block_size a power of two in
  *     [1, 1024].
  *   - The softmax scale must be a positive finite number (normally

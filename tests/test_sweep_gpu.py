@@ -142,8 +142,8 @@ def test_int8_prefill_sweep(case):
 
 
 # ---------------------------------------------------------------------------
-# the other kernels: bf16 at d = 64 (the vector decode kernels, the d = 64
-# matrix-core prefill) and fp32 at d = 64 and 128 (the row-streaming kernel)
+# the other shapes: bf16 at d = 64 (the matrix-core decode's and prefill's
+# d = 64 code) and fp32 at d = 64 and 128 (the row-streaming kernel)
 # ---------------------------------------------------------------------------
 
 def _other_cases(n, seed, kind):
