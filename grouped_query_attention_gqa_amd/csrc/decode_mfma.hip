@@ -441,11 +441,17 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                 qbias[rb] = 128.f * row_sum(qs);
             }
         }
-        auto step = [&](int k) {
+        // last: the wave's last tile of the segment, after which nothing is
+        // issued (so the wait is for every load the wave has in flight)
+        auto step = [&](int k, bool last) {
             const int key0 = tile_key0(k);
-            // tile k + NSTG - 1 goes into the stage read in the previous step
-            issue(k + NSTG - 1);
-            wait_vm<(NSTG - 1) * DMA_PER_TILE>();   // tile k has landed
+            if (!last) {
+                // tile k + NSTG - 1 goes into the stage read in the previous step
+                issue(k + NSTG - 1);
+                wait_vm<(NSTG - 1) * DMA_PER_TILE>();   // tile k has landed
+            } else {
+                wait_vm<0>();
+            }
             const char *kt = sw + (k % NSTG) * STG;
             const char *vt = F8 ? lds_vbf[F8 ? wave : 0] : kt + Stage<F8, D>::KV;
             uint4 kf[KS];
@@ -564,8 +570,9 @@ __global__ __launch_bounds__(NT, occ_of(RBW)) void decode_mfma_kernel(RowAttnPar
                 for (int rb = 0; rb < RBW; ++rb) acc[rb][db] = mfma_o(vf, pw[rb], acc[rb][db]);
             }
         };
-        for (int k = 0; k < n_w; ++k) step(k);
-        wait_vm<0>();   // the loads issued past the last tile have landed before the stages are reused
+        for (int k = 0; k + 1 < n_w; ++k) step(k, false);
+        if (n_w > 0) step(n_w - 1, true);
+        wait_vm<0>();   // (a wave with no tile here: its first-tile loads) before the stages are reused
 
         // ---- merge the 4 waves' pieces in LDS, in wave order ------------------
         if constexpr (I8) {
