@@ -246,14 +246,40 @@ def time_decode_only(db: DecodeBench, iters: int, warmup: int, call=None):
 # traffic figures from the committed rocprofv3 counter summaries
 # ---------------------------------------------------------------------------
 
+def source_code_only(text: str) -> str:
+    """C/C++ source without its comments, each run of whitespace made one
+    space: what the compiler sees, so that an edit of a comment keeps a hash
+    of it.  String and character literals are kept as written."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(names=DECODE_SOURCES) -> str:
-    """Hash of the kernel sources the traffic counters were taken on, and of
-    the compiler flags they are built with."""
+    """Hash of the code (comments left out) of the kernel sources the traffic
+    counters were taken on, and of the compiler flags they are built with."""
     from grouped_query_attention_gqa_amd import build as gbuild
     h = hashlib.sha256()
     for name in names:
-        with open(os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "grouped_query_attention_gqa_amd", "csrc", name), encoding="utf-8") as f:
+            h.update(source_code_only(f.read()).encode())
         h.update(" ".join(gbuild.COMMON_FLAGS + gbuild.FILE_FLAGS.get(name, [])).encode())
     return h.hexdigest()[:16]
 

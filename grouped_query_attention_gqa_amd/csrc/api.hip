@@ -325,9 +325,9 @@ gqa_status gqa::decode_step(const void *q, const void *k_new, const void *v_new,
         // k_new / v_new; every other path appends first
         p.k_new = static_cast<const char *>(k_new);
         p.v_new = static_cast<const char *>(v_new);
-        // the matrix-core decode writes the new bf16 rows itself; an FP8
-        // cache is written by the quantising append kernel, and so are the
-        // rest
+        // the matrix-core decode writes the new bf16 rows itself; a quantised
+        // (FP8 or INT8) cache is written by the quantising append kernel, and
+        // so are the rest
         if (v.elem_bytes != 2 || !decode_mfma_supported(p)) {
             AppendParams ap{};
             ap.cache = v;
@@ -375,7 +375,7 @@ gqa_status gqa_decode_multi(const void *q, const gqa_kv_cache *cache, const int3
     if (!scale_ok(scale)) return fail(GQA_ERR_INVALID_ARG, "scale not a positive finite number");
     const int32_t G = num_heads / v.K;
     if ((int64_t)s * G > 64) return fail(GQA_ERR_UNSUPPORTED, "s * G above 64");
-    if (v.elem_bytes == 4 || v.d != 128) return fail(GQA_ERR_UNSUPPORTED, "several positions need bf16 or FP8, d = 128");
+    if (v.elem_bytes == 4 || v.d != 128) return fail(GQA_ERR_UNSUPPORTED, "several positions need a bf16, FP8 or INT8 cache, d = 128");
     if (v.block_table && v.log2_bs < 4) return fail(GQA_ERR_UNSUPPORTED, "blocks below 16 tokens");
     DecodeLayout L;
     decode_layout(s * G, v.d, &L);

@@ -1,7 +1,7 @@
 // decode_mfma.hip -- decode on the matrix cores for bf16 caches at head size
-// 128 and 64 and FP8 caches at 128: every group size up to G = 64 (the
-// multi-query end) and a block of several newest query positions per
-// sequence (speculative-verify shaped).
+// 128 and 64 and 1-byte (FP8 E4M3 or INT8) caches at 128: every group size
+// up to G = 64 (the multi-query end) and a block of several newest query
+// positions per sequence (speculative-verify shaped).
 //
 // What it computes ("Grouped-Query Attention" concept page, 技术原理 steps
 // 2-4): for sequence b and KV group g, the R = mq * G rows -- query position i
@@ -72,7 +72,7 @@ constexpr int NW = NT / kWave;     // waves
 constexpr int TT = 16;             // keys per tile
 constexpr float TAU = 8.0f;        // lazy-rescale threshold (log2 units)
 constexpr int MAX_ROWS = 64;       // R = mq * G
-// Head dimensions: 128 (bf16 and FP8 caches) and 64 (bf16).  A bf16 row of D
+// Head dimensions: 128 (bf16 and 1-byte caches) and 64 (bf16).  A bf16 row of D
 // values is CPR 16-byte chunks, and one 1 KB LDS-direct load fills RPL rows.
 template <int D> struct Dim {
     static constexpr int RB = D * 2;          // bytes per bf16 K/V row
@@ -822,8 +822,8 @@ bool decode_mfma_supported(const RowAttnParams &p)
 {
     const int mq = p.mq > 1 ? p.mq : 1;
     // paged caches need blocks of at least 16 tokens (a tile stays in one block)
-    // bf16 at d = 128 or 64, or FP8 E4M3 with row scales at d = 128 (whose new
-    // rows the quantising append writes)
+    // bf16 at d = 128 or 64, or 1-byte codes (FP8 E4M3 or INT8) with row
+    // scales at d = 128 (whose new rows the quantising append writes)
     const bool f8 = p.cache.elem_bytes == 1;
     return !p.prefill && !p.whole_items && (p.cache.elem_bytes == 2 || f8) &&
            (p.cache.d == 128 || (p.cache.d == 64 && !f8)) &&

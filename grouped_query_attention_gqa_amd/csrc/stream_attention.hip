@@ -661,7 +661,7 @@ hipError_t launch_d(const RowAttnParams &p, int gp, hipStream_t s)
 hipError_t launch_merge_pieces(const RowAttnParams &p, int tt, int W, hipStream_t s)
 {
     const dim3 grid(p.cache.K, p.rows, (p.G + kMergeHeads - 1) / kMergeHeads);
-    const bool bf16 = p.cache.elem_bytes != 4;   // an FP8 cache has bf16 outputs
+    const bool bf16 = p.cache.elem_bytes != 4;   // a 1-byte (FP8 or INT8) cache has bf16 outputs
     if (p.cache.d == 128) {
         if (bf16) hipLaunchKernelGGL((merge_pieces_kernel<128, true>), grid, dim3(256), 0, s, p, tt, W);
         else hipLaunchKernelGGL((merge_pieces_kernel<128, false>), grid, dim3(256), 0, s, p, tt, W);
@@ -686,12 +686,12 @@ hipError_t launch_row_attention(const RowAttnParams &p0, int gp, hipStream_t str
         p.row0 = r0;
         p.rows = (int32_t)(p0.total_rows - r0 < kStreamRows ? p0.total_rows - r0 : kStreamRows);
         hipError_t e = hipErrorInvalidValue;
-        // bf16 at d = 128 and 64 and FP8 at d = 128: the matrix-core kernel,
+        // bf16 at d = 128 and 64 and 1-byte codes at d = 128: the matrix-core kernel,
         // whatever the group size; the rest (fp32, bf16 paged in blocks under
         // 16 tokens, more than 64 rows per KV head): this file's kernel
         if (decode_mfma_supported(p)) e = launch_decode_mfma(p, stream);
         else if (p.mq > 1) return hipErrorInvalidValue;   // several positions: the matrix-core kernel only
-        else if (p.cache.elem_bytes == 1) return hipErrorInvalidValue;   // FP8: the decode kernel only
+        else if (p.cache.elem_bytes == 1) return hipErrorInvalidValue;   // FP8 / INT8: the matrix-core kernel only
         else if (p.cache.d == 128) e = bf16 ? launch_d<128, true>(p, gp, stream) : launch_d<128, false>(p, gp, stream);
         else if (p.cache.d == 64) e = bf16 ? launch_d<64, true>(p, gp, stream) : launch_d<64, false>(p, gp, stream);
         if (e != hipSuccess) return e;

@@ -65,3 +65,22 @@ def test_traffic_is_scaled_by_the_copy_reading(tmp_path):
     assert s["fetch_scale"] == pytest.approx(2.0) and s["write_scale"] == pytest.approx(1.0)
     assert list(s["kernels"]) == ["main_kernel"]
     assert s["kernels"]["main_kernel"]["hbm_bytes"] == int(1000 * 1024 * 2 + 10 * 1024)
+
+
+def test_source_hash_ignores_comments_but_not_code():
+    src = ('// header\nint f(int x) { /* a block\n comment */ return x + 1; }  // tail\n'
+           'const char *s = "// kept: inside a string";\n')
+    base = bench.source_code_only(src)
+    assert "header" not in base and "block" not in base and "tail" not in base
+    assert '"// kept: inside a string"' in base
+    # an edited comment or reflowed whitespace: the same code
+    assert bench.source_code_only(src.replace("a block", "another").replace("  //", "\n//")) == base
+    # an edited statement or string: different code
+    assert bench.source_code_only(src.replace("x + 1", "x + 2")) != base
+    assert bench.source_code_only(src.replace("kept", "kept!")) != base
+
+
+def test_committed_traffic_is_keyed_to_the_current_code():
+    # every stored byte-counter figure was taken on the kernels as they stand
+    for key in bench.TRAFFIC_SOURCES:
+        assert bench.committed_traffic(key) is not None, key
