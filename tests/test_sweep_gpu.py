@@ -52,7 +52,7 @@ def _decode_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", _decode_cases(14, 20261202), ids=lambda c: f"decode{c['i']}")
+@pytest.mark.parametrize("case", _decode_cases(40, 20261202), ids=lambda c: f"decode{c['i']}")
 def test_decode_sweep(case):
     wl = W.WORKLOADS["llama3_8b_decode"].replace(B=case["B"], H=case["H"], K=case["K"], seed=case["seed"],
                                                 ctx=("uniform", 1, 900), paged=case["paged"],
@@ -82,7 +82,7 @@ def _prefill_cases(n, seed):
     return cases
 
 
-@pytest.mark.parametrize("case", _prefill_cases(12, 31337), ids=lambda c: f"prefill{c['i']}")
+@pytest.mark.parametrize("case", _prefill_cases(40, 31337), ids=lambda c: f"prefill{c['i']}")
 def test_prefill_sweep(case):
     wl = W.WORKLOADS["causal_prefill_4k"].replace(B=case["B"], s=case["s"], H=case["H"], K=case["K"],
                                                  seed=case["seed"], block_size=case["bs"])
@@ -108,7 +108,7 @@ def test_prefill_sweep(case):
     check_close(gpu_rows(out, rows, "bf16"), want, BF16_TOL, what)
 
 
-@pytest.mark.parametrize("case", _decode_cases(8, 777), ids=lambda c: f"fp8decode{c['i']}")
+@pytest.mark.parametrize("case", _decode_cases(20, 777), ids=lambda c: f"fp8decode{c['i']}")
 def test_fp8_decode_sweep(case):
     from test_fp8_gpu import _decode_case as fp8_decode_case
     # (the FP8 helper draws the contexts from the workload's seed)
@@ -117,7 +117,7 @@ def test_fp8_decode_sweep(case):
     fp8_decode_case(wl, f"sweep {case}", window=case["window"])
 
 
-@pytest.mark.parametrize("case", _prefill_cases(8, 4242), ids=lambda c: f"fp8prefill{c['i']}")
+@pytest.mark.parametrize("case", _prefill_cases(20, 4242), ids=lambda c: f"fp8prefill{c['i']}")
 def test_fp8_prefill_sweep(case):
     from test_fp8_gpu import _check_fp8_prefill
     _check_fp8_prefill(f"fp8 prefill sweep {case}", B=case["B"], H=case["H"], K=case["K"], s=case["s"],
@@ -125,7 +125,7 @@ def test_fp8_prefill_sweep(case):
                        window=case["window"], seed=case["seed"])
 
 
-@pytest.mark.parametrize("case", _decode_cases(8, 8888), ids=lambda c: f"int8decode{c['i']}")
+@pytest.mark.parametrize("case", _decode_cases(20, 8888), ids=lambda c: f"int8decode{c['i']}")
 def test_int8_decode_sweep(case):
     from test_fp8_gpu import _decode_case as q_decode_case
     wl = W.WORKLOADS["llama3_8b_decode"].replace(B=case["B"], H=case["H"], K=case["K"], seed=case["seed"],
@@ -133,7 +133,7 @@ def test_int8_decode_sweep(case):
     q_decode_case(wl, f"sweep {case}", window=case["window"], codec="int8")
 
 
-@pytest.mark.parametrize("case", _prefill_cases(8, 5353), ids=lambda c: f"int8prefill{c['i']}")
+@pytest.mark.parametrize("case", _prefill_cases(20, 5353), ids=lambda c: f"int8prefill{c['i']}")
 def test_int8_prefill_sweep(case):
     from test_fp8_gpu import _check_fp8_prefill
     _check_fp8_prefill(f"int8 prefill sweep {case}", B=case["B"], H=case["H"], K=case["K"], s=case["s"],
@@ -171,7 +171,7 @@ def _tol(dtype):
     return BF16_TOL if dtype == "bf16" else F32_TOL
 
 
-@pytest.mark.parametrize("case", _other_cases(12, 99, "decode"),
+@pytest.mark.parametrize("case", _other_cases(30, 99, "decode"),
                          ids=lambda c: f"decode_{c['dtype']}_d{c['d']}_{c['i']}")
 def test_other_decode_sweep(case):
     base = W.WORKLOADS["llama3_8b_decode"] if case["dtype"] == "bf16" else W.WORKLOADS["tiny_decode_f32"]
@@ -185,7 +185,7 @@ def test_other_decode_sweep(case):
     check_close(gpu_rows(out, rows, case["dtype"]), want, _tol(case["dtype"]), what)
 
 
-@pytest.mark.parametrize("case", _other_cases(10, 1234, "prefill"), ids=lambda c: f"prefill_{c['dtype']}_d{c['d']}_{c['i']}")
+@pytest.mark.parametrize("case", _other_cases(30, 1234, "prefill"), ids=lambda c: f"prefill_{c['dtype']}_d{c['d']}_{c['i']}")
 def test_other_prefill_sweep(case):
     base = W.WORKLOADS["causal_prefill_4k"] if case["dtype"] == "bf16" else W.WORKLOADS["tiny_prefill_f32"]
     wl = base.replace(B=case["B"], s=case["s"], H=case["H"], K=case["K"], d=case["d"], seed=case["seed"],
