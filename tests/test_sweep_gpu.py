@@ -8,7 +8,8 @@ is fixed by its seed; every output row is compared (bf16 tolerance 2e-2),
 and the bf16 prefill's cache bytes must equal the oracle's append.  The
 sweep reaches the decode kernel's uniform fast paths (whole visible tiles,
 tiles inside every row's window) and their edges, and the FP8 (and INT8) prefill's
-steady and masked tile code."""
+steady and masked tile code; the fused decode step and the decode of several
+newest positions per sequence draw their shapes the same way."""
 import numpy as np
 import pytest
 
@@ -140,6 +141,37 @@ def test_int8_prefill_sweep(case):
                        start=case["start"], paged=case["paged"], bs=case["bs"], causal=case["causal"],
                        window=case["window"], seed=case["seed"], codec="int8")
 
+
+
+# the fused decode step (append of the newest token + decode, checked against
+# append-then-decode bit for bit and against the oracle) and the decode of
+# several newest positions per sequence (s * G <= 64 rows per KV head)
+@pytest.mark.parametrize("case", _decode_cases(16, 6060), ids=lambda c: f"step{c['i']}")
+def test_step_sweep(case):
+    from test_decode_step_gpu import _step_case
+    wl = W.WORKLOADS["llama3_8b_decode"].replace(B=case["B"], H=case["H"], K=case["K"], seed=case["seed"],
+                                                ctx=("uniform", 1, 900), paged=case["paged"], block_size=case["bs"])
+    _step_case(wl, f"sweep {case}", window=case["window"])
+
+
+def _multi_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for c in _decode_cases(n, seed):
+        if c["H"] // c["K"] > 32:
+            c["H"], c["K"] = 32, 1
+        G = c["H"] // c["K"]
+        c["s"] = int(rng.integers(2, 64 // G + 1))
+        cases.append(c)
+    return cases
+
+
+@pytest.mark.parametrize("case", _multi_cases(16, 7070), ids=lambda c: f"multi{c['i']}")
+def test_multi_sweep(case):
+    from test_decode_multi_gpu import _multi_case
+    wl = W.WORKLOADS["llama3_8b_decode"].replace(B=case["B"], H=case["H"], K=case["K"], seed=case["seed"],
+                                                ctx=("uniform", 16, 900), paged=case["paged"], block_size=case["bs"])
+    _multi_case(wl, case["s"], f"sweep {case}", window=case["window"])
 
 # ---------------------------------------------------------------------------
 # the other shapes: bf16 at d = 64 (the matrix-core decode's and prefill's
